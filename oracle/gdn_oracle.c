@@ -1,0 +1,121 @@
+/*
+ * Float64 CPU oracle for the Gated DeltaNet recurrence.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark use it.  It shares no code, header or constant with the
+ * HIP library.
+ *
+ * What it computes (page "Inside Qwen3.8-27B: Hybrid DeltaNet Architecture,
+ * 256k Context, and 24GB Local Serving", section "Gated DeltaNet Mechanics"):
+ * each value head carries a fixed d x d memory matrix S.  At every token the
+ * delta rule first removes what S currently associates with the (normalized)
+ * key and then writes the new value under that key, with a per-token decay.
+ * The page's own formula did not survive text extraction; this follows the
+ * gated delta rule that matches every property the page states:
+ *
+ *     S_t = alpha_t * S_{t-1} * (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *     o_t = S_t q_t                                  (post-update state)
+ *
+ * S is d_v x d_k, stored row-major [d_v][d_k] (row = value index).  Value head
+ * h reads query/key head g = h / (Hv / Hqk) (contiguous groups: the 48 value
+ * heads share 16 query/key heads, page "Qwen 3.8 27B Review ...", section 3
+ * "Architecture: Gated DeltaNet Hybrid + FP8 Quantization").
+ *
+ * The token loop is strictly sequential, one token at a time, in float64.
+ * Independent (sequence, value-head) chains run in parallel under OpenMP;
+ * that changes no arithmetic.  The row-wise form below is the recurrence
+ * itself: row i of S_{t-1}(I - beta k k^T) is S_i - beta (S_i . k) k^T, which
+ * depends on row i of S only.
+ *
+ * Layouts (all float64, contiguous, row-major):
+ *   q, k   [B, T, Hqk, D]
+ *   v, o   [B, T, Hv,  D]
+ *   alpha, beta [B, T, Hv]
+ *   h0, ht [B, Hv, D, D]   h0 may be NULL (zero state); ht may be NULL (not
+ *                          emitted) and may be the same pointer as h0.
+ * Returns 0, or -1 for inconsistent sizes.
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* One (sequence, value head) chain over T tokens.  S (D x D) is in/out. */
+static void gdn_chain_f64(const double *q, const double *k, const double *v,
+                          const double *alpha, const double *beta,
+                          int64_t T, int64_t qk_tstride, int64_t v_tstride,
+                          int64_t gate_tstride, int64_t D, double *S, double *o)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        const double *qt = q + t * qk_tstride;
+        const double *kt = k + t * qk_tstride;
+        const double *vt = v + t * v_tstride;
+        double *ot = o + t * v_tstride;
+        const double a = alpha[t * gate_tstride];
+        const double b = beta[t * gate_tstride];
+        for (int64_t i = 0; i < D; ++i) {
+            double *Si = S + i * D;
+            /* u_i = (S_{t-1} k_t)_i */
+            double ui = 0.0;
+            for (int64_t j = 0; j < D; ++j)
+                ui += Si[j] * kt[j];
+            /* row i of  alpha S_{t-1} (I - beta k k^T) + beta v k^T */
+            for (int64_t j = 0; j < D; ++j)
+                Si[j] = a * (Si[j] - b * ui * kt[j]) + b * vt[i] * kt[j];
+            /* o_i = (S_t q_t)_i */
+            double oi = 0.0;
+            for (int64_t j = 0; j < D; ++j)
+                oi += Si[j] * qt[j];
+            ot[i] = oi;
+        }
+    }
+}
+
+int oracle_gdn_prefill(const double *q, const double *k, const double *v,
+                       const double *alpha, const double *beta,
+                       const double *h0, double *o, double *ht,
+                       int64_t B, int64_t T, int64_t Hqk, int64_t Hv, int64_t D)
+{
+    if (B < 0 || T < 0 || Hqk <= 0 || Hv <= 0 || D <= 0 || Hv % Hqk != 0)
+        return -1;
+    const int64_t G = Hv / Hqk;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < B * Hv; ++bh) {
+        const int64_t b = bh / Hv, h = bh % Hv, g = h / G;
+        double *S = (double *)malloc((size_t)(D * D) * sizeof(double));
+        if (!S) {
+#pragma omp atomic write
+            bad = 1;
+            continue;
+        }
+        if (h0)
+            memcpy(S, h0 + (b * Hv + h) * D * D, (size_t)(D * D) * sizeof(double));
+        else
+            memset(S, 0, (size_t)(D * D) * sizeof(double));
+        gdn_chain_f64(q + (b * T * Hqk + g) * D, k + (b * T * Hqk + g) * D,
+                      v + (b * T * Hv + h) * D, alpha + b * T * Hv + h,
+                      beta + b * T * Hv + h, T, Hqk * D, Hv * D, Hv, D, S,
+                      o + (b * T * Hv + h) * D);
+        if (ht)
+            memcpy(ht + (b * Hv + h) * D * D, S, (size_t)(D * D) * sizeof(double));
+        free(S);
+    }
+    return bad ? -2 : 0;
+}
+
+/*
+ * One decode step: the same recurrence applied to a single token per
+ * sequence (page "Inside Qwen3.8-27B ...", the note under "The Role of
+ * Periodic Gated Attention": at inference the state advances one token at a
+ * time).  q, k [B, Hqk, D]; v, o [B, Hv, D]; alpha, beta [B, Hv];
+ * state [B, Hv, D, D] updated in place.
+ */
+int oracle_gdn_decode_step(const double *q, const double *k, const double *v,
+                           const double *alpha, const double *beta,
+                           double *state, double *o,
+                           int64_t B, int64_t Hqk, int64_t Hv, int64_t D)
+{
+    return oracle_gdn_prefill(q, k, v, alpha, beta, state, o, state, B, 1, Hqk,
+                              Hv, D);
+}

@@ -1,0 +1,435 @@
+"""Pins for the float64 oracle, independent of the oracle's own code.
+
+The pages print no numeric worked example of the recurrence, so the oracle is
+pinned by what the mathematics and the pages fix:
+
+===========================  ==================================================
+pin                          what it fixes
+===========================  ==================================================
+identity (beta=0, alpha=1)   nothing written, nothing decayed: S_t = S_0 and
+                             o_t = S_0 q_t exactly
+pure decay (beta=0)          S_t = (prod alpha) S_0: closed form
+orthonormal retrieval        alpha=beta=1, orthonormal keys, S_0=0: the state
+                             is sum v_i k_i^T and querying q_t = k_t returns
+                             v_t (a textbook projection identity)
+rewrite same key             delete-before-write ("Gated DeltaNet Mechanics"):
+                             writing v1 then v2 under the same key leaves v2
+single token                 T=1 closed form in the delta form
+                             o = alpha S q + d (k.q), d = beta (v - alpha S k)
+product form (brute force)   S_T = S_0 prod P_t + sum beta_t v_t k_t^T
+                             prod_{s>t} P_s with P_t = alpha_t (I - beta_t k k^T)
+                             as explicit d x d matrices, tiny d and T
+head map                     value head h reads query/key head h // (Hv/Hqk)
+contraction bound            ||S_t|| <= alpha_t ||S_{t-1}|| + beta_t ||v_t||
+                             for unit keys and beta in [0, 1]
+empty sequence               T = 0 passes the state through
+===========================  ==================================================
+
+``test_mutants_are_caught`` runs every pin against deliberately broken copies
+of the recurrence (a dropped beta, a transposed outer product, the output read
+before the update, a wrong sign, decay on the wrong term, the wrong head map,
+the key used as the query, ...) and requires each mutant to fail at least one
+pin.  All of this runs on the CPU.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import scipy.stats
+
+import oracle
+from oracle import chunked_form
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- helpers
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+def unit(x):
+    return x / np.linalg.norm(x, axis=-1, keepdims=True)
+
+
+def rand_inputs(r, B, T, Hqk, Hv, D, h0=True, normalize=True):
+    q = r.standard_normal((B, T, Hqk, D))
+    k = r.standard_normal((B, T, Hqk, D))
+    if normalize:
+        q, k = unit(q), unit(k)
+    v = r.standard_normal((B, T, Hv, D))
+    beta = scipy.special.expit(r.standard_normal((B, T, Hv)))
+    alpha = np.exp(-0.05 * np.logaddexp(0.0, r.standard_normal((B, T, Hv))))
+    s0 = 0.3 * r.standard_normal((B, Hv, D, D)) if h0 else None
+    return q, k, v, alpha, beta, s0
+
+
+def c_impl(q, k, v, alpha, beta, h0):
+    return oracle.prefill(q, k, v, alpha, beta, h0)
+
+
+def np_impl(q, k, v, alpha, beta, h0):
+    return oracle.np_prefill(q, k, v, alpha, beta, h0)
+
+
+def make_mutant(kind):
+    """Deliberately broken recurrences used to show that the pins bite."""
+    def impl(q, k, v, alpha, beta, h0):
+        B, T, Hqk, D = q.shape
+        Hv = v.shape[2]
+        G = Hv // Hqk
+        o = np.zeros((B, T, Hv, D))
+        ht = np.zeros((B, Hv, D, D))
+        for b in range(B):
+            for h in range(Hv):
+                g = (h % Hqk) if kind == "head_map_mod" else h // G
+                S = np.zeros((D, D)) if h0 is None else h0[b, h].copy()
+                for t in range(T):
+                    kt, qt, vt = k[b, t, g], q[b, t, g], v[b, t, h]
+                    a, be = alpha[b, t, h], beta[b, t, h]
+                    Sp = S
+                    if kind == "no_beta_erase":
+                        S = a * (S - np.outer(S @ kt, kt)) + be * np.outer(vt, kt)
+                    elif kind == "transposed_write":
+                        S = a * (S - be * np.outer(S @ kt, kt)) + be * np.outer(kt, vt)
+                    elif kind == "alpha_on_write":
+                        S = a * ((S - be * np.outer(S @ kt, kt)) + be * np.outer(vt, kt))
+                    elif kind == "erase_sign":
+                        S = a * (S + be * np.outer(S @ kt, kt)) + be * np.outer(vt, kt)
+                    elif kind == "no_decay_on_erase":
+                        S = a * S - be * np.outer(S @ kt, kt) + be * np.outer(vt, kt)
+                    elif kind == "erase_transposed":
+                        S = a * (S - be * np.outer(kt, kt @ S)) + be * np.outer(vt, kt)
+                    elif kind == "no_beta_write":
+                        S = a * (S - be * np.outer(S @ kt, kt)) + np.outer(vt, kt)
+                    else:
+                        S = a * (S - be * np.outer(S @ kt, kt)) + be * np.outer(vt, kt)
+                    if kind == "pre_update_output":
+                        o[b, t, h] = Sp @ qt
+                    elif kind == "key_as_query":
+                        o[b, t, h] = S @ kt
+                    else:
+                        o[b, t, h] = S @ qt
+                ht[b, h] = S
+        return o, ht
+    return impl
+
+
+MUTANTS = ["no_beta_erase", "transposed_write", "alpha_on_write", "erase_sign",
+           "no_decay_on_erase", "erase_transposed", "no_beta_write",
+           "pre_update_output", "key_as_query", "head_map_mod"]
+
+
+# ---------------------------------------------------------------- the pins
+def pin_identity(impl):
+    r = rng(1)
+    q, k, v, alpha, beta, s0 = rand_inputs(r, 2, 9, 2, 6, 8)
+    beta[:] = 0.0
+    alpha[:] = 1.0
+    o, ht = impl(q, k, v, alpha, beta, s0)
+    np.testing.assert_array_equal(ht, s0)
+    G = 3
+    for h in range(6):
+        ref = np.einsum("bij,btj->bti", s0[:, h], q[:, :, h // G])
+        np.testing.assert_allclose(o[:, :, h], ref, rtol=0, atol=1e-13)
+
+
+def pin_pure_decay(impl):
+    r = rng(2)
+    q, k, v, alpha, beta, s0 = rand_inputs(r, 1, 12, 1, 2, 6)
+    beta[:] = 0.0
+    o, ht = impl(q, k, v, alpha, beta, s0)
+    gam = np.cumprod(alpha, axis=1)                     # [B,T,Hv]
+    for h in range(2):
+        np.testing.assert_allclose(ht[0, h], gam[0, -1, h] * s0[0, h], rtol=1e-13, atol=1e-15)
+        for t in range(12):
+            np.testing.assert_allclose(o[0, t, h], gam[0, t, h] * (s0[0, h] @ q[0, t, 0]),
+                                       rtol=1e-12, atol=1e-14)
+
+
+def pin_orthonormal_retrieval(impl):
+    r = rng(3)
+    D, T = 16, 16
+    Qm, _ = np.linalg.qr(r.standard_normal((D, D)))
+    keys = Qm.T                                  # rows orthonormal
+    k = keys[None, :T, None, :].copy()
+    q = k.copy()                                 # query each token with its own key
+    v = r.standard_normal((1, T, 1, D))
+    alpha = np.ones((1, T, 1))
+    beta = np.ones((1, T, 1))
+    o, ht = impl(q, k, v, alpha, beta, None)
+    np.testing.assert_allclose(o[0, :, 0], v[0, :, 0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(ht[0, 0], v[0, :, 0].T @ keys[:T], rtol=0, atol=1e-12)
+
+
+def pin_rewrite_same_key(impl):
+    r = rng(4)
+    D = 8
+    kk = unit(r.standard_normal(D))
+    other = unit(r.standard_normal(D))
+    v1, v2, v3 = r.standard_normal((3, D))
+    k = np.stack([kk, other, kk])[None, :, None, :]
+    q = np.stack([kk, kk, kk])[None, :, None, :]
+    v = np.stack([v1, v3, v2])[None, :, None, :]
+    alpha = np.ones((1, 3, 1))
+    beta = np.ones((1, 3, 1))
+    o, ht = impl(q, k, v, alpha, beta, None)
+    # after the last write the memory returns exactly v2 for the key kk, whatever
+    # was written under another key in between:
+    np.testing.assert_allclose(ht[0, 0] @ kk, v2, rtol=0, atol=1e-12)
+    # and the first read returns v1 (the only association so far)
+    np.testing.assert_allclose(o[0, 0, 0], v1, rtol=0, atol=1e-12)
+
+
+def pin_single_token(impl):
+    r = rng(5)
+    q, k, v, alpha, beta, s0 = rand_inputs(r, 3, 1, 1, 2, 7)
+    o, ht = impl(q, k, v, alpha, beta, s0)
+    for b in range(3):
+        for h in range(2):
+            S, qq, kk, vv = s0[b, h], q[b, 0, 0], k[b, 0, 0], v[b, 0, h]
+            a, be = alpha[b, 0, h], beta[b, 0, h]
+            d = be * (vv - a * (S @ kk))
+            np.testing.assert_allclose(o[b, 0, h], a * (S @ qq) + d * (kk @ qq),
+                                       rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(ht[b, h], a * S + np.outer(d, kk),
+                                       rtol=1e-12, atol=1e-13)
+
+
+def product_form(q, k, v, alpha, beta, s0):
+    """Brute-force closed form with explicit d x d matrices (one head)."""
+    T, D = k.shape
+    P = [alpha[t] * (np.eye(D) - beta[t] * np.outer(k[t], k[t])) for t in range(T)]
+    o = np.zeros((T, D))
+    S = None
+    for t_end in range(1, T + 1):
+        S = s0.copy()
+        for t in range(t_end):
+            S = S @ P[t]
+        for t in range(t_end):
+            term = beta[t] * np.outer(v[t], k[t])
+            for s in range(t + 1, t_end):
+                term = term @ P[s]
+            S = S + term
+        o[t_end - 1] = S @ q[t_end - 1]
+    return o, S
+
+
+def pin_product_form(impl):
+    r = rng(6)
+    for D, T in [(3, 5), (4, 6), (2, 4)]:
+        q, k, v, alpha, beta, s0 = rand_inputs(r, 1, T, 1, 1, D, normalize=False)
+        o, ht = impl(q, k, v, alpha, beta, s0)
+        ob, Sb = product_form(q[0, :, 0], k[0, :, 0], v[0, :, 0], alpha[0, :, 0],
+                              beta[0, :, 0], s0[0, 0])
+        np.testing.assert_allclose(o[0, :, 0], ob, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(ht[0, 0], Sb, rtol=1e-11, atol=1e-12)
+
+
+def pin_head_map(impl):
+    r = rng(7)
+    Hqk, Hv, D, T = 2, 6, 6, 5
+    q, k, v, alpha, beta, s0 = rand_inputs(r, 1, T, Hqk, Hv, D)
+    o, ht = impl(q, k, v, alpha, beta, s0)
+    for h in range(Hv):
+        g = h // (Hv // Hqk)
+        o1, ht1 = oracle.np_prefill(q[:, :, g:g + 1], k[:, :, g:g + 1], v[:, :, h:h + 1],
+                                    alpha[:, :, h:h + 1], beta[:, :, h:h + 1],
+                                    s0[:, h:h + 1])
+        np.testing.assert_allclose(o[:, :, h], o1[:, :, 0], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(ht[:, h], ht1[:, 0], rtol=1e-12, atol=1e-13)
+
+
+def pin_contraction(impl):
+    r = rng(8)
+    D, T = 8, 10
+    q, k, v, alpha, beta, s0 = rand_inputs(r, 1, T, 1, 1, D)
+    S_prev = s0[0, 0]
+    for t in range(T):
+        _, ht = impl(q[:, t:t + 1], k[:, t:t + 1], v[:, t:t + 1], alpha[:, t:t + 1],
+                     beta[:, t:t + 1], S_prev[None, None])
+        S = ht[0, 0]
+        bound = alpha[0, t, 0] * np.linalg.norm(S_prev, 2) + beta[0, t, 0] * np.linalg.norm(v[0, t, 0])
+        assert np.linalg.norm(S, 2) <= bound * (1 + 1e-12)
+        S_prev = S
+
+
+def pin_empty(impl):
+    r = rng(9)
+    q, k, v, alpha, beta, s0 = rand_inputs(r, 2, 0, 1, 3, 4)
+    o, ht = impl(q, k, v, alpha, beta, s0)
+    assert o.shape == (2, 0, 3, 4)
+    np.testing.assert_array_equal(ht, s0)
+
+
+PINS = [pin_identity, pin_pure_decay, pin_orthonormal_retrieval,
+        pin_rewrite_same_key, pin_single_token, pin_product_form, pin_head_map,
+        pin_contraction, pin_empty]
+
+
+# ---------------------------------------------------------------- tests
+@pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
+@pytest.mark.parametrize("impl", [c_impl, np_impl], ids=["c_oracle", "numpy_twin"])
+def test_oracle_pin(oracle_mod, impl, pin):
+    pin(impl)
+
+
+@pytest.mark.parametrize("kind", MUTANTS)
+def test_mutants_are_caught(kind):
+    impl = make_mutant(kind)
+    failed = []
+    for pin in PINS:
+        try:
+            pin(impl)
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, "mutant %s passed every pin" % kind
+
+
+def test_unmutated_reference_passes_all_pins():
+    impl = make_mutant("none")
+    for pin in PINS:
+        pin(impl)
+
+
+def test_c_oracle_matches_numpy_twin(oracle_mod):
+    r = rng(10)
+    q, k, v, alpha, beta, s0 = rand_inputs(r, 2, 11, 2, 6, 16)
+    o1, h1 = oracle.prefill(q, k, v, alpha, beta, s0)
+    o2, h2 = oracle.np_prefill(q, k, v, alpha, beta, s0)
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(h1, h2, rtol=1e-12, atol=1e-13)
+
+
+def test_decode_steps_equal_prefill(oracle_mod):
+    r = rng(11)
+    B, T, Hqk, Hv, D = 3, 9, 2, 6, 16
+    q, k, v, alpha, beta, s0 = rand_inputs(r, B, T, Hqk, Hv, D)
+    o_ref, h_ref = oracle.prefill(q, k, v, alpha, beta, s0)
+    st = s0
+    for t in range(T):
+        o_t, st = oracle.decode_step(q[:, t], k[:, t], v[:, t], alpha[:, t], beta[:, t], st)
+        np.testing.assert_allclose(o_t, o_ref[:, t], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(st, h_ref, rtol=1e-12, atol=1e-13)
+
+
+def test_varlen_equals_separate_sequences(oracle_mod):
+    r = rng(12)
+    lengths = [5, 0, 9, 1]
+    Hqk, Hv, D = 2, 6, 8
+    T = sum(lengths)
+    q, k, v, alpha, beta, _ = rand_inputs(r, 1, T, Hqk, Hv, D)
+    h0 = r.standard_normal((len(lengths), Hv, D, D))
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    o, ht = oracle.varlen(q[0], k[0], v[0], alpha[0], beta[0], cu, h0)
+    for n, L in enumerate(lengths):
+        s = cu[n]
+        o_n, ht_n = oracle.np_prefill(q[:, s:s + L], k[:, s:s + L], v[:, s:s + L],
+                                      alpha[:, s:s + L], beta[:, s:s + L], h0[n:n + 1])
+        np.testing.assert_allclose(o[s:s + L], o_n[0], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(ht[n], ht_n[0], rtol=1e-12, atol=1e-13)
+    np.testing.assert_array_equal(ht[1], h0[1])      # empty sequence passes h0
+
+
+def test_gate_rmsnorm_pins():
+    r = rng(13)
+    D = 128
+    # constant rows: rms(c*1) = |c|, so y = sign(c) * w * sigmoid(g) when eps = 0
+    c = np.array([2.5, -0.75, 1e-3])[:, None] * np.ones((3, D))
+    g = r.standard_normal((3, D))
+    w = r.standard_normal(D)
+    y = oracle.gate_rmsnorm(c, g, w, eps=0.0)
+    np.testing.assert_allclose(y, np.sign(c) * w * scipy.special.expit(g), rtol=1e-13)
+    # scale invariance with eps = 0; the norm equals the library 2-norm / sqrt(D)
+    o = r.standard_normal((5, 3, D))
+    gate = r.standard_normal((5, 3, D))
+    y1 = oracle.gate_rmsnorm(o, gate, None, 0.0)
+    y2 = oracle.gate_rmsnorm(7.0 * o, gate, None, 0.0)
+    np.testing.assert_allclose(y1, y2, rtol=1e-13)
+    ref = o / (np.linalg.norm(o, axis=-1, keepdims=True) / np.sqrt(D)) * scipy.special.expit(gate)
+    np.testing.assert_allclose(y1, ref, rtol=1e-12)
+    # gate 0 halves, eps enters under the root
+    y0 = oracle.gate_rmsnorm(o, np.zeros_like(o), None, 0.5)
+    np.testing.assert_allclose(y0, 0.5 * o / np.sqrt(np.mean(o * o, -1, keepdims=True) + 0.5),
+                               rtol=1e-13)
+
+
+@pytest.mark.parametrize("C", [1, 16, 64])
+def test_chunked_form_equals_sequential(oracle_mod, C):
+    """The block-parallel rewrite reaches the sequential result (to float64
+    rounding), including a partial last chunk and a non-zero initial state."""
+    r = rng(20 + C)
+    B, T, Hqk, Hv, D = 1, 150, 2, 6, 32
+    q, k, v, alpha, beta, s0 = rand_inputs(r, B, T, Hqk, Hv, D)
+    o_ref, h_ref = oracle.prefill(q, k, v, alpha, beta, s0)
+    o_c, h_c = chunked_form.chunked_prefill(q, k, v, alpha, beta, s0, C=C)
+    scale_o = np.abs(o_ref).max()
+    np.testing.assert_allclose(o_c, o_ref, rtol=0, atol=1e-12 * scale_o)
+    np.testing.assert_allclose(h_c, h_ref, rtol=0, atol=1e-12 * np.abs(h_ref).max())
+
+
+def test_chunked_form_full_head_dim(oracle_mod):
+    r = rng(30)
+    q, k, v, alpha, beta, s0 = rand_inputs(r, 1, 130, 1, 3, 128)
+    o_ref, h_ref = oracle.prefill(q, k, v, alpha, beta, s0)
+    o_c, h_c = chunked_form.chunked_prefill(q, k, v, alpha, beta, s0, C=64)
+    np.testing.assert_allclose(o_c, o_ref, rtol=0, atol=1e-11 * np.abs(o_ref).max())
+    np.testing.assert_allclose(h_c, h_ref, rtol=0, atol=1e-11 * np.abs(h_ref).max())
+
+
+def test_nan_isolation(oracle_mod):
+    r = rng(31)
+    q, k, v, alpha, beta, s0 = rand_inputs(r, 2, 6, 2, 6, 8)
+    v[1, 2, 4, 3] = np.nan
+    o, ht = oracle.prefill(q, k, v, alpha, beta, s0)
+    bad = np.zeros(o.shape, dtype=bool)
+    bad[1, 2:, 4] = True
+    assert np.isnan(o[1, 2, 4]).any()
+    assert np.isfinite(o[~bad]).all()
+    assert np.isfinite(np.delete(ht.reshape(12, -1), 1 * 6 + 4, axis=0)).all()
+
+
+def test_state_size_independent_of_T(oracle_mod):
+    r = rng(32)
+    shapes = set()
+    for T in (1, 64, 256):
+        q, k, v, alpha, beta, _ = rand_inputs(r, 1, T, 1, 3, 16)
+        _, ht = oracle.prefill(q, k, v, alpha, beta, None)
+        shapes.add(ht.shape)
+    assert shapes == {(1, 3, 16, 16)}
+
+
+def test_footprint_tens_of_megabytes():
+    """48 layers x 48 value heads x 128 x 128 at 2 bytes (BF16, the precision
+    the page computes in) is 72 MiB: 'tens of megabytes'."""
+    with open(os.path.join(GOLDEN, "pages_facts.json")) as f:
+        facts = json.load(f)
+    layers = facts["deltanet_layers"]["value"]
+    heads = facts["value_heads"]["value"]
+    d = facts["head_dim"]["value"]
+    lo, hi = facts["state_overhead_bytes_range"]["value"]
+    total = layers * heads * d * d * 2
+    assert total == 75_497_472 == 72 * 2 ** 20
+    assert lo <= total < hi
+    assert facts["value_heads"]["value"] % facts["qk_heads"]["value"] == 0
+    # a per-token KV cache of the same size would grow with context; the state does not
+    assert facts["total_layers"]["value"] - layers == 16
+
+
+def test_synth_inputs_deterministic_and_normalised():
+    import torch
+    import synth
+    a = synth.prefill_inputs(1, 70, torch.bfloat16, seed=5)
+    b = synth.prefill_inputs(1, 70, torch.bfloat16, seed=5)
+    for key in ("q", "k", "v", "alpha", "beta"):
+        assert torch.equal(a[key], b[key])
+    n = a["k"].double().norm(dim=-1)
+    assert torch.allclose(n, torch.ones_like(n), atol=1e-2)
+    assert (a["alpha"] > 0).all() and (a["alpha"] <= 1).all()
+    assert (a["beta"] >= 0).all() and (a["beta"] <= 1).all()
+    # the distributions match their definitions (sanity, not exactness)
+    x = -np.log(a["alpha"].double().numpy()) / 0.05       # softplus of N(0,1)
+    z = np.log(np.expm1(x))                                 # back to N(0,1)
+    assert scipy.stats.kstest(z.ravel(), "norm").pvalue > 1e-4
