@@ -1,0 +1,300 @@
+// Host side of the C ABI declared in include/gdn.h: argument checks (all of
+// them before anything is enqueued), workspace layout, and launches on the
+// caller's stream.  No allocation, no synchronisation, no global mutable state
+// beyond the thread-local last-error code.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "gdn.h"
+#include "gdn_device.hpp"
+#include "gdn_launch.hpp"
+
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+// Largest element count accepted for one tensor (keeps every int index the
+// kernels form far from overflow; a [T, 48, 128] tensor at this limit has
+// 2^26 tokens).
+constexpr int64_t kMaxElems = int64_t(1) << 38;
+
+struct Range {
+  uintptr_t lo, hi;   // [lo, hi); empty when lo == hi
+};
+
+Range span(const void* p, int64_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, p ? a + (uintptr_t)bytes : a};
+}
+
+bool overlap(Range a, Range b) {
+  if (a.lo == a.hi || b.lo == b.hi) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t esize(gdn_dtype dt) { return dt == GDN_BF16 ? 2 : 4; }
+
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Workspace layout: Tt [nc][Hv][64][64], QK [nc][Hqk][64][64] (element type),
+// G [nc][Hv][64] fp32, then for varlen the chunk table [nc][2] and the
+// per-sequence chunk offsets [N+1] (int32).
+struct WsLayout {
+  size_t tt, qk, gs, tab, seq, total;
+};
+
+WsLayout ws_layout(int64_t nc, int64_t Hqk, int64_t Hv, gdn_dtype dt, int64_t nseq_varlen) {
+  WsLayout w{};
+  const size_t es = esize(dt);
+  size_t off = 0;
+  w.tt = off;
+  off += round256((size_t)nc * Hv * gdn::kC * gdn::kC * es);
+  w.qk = off;
+  off += round256((size_t)nc * Hqk * gdn::kC * gdn::kC * es);
+  w.gs = off;
+  off += round256((size_t)nc * Hv * gdn::kC * sizeof(float));
+  w.tab = off;
+  w.seq = off;
+  if (nseq_varlen >= 0) {
+    off += round256((size_t)nc * 2 * sizeof(int32_t));
+    w.seq = off;
+    off += round256((size_t)(nseq_varlen + 1) * sizeof(int32_t));
+  }
+  w.total = off;
+  return w;
+}
+
+gdn_status check_dims(int64_t H_qk, int64_t H_v, int64_t D, gdn_dtype dt) {
+  if (H_qk <= 0 || H_v <= 0 || D <= 0) return GDN_ERR_SHAPE;
+  if (H_v % H_qk != 0) return GDN_ERR_SHAPE;
+  if (D != gdn::kD) return GDN_ERR_UNSUPPORTED;
+  if (dt != GDN_F32 && dt != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+  if (H_v > 4096) return GDN_ERR_UNSUPPORTED;
+  return GDN_OK;
+}
+
+gdn_status fail_hip(hipError_t e) {
+  if (e == hipSuccess) return GDN_OK;
+  g_last_hip = (int)e;
+  return GDN_ERR_HIP;
+}
+
+// Checks shared by the packed and fixed-length prefill.  ntok = all tokens,
+// nseq = number of states.
+gdn_status check_prefill(const void* q, const void* k, const void* v, const float* alpha,
+                         const float* beta, const float* h0, const void* o, const float* ht,
+                         const void* gate, const float* norm_w, const void* cu, int64_t cu_len,
+                         int64_t ntok, int64_t nseq, int64_t H_qk, int64_t H_v, gdn_dtype dt,
+                         const void* workspace, size_t workspace_bytes, size_t need) {
+  const int64_t es = (int64_t)esize(dt);
+  const int64_t D = gdn::kD;
+  if (ntok > 0 && (!q || !k || !v || !alpha || !beta || !o)) return GDN_ERR_NULL;
+  if (ntok * H_v * D > kMaxElems || nseq * H_v * D * D > kMaxElems) return GDN_ERR_UNSUPPORTED;
+  if (need > 0 && !workspace) return GDN_ERR_WORKSPACE;
+  if (workspace_bytes < need) return GDN_ERR_WORKSPACE;
+  const void* p16[] = {q, k, v, o, h0, ht, gate, workspace};
+  for (const void* p : p16)
+    if (!aligned(p, 16)) return GDN_ERR_ALIGN;
+  if (!aligned(alpha, 4) || !aligned(beta, 4) || !aligned(norm_w, 4) || !aligned(cu, 4))
+    return GDN_ERR_ALIGN;
+
+  const Range rq = span(q, ntok * H_qk * D * es), rk = span(k, ntok * H_qk * D * es);
+  const Range rv = span(v, ntok * H_v * D * es), ro = span(o, ntok * H_v * D * es);
+  const Range ra = span(alpha, ntok * H_v * 4), rb = span(beta, ntok * H_v * 4);
+  const Range rh0 = span(h0, nseq * H_v * D * D * 4), rht = span(ht, nseq * H_v * D * D * 4);
+  const Range rg = span(gate, gate ? ntok * H_v * D * es : 0);
+  const Range rw = span(norm_w, norm_w ? D * 4 : 0);
+  const Range rcu = span(cu, cu ? cu_len * 4 : 0);
+  const Range rws = span(workspace, (int64_t)need);
+  // o and the workspace may overlap nothing; ht may overlap nothing except
+  // that it may be exactly h0 (in-place carry).
+  const bool ht_in_place = ht && h0 && (const void*)ht == (const void*)h0;
+  const Range inputs[] = {rq, rk, rv, ra, rb, rg, rw, rcu};
+  for (const Range& in : inputs)
+    if (overlap(ro, in) || overlap(rws, in) || overlap(rht, in)) return GDN_ERR_ALIAS;
+  if (overlap(ro, rh0) || overlap(rws, rh0)) return GDN_ERR_ALIAS;
+  if (!ht_in_place && overlap(rht, rh0)) return GDN_ERR_ALIAS;
+  if (overlap(ro, rht) || overlap(ro, rws) || overlap(rht, rws)) return GDN_ERR_ALIAS;
+  return GDN_OK;
+}
+
+enum Phase { kPrepare = 1, kScan = 2, kBoth = 3 };
+
+gdn_status prefill_fixed(const void* q, const void* k, const void* v, const float* alpha,
+                         const float* beta, const float* h0, void* o, float* ht, int32_t B,
+                         int32_t T, int32_t H_qk, int32_t H_v, int32_t D, gdn_dtype dt,
+                         void* workspace, size_t workspace_bytes, void* stream, int phase) {
+  gdn_status s = check_dims(H_qk, H_v, D, dt);
+  if (s != GDN_OK) return s;
+  if (B < 0 || T < 0) return GDN_ERR_SHAPE;
+  if (B > 65535) return GDN_ERR_UNSUPPORTED;
+  const int64_t Nc = ((int64_t)T + gdn::kC - 1) / gdn::kC;
+  const int64_t nc = (int64_t)B * Nc;
+  if (nc > (int64_t(1) << 30)) return GDN_ERR_UNSUPPORTED;
+  const WsLayout L = ws_layout(nc, H_qk, H_v, dt, -1);
+  const size_t need = nc > 0 ? L.total : 0;
+  s = check_prefill(q, k, v, alpha, beta, h0, o, ht, nullptr, nullptr, nullptr, 0,
+                    (int64_t)B * T, B, H_qk, H_v, dt, workspace, workspace_bytes, need);
+  if (s != GDN_OK) return s;
+
+  gdn::PrefillLaunch a{};
+  a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.h0 = h0; a.o = o; a.ht = ht;
+  a.gate = nullptr; a.norm_w = nullptr; a.norm_eps = 0.f;
+  char* ws = static_cast<char*>(workspace);
+  a.Tt = ws ? ws + L.tt : nullptr;
+  a.QK = ws ? ws + L.qk : nullptr;
+  a.Gs = ws ? reinterpret_cast<float*>(ws + L.gs) : nullptr;
+  a.cm = gdn::ChunkMap{nullptr, nullptr, T, (int)Nc, (int)nc};
+  a.nseq = B;
+  a.nc_launch = (int)nc;
+  a.Hqk = H_qk; a.Hv = H_v;
+  a.bf16_io = dt == GDN_BF16;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((phase & kPrepare) && nc > 0) {
+    s = fail_hip(gdn::launch_prepare(a, st));
+    if (s != GDN_OK) return s;
+  }
+  if (phase & kScan) {
+    if (!ht && T == 0) return GDN_OK;
+    s = fail_hip(gdn::launch_scan(a, st));
+  }
+  return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_abi_version(void) { return 100; }
+
+int gdn_last_hip_error(void) { return g_last_hip; }
+
+const char* gdn_status_str(gdn_status s) {
+  switch (s) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_ERR_NULL: return "GDN_ERR_NULL: a required pointer is NULL";
+    case GDN_ERR_SHAPE: return "GDN_ERR_SHAPE: negative or inconsistent sizes";
+    case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED: unsupported head dim, dtype or size";
+    case GDN_ERR_ALIGN: return "GDN_ERR_ALIGN: misaligned pointer";
+    case GDN_ERR_ALIAS: return "GDN_ERR_ALIAS: an output overlaps another buffer";
+    case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE: workspace missing or too small";
+    case GDN_ERR_HIP: return "GDN_ERR_HIP: a HIP launch failed";
+    default: return "unknown gdn_status";
+  }
+}
+
+size_t gdn_prefill_workspace_bytes(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t D,
+                                   gdn_dtype dt) {
+  if (check_dims(H_qk, H_v, D, dt) != GDN_OK || B < 0 || T < 0) return 0;
+  const int64_t nc = (int64_t)B * (((int64_t)T + gdn::kC - 1) / gdn::kC);
+  if (nc == 0) return 0;
+  return ws_layout(nc, H_qk, H_v, dt, -1).total;
+}
+
+size_t gdn_varlen_workspace_bytes(int32_t N, int32_t T_tot, int32_t H_qk, int32_t H_v,
+                                  int32_t D, gdn_dtype dt) {
+  if (check_dims(H_qk, H_v, D, dt) != GDN_OK || N < 0 || T_tot < 0) return 0;
+  const int64_t nc = ((int64_t)T_tot + gdn::kC - 1) / gdn::kC + N;
+  return ws_layout(nc, H_qk, H_v, dt, N).total;
+}
+
+gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v, const float* alpha,
+                               const float* beta, const float* h0, void* o, float* ht,
+                               int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t D,
+                               gdn_dtype dt, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  return prefill_fixed(q, k, v, alpha, beta, h0, o, ht, B, T, H_qk, H_v, D, dt, workspace,
+                       workspace_bytes, stream, kBoth);
+}
+
+gdn_status gdn_prefill_prepare(const void* q, const void* k, const void* v, const float* alpha,
+                               const float* beta, const float* h0, void* o, float* ht,
+                               int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t D,
+                               gdn_dtype dt, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  return prefill_fixed(q, k, v, alpha, beta, h0, o, ht, B, T, H_qk, H_v, D, dt, workspace,
+                       workspace_bytes, stream, kPrepare);
+}
+
+gdn_status gdn_prefill_scan(const void* q, const void* k, const void* v, const float* alpha,
+                            const float* beta, const float* h0, void* o, float* ht, int32_t B,
+                            int32_t T, int32_t H_qk, int32_t H_v, int32_t D, gdn_dtype dt,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_fixed(q, k, v, alpha, beta, h0, o, ht, B, T, H_qk, H_v, D, dt, workspace,
+                       workspace_bytes, stream, kScan);
+}
+
+gdn_status gdn_decode_step(const void* q, const void* k, const void* v, const float* alpha,
+                           const float* beta, float* state, void* o, int32_t B, int32_t H_qk,
+                           int32_t H_v, int32_t D, gdn_dtype dt, void* stream) {
+  gdn_status s = check_dims(H_qk, H_v, D, dt);
+  if (s != GDN_OK) return s;
+  if (B < 0) return GDN_ERR_SHAPE;
+  if (B == 0) return GDN_OK;
+  if (!q || !k || !v || !alpha || !beta || !state || !o) return GDN_ERR_NULL;
+  const int64_t es = (int64_t)esize(dt), Dl = gdn::kD;
+  if ((int64_t)B * H_v > (int64_t(1) << 30)) return GDN_ERR_UNSUPPORTED;
+  const void* p16[] = {q, k, v, o, state};
+  for (const void* p : p16)
+    if (!aligned(p, 16)) return GDN_ERR_ALIGN;
+  if (!aligned(alpha, 4) || !aligned(beta, 4)) return GDN_ERR_ALIGN;
+  const Range rq = span(q, B * H_qk * Dl * es), rk = span(k, B * H_qk * Dl * es);
+  const Range rv = span(v, B * H_v * Dl * es), ro = span(o, B * H_v * Dl * es);
+  const Range ra = span(alpha, B * H_v * 4), rb = span(beta, B * H_v * 4);
+  const Range rs = span(state, (int64_t)B * H_v * Dl * Dl * 4);
+  const Range ins[] = {rq, rk, rv, ra, rb};
+  for (const Range& in : ins)
+    if (overlap(ro, in) || overlap(rs, in)) return GDN_ERR_ALIAS;
+  if (overlap(ro, rs)) return GDN_ERR_ALIAS;
+  return fail_hip(gdn::launch_decode_step(q, k, v, alpha, beta, state, o, B, H_qk, H_v,
+                                          dt == GDN_BF16, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_prefill_varlen(const void* q, const void* k, const void* v, const float* alpha,
+                              const float* beta, const int32_t* cu_seqlens, int32_t N,
+                              int32_t T_tot, const float* h0, void* o, float* ht,
+                              const void* gate, const float* norm_weight, float norm_eps,
+                              int32_t H_qk, int32_t H_v, int32_t D, gdn_dtype dt,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  gdn_status s = check_dims(H_qk, H_v, D, dt);
+  if (s != GDN_OK) return s;
+  if (N < 0 || T_tot < 0) return GDN_ERR_SHAPE;
+  if (N == 0) return T_tot == 0 ? GDN_OK : GDN_ERR_SHAPE;
+  if (N > 65535) return GDN_ERR_UNSUPPORTED;
+  if (!cu_seqlens) return GDN_ERR_NULL;
+  if (!(norm_eps >= 0.f)) return GDN_ERR_SHAPE;
+  const int64_t nc = ((int64_t)T_tot + gdn::kC - 1) / gdn::kC + N;
+  if (nc > (int64_t(1) << 30)) return GDN_ERR_UNSUPPORTED;
+  const WsLayout L = ws_layout(nc, H_qk, H_v, dt, N);
+  s = check_prefill(q, k, v, alpha, beta, h0, o, ht, gate, norm_weight, cu_seqlens, N + 1,
+                    T_tot, N, H_qk, H_v, dt, workspace, workspace_bytes, L.total);
+  if (s != GDN_OK) return s;
+
+  char* ws = static_cast<char*>(workspace);
+  int32_t* tab = reinterpret_cast<int32_t*>(ws + L.tab);
+  int32_t* seq_off = reinterpret_cast<int32_t*>(ws + L.seq);
+  gdn::PrefillLaunch a{};
+  a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.h0 = h0; a.o = o; a.ht = ht;
+  a.gate = gate; a.norm_w = norm_weight; a.norm_eps = norm_eps;
+  a.Tt = ws + L.tt;
+  a.QK = ws + L.qk;
+  a.Gs = reinterpret_cast<float*>(ws + L.gs);
+  a.cm = gdn::ChunkMap{tab, seq_off, 0, 0, (int)nc};
+  a.nseq = N;
+  a.nc_launch = (int)nc;
+  a.Hqk = H_qk; a.Hv = H_v;
+  a.bf16_io = dt == GDN_BF16;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  s = fail_hip(gdn::launch_varlen_table(cu_seqlens, N, T_tot, (int)nc, tab, seq_off, st));
+  if (s != GDN_OK) return s;
+  s = fail_hip(gdn::launch_prepare(a, st));
+  if (s != GDN_OK) return s;
+  return fail_hip(gdn::launch_scan(a, st));
+}
+
+}  // extern "C"

@@ -1,0 +1,132 @@
+// Decode step: one token per sequence, state read and rewritten in place.
+//
+// One step of the recurrence (page "Inside Qwen3.8-27B: Hybrid DeltaNet
+// Architecture, 256k Context, and 24GB Local Serving", section "Gated DeltaNet
+// Mechanics"; at inference the state advances token by token, per the note
+// under "The Role of Periodic Gated Attention"):
+//
+//   S' = alpha S (I - beta k k^T) + beta v k^T,   o = S' q
+//
+// Row i of S (a value row, 128 floats) evolves alone, from the OLD row:
+//   u_i = S_i . k,  p_i = S_i . q,  d_i = beta (v_i - alpha u_i)
+//   S'_i = alpha S_i + d_i k,       o_i = alpha p_i + d_i (k . q)
+//
+// The step moves 2 x 64 KiB of fp32 state per (sequence, value head) and does
+// ~6 flops per state element, so it is bound by HBM bandwidth.  Layout of the
+// work: one 256-thread workgroup per (sequence, value head); 8 lanes share one
+// state row, each lane owning 4 float4 column groups (columns 4*l8 + 32*i), so
+// every load/store instruction of a wave covers 8 full 128-byte row segments.
+// Each thread keeps 16 float4 (4 rows) in flight; dot products are reduced
+// across the 8 lanes of a row with xor shuffles.
+#include "gdn_device.hpp"
+#include "gdn_launch.hpp"
+
+namespace gdn {
+
+template <typename E>
+__device__ __forceinline__ f32x4 load4(const E* p);
+template <>
+__device__ __forceinline__ f32x4 load4<float>(const float* p) {
+  return *reinterpret_cast<const f32x4*>(p);
+}
+template <>
+__device__ __forceinline__ f32x4 load4<bf16>(const bf16* p) {
+  bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+
+__device__ __forceinline__ float sum8(float x) {
+  x += __shfl_xor(x, 1, 64);
+  x += __shfl_xor(x, 2, 64);
+  x += __shfl_xor(x, 4, 64);
+  return x;
+}
+
+__device__ __forceinline__ float dot4(const f32x4& a, const f32x4& b) {
+  return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
+}
+
+template <typename E>
+__global__ __launch_bounds__(256) void decode_step_kernel(
+    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
+    const float* __restrict__ alpha, const float* __restrict__ beta,
+    float* __restrict__ state, E* __restrict__ o, int Hqk, int Hv, int G) {
+  const int bh = blockIdx.x;             // b * Hv + h
+  const int b = bh / Hv, h = bh - (bh / Hv) * Hv;
+  const int gq = h / G;                  // query/key head read by value head h
+  const int tid = threadIdx.x;
+  const int l8 = tid & 7;                // lane within the row's 8-lane group
+  const int rg = tid >> 3;               // 0..31: row within one pass
+
+  const E* qp = q + ((size_t)b * Hqk + gq) * kD;
+  const E* kp = k + ((size_t)b * Hqk + gq) * kD;
+  float* S = state + (size_t)bh * kD * kD;
+
+  // Issue the state loads first: 4 rows x 4 float4 per thread.
+  f32x4 s[4][4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      s[p][i] = __builtin_nontemporal_load(
+          reinterpret_cast<const f32x4*>(S + (rg + 32 * p) * kD + 4 * l8 + 32 * i));
+
+  f32x4 kr[4], qr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    kr[i] = load4<E>(kp + 4 * l8 + 32 * i);
+    qr[i] = load4<E>(qp + 4 * l8 + 32 * i);
+  }
+  const float a = alpha[bh], be = beta[bh];
+  float vr[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) vr[p] = to_f32(v[(size_t)bh * kD + rg + 32 * p]);
+
+  float kq = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) kq += dot4(kr[i], qr[i]);
+  kq = sum8(kq);
+
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    float u = 0.f, pq = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      u += dot4(s[p][i], kr[i]);
+      pq += dot4(s[p][i], qr[i]);
+    }
+    u = sum8(u);
+    pq = sum8(pq);
+    const float d = be * (vr[p] - a * u);
+    const int row = rg + 32 * p;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f32x4 n;
+      n[0] = a * s[p][i][0] + d * kr[i][0];
+      n[1] = a * s[p][i][1] + d * kr[i][1];
+      n[2] = a * s[p][i][2] + d * kr[i][2];
+      n[3] = a * s[p][i][3] + d * kr[i][3];
+      __builtin_nontemporal_store(n, reinterpret_cast<f32x4*>(S + row * kD + 4 * l8 + 32 * i));
+    }
+    if (l8 == 0) o[(size_t)bh * kD + row] = from_f32<E>(a * pq + d * kq);
+  }
+}
+
+hipError_t launch_decode_step(const void* q, const void* k, const void* v,
+                              const float* alpha, const float* beta, float* state,
+                              void* o, int B, int Hqk, int Hv, bool bf16_io,
+                              hipStream_t stream) {
+  const int G = Hv / Hqk;
+  dim3 grid((unsigned)(B * Hv)), block(256);
+  if (bf16_io)
+    hipLaunchKernelGGL(decode_step_kernel<bf16>, grid, block, 0, stream,
+                       (const bf16*)q, (const bf16*)k, (const bf16*)v, alpha, beta,
+                       state, (bf16*)o, Hqk, Hv, G);
+  else
+    hipLaunchKernelGGL(decode_step_kernel<float>, grid, block, 0, stream,
+                       (const float*)q, (const float*)k, (const float*)v, alpha,
+                       beta, state, (float*)o, Hqk, Hv, G);
+  return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -1,0 +1,131 @@
+// Device-side building blocks for the gfx950 Gated DeltaNet kernels:
+// element types, conversions, and the MFMA fragment helpers.
+//
+// MFMA fragment layouts used throughout (gfx950, wave64; lane = 0..63,
+// r = lane % 16, g = lane / 16):
+//
+//  * 16x16 accumulator tile (both v_mfma_f32_16x16x32_bf16 and
+//    v_mfma_f32_16x16x4_f32): lane holds rows 4g + i (i = 0..3) of column r.
+//  * bf16, K = 32 per instruction: lane (row r of A / column r of B, group g)
+//    supplies 8 K-slots.  Any K order works as long as A and B agree, so the
+//    library uses the order that makes an accumulator pair usable as a B
+//    operand without leaving registers: slot j < 4 is K = 4g + j, slot j >= 4
+//    is K = 16 + 4g + (j - 4).  Two stacked 16x16 accumulator tiles (rows 0-15
+//    and 16-31 of a 32-row block) are then exactly one B fragment.
+//  * fp32, K = 4 per instruction: step s of a 16-row K block takes K = 4g + s,
+//    so element s of an accumulator tile is the B operand of step s.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kD = 128;     // head dimension (d_k = d_v)
+constexpr int kC = 64;      // tokens per chunk
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+template <typename E> __device__ __forceinline__ E from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // RNE
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+// Orders this wave's LDS traffic: every earlier LDS access has completed and
+// no later one is hoisted above this point.
+__device__ __forceinline__ void wave_lds_fence() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Two accumulator tiles (K rows 0-15 and 16-31 of a 32-row block) -> one
+// bf16 B fragment in the library's K order.
+__device__ __forceinline__ bf16x8 pack_b(const f32x4& lo, const f32x4& hi) {
+  bf16x8 r;
+  r[0] = (bf16)lo[0]; r[1] = (bf16)lo[1]; r[2] = (bf16)lo[2]; r[3] = (bf16)lo[3];
+  r[4] = (bf16)hi[0]; r[5] = (bf16)hi[1]; r[6] = (bf16)hi[2]; r[7] = (bf16)hi[3];
+  return r;
+}
+
+// A fragment (bf16) from a row-major LDS matrix, K order as above:
+// row `row`, K block starting at column k0 (multiple of 32).
+__device__ __forceinline__ bf16x8 lds_a_bf16(const bf16* A, int lda, int row, int k0) {
+  const int g = lane_id() >> 4;
+  const bf16* p = A + row * lda + k0 + 4 * g;
+  bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
+  bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 16);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Plain A/B fragment (bf16, hardware-natural K order k = 8g + j) of a
+// row-major LDS matrix whose rows are indexed by the fragment's M (for A) or
+// N (for B): used when both operands come from LDS (Gram matrices).
+__device__ __forceinline__ bf16x8 lds_row8_bf16(const bf16* A, int lda, int row, int k0) {
+  const int g = lane_id() >> 4;
+  return *reinterpret_cast<const bf16x8*>(A + row * lda + k0 + 8 * g);
+}
+
+// acc(16 x 16) += A[row0 .. row0+15][k-range] * B, where B's K rows come as
+// accumulator tiles bt[0 .. nkb-1] (16 K rows each) and A is row-major in LDS
+// with the K range starting at column kcol0.  fp32 and bf16 versions.
+template <int NKB>
+__device__ __forceinline__ void mma_acc_bf16(f32x4& acc, const bf16* A, int lda,
+                                             int row0, int kcol0, const bf16x8* b) {
+  const int r = lane_id() & 15;
+#pragma unroll
+  for (int kk = 0; kk < NKB / 2; ++kk)
+    acc = mfma_bf16(lds_a_bf16(A, lda, row0 + r, kcol0 + 32 * kk), b[kk], acc);
+}
+
+template <int NKB>
+__device__ __forceinline__ void mma_acc_f32(f32x4& acc, const float* A, int lda,
+                                            int row0, int kcol0, const f32x4* bt) {
+  const int r = lane_id() & 15, g = lane_id() >> 4;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    const float* p = A + (row0 + r) * lda + kcol0 + 16 * kb + 4 * g;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = mfma_f32(p[s], bt[kb][s], acc);
+  }
+}
+
+// fp32 variant whose A operand is the TRANSPOSE of a row-major LDS matrix:
+// acc += (M^T)[row0 .. row0+15][k-range] * B, i.e. A[m][k] = M[k][m].
+template <int NKB>
+__device__ __forceinline__ void mma_acc_f32_tA(f32x4& acc, const float* M, int ldm,
+                                               int row0, int kcol0, const f32x4* bt) {
+  const int r = lane_id() & 15, g = lane_id() >> 4;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      acc = mfma_f32(M[(kcol0 + 16 * kb + 4 * g + s) * ldm + row0 + r], bt[kb][s], acc);
+  }
+}
+
+// Wave-wide inclusive prefix sum over 64 lanes.
+__device__ __forceinline__ float wave_inclusive_sum(float x) {
+  const int l = lane_id();
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    float y = __shfl_up(x, off, 64);
+    if (l >= off) x += y;
+  }
+  return x;
+}
+
+}  // namespace gdn

@@ -1,0 +1,40 @@
+// Host <-> kernel interface shared by the launch code and the C ABI layer.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// Where chunk `cid` lives.  Fixed-length batches compute it; packed varlen
+// batches read a table built on the device from cu_seqlens.
+struct ChunkMap {
+  const int32_t* tab;      // varlen: [nc_max][2] {first token, length}; null otherwise
+  const int32_t* seq_off;  // varlen: [N+1] first chunk of each sequence
+  int T, Nc;               // fixed-length: tokens and chunks per sequence
+  int nc_max;              // chunks the workspace holds
+};
+
+struct PrefillLaunch {
+  const void *q, *k, *v;
+  const float *alpha, *beta, *h0;
+  void* o;
+  float* ht;
+  const void* gate;        // null: plain output; else fused RMSNorm * sigmoid(gate)
+  const float* norm_w;
+  float norm_eps;
+  void *Tt, *QK;           // workspace regions
+  float* Gs;
+  ChunkMap cm;
+  int nseq, nc_launch, Hqk, Hv;
+  bool bf16_io;
+};
+
+hipError_t launch_prepare(const PrefillLaunch& a, hipStream_t st);
+hipError_t launch_scan(const PrefillLaunch& a, hipStream_t st);
+hipError_t launch_varlen_table(const int32_t* cu, int N, int T_tot, int nc_max, int32_t* tab,
+                               int32_t* seq_off, hipStream_t st);
+hipError_t launch_decode_step(const void* q, const void* k, const void* v, const float* alpha,
+                              const float* beta, float* state, void* o, int B, int Hqk, int Hv,
+                              bool bf16_io, hipStream_t stream);
+
+}  // namespace gdn

@@ -1,0 +1,267 @@
+"""Python binding of libgdn.so (the C ABI in include/gdn.h).
+
+Argument marshalling only: every step of the recurrence runs in the library's
+HIP kernels.  PyTorch provides device memory and the current HIP stream; the
+functions here check dtypes, shapes and contiguity, allocate outputs and the
+workspace with torch when the caller does not pass them, and hand raw
+pointers to the library.  There is no fallback: if libgdn.so is missing or
+fails to load, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_F32 = 0
+GDN_BF16 = 1
+CHUNK = 64
+HEAD_DIM = 128
+
+_STATUS = {0: "GDN_OK", -1: "GDN_ERR_NULL", -2: "GDN_ERR_SHAPE", -3: "GDN_ERR_UNSUPPORTED",
+           -4: "GDN_ERR_ALIGN", -5: "GDN_ERR_ALIAS", -6: "GDN_ERR_WORKSPACE", -7: "GDN_ERR_HIP"}
+
+
+class GDNError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            "libgdn.so not found at %s; build it with "
+            "`python -m hybrid_linear_attention_amd.build`" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz, i32, f32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_float
+    pre = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int, vp, sz, vp]
+    for name in ("gdn_prefill_chunked", "gdn_prefill_prepare", "gdn_prefill_scan"):
+        fn = getattr(lib, name)
+        fn.argtypes = pre
+        fn.restype = ctypes.c_int
+    lib.gdn_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int]
+    lib.gdn_prefill_workspace_bytes.restype = sz
+    lib.gdn_varlen_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int]
+    lib.gdn_varlen_workspace_bytes.restype = sz
+    lib.gdn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                    ctypes.c_int, vp]
+    lib.gdn_decode_step.restype = ctypes.c_int
+    lib.gdn_prefill_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp,
+                                       f32, i32, i32, i32, ctypes.c_int, vp, sz, vp]
+    lib.gdn_prefill_varlen.restype = ctypes.c_int
+    lib.gdn_status_str.argtypes = [ctypes.c_int]
+    lib.gdn_status_str.restype = ctypes.c_char_p
+    lib.gdn_last_hip_error.argtypes = []
+    lib.gdn_last_hip_error.restype = ctypes.c_int
+    lib.gdn_abi_version.argtypes = []
+    lib.gdn_abi_version.restype = ctypes.c_int
+    return lib
+
+
+lib = _load()
+
+
+# ---------------------------------------------------------------- helpers
+def status_str(status: int) -> str:
+    return lib.gdn_status_str(status).decode()
+
+
+def last_hip_error() -> int:
+    return lib.gdn_last_hip_error()
+
+
+def abi_version() -> int:
+    return lib.gdn_abi_version()
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        extra = ""
+        if rc == -7:
+            extra = " (hipError %d)" % last_hip_error()
+        raise GDNError(rc, "%s: %s%s" % (what, status_str(rc), extra))
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    if t.dtype == torch.float32:
+        return GDN_F32
+    raise TypeError("q/k/v must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _req(t, name, dtype=None, ndim=None, device=None):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError("%s must have %d dims, got shape %s" % (name, ndim, tuple(t.shape)))
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+
+
+def prefill_workspace_bytes(B, T, H_qk, H_v, D=HEAD_DIM, dtype=torch.bfloat16) -> int:
+    dt = GDN_BF16 if dtype == torch.bfloat16 else GDN_F32
+    return int(lib.gdn_prefill_workspace_bytes(B, T, H_qk, H_v, D, dt))
+
+
+def varlen_workspace_bytes(N, T_tot, H_qk, H_v, D=HEAD_DIM, dtype=torch.bfloat16) -> int:
+    dt = GDN_BF16 if dtype == torch.bfloat16 else GDN_F32
+    return int(lib.gdn_varlen_workspace_bytes(N, T_tot, H_qk, H_v, D, dt))
+
+
+def _workspace(nbytes, device, workspace):
+    if nbytes == 0:
+        return None
+    if workspace is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError("workspace too small: %d < %d bytes" %
+                         (workspace.numel() * workspace.element_size(), nbytes))
+    return workspace
+
+
+# ---------------------------------------------------------------- prefill
+def _prefill_args(q, k, v, alpha, beta, h0, o, ht, output_final_state, workspace):
+    _req(q, "q", ndim=4)
+    dtype, dev = q.dtype, q.device
+    B, T, H_qk, D = q.shape
+    _req(k, "k", dtype, 4, dev)
+    _req(v, "v", dtype, 4, dev)
+    H_v = v.shape[2]
+    if tuple(k.shape) != (B, T, H_qk, D) or tuple(v.shape) != (B, T, H_v, D):
+        raise ValueError("q/k [B,T,Hqk,D] and v [B,T,Hv,D] disagree: %s %s %s"
+                         % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
+    for name, t in (("alpha", alpha), ("beta", beta)):
+        _req(t, name, torch.float32, 3, dev)
+        if tuple(t.shape) != (B, T, H_v):
+            raise ValueError("%s must be [B,T,Hv]" % name)
+    _req(h0, "h0", torch.float32, 4, dev)
+    if h0 is not None and tuple(h0.shape) != (B, H_v, D, D):
+        raise ValueError("h0 must be [B,Hv,D,D]")
+    if o is None:
+        o = torch.empty((B, T, H_v, D), dtype=dtype, device=dev)
+    _req(o, "o", dtype, 4, dev)
+    if ht is None and output_final_state:
+        ht = torch.empty((B, H_v, D, D), dtype=torch.float32, device=dev)
+    _req(ht, "ht", torch.float32, 4, dev)
+    nbytes = prefill_workspace_bytes(B, T, H_qk, H_v, D, dtype)
+    ws = _workspace(nbytes, dev, workspace)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(h0), _ptr(o), _ptr(ht),
+            B, T, H_qk, H_v, D, _dt(q), _ptr(ws), nbytes, _stream(dev))
+    return args, o, ht, ws
+
+
+def prefill_chunked(q, k, v, alpha, beta, h0=None, *, o=None, ht=None,
+                    output_final_state=True, workspace=None):
+    """Chunked prefill of B equal-length sequences (gdn_prefill_chunked).
+    q, k [B,T,Hqk,128]; v [B,T,Hv,128] (bf16 or fp32); alpha, beta [B,T,Hv]
+    fp32; h0 [B,Hv,128,128] fp32 or None.  Returns (o, ht)."""
+    args, o, ht, _ = _prefill_args(q, k, v, alpha, beta, h0, o, ht, output_final_state,
+                                   workspace)
+    _check(lib.gdn_prefill_chunked(*args), "gdn_prefill_chunked")
+    return o, ht
+
+
+def prefill_prepare(q, k, v, alpha, beta, h0, o, ht, workspace):
+    """First half of prefill_chunked (gdn_prefill_prepare): in-chunk solve into
+    the workspace.  All buffers are the caller's."""
+    args, _, _, _ = _prefill_args(q, k, v, alpha, beta, h0, o, ht, ht is not None, workspace)
+    _check(lib.gdn_prefill_prepare(*args), "gdn_prefill_prepare")
+
+
+def prefill_scan(q, k, v, alpha, beta, h0, o, ht, workspace):
+    """Second half of prefill_chunked (gdn_prefill_scan): serial carry and
+    outputs, reading what prefill_prepare left in the workspace."""
+    args, _, _, _ = _prefill_args(q, k, v, alpha, beta, h0, o, ht, ht is not None, workspace)
+    _check(lib.gdn_prefill_scan(*args), "gdn_prefill_scan")
+
+
+# ---------------------------------------------------------------- decode
+def decode_step(q, k, v, alpha, beta, state, *, o=None):
+    """One token per sequence (gdn_decode_step); ``state`` [B,Hv,128,128]
+    fp32 is updated in place.  Returns o [B,Hv,128]."""
+    _req(q, "q", ndim=3)
+    dtype, dev = q.dtype, q.device
+    B, H_qk, D = q.shape
+    _req(k, "k", dtype, 3, dev)
+    _req(v, "v", dtype, 3, dev)
+    H_v = v.shape[1]
+    if tuple(k.shape) != (B, H_qk, D) or tuple(v.shape) != (B, H_v, D):
+        raise ValueError("q/k [B,Hqk,D] and v [B,Hv,D] disagree")
+    for name, t in (("alpha", alpha), ("beta", beta)):
+        _req(t, name, torch.float32, 2, dev)
+        if tuple(t.shape) != (B, H_v):
+            raise ValueError("%s must be [B,Hv]" % name)
+    _req(state, "state", torch.float32, 4, dev)
+    if tuple(state.shape) != (B, H_v, D, D):
+        raise ValueError("state must be [B,Hv,D,D]")
+    if o is None:
+        o = torch.empty((B, H_v, D), dtype=dtype, device=dev)
+    _req(o, "o", dtype, 3, dev)
+    rc = lib.gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state),
+                             _ptr(o), B, H_qk, H_v, D, _dt(q), _stream(dev))
+    _check(rc, "gdn_decode_step")
+    return o
+
+
+# ---------------------------------------------------------------- varlen
+def prefill_varlen(q, k, v, alpha, beta, cu_seqlens, h0=None, *, gate=None,
+                   norm_weight=None, norm_eps=1e-6, o=None, ht=None,
+                   output_final_state=True, workspace=None):
+    """Packed sequences (gdn_prefill_varlen).  q, k [T_tot,Hqk,128]; v, gate
+    [T_tot,Hv,128]; alpha, beta [T_tot,Hv]; cu_seqlens int32 [N+1] on the
+    device; h0 [N,Hv,128,128] or None.  Returns (o or gated y, ht)."""
+    _req(q, "q", ndim=3)
+    dtype, dev = q.dtype, q.device
+    T_tot, H_qk, D = q.shape
+    _req(k, "k", dtype, 3, dev)
+    _req(v, "v", dtype, 3, dev)
+    H_v = v.shape[1]
+    if tuple(k.shape) != (T_tot, H_qk, D) or tuple(v.shape) != (T_tot, H_v, D):
+        raise ValueError("q/k [T,Hqk,D] and v [T,Hv,D] disagree")
+    for name, t in (("alpha", alpha), ("beta", beta)):
+        _req(t, name, torch.float32, 2, dev)
+        if tuple(t.shape) != (T_tot, H_v):
+            raise ValueError("%s must be [T_tot,Hv]" % name)
+    _req(cu_seqlens, "cu_seqlens", torch.int32, 1, dev)
+    N = cu_seqlens.shape[0] - 1
+    _req(h0, "h0", torch.float32, 4, dev)
+    if h0 is not None and tuple(h0.shape) != (N, H_v, D, D):
+        raise ValueError("h0 must be [N,Hv,D,D]")
+    _req(gate, "gate", dtype, 3, dev)
+    if gate is not None and tuple(gate.shape) != (T_tot, H_v, D):
+        raise ValueError("gate must be [T_tot,Hv,D]")
+    _req(norm_weight, "norm_weight", torch.float32, 1, dev)
+    if o is None:
+        o = torch.empty((T_tot, H_v, D), dtype=dtype, device=dev)
+    _req(o, "o", dtype, 3, dev)
+    if ht is None and output_final_state:
+        ht = torch.empty((N, H_v, D, D), dtype=torch.float32, device=dev)
+    _req(ht, "ht", torch.float32, 4, dev)
+    nbytes = varlen_workspace_bytes(N, T_tot, H_qk, H_v, D, dtype)
+    ws = _workspace(nbytes, dev, workspace)
+    rc = lib.gdn_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                _ptr(cu_seqlens), N, T_tot, _ptr(h0), _ptr(o), _ptr(ht),
+                                _ptr(gate), _ptr(norm_weight), float(norm_eps), H_qk, H_v, D,
+                                _dt(q), _ptr(ws), nbytes, _stream(dev))
+    _check(rc, "gdn_prefill_varlen")
+    return o, ht

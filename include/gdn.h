@@ -1,0 +1,197 @@
+/*
+ * gdn.h - C ABI of the Gated DeltaNet recurrence library for AMD MI355X
+ * (gfx950).
+ *
+ * The operation.  Each value head keeps a fixed d x d memory matrix S
+ * (page "Inside Qwen3.8-27B: Hybrid DeltaNet Architecture, 256k Context, and
+ * 24GB Local Serving", section "Gated DeltaNet Mechanics": a delta rule that
+ * erases the current association of a normalized key before writing the new
+ * value, under a per-token decay, with a state whose size does not depend on
+ * the context length).  The page's update formula is missing from its text;
+ * the library computes the gated delta rule that has every property the page
+ * lists:
+ *
+ *     S_t = alpha_t * S_{t-1} * (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *     o_t = S_t q_t                                   (state after the update)
+ *
+ * Shapes follow the 27B model's DeltaNet layers (page "Qwen 3.8 27B Review:
+ * Native Vision, FP8 Quantization & 1M Context in a Compact Dense Model",
+ * section 3): 16 query/key heads, 48 value heads, head dim 128.  Value head h
+ * reads query/key head h / (H_v / H_qk): contiguous groups of H_v / H_qk value
+ * heads share one query/key head.  Only D = 128 is supported.
+ *
+ * Prefill uses the block-parallel (chunked) form of the same recurrence (same
+ * page as above, the note under "The Role of Periodic Gated Attention"), 64
+ * tokens per chunk: an in-chunk triangular (UT) solve and a serial carry of the
+ * state from chunk to chunk, with the state resident on chip.  Decode advances
+ * every sequence by one token (same note: sequential at inference).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers of the current HIP device,
+ *    contiguous, row-major, in the layouts given per call.  q, k, v, o and
+ *    gate have the element type `dt`; alpha, beta, states (h0, ht, state) and
+ *    norm_weight are always float32.
+ *  - State layout [.., H_v, D, D]: row = value index, column = key index
+ *    (S is d_v x d_k), so one value row is D contiguous floats.
+ *  - q and k are expected L2-normalised per (token, head) by the caller;
+ *    alpha in (0, 1], beta in [0, 1].  These are preconditions (not checked):
+ *    alpha = 0 is not supported (the chunked form works with log(alpha)).
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *    enqueues work on that stream and returns; it never allocates, frees or
+ *    synchronises.  Device faults surface at the caller's next synchronisation.
+ *  - The caller owns every buffer, including the workspace; the library keeps
+ *    no global mutable state, so calls from several host threads are safe.
+ *  - Every argument check runs on the host before anything is enqueued: a
+ *    call that returns an error has enqueued nothing.
+ *  - Pointers must be 16-byte aligned (alpha, beta: 4-byte).  Outputs must not
+ *    overlap inputs, except that `ht` may be exactly `h0` (in-place carry).
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+typedef int gdn_status;
+#define GDN_OK 0
+#define GDN_ERR_NULL (-1)        /* a required pointer is NULL               */
+#define GDN_ERR_SHAPE (-2)       /* negative or inconsistent sizes          */
+#define GDN_ERR_UNSUPPORTED (-3) /* D != 128, unknown dtype, size overflow  */
+#define GDN_ERR_ALIGN (-4)       /* a pointer is not aligned                */
+#define GDN_ERR_ALIAS (-5)       /* an output overlaps another buffer       */
+#define GDN_ERR_WORKSPACE (-6)   /* workspace missing or too small          */
+#define GDN_ERR_HIP (-7)         /* a HIP launch failed; see gdn_last_hip_error */
+
+/* Tokens per chunk of the block-parallel prefill. */
+#define GDN_CHUNK 64
+
+/*
+ * gdn_prefill_chunked - chunked prefill of B sequences of equal length T.
+ *
+ *   q, k   [B, T, H_qk, D]  dt
+ *   v      [B, T, H_v, D]   dt
+ *   alpha  [B, T, H_v]      float32   per-token decay of the state
+ *   beta   [B, T, H_v]      float32   per-token write strength
+ *   h0     [B, H_v, D, D]   float32   initial state, or NULL for zeros
+ *   o      [B, T, H_v, D]   dt        output o_t = S_t q_t
+ *   ht     [B, H_v, D, D]   float32   final state, or NULL (not written);
+ *                                     may be exactly h0
+ *   workspace, workspace_bytes: at least gdn_prefill_workspace_bytes(...)
+ *                                     bytes of device memory, contents
+ *                                     ignored on entry and clobbered
+ * T = 0 is allowed: then ht receives h0 (or zeros).  The state size, and so
+ * h0/ht, does not depend on T.
+ */
+gdn_status gdn_prefill_chunked(const void *q, const void *k, const void *v,
+                               const float *alpha, const float *beta,
+                               const float *h0, void *o, float *ht,
+                               int32_t B, int32_t T, int32_t H_qk, int32_t H_v,
+                               int32_t D, gdn_dtype dt, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/* Workspace bytes for gdn_prefill_chunked (0 on unsupported arguments).
+ * Grows with the number of chunks (per-chunk solve results), never with the
+ * state. */
+size_t gdn_prefill_workspace_bytes(int32_t B, int32_t T, int32_t H_qk,
+                                   int32_t H_v, int32_t D, gdn_dtype dt);
+
+/*
+ * The two stream-ordered halves of gdn_prefill_chunked, same arguments.
+ * gdn_prefill_prepare runs the fully parallel in-chunk part (gate prefix,
+ * Gram matrices, triangular solve) into the workspace; gdn_prefill_scan runs
+ * the serial inter-chunk state carry and the outputs from it.  Calling
+ * prepare then scan on one stream with one workspace is exactly
+ * gdn_prefill_chunked.  They exist so that each half can be timed alone.
+ */
+gdn_status gdn_prefill_prepare(const void *q, const void *k, const void *v,
+                               const float *alpha, const float *beta,
+                               const float *h0, void *o, float *ht,
+                               int32_t B, int32_t T, int32_t H_qk, int32_t H_v,
+                               int32_t D, gdn_dtype dt, void *workspace,
+                               size_t workspace_bytes, void *stream);
+gdn_status gdn_prefill_scan(const void *q, const void *k, const void *v,
+                            const float *alpha, const float *beta,
+                            const float *h0, void *o, float *ht,
+                            int32_t B, int32_t T, int32_t H_qk, int32_t H_v,
+                            int32_t D, gdn_dtype dt, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/*
+ * gdn_decode_step - one token for each of B sequences, state updated in place
+ * (page "Inside Qwen3.8-27B ...", note under "The Role of Periodic Gated
+ * Attention": at inference the state advances one token at a time).
+ *
+ *   q, k   [B, H_qk, D]     dt
+ *   v      [B, H_v, D]      dt
+ *   alpha, beta [B, H_v]    float32
+ *   state  [B, H_v, D, D]   float32, read and overwritten with S_t
+ *   o      [B, H_v, D]      dt
+ * No workspace.  The update is not transactional: a caller that may need
+ * the previous state keeps a copy.
+ */
+gdn_status gdn_decode_step(const void *q, const void *k, const void *v,
+                           const float *alpha, const float *beta, float *state,
+                           void *o, int32_t B, int32_t H_qk, int32_t H_v,
+                           int32_t D, gdn_dtype dt, void *stream);
+
+/*
+ * gdn_prefill_varlen - N sequences of different lengths packed along the
+ * token axis (several concurrent sequences, as a serving engine batches them:
+ * page "Inside Qwen3.8-27B ...", section "Serving Qwen3.8-27B: Recipes for
+ * vLLM and SGLang").  Each sequence is an independent recurrence from its own
+ * initial state; chunks restart at every sequence start.
+ *
+ *   q, k        [T_tot, H_qk, D]  dt
+ *   v           [T_tot, H_v, D]   dt
+ *   alpha, beta [T_tot, H_v]      float32
+ *   cu_seqlens  [N + 1]           int32 DEVICE pointer: cu_seqlens[0] = 0,
+ *                                 non-decreasing, cu_seqlens[N] = T_tot
+ *                                 (precondition; never read on the host).
+ *                                 Zero-length sequences are allowed.
+ *   h0          [N, H_v, D, D]    float32 or NULL (zeros)
+ *   o           [T_tot, H_v, D]   dt
+ *   ht          [N, H_v, D, D]    float32 or NULL; may be exactly h0
+ *   gate        [T_tot, H_v, D]   dt or NULL.  When given, o receives
+ *                 y = o_t / sqrt(mean_d(o_t^2) + norm_eps) * w * sigmoid(gate)
+ *                 per (token, head): an RMS normalisation over the head dim
+ *                 (as the card "Qwen3.8 (27B)" describes RMSNorm for QK-Norm)
+ *                 followed by a learned sigmoid output gate (as the same card
+ *                 describes Gated Attention's output gate).
+ *   norm_weight [D] float32 or NULL (all ones); used only with gate.
+ *   workspace   at least gdn_varlen_workspace_bytes(...) bytes.
+ */
+gdn_status gdn_prefill_varlen(const void *q, const void *k, const void *v,
+                              const float *alpha, const float *beta,
+                              const int32_t *cu_seqlens, int32_t N,
+                              int32_t T_tot, const float *h0, void *o,
+                              float *ht, const void *gate,
+                              const float *norm_weight, float norm_eps,
+                              int32_t H_qk, int32_t H_v, int32_t D,
+                              gdn_dtype dt, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/* Workspace bytes for gdn_prefill_varlen.  Sized for ceil(T_tot/64) + N
+ * chunks, so the host never needs to read cu_seqlens. */
+size_t gdn_varlen_workspace_bytes(int32_t N, int32_t T_tot, int32_t H_qk,
+                                  int32_t H_v, int32_t D, gdn_dtype dt);
+
+/* Human-readable name of a status code (static string). */
+const char *gdn_status_str(gdn_status s);
+
+/* The hipError_t of the last failed launch on the calling thread (0 if none). */
+int gdn_last_hip_error(void);
+
+/* ABI version: 100 * major + minor. */
+int gdn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDN_H */

@@ -1,0 +1,196 @@
+"""Host-only checks of the C ABI: the library loads, exports every entry point
+include/gdn.h declares, sizes workspaces as documented, and rejects bad
+arguments with the documented status code before anything is enqueued.
+
+Every call here fails validation on purpose (fake, never-dereferenced device
+addresses), so no kernel is launched and no GPU is needed.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+OK, ENULL, ESHAPE, EUNSUP, EALIGN, EALIAS, EWS, EHIP = 0, -1, -2, -3, -4, -5, -6, -7
+F32, BF16 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def gdn():
+    from hybrid_linear_attention_amd import gdn as g
+    return g
+
+
+@pytest.fixture(scope="module")
+def lib(gdn):
+    return gdn.lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("gdn_prefill_chunked", "gdn_decode_step", "gdn_prefill_varlen"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(gdn):
+    for code in (OK, ENULL, ESHAPE, EUNSUP, EALIGN, EALIAS, EWS, EHIP):
+        s = gdn.status_str(code)
+        assert s.startswith("GDN_")
+    assert "unknown" in gdn.status_str(12345)
+    assert gdn.abi_version() == 100
+
+
+def test_workspace_sizes(gdn):
+    # per chunk: Tt (48 x 64 x 64) + QK (16 x 64 x 64) elements + G (48 x 64) fp32
+    per_chunk_bf16 = 48 * 4096 * 2 + 16 * 4096 * 2 + 48 * 64 * 4
+    assert gdn.prefill_workspace_bytes(1, 0, 16, 48) == 0
+    w1 = gdn.prefill_workspace_bytes(1, 64, 16, 48)
+    w2 = gdn.prefill_workspace_bytes(1, 128, 16, 48)
+    w3 = gdn.prefill_workspace_bytes(1, 65, 16, 48)
+    assert w2 - w1 == per_chunk_bf16
+    assert w3 == w2                       # a ragged tail is one more chunk
+    assert gdn.prefill_workspace_bytes(2, 64, 16, 48) == w2
+    w32 = gdn.prefill_workspace_bytes(1, 64, 16, 48, dtype=__import__("torch").float32)
+    assert w32 > w1
+    # the state never lives in the workspace: nothing in it scales with D*D per head
+    assert w1 < 48 * 128 * 128 * 4
+    assert gdn.prefill_workspace_bytes(1, 64, 16, 48, D=64) == 0
+    assert gdn.prefill_workspace_bytes(1, 64, 16, 47) == 0
+    # varlen: ceil(T_tot/64) + N chunks plus the chunk table
+    assert gdn.varlen_workspace_bytes(3, 100, 16, 48) >= gdn.prefill_workspace_bytes(1, 64 * 5, 16, 48)
+
+
+# fake device addresses, 256-byte aligned and far apart (never dereferenced)
+BASE = 0x7F0000000000
+STRIDE = 1 << 36
+
+
+def addr(i, off=0):
+    return ctypes.c_void_p(BASE + i * STRIDE + off)
+
+
+def prefill_call(lib, name="gdn_prefill_chunked", **kw):
+    args = dict(q=addr(0), k=addr(1), v=addr(2), alpha=addr(3), beta=addr(4), h0=addr(5),
+                o=addr(6), ht=addr(7), B=1, T=128, Hqk=16, Hv=48, D=128, dt=BF16,
+                ws=addr(8), ws_bytes=1 << 40, stream=None)
+    args.update(kw)
+    fn = getattr(lib, name)
+    return fn(args["q"], args["k"], args["v"], args["alpha"], args["beta"], args["h0"],
+              args["o"], args["ht"], args["B"], args["T"], args["Hqk"], args["Hv"], args["D"],
+              args["dt"], args["ws"], args["ws_bytes"], args["stream"])
+
+
+@pytest.mark.parametrize("name", ["gdn_prefill_chunked", "gdn_prefill_prepare", "gdn_prefill_scan"])
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=64), EUNSUP),
+    (dict(dt=7), EUNSUP),
+    (dict(Hv=47), ESHAPE),
+    (dict(Hqk=0), ESHAPE),
+    (dict(T=-1), ESHAPE),
+    (dict(B=-2), ESHAPE),
+    (dict(q=None), ENULL),
+    (dict(alpha=None), ENULL),
+    (dict(o=None), ENULL),
+    (dict(ws=None), EWS),
+    (dict(ws_bytes=1000), EWS),
+    (dict(q=addr(0, 8)), EALIGN),
+    (dict(alpha=addr(3, 2)), EALIGN),
+    (dict(ht=addr(7, 4)), EALIGN),
+    (dict(o=addr(0, 256)), EALIAS),           # o inside q
+    (dict(ht=addr(5, 1024)), EALIAS),         # ht overlaps h0 without being h0
+    (dict(ws=addr(6, 4096)), EALIAS),         # workspace inside o
+    (dict(ht=addr(2)), EALIAS),               # ht is v
+])
+def test_prefill_validation(lib, name, kw, code):
+    assert prefill_call(lib, name, **kw) == code
+
+
+def decode_call(lib, **kw):
+    args = dict(q=addr(0), k=addr(1), v=addr(2), alpha=addr(3), beta=addr(4), state=addr(5),
+                o=addr(6), B=64, Hqk=16, Hv=48, D=128, dt=BF16, stream=None)
+    args.update(kw)
+    return lib.gdn_decode_step(args["q"], args["k"], args["v"], args["alpha"], args["beta"],
+                               args["state"], args["o"], args["B"], args["Hqk"], args["Hv"],
+                               args["D"], args["dt"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=256), EUNSUP),
+    (dict(Hv=40, Hqk=16), ESHAPE),
+    (dict(B=-1), ESHAPE),
+    (dict(state=None), ENULL),
+    (dict(beta=None), ENULL),
+    (dict(v=addr(2, 4)), EALIGN),
+    (dict(o=addr(5, 512)), EALIAS),           # o inside the state
+    (dict(state=addr(0, 0)), EALIAS),         # state is q
+])
+def test_decode_validation(lib, kw, code):
+    assert decode_call(lib, **kw) == code
+
+
+def test_decode_empty_batch_is_a_no_op(lib):
+    assert decode_call(lib, B=0) == OK
+
+
+def varlen_call(lib, **kw):
+    args = dict(q=addr(0), k=addr(1), v=addr(2), alpha=addr(3), beta=addr(4), cu=addr(9),
+                N=4, T_tot=1000, h0=addr(5), o=addr(6), ht=addr(7), gate=addr(10),
+                w=addr(11), eps=1e-6, Hqk=16, Hv=48, D=128, dt=BF16, ws=addr(8),
+                ws_bytes=1 << 40, stream=None)
+    args.update(kw)
+    return lib.gdn_prefill_varlen(args["q"], args["k"], args["v"], args["alpha"], args["beta"],
+                                  args["cu"], args["N"], args["T_tot"], args["h0"], args["o"],
+                                  args["ht"], args["gate"], args["w"], args["eps"], args["Hqk"],
+                                  args["Hv"], args["D"], args["dt"], args["ws"],
+                                  args["ws_bytes"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=64), EUNSUP),
+    (dict(N=-1), ESHAPE),
+    (dict(N=0), ESHAPE),                      # tokens but no sequences
+    (dict(cu=None), ENULL),
+    (dict(eps=-1.0), ESHAPE),
+    (dict(eps=float("nan")), ESHAPE),
+    (dict(ws_bytes=10), EWS),
+    (dict(cu=addr(9, 2)), EALIGN),
+    (dict(gate=addr(10, 8)), EALIGN),
+    (dict(o=addr(10, 0)), EALIAS),            # o is the gate
+    (dict(ws=addr(9, 0)), EALIAS),            # workspace over cu_seqlens
+])
+def test_varlen_validation(lib, kw, code):
+    assert varlen_call(lib, **kw) == code
+
+
+def test_varlen_empty_is_a_no_op(lib):
+    assert varlen_call(lib, N=0, T_tot=0) == OK
+
+
+def test_binding_rejects_bad_tensors(gdn):
+    import torch
+    q = torch.zeros(1, 64, 16, 128)
+    with pytest.raises(ValueError):
+        gdn.prefill_chunked(q, q, torch.zeros(1, 64, 48, 64), torch.zeros(1, 64, 48),
+                            torch.zeros(1, 64, 48))
+    with pytest.raises(TypeError):
+        gdn.prefill_chunked(q.half(), q.half(), torch.zeros(1, 64, 48, 128).half(),
+                            torch.zeros(1, 64, 48), torch.zeros(1, 64, 48))
+    with pytest.raises(ValueError):
+        gdn.decode_step(torch.zeros(2, 16, 128), torch.zeros(2, 16, 128), torch.zeros(2, 48, 128),
+                        torch.zeros(2, 48), torch.zeros(2, 48), torch.zeros(2, 48, 128, 64))

@@ -1,0 +1,349 @@
+"""GPU parity: the HIP library, called through its C ABI, against the float64
+oracle on the same seeded inputs.
+
+Tolerances (relative L2 error per tensor, e = ||x - ref|| / ||ref||, float64):
+* fp32 inputs: 1e-5;  bf16 inputs: 2e-2.
+
+Small cases span several 64-token chunks and a ragged tail and are checked on
+every element; the full-size workloads run in the benchmark's launch
+configuration and are checked in full (T = 8192 prefill, 64 x 256 decode) or
+on sampled value heads that the oracle computes one by one (T = 262,144 and
+the packed varlen batch).
+"""
+import os
+import sys
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-2}
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def gdn():
+    from hybrid_linear_attention_amd import gdn as g
+    return g
+
+
+def rel(x, ref):
+    x = x.detach().cpu().double().numpy() if isinstance(x, torch.Tensor) else np.asarray(x)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.linalg.norm(ref)
+    return float(np.linalg.norm(x - ref) / (den if den > 0 else 1.0))
+
+
+def to_dev(d):
+    return {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+
+
+def run_prefill(gdn, inp, h0=True):
+    d = to_dev(inp)
+    o, ht = gdn.prefill_chunked(d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                                d["h0"] if h0 else None)
+    torch.cuda.synchronize()
+    return o, ht
+
+
+def oracle_prefill(inp, h0=True):
+    return oracle.prefill(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"],
+                          inp["h0"] if h0 else None)
+
+
+# ------------------------------------------------------------------ small prefill
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+@pytest.mark.parametrize("B,T,h0std", [(1, 64, 0.0), (1, 200, 0.02), (2, 130, 0.02),
+                                       (1, 1, 0.02), (3, 63, 0.0), (1, 321, 0.5)])
+def test_prefill_small(gdn, dtype, B, T, h0std):
+    say("prefill_small", dtype, B, T, h0std)
+    inp = synth.prefill_inputs(B, T, dtype, seed=7 + T + B, h0_std=h0std)
+    o, ht = run_prefill(gdn, inp)
+    o_ref, ht_ref = oracle_prefill(inp)
+    eo, eh = rel(o, o_ref), rel(ht, ht_ref)
+    say("  rel o %.3e ht %.3e" % (eo, eh))
+    assert eo <= TOL[dtype] and eh <= TOL[dtype]
+    # element-wise: no single output far off (guards against a masked-row bug
+    # hiding in the norm)
+    err = np.abs(o.cpu().double().numpy() - o_ref).max() / np.abs(o_ref).max()
+    assert err <= 20 * TOL[dtype]
+
+
+def test_prefill_T0_passes_state(gdn):
+    inp = synth.prefill_inputs(2, 0, torch.bfloat16, seed=3, h0_std=0.1)
+    o, ht = run_prefill(gdn, inp)
+    assert o.shape == (2, 0, 48, 128)
+    assert torch.equal(ht.cpu(), inp["h0"])
+
+
+def test_prefill_without_h0_and_without_ht(gdn):
+    inp = synth.prefill_inputs(1, 100, torch.bfloat16, seed=4)
+    d = to_dev(inp)
+    o, ht = gdn.prefill_chunked(d["q"], d["k"], d["v"], d["alpha"], d["beta"], None,
+                                output_final_state=False)
+    torch.cuda.synchronize()
+    assert ht is None
+    o_ref, _ = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], None)
+    assert rel(o, o_ref) <= 2e-2
+
+
+def test_prepare_then_scan_equals_chunked(gdn):
+    inp = to_dev(synth.prefill_inputs(1, 300, torch.bfloat16, seed=5, h0_std=0.02))
+    o1, ht1 = gdn.prefill_chunked(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["h0"])
+    o2 = torch.empty_like(o1)
+    ht2 = torch.empty_like(ht1)
+    ws = torch.empty(gdn.prefill_workspace_bytes(1, 300, 16, 48), dtype=torch.uint8, device=DEV)
+    gdn.prefill_prepare(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["h0"], o2, ht2, ws)
+    gdn.prefill_scan(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["h0"], o2, ht2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(ht1, ht2)
+
+
+def test_prefill_deterministic(gdn):
+    inp = synth.prefill_inputs(1, 500, torch.bfloat16, seed=6, h0_std=0.02)
+    o1, ht1 = run_prefill(gdn, inp)
+    o2, ht2 = run_prefill(gdn, inp)
+    assert torch.equal(o1, o2) and torch.equal(ht1, ht2)
+
+
+def test_prefill_in_place_carry_and_split(gdn):
+    """ht may be exactly h0; two calls with the state carried equal one call."""
+    T1, T2 = 130, 77
+    inp = synth.prefill_inputs(1, T1 + T2, torch.bfloat16, seed=8, h0_std=0.02)
+    d = to_dev(inp)
+    o_all, ht_all = gdn.prefill_chunked(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["h0"])
+    st = d["h0"].clone()
+    sl1 = [x[:, :T1].contiguous() for x in (d["q"], d["k"], d["v"], d["alpha"], d["beta"])]
+    sl2 = [x[:, T1:].contiguous() for x in (d["q"], d["k"], d["v"], d["alpha"], d["beta"])]
+    o1, _ = gdn.prefill_chunked(*sl1, st, ht=st)
+    o2, _ = gdn.prefill_chunked(*sl2, st, ht=st)
+    torch.cuda.synchronize()
+    o_ref, ht_ref = oracle_prefill(inp)
+    assert rel(torch.cat([o1, o2], 1), o_ref) <= 2e-2
+    assert rel(st, ht_ref) <= 2e-2
+    assert rel(o_all, o_ref) <= 2e-2 and rel(ht_all, ht_ref) <= 2e-2
+
+
+def test_prefill_identity_invariant_fp32(gdn):
+    """beta = 0, alpha = 1: the state is untouched and o_t = S0 q_t."""
+    inp = synth.prefill_inputs(1, 150, torch.float32, seed=9, h0_std=0.3)
+    inp["beta"].zero_()
+    inp["alpha"].fill_(1.0)
+    o, ht = run_prefill(gdn, inp)
+    assert rel(ht, inp["h0"].double().numpy()) <= 1e-6
+    S0 = inp["h0"][0].double()
+    qh = inp["q"][0].double()[:, torch.arange(48) // 3]           # [T,48,D]
+    ref = torch.einsum("hij,thj->thi", S0, qh)
+    assert rel(o[0], ref.numpy()) <= 1e-5
+
+
+def test_prefill_orthonormal_retrieval_fp32(gdn):
+    """alpha = beta = 1, orthonormal keys, S0 = 0: querying with k_t returns v_t."""
+    T = 128
+    g = torch.Generator().manual_seed(11)
+    keys = []
+    for _ in range(16):
+        Qm, _ = torch.linalg.qr(torch.randn(128, 128, generator=g, dtype=torch.float64))
+        keys.append(Qm.T[:T])
+    k = torch.stack(keys, 1)[None].float().contiguous()           # [1,T,16,128]
+    v = torch.randn(1, T, 48, 128, generator=g).contiguous()
+    ones = torch.ones(1, T, 48)
+    inp = dict(q=k.clone(), k=k, v=v, alpha=ones.clone(), beta=ones.clone(), h0=None)
+    o, ht = run_prefill(gdn, inp, h0=False)
+    assert rel(o, v.double().numpy()) <= 1e-5
+
+
+def test_head_map_contiguous_groups(gdn):
+    """Value head h reads query/key head h // 3: permuting query/key heads
+    permutes exactly the matching value-head groups."""
+    inp = synth.prefill_inputs(1, 96, torch.float32, seed=12, h0_std=0.0)
+    o, _ = run_prefill(gdn, inp, h0=False)
+    perm = torch.tensor([1, 0] + list(range(2, 16)))
+    inp2 = dict(inp)
+    inp2["q"] = inp["q"][:, :, perm].contiguous()
+    inp2["k"] = inp["k"][:, :, perm].contiguous()
+    vperm = torch.cat([torch.arange(3, 6), torch.arange(0, 3), torch.arange(6, 48)])
+    inp2["v"] = inp["v"][:, :, vperm].contiguous()
+    inp2["alpha"] = inp["alpha"][:, :, vperm].contiguous()
+    inp2["beta"] = inp["beta"][:, :, vperm].contiguous()
+    o2, _ = run_prefill(gdn, inp2, h0=False)
+    assert torch.allclose(o2[:, :, vperm], o, rtol=0, atol=1e-6)
+
+
+# ------------------------------------------------------------------ decode
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+def test_decode_small(gdn, dtype):
+    B, steps = 5, 6
+    say("decode_small", dtype)
+    st = synth.decode_state(B, seed=21, std=0.05).to(DEV)
+    ref = st.cpu().double().numpy().copy()
+    worst = 0.0
+    for s in range(steps):
+        d = synth.decode_step_inputs(B, s, dtype, seed=21)
+        dd = to_dev(d)
+        o = gdn.decode_step(dd["q"], dd["k"], dd["v"], dd["alpha"], dd["beta"], st)
+        o_ref, ref = oracle.decode_step(d["q"], d["k"], d["v"], d["alpha"], d["beta"], ref,
+                                         inplace=True)
+        torch.cuda.synchronize()
+        worst = max(worst, rel(o, o_ref))
+    worst = max(worst, rel(st, ref))
+    say("  worst rel %.3e" % worst)
+    assert worst <= TOL[dtype]
+
+
+def test_decode_steps_equal_fp32_prefill(gdn):
+    """256 fp32 decode steps reach the fp32 chunked prefill of the same tokens."""
+    T = 256
+    inp = synth.prefill_inputs(1, T, torch.float32, seed=22, h0_std=0.02)
+    o_p, ht_p = run_prefill(gdn, inp)
+    d = to_dev(inp)
+    st = d["h0"].clone()
+    outs = []
+    for t in range(T):
+        outs.append(gdn.decode_step(d["q"][:, t].contiguous(), d["k"][:, t].contiguous(),
+                                    d["v"][:, t].contiguous(), d["alpha"][:, t].contiguous(),
+                                    d["beta"][:, t].contiguous(), st))
+    torch.cuda.synchronize()
+    o_d = torch.stack(outs, 1)
+    assert rel(o_d, o_p.cpu().double().numpy()) <= 1e-5
+    assert rel(st, ht_p.cpu().double().numpy()) <= 1e-5
+
+
+# ------------------------------------------------------------------ varlen
+@pytest.mark.parametrize("gated", [False, True], ids=["plain", "gated"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+def test_varlen_small(gdn, dtype, gated):
+    lengths = [1, 64, 0, 130, 65, 257]
+    say("varlen_small", dtype, gated)
+    inp = synth.varlen_inputs(lengths, dtype=dtype, seed=31, h0_std=0.05, gate=gated)
+    d = to_dev(inp)
+    w = torch.linspace(0.5, 1.5, 128)
+    y, ht = gdn.prefill_varlen(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["cu_seqlens"],
+                               d["h0"], gate=d["gate"], norm_weight=w.to(DEV) if gated else None,
+                               norm_eps=1e-6)
+    torch.cuda.synchronize()
+    y_ref, ht_ref = oracle.varlen(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"],
+                                  inp["cu_seqlens"].numpy(), inp["h0"], gate=inp["gate"],
+                                  norm_weight=w.numpy() if gated else None, eps=1e-6)
+    cu = inp["cu_seqlens"].tolist()
+    for n in range(len(lengths)):
+        s, e = cu[n], cu[n + 1]
+        if e > s:
+            assert rel(y[s:e], y_ref[s:e]) <= TOL[dtype], n
+        assert rel(ht[n], ht_ref[n]) <= TOL[dtype], n
+    assert torch.equal(ht[2].cpu(), inp["h0"][2])          # empty sequence
+
+
+def test_varlen_equals_separate_calls(gdn):
+    lengths = [100, 7, 200]
+    inp = to_dev(synth.varlen_inputs(lengths, dtype=torch.bfloat16, seed=32, h0_std=0.02, gate=False))
+    y, ht = gdn.prefill_varlen(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"],
+                               inp["cu_seqlens"], inp["h0"])
+    cu = inp["cu_seqlens"].tolist()
+    for n in range(3):
+        s, e = cu[n], cu[n + 1]
+        o_n, ht_n = gdn.prefill_chunked(*(x[None, s:e].contiguous() for x in
+                                          (inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"])),
+                                        inp["h0"][n:n + 1].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(o_n[0], y[s:e])
+        assert torch.equal(ht_n[0], ht[n])
+
+
+# ------------------------------------------------------------------ full-size workloads
+def test_config0_T256_fp32(gdn):
+    c = synth.CONFIGS[0]
+    inp = synth.config_inputs(0)
+    o, ht = run_prefill(gdn, inp, h0=False)
+    o_ref, ht_ref = oracle_prefill(inp, h0=False)
+    eo, eh = rel(o, o_ref), rel(ht, ht_ref)
+    say("config0 rel o %.3e ht %.3e" % (eo, eh))
+    assert eo <= 1e-5 and eh <= 1e-5 and c["dtype"] == torch.float32
+
+
+def test_config1_T8192_bf16(gdn):
+    inp = synth.config_inputs(1)
+    t0 = time.time()
+    o, ht = run_prefill(gdn, inp, h0=False)
+    o_ref, ht_ref = oracle_prefill(inp, h0=False)
+    eo, eh = rel(o, o_ref), rel(ht, ht_ref)
+    say("config1 rel o %.3e ht %.3e (%.1fs)" % (eo, eh, time.time() - t0))
+    assert eo <= 2e-2 and eh <= 2e-2
+
+
+def test_config2_decode_64x256_bf16(gdn):
+    c = synth.CONFIGS[2]
+    B, steps = c["B"], c["steps"]
+    st = synth.decode_state(B, c["seed"], c["h0_std"])
+    ref = st.double().numpy().copy()
+    st = st.to(DEV)
+    worst = 0.0
+    t0 = time.time()
+    for s in range(steps):
+        d = synth.decode_step_inputs(B, s, c["dtype"], seed=c["seed"])
+        dd = to_dev(d)
+        o = gdn.decode_step(dd["q"], dd["k"], dd["v"], dd["alpha"], dd["beta"], st)
+        o_ref, ref = oracle.decode_step(d["q"], d["k"], d["v"], d["alpha"], d["beta"], ref,
+                                         inplace=True)
+        worst = max(worst, rel(o, o_ref))
+        if s % 64 == 0:
+            say("  decode step %d worst %.3e (%.1fs)" % (s, worst, time.time() - t0))
+    worst = max(worst, rel(st, ref))
+    say("config2 worst rel %.3e" % worst)
+    assert worst <= 2e-2
+
+
+def test_config3_T262144_sampled_heads(gdn):
+    c = synth.CONFIGS[3]
+    inp = synth.config_inputs(3)
+    say("config3 inputs ready")
+    o, ht = run_prefill(gdn, inp)
+    heads = [0, 25, 47]
+    sub = oracle.subset_heads(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"],
+                              inp["h0"], heads, 16, 48)
+    t0 = time.time()
+    o_ref, ht_ref = oracle.prefill(*sub)
+    say("config3 oracle %.1fs" % (time.time() - t0))
+    for i, h in enumerate(heads):
+        eo, eh = rel(o[0, :, h], o_ref[0, :, i]), rel(ht[0, h], ht_ref[0, i])
+        say("config3 head %d rel o %.3e ht %.3e" % (h, eo, eh))
+        assert eo <= 2e-2 and eh <= 2e-2
+    assert c["T"] == 262144
+
+
+def test_config4_varlen_sampled_heads(gdn):
+    c = synth.CONFIGS[4]
+    inp = synth.config_inputs(4)
+    say("config4 lengths", inp["lengths"])
+    d = to_dev(inp)
+    y, ht = gdn.prefill_varlen(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["cu_seqlens"],
+                               d["h0"], gate=d["gate"], norm_eps=1e-6)
+    torch.cuda.synchronize()
+    heads = [4, 31]
+    q_s, k_s, v_s, a_s, b_s, h_s = oracle.subset_heads(inp["q"], inp["k"], inp["v"],
+                                                       inp["alpha"], inp["beta"], inp["h0"],
+                                                       heads, 16, 48)
+    gate_s = inp["gate"][:, heads]
+    t0 = time.time()
+    y_ref, ht_ref = oracle.varlen(q_s, k_s, v_s, a_s, b_s, inp["cu_seqlens"].numpy(), h_s,
+                                  gate=gate_s, eps=1e-6)
+    say("config4 oracle %.1fs" % (time.time() - t0))
+    cu = inp["cu_seqlens"].tolist()
+    for n in range(c["N"]):
+        s, e = cu[n], cu[n + 1]
+        for i, h in enumerate(heads):
+            ey = rel(y[s:e, h], y_ref[s:e, i])
+            eh = rel(ht[n, h], ht_ref[n, i])
+            assert ey <= 2e-2 and eh <= 2e-2, (n, h, ey, eh)
+    say("config4 ok")
