@@ -127,12 +127,17 @@ def prefill(q, k, v, alpha, beta, h0=None):
     return o, ht
 
 
-def decode_step(q, k, v, alpha, beta, state):
+def decode_step(q, k, v, alpha, beta, state, inplace=False):
     """One token per sequence.  q, k ``[B,Hqk,D]``; v ``[B,Hv,D]``;
-    alpha, beta ``[B,Hv]``; state ``[B,Hv,D,D]``.  Returns ``(o, new_state)``;
-    the input state is not modified."""
+    alpha, beta ``[B,Hv]``; state ``[B,Hv,D,D]``.  Returns ``(o, new_state)``.
+    With ``inplace=True`` and a C-contiguous float64 ndarray state, that array
+    is advanced in place and returned; otherwise the input is not modified."""
     q, k, v, alpha, beta = (_f64(x) for x in (q, k, v, alpha, beta))
-    st = _f64(state).copy()
+    if (inplace and isinstance(state, np.ndarray) and state.dtype == np.float64
+            and state.flags.c_contiguous):
+        st = state
+    else:
+        st = _f64(state).copy()
     B, Hqk, D = q.shape
     Hv = v.shape[1]
     assert st.shape == (B, Hv, D, D)
@@ -205,13 +210,20 @@ def subset_heads(q, k, v, alpha, beta, h0, heads, Hqk, Hv):
     heads = np.asarray(heads, dtype=np.int64)
     G = Hv // Hqk
     qk_idx = heads // G
-    pick = lambda x, idx, ax: np.ascontiguousarray(np.take(x, idx, axis=ax))
-    q_s = pick(_f64(q), qk_idx, -2)
-    k_s = pick(_f64(k), qk_idx, -2)
-    v_s = pick(_f64(v), heads, -2)
-    a_s = pick(_f64(alpha), heads, -1)
-    b_s = pick(_f64(beta), heads, -1)
-    h_s = None if h0 is None else pick(_f64(h0), heads, 1)
+
+    def pick(x, idx, ax):
+        if hasattr(x, "index_select"):            # gather before widening
+            import torch
+            x = x.index_select(ax % x.dim(), torch.as_tensor(idx))
+            return np.ascontiguousarray(_f64(x))
+        return np.ascontiguousarray(np.take(_f64(x), idx, axis=ax))
+
+    q_s = pick(q, qk_idx, -2)
+    k_s = pick(k, qk_idx, -2)
+    v_s = pick(v, heads, -2)
+    a_s = pick(alpha, heads, -1)
+    b_s = pick(beta, heads, -1)
+    h_s = None if h0 is None else pick(h0, heads, 1)
     return q_s, k_s, v_s, a_s, b_s, h_s
 
 
