@@ -1,0 +1,227 @@
+"""Benchmark of the Gated DeltaNet recurrence on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--decode-steps S] [--extended] [--copy-calibration]
+
+One step = one chunked prefill call of the T = 8192 workload (batch 1, 16
+query/key heads, 48 value heads, head dim 128, bf16 q/k/v, fp32 gates, zero
+initial state, final state emitted): the prepare kernel followed by the scan
+kernel, on inputs already resident in HBM.  The decode workload (64 sequences
+x 1 token, fp32 state 64 x 48 x 128 x 128 updated in place) is timed in the
+same run and reported under "decode".  Prints one JSON line.
+
+Rates:
+* prefill: tokens/s = T / step time; TFLOP/s from the method's algorithmic
+  FLOP count per call (below), against the dense bf16 MFMA peak;
+* decode: state GB/s = 2 x 64 x 48 x 128 x 128 x 4 bytes / step time,
+  against the HBM peak.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+import synth
+
+D, C, HQK, HV = 128, 64, 16, 48
+PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
+
+
+def prefill_flops(T, B=1):
+    """Algorithmic FLOPs of one chunked prefill call: per chunk and value head
+    6Cd^2 + 6C^2d + C^3/3, plus 4C^2d per chunk and query/key head (the two
+    Gram matrices, shared by the value heads of the group)."""
+    nc = B * ((T + C - 1) // C)
+    return nc * (HV * (6 * C * D * D + 6 * C * C * D + C ** 3 / 3) + HQK * 4 * C * C * D)
+
+
+def scan_flops(T, B=1):
+    """Algorithmic FLOPs of the scan kernel per launch: per chunk and value
+    head, K S^T, Q S^T and the state update (2Cd^2 each) plus Tt X and M Dl
+    (2C^2d each)."""
+    nc = B * ((T + C - 1) // C)
+    return nc * HV * (6 * C * D * D + 4 * C * C * D)
+
+
+def decode_state_bytes(B):
+    return 2 * B * HV * D * D * 4
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def timed_prefill(gdn, inp, steps, warmup):
+    dev = inp["q"].device
+    T = inp["q"].shape[1]
+    o = torch.empty((1, T, HV, D), dtype=inp["q"].dtype, device=dev)
+    ht = torch.empty((1, HV, D, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(gdn.prefill_workspace_bytes(1, T, HQK, HV, D, inp["q"].dtype),
+                     dtype=torch.uint8, device=dev)
+    args = (inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], None, o, ht, ws)
+    for _ in range(warmup):
+        gdn.prefill_prepare(*args)
+        gdn.prefill_scan(*args)
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        gdn.prefill_prepare(*args)
+        ev[i][1].record(stream)
+        gdn.prefill_scan(*args)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prep = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    scan = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    step = ev[0][0].elapsed_time(ev[-1][2]) / steps
+    return dict(step_ms=step, prepare_ms=prep, scan_ms=scan, wall_s=wall)
+
+
+def timed_decode(gdn, B, steps, warmup, dtype=torch.bfloat16):
+    dev = "cuda:0"
+    state = synth.decode_state(B, 1002, 0.02).to(dev)
+    sets = [{k: v.to(dev) for k, v in synth.decode_step_inputs(B, s, dtype, seed=1002).items()}
+            for s in range(4)]
+    o = torch.empty((B, HV, D), dtype=dtype, device=dev)
+
+    def step(i):
+        d = sets[i % len(sets)]
+        gdn.decode_step(d["q"], d["k"], d["v"], d["alpha"], d["beta"], state, o=o)
+
+    for i in range(warmup):
+        step(i)
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    gbs = decode_state_bytes(B) / (ms * 1e-3) / 1e9
+    return dict(step_ms=ms, gbs=gbs)
+
+
+def cpu_baseline(inp, T_sample):
+    """The float64 oracle, untuned, on a bounded sample of the same workload:
+    the first T_sample tokens of every value head."""
+    import oracle
+    oracle.build(force=False)
+    sl = {k: inp[k][:, :T_sample].cpu() for k in ("q", "k", "v", "alpha", "beta")}
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    oracle.prefill(sl["q"], sl["k"], sl["v"], sl["alpha"], sl["beta"], None)
+    dt = time.perf_counter() - t0
+    return dict(value=T_sample / dt, unit="tokens/s", cores=threads, kind="oracle",
+                sample="first %d of 8192 tokens, all 48 value heads, batch 1, float64 "
+                       "sequential recurrence (%.1f s)" % (T_sample, dt))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=8192)
+    ap.add_argument("--extended", action="store_true",
+                    help="also time the T=262,144 prefill and the packed varlen batch")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one plain 1 GiB device copy (for scaling HBM byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    from hybrid_linear_attention_amd import gdn
+
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 1 GiB read + 1 GiB written")
+
+    cfg = synth.CONFIGS[1]
+    T = cfg["T"]
+    inp_cpu = synth.config_inputs(1)
+    inp = {k: (v.to("cuda") if isinstance(v, torch.Tensor) else v) for k, v in inp_cpu.items()}
+    log("prefill T=%d: warmup %d, steps %d" % (T, args.warmup, args.steps))
+    pre = timed_prefill(gdn, inp, args.steps, args.warmup)
+    log("prefill step %.3f ms (prepare %.3f, scan %.3f)" %
+        (pre["step_ms"], pre["prepare_ms"], pre["scan_ms"]))
+    tok_s = T / (pre["step_ms"] * 1e-3)
+    tflops = prefill_flops(T) / (pre["step_ms"] * 1e-3) / 1e12
+
+    dominant = "scan" if pre["scan_ms"] >= pre["prepare_ms"] else "prepare"
+    scan_tflops = scan_flops(T) / (pre["scan_ms"] * 1e-3) / 1e12
+
+    log("decode B=64: %d steps" % args.decode_steps)
+    dec = timed_decode(gdn, 64, args.decode_steps, 16)
+    log("decode step %.4f ms, %.1f GB/s" % (dec["step_ms"], dec["gbs"]))
+
+    out = {
+        "metric": "GDN prefill tokens/s @T=8192 (% MFMA peak) + decode state GB/s (% HBM peak)",
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pre["step_ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "chunked prefill, batch 1, T=8192, 16 QK / 48 V heads, head "
+                               "dim 128, chunk 64, bf16 q/k/v, fp32 alpha/beta/state, "
+                               "zero initial state, final state emitted",
+                   "global_batch": 1, "seq_len": T, "parallelism": "single GPU"},
+        "prefill": {"tflops_algorithmic": tflops, "frac_bf16_mfma_peak": tflops / PEAK_BF16_TFLOPS,
+                    "prepare_ms": pre["prepare_ms"], "scan_ms": pre["scan_ms"],
+                    "gflop_per_call": prefill_flops(T) / 1e9},
+        "roofline": {"bound": "mfma", "kernel": dominant,
+                     "achieved": scan_tflops if dominant == "scan" else None,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": (scan_tflops / PEAK_BF16_TFLOPS) if dominant == "scan" else None,
+                     "traffic": None},
+        "decode": {"metric": "decode state GB/s", "value": dec["gbs"], "unit": "GB/s",
+                   "ms_per_step": dec["step_ms"], "steps": args.decode_steps,
+                   "workload": "64 sequences x 1 token, fp32 state [64,48,128,128] in place, "
+                               "bf16 q/k/v",
+                   "roofline": {"bound": "hbm", "achieved": dec["gbs"], "peak": PEAK_HBM_GBS,
+                                "unit": "GB/s", "frac": dec["gbs"] / PEAK_HBM_GBS,
+                                "traffic": None}},
+    }
+    if args.extended:
+        log("extended: T=262144")
+        inp3 = {k: (v.to("cuda") if isinstance(v, torch.Tensor) else v)
+                for k, v in synth.config_inputs(3).items()}
+        r3 = timed_prefill(gdn, inp3, 3, 1)
+        out["long_context"] = {"T": 262144, "ms": r3["step_ms"],
+                               "tokens_per_s": 262144 / (r3["step_ms"] * 1e-3),
+                               "tflops_algorithmic": prefill_flops(262144) / (r3["step_ms"] * 1e-3) / 1e12}
+        del inp3
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) on %d tokens" % args.cpu_tokens)
+        out["cpu_baseline"] = cpu_baseline(inp_cpu, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -41,11 +41,12 @@ size_t esize(gdn_dtype dt) { return dt == GDN_BF16 ? 2 : 4; }
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Workspace layout: Tt [nc][Hv][64][64], QK [nc][Hqk][64][64] (element type),
-// G [nc][Hv][64] fp32, then for varlen the chunk table [nc][2] and the
-// per-sequence chunk offsets [N+1] (int32).
+// Workspace layout: Tt [nc][Hv][64][64], M [nc][Hv][64][64] and
+// K^T [nc][Hqk][128][64] (element type), gam and dec [nc][Hv][64] fp32, then
+// for varlen the chunk table [nc][2] and the per-sequence chunk offsets [N+1]
+// (int32).
 struct WsLayout {
-  size_t tt, qk, gs, tab, seq, total;
+  size_t tt, m, kt, gam, dec, tab, seq, total;
 };
 
 WsLayout ws_layout(int64_t nc, int64_t Hqk, int64_t Hv, gdn_dtype dt, int64_t nseq_varlen) {
@@ -54,9 +55,13 @@ WsLayout ws_layout(int64_t nc, int64_t Hqk, int64_t Hv, gdn_dtype dt, int64_t ns
   size_t off = 0;
   w.tt = off;
   off += round256((size_t)nc * Hv * gdn::kC * gdn::kC * es);
-  w.qk = off;
-  off += round256((size_t)nc * Hqk * gdn::kC * gdn::kC * es);
-  w.gs = off;
+  w.m = off;
+  off += round256((size_t)nc * Hv * gdn::kC * gdn::kC * es);
+  w.kt = off;
+  off += round256((size_t)nc * Hqk * gdn::kD * gdn::kC * es);
+  w.gam = off;
+  off += round256((size_t)nc * Hv * gdn::kC * sizeof(float));
+  w.dec = off;
   off += round256((size_t)nc * Hv * gdn::kC * sizeof(float));
   w.tab = off;
   w.seq = off;
@@ -147,8 +152,10 @@ gdn_status prefill_fixed(const void* q, const void* k, const void* v, const floa
   a.gate = nullptr; a.norm_w = nullptr; a.norm_eps = 0.f;
   char* ws = static_cast<char*>(workspace);
   a.Tt = ws ? ws + L.tt : nullptr;
-  a.QK = ws ? ws + L.qk : nullptr;
-  a.Gs = ws ? reinterpret_cast<float*>(ws + L.gs) : nullptr;
+  a.M = ws ? ws + L.m : nullptr;
+  a.KT = ws ? ws + L.kt : nullptr;
+  a.gam = ws ? reinterpret_cast<float*>(ws + L.gam) : nullptr;
+  a.dec = ws ? reinterpret_cast<float*>(ws + L.dec) : nullptr;
   a.cm = gdn::ChunkMap{nullptr, nullptr, T, (int)Nc, (int)nc};
   a.nseq = B;
   a.nc_launch = (int)nc;
@@ -282,8 +289,10 @@ gdn_status gdn_prefill_varlen(const void* q, const void* k, const void* v, const
   a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.h0 = h0; a.o = o; a.ht = ht;
   a.gate = gate; a.norm_w = norm_weight; a.norm_eps = norm_eps;
   a.Tt = ws + L.tt;
-  a.QK = ws + L.qk;
-  a.Gs = reinterpret_cast<float*>(ws + L.gs);
+  a.M = ws + L.m;
+  a.KT = ws + L.kt;
+  a.gam = reinterpret_cast<float*>(ws + L.gam);
+  a.dec = reinterpret_cast<float*>(ws + L.dec);
   a.cm = gdn::ChunkMap{tab, seq_off, 0, 0, (int)nc};
   a.nseq = N;
   a.nc_launch = (int)nc;

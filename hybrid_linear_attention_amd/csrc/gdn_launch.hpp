@@ -22,8 +22,8 @@ struct PrefillLaunch {
   const void* gate;        // null: plain output; else fused RMSNorm * sigmoid(gate)
   const float* norm_w;
   float norm_eps;
-  void *Tt, *QK;           // workspace regions
-  float* Gs;
+  void *Tt, *M, *KT;       // workspace regions
+  float *gam, *dec;
   ChunkMap cm;
   int nseq, nc_launch, Hqk, Hv;
   bool bf16_io;

@@ -24,14 +24,16 @@
 //    matrices K K^T and Q K^T on MFMA (once per query/key head, shared by the
 //    H_v/H_qk value heads that read it), gate prefix G, and the triangular
 //    solve in fp32 (16x16 diagonal blocks by substitution, off-diagonal blocks
-//    by fp32 MFMA).  Writes Tt, Q K^T and G to the workspace.
+//    by fp32 MFMA).  Writes Tt, the masked output matrix M and G to the
+//    workspace.
 //  * scan     (grid: value-row slices x value heads x sequences) - the serial
 //    chain.  Each wave owns 16 value rows of one head's state and keeps them,
 //    transposed (S^T, d_k x 16), in fp32 MFMA accumulators for the whole
 //    sequence.  Per chunk every product feeds the next one straight from
 //    registers: the accumulator tiles of S^T, X and Dl are the B operands of the
 //    following MFMAs (see gdn_device.hpp for the K order that makes this work),
-//    so only the shared chunk operands (K, K^T, Q, Tt, M, V) go through LDS.
+//    so only the shared chunk operands (K, K^T, Q, Tt, M, V) go through LDS;
+//    those are fetched into registers one chunk ahead.
 //    Rows of the state never interact, so the value rows split across waves
 //    and workgroups with no communication at all.
 #include "gdn_device.hpp"
@@ -43,10 +45,17 @@ namespace gdn {
 
 template <typename E>
 struct Work {
-  E* Tt;      // [nc][Hv][64][64]  (I + A)^-1 diag(beta)
-  E* QK;      // [nc][Hqk][64][64] Q K^T (unmasked)
-  float* Gs;  // [nc][Hv][64]      gate prefix G
+  E* Tt;       // [nc][Hv][64][64]   (I + A)^-1 diag(beta)
+  E* M;        // [nc][Hv][64][64]   (Q K^T * exp(G_i - G_j)) on and below the diagonal
+  E* KT;       // [nc][Hqk][128][64] K^T of the chunk (bf16 path only)
+  float* gam;  // [nc][Hv][64]       exp(G_t)
+  float* dec;  // [nc][Hv][64]       exp(G_last - G_t)
 };
+
+// Gates are kept in base 2 so that the hardware v_exp_f32 / v_log_f32 apply
+// directly: G2_t = sum_{j<=t} log2(alpha_j), exp(G_i - G_j) = 2^(G2_i - G2_j).
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 __device__ __forceinline__ void chunk_of(const ChunkMap& cm, int cid, int& tok0, int& L) {
   if (cm.tab) {
@@ -79,7 +88,8 @@ struct PrepSmem {
     } in;
     float buf[4][kC * kLdT];        // per-wave A -> T buffers (after the Grams)
   } u;
-  float gram[kC * kLdT];
+  float gram[kC * kLdT];            // K K^T
+  float qkg[kC * kLdT];             // Q K^T
   float gate[4][kC];
   float bet[4][kC];
 };
@@ -157,15 +167,28 @@ __global__ __launch_bounds__(256) void prepare_kernel(
       }
     }
   }
-  E* qk_out = ws.QK + ((size_t)cid * Hqk + gq) * kC * kC;
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 16 * w + 4 * g + i, col = 16 * nt + r;
       sm.gram[row * kLdT + col] = kk[nt][i];
-      qk_out[row * kC + col] = from_f32<E>(qk[nt][i]);
+      sm.qkg[row * kLdT + col] = qk[nt][i];
     }
+  if constexpr (BF) {
+    // K^T of the chunk for the scan's state update, [128 d_k][64 tokens]:
+    // each thread writes 16-byte pieces (8 tokens of one d_k column).
+    const bf16* Ks = reinterpret_cast<const bf16*>(sm.u.in.Ks);
+    bf16* kt = reinterpret_cast<bf16*>(ws.KT) + ((size_t)cid * Hqk + gq) * kD * kC;
+#pragma unroll
+    for (int it = 0; it < kD * kC / 8 / 256; ++it) {
+      const int p = tid + 256 * it, dk = p >> 3, tb = p & 7;
+      bf16x8 col;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) col[e] = Ks[(8 * tb + e) * LDK + dk];
+      *reinterpret_cast<bf16x8*>(kt + dk * kC + 8 * tb) = col;
+    }
+  }
   __syncthreads();   // K/Q tiles are dead from here on; buf[] reuses them
 
   // One wave per value head of this query/key group.
@@ -175,17 +198,21 @@ __global__ __launch_bounds__(256) void prepare_kernel(
     const size_t gi = (size_t)(tok0 + l) * Hv + h;
     const float al = (l < L) ? alpha[gi] : 1.f;
     const float bl = (l < L) ? beta[gi] : 0.f;
-    const float Gl = wave_inclusive_sum(logf(al));
-    ws.Gs[((size_t)cid * Hv + h) * kC + l] = Gl;
+    const float Gl = wave_inclusive_sum(hw_log2(al));
+    const float Glast = __shfl(Gl, kC - 1, 64);
+    ws.gam[((size_t)cid * Hv + h) * kC + l] = hw_exp2(Gl);
+    ws.dec[((size_t)cid * Hv + h) * kC + l] = hw_exp2(Glast - Gl);
     sm.gate[w][l] = Gl;
     sm.bet[w][l] = bl;
     wave_lds_fence();
 
-    // A[i][j] = beta_i exp(G_i - G_j) (k_i . k_j) for j < i; lane = column j.
+    // A[i][j] = beta_i exp(G_i - G_j) (k_i . k_j) for j < i, and the output
+    // mask M[i][j] = exp(G_i - G_j) (q_i . k_j) for j <= i; lane = column j.
+    E* mo = ws.M + ((size_t)cid * Hv + h) * kC * kC;
     for (int i = 0; i < kC; ++i) {
-      float a = 0.f;
-      if (l < i) a = sm.bet[w][i] * expf(sm.gate[w][i] - Gl) * sm.gram[i * kLdT + l];
-      A[i * kLdT + l] = a;
+      const float dg = (l <= i) ? hw_exp2(sm.gate[w][i] - Gl) : 0.f;
+      A[i * kLdT + l] = (l < i) ? sm.bet[w][i] * dg * sm.gram[i * kLdT + l] : 0.f;
+      mo[i * kC + l] = from_f32<E>(dg * sm.qkg[i * kLdT + l]);
     }
     wave_lds_fence();
 
@@ -311,100 +338,134 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
       ST[t] = hp ? *reinterpret_cast<const f32x4*>(hp + 16 * t + 4 * g) : zero4();
   }
 
-  int prev_tok0 = 0, prev_L = 0;
-  for (int c = 0; c <= nch; ++c) {
-    // ---- phase 1: write out the previous chunk's outputs, stage this chunk.
-    if (c > 0) {
-      if constexpr (GATED) {
-        // y = o / sqrt(mean(o^2) + eps) * w * sigmoid(gate), whole head per row.
-        static_assert(!GATED || NW == 8, "the fused epilogue needs the whole head");
-        const int row = tid >> 3, part = tid & 7;
-        if (row < prev_L) {
-          const float* orow = sm.Os + row * LDO + 16 * part;
-          float ss = 0.f;
+  // Chunk operands are fetched into registers one chunk ahead (issued right
+  // after the staging barrier, consumed at the next staging), so their global
+  // latency hides behind the current chunk's MFMA work.
+  constexpr int KP = kC * (kD / EPV) / NT;          // 16-byte pieces of K (and Q) per thread
+  constexpr int VP = BF ? kC * (16 * NW / 8) / NT : 1;
+  constexpr int TP = kC * kC / EPV / NT;            // pieces of Tt (and M) per thread
+  static_assert(KP * NT == kC * (kD / EPV) && TP * NT == kC * kC / EPV, "piece split");
+  uint4 rk[KP], rq[KP], rv[VP], rt[TP], rm[TP];
+  float rg = 0.f, rgl = 0.f;
+
+  auto fetch = [&](int cid, int tok0, int L) {
 #pragma unroll
-          for (int j = 0; j < 16; ++j) ss += orow[j] * orow[j];
-          ss += __shfl_xor(ss, 1, 64);
-          ss += __shfl_xor(ss, 2, 64);
-          ss += __shfl_xor(ss, 4, 64);
-          const float rn = rsqrtf(ss * (1.f / kD) + norm_eps);
-          const size_t base = ((size_t)(prev_tok0 + row) * Hv + h) * kD + 16 * part;
-          const E* gp = gate + base;
-          E* op = o + base;
+    for (int it = 0; it < KP; ++it) {
+      const int p = tid + NT * it, t = p & 63, cb = p >> 6;
+      const size_t off = ((size_t)(tok0 + t) * Hqk + gq) * kD + cb * EPV;
+      rk[it] = ld16(k + off, t < L);
+      rq[it] = ld16(q + off, t < L);
+    }
+    if constexpr (BF) {
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const float wj = norm_w ? norm_w[16 * part + j] : 1.f;
-            const float sg = 1.f / (1.f + __expf(-to_f32(gp[j])));
-            op[j] = from_f32<E>(orow[j] * rn * wj * sg);
-          }
-        }
-      } else {
-        constexpr int PPR = 16 * NW / EPV;          // 16-byte pieces per output row
-        for (int p = tid; p < kC * PPR; p += NT) {
-          const int t = p / PPR, cb = p - (p / PPR) * PPR;
-          if (t < prev_L) {
-            const uint4 val = *reinterpret_cast<const uint4*>(sm.Os + t * LDO + cb * EPV);
-            *reinterpret_cast<uint4*>(o + ((size_t)(prev_tok0 + t) * Hv + h) * kD + dvb +
-                                      cb * EPV) = val;
-          }
-        }
+      for (int it = 0; it < VP; ++it) {
+        const int p = tid + NT * it, t = p & 63, cb = p >> 6;
+        rv[it] = ld16(v + ((size_t)(tok0 + t) * Hv + h) * kD + dvb + cb * 8, t < L);
       }
     }
-    if (c == nch) break;
-
-    const int cid = cid0 + c;
-    int tok0, L;
-    chunk_of(cm, cid, tok0, L);
-    {
-      // K (row-major, and transposed for bf16) and Q.  Lanes run along the
-      // token axis so the transposed 2-byte LDS writes hit distinct banks.
-      constexpr int PPR = kD / EPV;
-      for (int p = tid; p < kC * PPR; p += NT) {
-        const int t = p & 63, cb = p >> 6;
-        const size_t off = ((size_t)(tok0 + t) * Hqk + gq) * kD + cb * EPV;
-        const uint4 kv = ld16(k + off, t < L);
-        const uint4 qv = ld16(q + off, t < L);
-        uint2* dk = reinterpret_cast<uint2*>(sm.Ks + t * LDK + cb * EPV);
-        uint2* dq = reinterpret_cast<uint2*>(sm.Qs + t * LDK + cb * EPV);
-        dk[0] = uint2{kv.x, kv.y}; dk[1] = uint2{kv.z, kv.w};
-        dq[0] = uint2{qv.x, qv.y}; dq[1] = uint2{qv.z, qv.w};
-        if constexpr (BF) {
-          const bf16* e8 = reinterpret_cast<const bf16*>(&kv);
+    const E* tsrc = ws.Tt + ((size_t)cid * Hv + h) * kC * kC;
+    const E* msrc = ws.M + ((size_t)cid * Hv + h) * kC * kC;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) sm.KT[(cb * 8 + e) * kLdT + t] = e8[e];
-        }
-      }
-      // V slice, transposed (bf16 only; the fp32 path reads V in place).
+    for (int it = 0; it < TP; ++it) {
+      const int p = tid + NT * it;
+      rt[it] = *reinterpret_cast<const uint4*>(tsrc + p * EPV);
+      rm[it] = *reinterpret_cast<const uint4*>(msrc + p * EPV);
+    }
+    if (tid < kC) {
+      rg = ws.gam[((size_t)cid * Hv + h) * kC + tid];
+      rgl = ws.dec[((size_t)cid * Hv + h) * kC + tid];
+    }
+  };
+
+  auto stage = [&]() {
+#pragma unroll
+    for (int it = 0; it < KP; ++it) {
+      const int p = tid + NT * it, t = p & 63, cb = p >> 6;
+      uint2* dk = reinterpret_cast<uint2*>(sm.Ks + t * LDK + cb * EPV);
+      uint2* dq = reinterpret_cast<uint2*>(sm.Qs + t * LDK + cb * EPV);
+      dk[0] = uint2{rk[it].x, rk[it].y}; dk[1] = uint2{rk[it].z, rk[it].w};
+      dq[0] = uint2{rq[it].x, rq[it].y}; dq[1] = uint2{rq[it].z, rq[it].w};
       if constexpr (BF) {
-        constexpr int VPR = 16 * NW / 8;
-        for (int p = tid; p < kC * VPR; p += NT) {
-          const int t = p & 63, cb = p >> 6;
-          const uint4 vv =
-              ld16(v + ((size_t)(tok0 + t) * Hv + h) * kD + dvb + cb * 8, t < L);
-          const bf16* e8 = reinterpret_cast<const bf16*>(&vv);
+        const bf16* e8 = reinterpret_cast<const bf16*>(&rk[it]);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) sm.Vt[(cb * 8 + e) * kLdT + t] = e8[e];
-        }
-      }
-      // Tt, and M = (Q K^T) * exp(G_i - G_j) on and below the diagonal.
-      const E* tsrc = ws.Tt + ((size_t)cid * Hv + h) * kC * kC;
-      const E* qsrc = ws.QK + ((size_t)cid * Hqk + gq) * kC * kC;
-      const float* gsrc = ws.Gs + ((size_t)cid * Hv + h) * kC;
-      for (int e = tid; e < kC * kC; e += NT) {
-        const int i = e >> 6, j = e & 63;
-        sm.Tt[i * kLdT + j] = tsrc[e];
-        float m = 0.f;
-        if (j <= i) m = to_f32(qsrc[e]) * __expf(gsrc[i] - gsrc[j]);
-        sm.Ms[i * kLdT + j] = from_f32<E>(m);
-      }
-      if (tid < kC) {
-        const float Gt = gsrc[tid], Gl = gsrc[kC - 1];
-        sm.gam[tid] = __expf(Gt);
-        sm.dec[tid] = __expf(Gl - Gt);
+        for (int e = 0; e < 8; ++e) sm.KT[(cb * 8 + e) * kLdT + t] = e8[e];
       }
     }
-    __syncthreads();
+    if constexpr (BF) {
+#pragma unroll
+      for (int it = 0; it < VP; ++it) {
+        const int p = tid + NT * it, t = p & 63, cb = p >> 6;
+        const bf16* e8 = reinterpret_cast<const bf16*>(&rv[it]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sm.Vt[(cb * 8 + e) * kLdT + t] = e8[e];
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < TP; ++it) {
+      const int e0 = (tid + NT * it) * EPV, i = e0 >> 6, j = e0 & 63;
+      uint2* dt = reinterpret_cast<uint2*>(sm.Tt + i * kLdT + j);
+      uint2* dm = reinterpret_cast<uint2*>(sm.Ms + i * kLdT + j);
+      dt[0] = uint2{rt[it].x, rt[it].y}; dt[1] = uint2{rt[it].z, rt[it].w};
+      dm[0] = uint2{rm[it].x, rm[it].y}; dm[1] = uint2{rm[it].z, rm[it].w};
+    }
+    if (tid < kC) {
+      sm.gam[tid] = rg;
+      sm.dec[tid] = rgl;
+    }
+  };
 
+  auto write_out = [&](int otok0, int oL) {
+    if constexpr (GATED) {
+      // y = o / sqrt(mean(o^2) + eps) * w * sigmoid(gate), whole head per row.
+      static_assert(!GATED || NW == 8, "the fused epilogue needs the whole head");
+      const int row = tid >> 3, part = tid & 7;
+      if (row < oL) {
+        const float* orow = sm.Os + row * LDO + 16 * part;
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) ss += orow[j] * orow[j];
+        ss += __shfl_xor(ss, 1, 64);
+        ss += __shfl_xor(ss, 2, 64);
+        ss += __shfl_xor(ss, 4, 64);
+        const float rn = rsqrtf(ss * (1.f / kD) + norm_eps);
+        const size_t base = ((size_t)(otok0 + row) * Hv + h) * kD + 16 * part;
+        const E* gp = gate + base;
+        E* op = o + base;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const float wj = norm_w ? norm_w[16 * part + j] : 1.f;
+          const float sg = 1.f / (1.f + __expf(-to_f32(gp[j])));
+          op[j] = from_f32<E>(orow[j] * rn * wj * sg);
+        }
+      }
+    } else {
+      constexpr int PPR = 16 * NW / EPV;            // 16-byte pieces per output row
+      for (int p = tid; p < kC * PPR; p += NT) {
+        const int t = p / PPR, cb = p - (p / PPR) * PPR;
+        if (t < oL) {
+          const uint4 val = *reinterpret_cast<const uint4*>(sm.Os + t * LDO + cb * EPV);
+          *reinterpret_cast<uint4*>(o + ((size_t)(otok0 + t) * Hv + h) * kD + dvb +
+                                    cb * EPV) = val;
+        }
+      }
+    }
+  };
+
+  int tok0 = 0, L = 0, ptok0 = 0, pL = 0;
+  if (nch > 0) {
+    chunk_of(cm, cid0, tok0, L);
+    fetch(cid0, tok0, L);
+  }
+  for (int c = 0; c < nch; ++c) {
+    // ---- phase 1: registers -> LDS for chunk c; chunk c-1's outputs -> HBM.
+    stage();
+    if (c > 0) write_out(ptok0, pL);
+    __syncthreads();
+    int ntok0 = 0, nL = 0;
+    if (c + 1 < nch) {
+      chunk_of(cm, cid0 + c + 1, ntok0, nL);
+      fetch(cid0 + c + 1, ntok0, nL);
+    }
     // ---- phase 2: this wave's 16 value rows.
     const float gL = sm.gam[kC - 1];
     f32x4 P[4], QS[4], X[4], Dl[4];
@@ -508,15 +569,371 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
       for (int t = 0; t < 8; ++t)
         mma_acc_f32_tA<4>(ST[t], reinterpret_cast<const float*>(sm.Ks), LDK, 16 * t, 0, Dl);
     }
-    prev_tok0 = tok0;
-    prev_L = L;
+    ptok0 = tok0;
+    pL = L;
+    tok0 = ntok0;
+    L = nL;
     __syncthreads();
   }
+  if (nch > 0) write_out(ptok0, pL);
 
   if (ht) {
     float* hp = ht + (((size_t)seq * Hv + h) * kD + dv0 + r) * kD;
 #pragma unroll
     for (int t = 0; t < 8; ++t) *reinterpret_cast<f32x4*>(hp + 16 * t + 4 * g) = ST[t];
+  }
+}
+
+// ---------------------------------------------------------------- split scan (bf16)
+// The bf16 scan with the work of each 16-row value slice split between two
+// waves and the chunk operands brought in by a third:
+//
+//  * chain wave (one per slice): the serial part only.  P = K S^T, X, Dl =
+//    Tt X, the state update; it hands S^T (as the B fragments it built for P)
+//    and Dl to the output wave through LDS.  40 MFMAs per chunk.
+//  * output wave (one per slice), one chunk behind: O = diag(gam) Q S^T + M Dl
+//    with its Q and M fragments loaded straight from global memory into
+//    registers one chunk ahead.  22 MFMAs per chunk.
+//  * producer wave: copies K, K^T, Tt, gam and dec of chunk c+2 from global
+//    memory straight into LDS (global_load_lds_dwordx4, no registers) while
+//    chunk c is computed; three LDS slots rotate.
+//
+// Token and d_k order.  An accumulator tile pair holds, per lane group g, rows
+// {4g..4g+3} and {16+4g..16+4g+3} of a 32-row block; used as a B fragment these
+// are the K slots.  Inside each 32-row block the library stores logical row
+// x at physical position prow(x) = 8*((x%16)/4) + 4*(x/16) + x%4, so that the 8
+// K slots of lane group g are the 8 consecutive physical rows 8g..8g+7 and
+// every A fragment is a single 16-byte LDS read.  The permutation is applied to
+// tokens (rows of P, X, Dl) and to d_k (rows of S^T); it is undone where the
+// state is loaded and stored.  LDS rows are XOR-swizzled in 16-byte pieces
+// (swz) so the 16 gathered rows of an A fragment hit distinct banks.
+namespace split {
+constexpr int kSlices = 2;                   // 16-row value slices per workgroup
+constexpr int kRows = 16 * kSlices;          // value rows per workgroup
+constexpr int kNsl = kD / kRows;             // workgroups per value head
+constexpr int kWaves = 2 * kSlices + 1;      // chain x2, output x2, producer
+constexpr int kSlots = 3;
+constexpr int kKB = kC * kD * 2;             // K tile, bytes
+constexpr int kKTB = kD * kC * 2;            // K^T tile
+constexpr int kTB = kC * kC * 2;             // Tt tile
+constexpr int kDmaOps = kKB / 1024 + kKTB / 1024 + kTB / 1024 + 2;
+
+constexpr int kGdSlots = 4;                  // gam/dec ring: chunks c-1 .. c+2 live
+struct Slot {
+  alignas(16) uint8_t K[kKB];
+  alignas(16) uint8_t KT[kKTB];
+  alignas(16) uint8_t T[kTB];
+};
+struct GateSlot {
+  alignas(16) float gam[kC];
+  alignas(16) float dec[kC];
+};
+struct Hand {
+  bf16x8 sb[4][64];                          // S^T B fragments of the chain wave
+  bf16x8 db[2][64];                          // Dl B fragments
+};
+struct Smem {
+  Slot slot[kSlots];
+  GateSlot gd[kGdSlots];
+  Hand hand[2][kSlices];
+  alignas(16) bf16 ost[kSlices][kC * 16];    // per output wave O staging
+};
+
+// row x (0..31 within a 32-row block, tile t2 = x / 16, r = x % 16) -> physical
+__device__ __forceinline__ int prow(int t, int r) {
+  return 32 * (t >> 1) + 8 * (r >> 2) + 4 * (t & 1) + (r & 3);
+}
+__device__ __forceinline__ int swz(int row) { return (row & 3) | ((row >> 1) & 4); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_dst, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_dst, 4, 0, 0);
+}
+
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+}  // namespace split
+
+__global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const float* __restrict__ h0, bf16* __restrict__ o, float* __restrict__ ht, Work<bf16> ws,
+    ChunkMap cm, int Hqk, int Hv, int G) {
+  using namespace split;
+  __shared__ Smem sm;
+
+  const int nlin = Hv * kNsl;
+  int lin = blockIdx.x;
+  const int per_group = G * kNsl;
+  if ((Hqk & 7) == 0) {
+    const int xcd = lin & 7, j = lin >> 3;
+    lin = (xcd + 8 * (j / per_group)) * per_group + (j - (j / per_group) * per_group);
+  }
+  if (lin >= nlin) return;                          // whole workgroup leaves together
+  const int h = lin / kNsl, sl = lin - (lin / kNsl) * kNsl;
+  const int gq = h / G;
+  const int seq = blockIdx.y;
+  const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
+  const int dvb = sl * kRows;
+
+  int cid0, nch;
+  if (cm.tab) {
+    cid0 = cm.seq_off[seq];
+    nch = min(cm.seq_off[seq + 1], cm.nc_max) - cid0;
+  } else {
+    cid0 = seq * cm.Nc;
+    nch = cm.Nc;
+  }
+
+  const size_t hv_stride = (size_t)Hv * kD;         // elements between tokens of v / o
+  const size_t qk_stride = (size_t)Hqk * kD;
+
+  if (w == 2 * kSlices) {
+    // ------------------------------------------------------------ producer
+    auto issue = [&](int c) {
+      const int cid = cid0 + c;
+      int tok0, L;
+      chunk_of(cm, cid, tok0, L);
+      Slot& S = sm.slot[c % kSlots];
+      const bf16* kbase = k + (size_t)tok0 * qk_stride + (size_t)gq * kD;
+#pragma unroll
+      for (int it = 0; it < kKB / 1024; ++it) {
+        const int row = 4 * it + (l >> 4), p = (l & 15) ^ swz(row);
+        dma16(kbase + (size_t)min(row, L - 1) * qk_stride + 8 * p, S.K + 1024 * it);
+      }
+      const bf16* ktb = ws.KT + ((size_t)cid * Hqk + gq) * kD * kC;
+#pragma unroll
+      for (int it = 0; it < kKTB / 1024; ++it) {
+        const int row = 8 * it + (l >> 3), p = (l & 7) ^ swz(row);
+        dma16(ktb + row * kC + 8 * p, S.KT + 1024 * it);
+      }
+      const bf16* tb = ws.Tt + ((size_t)cid * Hv + h) * kC * kC;
+#pragma unroll
+      for (int it = 0; it < kTB / 1024; ++it) {
+        const int row = 8 * it + (l >> 3), p = (l & 7) ^ swz(row);
+        dma16(tb + row * kC + 8 * p, S.T + 1024 * it);
+      }
+      GateSlot& Gd = sm.gd[c % kGdSlots];
+      dma4(ws.gam + ((size_t)cid * Hv + h) * kC + l, Gd.gam);
+      dma4(ws.dec + ((size_t)cid * Hv + h) * kC + l, Gd.dec);
+    };
+    if (nch > 0) issue(0);
+    if (nch > 1) {
+      issue(1);
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaOps) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    barrier_lds();
+    for (int i = 0; i <= nch; ++i) {
+      if (i + 2 < nch) {
+        issue(i + 2);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaOps) : "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      barrier_lds();
+    }
+    return;
+  }
+
+  if (w < kSlices) {
+    // ------------------------------------------------------------ chain wave
+    const int s = w, dv0 = dvb + 16 * s;
+    // S^T accumulator tiles: ST[t][i] = S[dv0 + r][prow(t, 4g + i)].
+    f32x4 ST[8];
+    {
+      const float* hp = h0 ? h0 + (((size_t)seq * Hv + h) * kD + dv0 + r) * kD : nullptr;
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        ST[t] = hp ? *reinterpret_cast<const f32x4*>(hp + prow(t, 4 * g)) : zero4();
+    }
+    // V of this lane's 16 tokens (physical 32kk + 8g + 0..7) and value row.
+    auto load_v = [&](int c, bf16* vr) {
+      int tok0, L;
+      chunk_of(cm, cid0 + c, tok0, L);
+      const bf16* vb = v + (size_t)tok0 * hv_stride + (size_t)h * kD + dv0 + r;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int t = 32 * (e >> 3) + 8 * g + (e & 7);
+        vr[e] = (t < L) ? vb[(size_t)t * hv_stride] : (bf16)0.f;
+      }
+    };
+    bf16 vcur[16], vnext[16];
+    if (nch > 0) load_v(0, vcur);
+    barrier_lds();
+    for (int i = 0; i <= nch; ++i) {
+      if (i < nch) {
+        if (i + 1 < nch) load_v(i + 1, vnext);
+        const Slot& S = sm.slot[i % kSlots];
+        const GateSlot& Gd = sm.gd[i % kGdSlots];
+        Hand& H = sm.hand[i & 1][s];
+        bf16x8 SB[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          SB[kk] = pack_b(ST[2 * kk], ST[2 * kk + 1]);
+          H.sb[kk][l] = SB[kk];
+        }
+        // P = K S^T  (rows: physical tokens prow(mt, r))
+        f32x4 P[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          P[mt] = zero4();
+          const int row = prow(mt, r);
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) {
+            const int p = (4 * kk + g) ^ swz(row);
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(S.K + row * 256 + 16 * p);
+            P[mt] = mfma_bf16(a, SB[kk], P[mt]);
+          }
+        }
+        // X = V - diag(gam) P; this lane's rows are tokens 32(mt/2) + 8g + 4(mt%2) + i.
+        f32x4 X[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const f32x4 gm = *reinterpret_cast<const f32x4*>(Gd.gam + 32 * (mt >> 1) + 8 * g + 4 * (mt & 1));
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            X[mt][i] = (float)vcur[8 * (mt >> 1) + 4 * (mt & 1) + i] - gm[i] * P[mt][i];
+        }
+        const bf16x8 XB[2] = {pack_b(X[0], X[1]), pack_b(X[2], X[3])};
+        // Dl = Tt X
+        f32x4 Dl[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          Dl[mt] = zero4();
+          const int row = prow(mt, r);
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            const int p = (4 * kk + g) ^ swz(row);
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(S.T + row * 128 + 16 * p);
+            Dl[mt] = mfma_bf16(a, XB[kk], Dl[mt]);
+          }
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) H.db[kk][l] = pack_b(Dl[2 * kk], Dl[2 * kk + 1]);
+        // state update: S^T <- gam_last S^T + K^T diag(dec) Dl
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const f32x4 dc = *reinterpret_cast<const f32x4*>(Gd.dec + 32 * (mt >> 1) + 8 * g + 4 * (mt & 1));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Dl[mt][i] *= dc[i];
+        }
+        const bf16x8 DTB[2] = {pack_b(Dl[0], Dl[1]), pack_b(Dl[2], Dl[3])};
+        const float gL = Gd.gam[kC - 1];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          ST[t] *= gL;
+          const int row = prow(t, r);
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            const int p = (4 * kk + g) ^ swz(row);
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(S.KT + row * 128 + 16 * p);
+            ST[t] = mfma_bf16(a, DTB[kk], ST[t]);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) vcur[e] = vnext[e];
+      }
+      barrier_lds();
+    }
+    if (ht) {
+      float* hp = ht + (((size_t)seq * Hv + h) * kD + dv0 + r) * kD;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) *reinterpret_cast<f32x4*>(hp + prow(t, 4 * g)) = ST[t];
+    }
+    return;
+  }
+
+  // -------------------------------------------------------------- output wave
+  const int s = w - kSlices, dv0 = dvb + 16 * s;
+  // Operands of one chunk in registers: Q fragments (natural token rows 16mt + r,
+  // K slots d_k 32kk + 8g + j) and M fragments (K slots tokens 32kk + 8g + j;
+  // the upper half of rows 0..31 is zero and skipped).  gam comes from the LDS
+  // gate ring.
+  struct Ops {
+    bf16x8 qf[4][4];
+    bf16x8 mf[6];
+    int tok0, L;
+  };
+  auto load_ops = [&](int c, Ops& op) {
+    const int cid = cid0 + c;
+    chunk_of(cm, cid, op.tok0, op.L);
+    const bf16* qb = q + (size_t)op.tok0 * qk_stride + (size_t)gq * kD + 8 * g;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const bf16* qr = qb + (size_t)min(16 * mt + r, op.L - 1) * qk_stride;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) op.qf[mt][kk] = *reinterpret_cast<const bf16x8*>(qr + 32 * kk);
+    }
+    const bf16* mb = ws.M + ((size_t)cid * Hv + h) * kC * kC + 8 * g;
+    op.mf[0] = *reinterpret_cast<const bf16x8*>(mb + (0 + r) * kC);
+    op.mf[1] = *reinterpret_cast<const bf16x8*>(mb + (16 + r) * kC);
+    op.mf[2] = *reinterpret_cast<const bf16x8*>(mb + (32 + r) * kC);
+    op.mf[3] = *reinterpret_cast<const bf16x8*>(mb + (32 + r) * kC + 32);
+    op.mf[4] = *reinterpret_cast<const bf16x8*>(mb + (48 + r) * kC);
+    op.mf[5] = *reinterpret_cast<const bf16x8*>(mb + (48 + r) * kC + 32);
+  };
+  auto emit = [&](int c, const Ops& op) {
+    const Hand& H = sm.hand[c & 1][s];
+    const GateSlot& Gd = sm.gd[c % kGdSlots];
+    bf16x8 SB[4], DB[2];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) SB[kk] = H.sb[kk][l];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) DB[kk] = H.db[kk][l];
+    f32x4 O[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      O[mt] = zero4();
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) O[mt] = mfma_bf16(op.qf[mt][kk], SB[kk], O[mt]);
+      const f32x4 gm = *reinterpret_cast<const f32x4*>(Gd.gam + 16 * mt + 4 * g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) O[mt][i] *= gm[i];
+    }
+    O[0] = mfma_bf16(op.mf[0], DB[0], O[0]);
+    O[1] = mfma_bf16(op.mf[1], DB[0], O[1]);
+    O[2] = mfma_bf16(op.mf[2], DB[0], O[2]);
+    O[2] = mfma_bf16(op.mf[3], DB[1], O[2]);
+    O[3] = mfma_bf16(op.mf[4], DB[0], O[3]);
+    O[3] = mfma_bf16(op.mf[5], DB[1], O[3]);
+    bf16* st = sm.ost[s];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st[(16 * mt + 4 * g + i) * 16 + r] = (bf16)O[mt][i];
+    wave_lds_fence();
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int pc = l + 64 * j, t = pc >> 1, half = pc & 1;
+      if (t < op.L) {
+        const uint4 val = *reinterpret_cast<const uint4*>(st + t * 16 + 8 * half);
+        *reinterpret_cast<uint4*>(o + (size_t)(op.tok0 + t) * hv_stride + (size_t)h * kD + dv0 +
+                                  8 * half) = val;
+      }
+    }
+    wave_lds_fence();
+  };
+  // Iteration i emits chunk i-1 and then refills the same register set with
+  // chunk i+1, so each set is loaded about one and a half iterations before
+  // use.  Even chunks use set A, odd chunks set B; every role executes
+  // exactly nch + 1 loop barriers after the prologue barrier.
+  Ops opA, opB;
+  if (nch > 0) load_ops(0, opA);
+  barrier_lds();
+  for (int i = 0; i <= nch; i += 2) {
+    if (i >= 1) emit(i - 1, opB);
+    if (i + 1 < nch) load_ops(i + 1, opB);
+    barrier_lds();
+    if (i + 1 > nch) break;
+    emit(i, opA);
+    if (i + 2 < nch) load_ops(i + 2, opA);
+    barrier_lds();
   }
 }
 
@@ -571,7 +988,7 @@ __global__ __launch_bounds__(256) void varlen_table_kernel(const int32_t* __rest
 template <typename E>
 static hipError_t launch_prepare_t(const PrefillLaunch& a, hipStream_t st) {
   if (a.nc_launch <= 0) return hipSuccess;
-  Work<E> ws{(E*)a.Tt, (E*)a.QK, a.Gs};
+  Work<E> ws{(E*)a.Tt, (E*)a.M, (E*)a.KT, a.gam, a.dec};
   dim3 grid((unsigned)a.nc_launch, (unsigned)a.Hqk), block(256);
   hipLaunchKernelGGL(prepare_kernel<E>, grid, block, 0, st, (const E*)a.q, (const E*)a.k,
                      a.alpha, a.beta, ws, a.cm, a.Hqk, a.Hv, a.Hv / a.Hqk);
@@ -581,7 +998,7 @@ static hipError_t launch_prepare_t(const PrefillLaunch& a, hipStream_t st) {
 template <typename E, int NW, bool GATED>
 static hipError_t launch_scan_t(const PrefillLaunch& a, hipStream_t st) {
   if (a.nseq <= 0) return hipSuccess;
-  Work<E> ws{(E*)a.Tt, (E*)a.QK, a.Gs};
+  Work<E> ws{(E*)a.Tt, (E*)a.M, (E*)a.KT, a.gam, a.dec};
   constexpr int NSL = kD / (16 * NW);
   int nlin = a.Hv * NSL;
   if ((a.Hqk & 7) == 0) nlin = ((nlin + 7) / 8) * 8;
@@ -596,10 +1013,22 @@ hipError_t launch_prepare(const PrefillLaunch& a, hipStream_t st) {
   return a.bf16_io ? launch_prepare_t<bf16>(a, st) : launch_prepare_t<float>(a, st);
 }
 
+static hipError_t launch_scan_split(const PrefillLaunch& a, hipStream_t st) {
+  if (a.nseq <= 0) return hipSuccess;
+  Work<bf16> ws{(bf16*)a.Tt, (bf16*)a.M, (bf16*)a.KT, a.gam, a.dec};
+  int nlin = a.Hv * split::kNsl;
+  if ((a.Hqk & 7) == 0) nlin = ((nlin + 7) / 8) * 8;
+  dim3 grid((unsigned)nlin, (unsigned)a.nseq), block(64 * split::kWaves);
+  hipLaunchKernelGGL(scan_split_kernel, grid, block, 0, st, (const bf16*)a.q, (const bf16*)a.k,
+                     (const bf16*)a.v, a.h0, (bf16*)a.o, a.ht, ws, a.cm, a.Hqk, a.Hv,
+                     a.Hv / a.Hqk);
+  return hipGetLastError();
+}
+
 hipError_t launch_scan(const PrefillLaunch& a, hipStream_t st) {
   if (a.gate)
     return a.bf16_io ? launch_scan_t<bf16, 8, true>(a, st) : launch_scan_t<float, 8, true>(a, st);
-  return a.bf16_io ? launch_scan_t<bf16, 4, false>(a, st) : launch_scan_t<float, 4, false>(a, st);
+  return a.bf16_io ? launch_scan_split(a, st) : launch_scan_t<float, 4, false>(a, st);
 }
 
 hipError_t launch_varlen_table(const int32_t* cu, int N, int T_tot, int nc_max, int32_t* tab,
