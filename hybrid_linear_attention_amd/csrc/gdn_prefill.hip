@@ -57,10 +57,17 @@ struct Work {
 __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// The chunk table is read through the constant address space: every caller
+// passes a wave-uniform chunk id, so these become scalar loads.  A vector load
+// here would make any wait for it (vector loads complete in order) also wait
+// for the producer's in-flight global->LDS copies.
+typedef const __attribute__((address_space(4))) int32_t const_i32;
+
 __device__ __forceinline__ void chunk_of(const ChunkMap& cm, int cid, int& tok0, int& L) {
   if (cm.tab) {
-    tok0 = cm.tab[2 * cid];
-    L = cm.tab[2 * cid + 1];
+    const_i32* t = (const_i32*)cm.tab;
+    tok0 = t[2 * cid];
+    L = t[2 * cid + 1];
   } else {
     const int b = cid / cm.Nc, j = cid - (cid / cm.Nc) * cm.Nc;
     tok0 = b * cm.T + kC * j;
@@ -121,17 +128,32 @@ __global__ __launch_bounds__(256) void prepare_kernel(
   if (L <= 0) return;                            // unused varlen table slot
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
 
-  // Stage the chunk's K and Q rows (zero beyond L).
+  // Gates of the value head this wave will solve first (issued before the
+  // K/Q loads so both latencies overlap).
+  float al0 = 1.f, bl0 = 0.f;
+  if (w < G && l < L) {
+    const size_t gi = (size_t)(tok0 + l) * Hv + gq * G + w;
+    al0 = alpha[gi];
+    bl0 = beta[gi];
+  }
+
+  // Stage the chunk's K and Q rows (zero beyond L): every load is issued
+  // before the first LDS write.
   constexpr int PPR = kD / EPV;                  // 16-byte pieces per row
-  for (int p = tid; p < kC * PPR; p += 256) {
-    const int t = p / PPR, cb = p - (p / PPR) * PPR;
+  constexpr int NP = kC * PPR / 256;             // pieces per thread
+  uint4 kv[NP], qv[NP];
+#pragma unroll
+  for (int it = 0; it < NP; ++it) {
+    const int p = tid + 256 * it, t = p / PPR, cb = p - (p / PPR) * PPR;
     const size_t off = ((size_t)(tok0 + t) * Hqk + gq) * kD + cb * EPV;
-    const uint4 kv = ld16(k + off, t < L);
-    const uint4 qv = ld16(q + off, t < L);
-    uint2* dk = reinterpret_cast<uint2*>(sm.u.in.Ks + t * LDK + cb * EPV);
-    uint2* dq = reinterpret_cast<uint2*>(sm.u.in.Qs + t * LDK + cb * EPV);
-    dk[0] = uint2{kv.x, kv.y}; dk[1] = uint2{kv.z, kv.w};
-    dq[0] = uint2{qv.x, qv.y}; dq[1] = uint2{qv.z, qv.w};
+    kv[it] = ld16(k + off, t < L);
+    qv[it] = ld16(q + off, t < L);
+  }
+#pragma unroll
+  for (int it = 0; it < NP; ++it) {
+    const int p = tid + 256 * it, t = p / PPR, cb = p - (p / PPR) * PPR;
+    *reinterpret_cast<uint4*>(sm.u.in.Ks + t * LDK + cb * EPV) = kv[it];
+    *reinterpret_cast<uint4*>(sm.u.in.Qs + t * LDK + cb * EPV) = qv[it];
   }
   __syncthreads();
 
@@ -195,9 +217,12 @@ __global__ __launch_bounds__(256) void prepare_kernel(
   float* A = sm.u.buf[w];
   for (int rr = w; rr < G; rr += 4) {
     const int h = gq * G + rr;
-    const size_t gi = (size_t)(tok0 + l) * Hv + h;
-    const float al = (l < L) ? alpha[gi] : 1.f;
-    const float bl = (l < L) ? beta[gi] : 0.f;
+    float al = al0, bl = bl0;
+    if (rr >= 4) {
+      const size_t gi = (size_t)(tok0 + l) * Hv + h;
+      al = (l < L) ? alpha[gi] : 1.f;
+      bl = (l < L) ? beta[gi] : 0.f;
+    }
     const float Gl = wave_inclusive_sum(hw_log2(al));
     const float Glast = __shfl(Gl, kC - 1, 64);
     ws.gam[((size_t)cid * Hv + h) * kC + l] = hw_exp2(Gl);
@@ -207,12 +232,45 @@ __global__ __launch_bounds__(256) void prepare_kernel(
     wave_lds_fence();
 
     // A[i][j] = beta_i exp(G_i - G_j) (k_i . k_j) for j < i, and the output
-    // mask M[i][j] = exp(G_i - G_j) (q_i . k_j) for j <= i; lane = column j.
+    // mask M[i][j] = exp(G_i - G_j) (q_i . k_j) for j <= i.  Lane = (8-column
+    // block cb, row group rg); rows rg, rg + 8, ...
     E* mo = ws.M + ((size_t)cid * Hv + h) * kC * kC;
-    for (int i = 0; i < kC; ++i) {
-      const float dg = (l <= i) ? hw_exp2(sm.gate[w][i] - Gl) : 0.f;
-      A[i * kLdT + l] = (l < i) ? sm.bet[w][i] * dg * sm.gram[i * kLdT + l] : 0.f;
-      mo[i * kC + l] = from_f32<E>(dg * sm.qkg[i * kLdT + l]);
+    {
+      const int cb = l & 7, rg = l >> 3;
+      float gj[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gj[e] = sm.gate[w][8 * cb + e];
+#pragma unroll
+      for (int i0 = 0; i0 < 8; ++i0) {
+        const int i = 8 * i0 + rg;
+        const float gi_ = sm.gate[w][i], bi = sm.bet[w][i];
+        const f32x4 k0 = *reinterpret_cast<const f32x4*>(sm.gram + i * kLdT + 8 * cb);
+        const f32x4 k1 = *reinterpret_cast<const f32x4*>(sm.gram + i * kLdT + 8 * cb + 4);
+        const f32x4 q0 = *reinterpret_cast<const f32x4*>(sm.qkg + i * kLdT + 8 * cb);
+        const f32x4 q1 = *reinterpret_cast<const f32x4*>(sm.qkg + i * kLdT + 8 * cb + 4);
+        const float kk8[8] = {k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
+        const float qk8[8] = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
+        float a8[8];
+        E m8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = 8 * cb + e;
+          const float dg = (j <= i) ? hw_exp2(gi_ - gj[e]) : 0.f;
+          a8[e] = (j < i) ? bi * dg * kk8[e] : 0.f;
+          m8[e] = from_f32<E>(dg * qk8[e]);
+        }
+        *reinterpret_cast<f32x4*>(A + i * kLdT + 8 * cb) = f32x4{a8[0], a8[1], a8[2], a8[3]};
+        *reinterpret_cast<f32x4*>(A + i * kLdT + 8 * cb + 4) = f32x4{a8[4], a8[5], a8[6], a8[7]};
+        if constexpr (BF) {
+          bf16x8 mv;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) mv[e] = m8[e];
+          *reinterpret_cast<bf16x8*>(mo + i * kC + 8 * cb) = mv;
+        } else {
+          *reinterpret_cast<f32x4*>(mo + i * kC + 8 * cb) = f32x4{m8[0], m8[1], m8[2], m8[3]};
+          *reinterpret_cast<f32x4*>(mo + i * kC + 8 * cb + 4) = f32x4{m8[4], m8[5], m8[6], m8[7]};
+        }
+      }
     }
     wave_lds_fence();
 
@@ -263,9 +321,32 @@ __global__ __launch_bounds__(256) void prepare_kernel(
       wave_lds_fence();
     }
 
-    // Tt = T diag(beta): lane = column j, coalesced rows.
+    // Tt = T diag(beta): lane = (8-column block, row group), 16-byte stores.
     E* tt = ws.Tt + ((size_t)cid * Hv + h) * kC * kC;
-    for (int i = 0; i < kC; ++i) tt[i * kC + l] = from_f32<E>(A[i * kLdT + l] * bl);
+    {
+      const int cb = l & 7, rg = l >> 3;
+      float bj[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bj[e] = sm.bet[w][8 * cb + e];
+#pragma unroll
+      for (int i0 = 0; i0 < 8; ++i0) {
+        const int i = 8 * i0 + rg;
+        const f32x4 t0 = *reinterpret_cast<const f32x4*>(A + i * kLdT + 8 * cb);
+        const f32x4 t1 = *reinterpret_cast<const f32x4*>(A + i * kLdT + 8 * cb + 4);
+        const float t8[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+        if constexpr (BF) {
+          bf16x8 tv;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) tv[e] = (bf16)(t8[e] * bj[e]);
+          *reinterpret_cast<bf16x8*>(tt + i * kC + 8 * cb) = tv;
+        } else {
+          *reinterpret_cast<f32x4*>(tt + i * kC + 8 * cb) =
+              f32x4{t8[0] * bj[0], t8[1] * bj[1], t8[2] * bj[2], t8[3] * bj[3]};
+          *reinterpret_cast<f32x4*>(tt + i * kC + 8 * cb + 4) =
+              f32x4{t8[4] * bj[4], t8[5] * bj[5], t8[6] * bj[6], t8[7] * bj[7]};
+        }
+      }
+    }
     wave_lds_fence();
   }
 }
@@ -321,8 +402,9 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
 
   int cid0, nch;
   if (cm.tab) {
-    cid0 = cm.seq_off[seq];
-    nch = min(cm.seq_off[seq + 1], cm.nc_max) - cid0;
+    const_i32* so = (const_i32*)cm.seq_off;
+    cid0 = so[seq];
+    nch = min(so[seq + 1], cm.nc_max) - cid0;
   } else {
     cid0 = seq * cm.Nc;
     nch = cm.Nc;
@@ -611,18 +693,24 @@ namespace split {
 constexpr int kSlices = 2;                   // 16-row value slices per workgroup
 constexpr int kRows = 16 * kSlices;          // value rows per workgroup
 constexpr int kNsl = kD / kRows;             // workgroups per value head
-constexpr int kWaves = 2 * kSlices + 1;      // chain x2, output x2, producer
+constexpr int kWaves = 2 * kSlices + 2;      // chain x2, output x2, producer x2
 constexpr int kSlots = 3;
 constexpr int kKB = kC * kD * 2;             // K tile, bytes
 constexpr int kKTB = kD * kC * 2;            // K^T tile
 constexpr int kTB = kC * kC * 2;             // Tt tile
-constexpr int kDmaOps = kKB / 1024 + kKTB / 1024 + kTB / 1024 + 2;
+constexpr int kVB = kC * kRows * 2;          // V tile of the workgroup's value rows
+// Copy ops per chunk of the two producer waves (each keeps two chunks in
+// flight, within the 63 outstanding vector-memory ops a wave can count).
+constexpr int kDmaOps0 = kKB / 1024 + kVB / 1024 + 2;    // K, V, gam, dec
+constexpr int kDmaOps1 = kKTB / 1024 + kTB / 1024;        // K^T, Tt
+static_assert(2 * kDmaOps0 <= 63 && 2 * kDmaOps1 <= 63, "vmcnt range");
 
 constexpr int kGdSlots = 4;                  // gam/dec ring: chunks c-1 .. c+2 live
 struct Slot {
   alignas(16) uint8_t K[kKB];
   alignas(16) uint8_t KT[kKTB];
   alignas(16) uint8_t T[kTB];
+  alignas(16) uint8_t V[kVB];                // [64 tokens][32 value rows], 64-byte rows
 };
 struct GateSlot {
   alignas(16) float gam[kC];
@@ -636,7 +724,6 @@ struct Smem {
   Slot slot[kSlots];
   GateSlot gd[kGdSlots];
   Hand hand[2][kSlices];
-  alignas(16) bf16 ost[kSlices][kC * 16];    // per output wave O staging
 };
 
 // row x (0..31 within a 32-row block, tile t2 = x / 16, r = x % 16) -> physical
@@ -644,6 +731,9 @@ __device__ __forceinline__ int prow(int t, int r) {
   return 32 * (t >> 1) + 8 * (r >> 2) + 4 * (t & 1) + (r & 3);
 }
 __device__ __forceinline__ int swz(int row) { return (row & 3) | ((row >> 1) & 4); }
+// V tile rows are 4 pieces of 16 bytes; a chain wave reads 8 consecutive tokens
+// 8 apart per lane group, so the piece order is rotated by (token / 8) % 4.
+__device__ __forceinline__ int vswz(int tok) { return (tok >> 3) & 3; }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -682,8 +772,9 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
 
   int cid0, nch;
   if (cm.tab) {
-    cid0 = cm.seq_off[seq];
-    nch = min(cm.seq_off[seq + 1], cm.nc_max) - cid0;
+    const_i32* so = (const_i32*)cm.seq_off;
+    cid0 = so[seq];
+    nch = min(so[seq + 1], cm.nc_max) - cid0;
   } else {
     cid0 = seq * cm.Nc;
     nch = cm.Nc;
@@ -692,39 +783,56 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
   const size_t hv_stride = (size_t)Hv * kD;         // elements between tokens of v / o
   const size_t qk_stride = (size_t)Hqk * kD;
 
-  if (w == 2 * kSlices) {
-    // ------------------------------------------------------------ producer
+  if (w >= 2 * kSlices) {
+    // ------------------------------------------------------------ producers
+    const int pw = w - 2 * kSlices;
     auto issue = [&](int c) {
       const int cid = cid0 + c;
       int tok0, L;
       chunk_of(cm, cid, tok0, L);
       Slot& S = sm.slot[c % kSlots];
-      const bf16* kbase = k + (size_t)tok0 * qk_stride + (size_t)gq * kD;
+      if (pw == 0) {
+        const bf16* kbase = k + (size_t)tok0 * qk_stride + (size_t)gq * kD;
 #pragma unroll
-      for (int it = 0; it < kKB / 1024; ++it) {
-        const int row = 4 * it + (l >> 4), p = (l & 15) ^ swz(row);
-        dma16(kbase + (size_t)min(row, L - 1) * qk_stride + 8 * p, S.K + 1024 * it);
-      }
-      const bf16* ktb = ws.KT + ((size_t)cid * Hqk + gq) * kD * kC;
+        for (int it = 0; it < kKB / 1024; ++it) {
+          const int row = 4 * it + (l >> 4), p = (l & 15) ^ swz(row);
+          dma16(kbase + (size_t)min(row, L - 1) * qk_stride + 8 * p, S.K + 1024 * it);
+        }
+        const bf16* vbase = v + (size_t)tok0 * hv_stride + (size_t)h * kD + dvb;
 #pragma unroll
-      for (int it = 0; it < kKTB / 1024; ++it) {
-        const int row = 8 * it + (l >> 3), p = (l & 7) ^ swz(row);
-        dma16(ktb + row * kC + 8 * p, S.KT + 1024 * it);
-      }
-      const bf16* tb = ws.Tt + ((size_t)cid * Hv + h) * kC * kC;
+        for (int it = 0; it < kVB / 1024; ++it) {
+          const int row = 16 * it + (l >> 2), p = (l & 3) ^ vswz(row);
+          dma16(vbase + (size_t)min(row, L - 1) * hv_stride + 8 * p, S.V + 1024 * it);
+        }
+        GateSlot& Gd = sm.gd[c % kGdSlots];
+        dma4(ws.gam + ((size_t)cid * Hv + h) * kC + l, Gd.gam);
+        dma4(ws.dec + ((size_t)cid * Hv + h) * kC + l, Gd.dec);
+      } else {
+        const bf16* ktb = ws.KT + ((size_t)cid * Hqk + gq) * kD * kC;
 #pragma unroll
-      for (int it = 0; it < kTB / 1024; ++it) {
-        const int row = 8 * it + (l >> 3), p = (l & 7) ^ swz(row);
-        dma16(tb + row * kC + 8 * p, S.T + 1024 * it);
+        for (int it = 0; it < kKTB / 1024; ++it) {
+          const int row = 8 * it + (l >> 3), p = (l & 7) ^ swz(row);
+          dma16(ktb + row * kC + 8 * p, S.KT + 1024 * it);
+        }
+        const bf16* tb = ws.Tt + ((size_t)cid * Hv + h) * kC * kC;
+#pragma unroll
+        for (int it = 0; it < kTB / 1024; ++it) {
+          const int row = 8 * it + (l >> 3), p = (l & 7) ^ swz(row);
+          dma16(tb + row * kC + 8 * p, S.T + 1024 * it);
+        }
       }
-      GateSlot& Gd = sm.gd[c % kGdSlots];
-      dma4(ws.gam + ((size_t)cid * Hv + h) * kC + l, Gd.gam);
-      dma4(ws.dec + ((size_t)cid * Hv + h) * kC + l, Gd.dec);
+    };
+    // Wait until only the copies of the newest chunk are outstanding.
+    auto wait_all_but_last = [&]() {
+      if (pw == 0)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaOps0) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaOps1) : "memory");
     };
     if (nch > 0) issue(0);
     if (nch > 1) {
       issue(1);
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaOps) : "memory");
+      wait_all_but_last();
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
@@ -732,7 +840,7 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
     for (int i = 0; i <= nch; ++i) {
       if (i + 2 < nch) {
         issue(i + 2);
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaOps) : "memory");
+        wait_all_but_last();
       } else {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
@@ -752,26 +860,21 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
       for (int t = 0; t < 8; ++t)
         ST[t] = hp ? *reinterpret_cast<const f32x4*>(hp + prow(t, 4 * g)) : zero4();
     }
-    // V of this lane's 16 tokens (physical 32kk + 8g + 0..7) and value row.
-    auto load_v = [&](int c, bf16* vr) {
-      int tok0, L;
-      chunk_of(cm, cid0 + c, tok0, L);
-      const bf16* vb = v + (size_t)tok0 * hv_stride + (size_t)h * kD + dv0 + r;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int t = 32 * (e >> 3) + 8 * g + (e & 7);
-        vr[e] = (t < L) ? vb[(size_t)t * hv_stride] : (bf16)0.f;
-      }
-    };
-    bf16 vcur[16], vnext[16];
-    if (nch > 0) load_v(0, vcur);
     barrier_lds();
     for (int i = 0; i <= nch; ++i) {
       if (i < nch) {
-        if (i + 1 < nch) load_v(i + 1, vnext);
         const Slot& S = sm.slot[i % kSlots];
         const GateSlot& Gd = sm.gd[i % kGdSlots];
         Hand& H = sm.hand[i & 1][s];
+        // A fragments of P = K S^T, all issued before the first MFMA.
+        bf16x8 AK[4][4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const int row = prow(mt, r);
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk)
+            AK[mt][kk] = *reinterpret_cast<const bf16x8*>(S.K + row * 256 + 16 * ((4 * kk + g) ^ swz(row)));
+        }
         bf16x8 SB[4];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
@@ -781,39 +884,50 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
         // P = K S^T  (rows: physical tokens prow(mt, r))
         f32x4 P[4];
 #pragma unroll
+        for (int mt = 0; mt < 4; ++mt) P[mt] = zero4();
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) P[mt] = mfma_bf16(AK[mt][kk], SB[kk], P[mt]);
+        // Tt fragments and this lane's V values (tokens 32(mt/2) + 8g + 4(mt%2) + i)
+        bf16x8 AT[4][2];
+#pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-          P[mt] = zero4();
           const int row = prow(mt, r);
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            const int p = (4 * kk + g) ^ swz(row);
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(S.K + row * 256 + 16 * p);
-            P[mt] = mfma_bf16(a, SB[kk], P[mt]);
-          }
+          for (int kk = 0; kk < 2; ++kk)
+            AT[mt][kk] = *reinterpret_cast<const bf16x8*>(S.T + row * 128 + 16 * ((4 * kk + g) ^ swz(row)));
         }
-        // X = V - diag(gam) P; this lane's rows are tokens 32(mt/2) + 8g + 4(mt%2) + i.
+        // V at tokens 32(mt/2) + 8g + 4(mt%2) + i: the swizzle term vswz(token)
+        // is g for all of them, so the reads are fixed offsets from one base.
+        // Rows beyond L hold a copy of the last token; they only meet the zero
+        // columns of Tt, so they need no masking.
+        const int col = 16 * s + r;                   // value row within the workgroup
+        const bf16* vl = reinterpret_cast<const bf16*>(S.V) + 8 * g * kRows +
+                         8 * ((col >> 3) ^ g) + (col & 7);
+        float vv[4][4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i2 = 0; i2 < 4; ++i2)
+            vv[mt][i2] = (float)vl[(32 * (mt >> 1) + 4 * (mt & 1) + i2) * kRows];
+        // X = V - diag(gam) P
         f32x4 X[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           const f32x4 gm = *reinterpret_cast<const f32x4*>(Gd.gam + 32 * (mt >> 1) + 8 * g + 4 * (mt & 1));
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            X[mt][i] = (float)vcur[8 * (mt >> 1) + 4 * (mt & 1) + i] - gm[i] * P[mt][i];
+          for (int i2 = 0; i2 < 4; ++i2) X[mt][i2] = vv[mt][i2] - gm[i2] * P[mt][i2];
         }
         const bf16x8 XB[2] = {pack_b(X[0], X[1]), pack_b(X[2], X[3])};
         // Dl = Tt X
         f32x4 Dl[4];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          Dl[mt] = zero4();
-          const int row = prow(mt, r);
+        for (int mt = 0; mt < 4; ++mt) Dl[mt] = zero4();
 #pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            const int p = (4 * kk + g) ^ swz(row);
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(S.T + row * 128 + 16 * p);
-            Dl[mt] = mfma_bf16(a, XB[kk], Dl[mt]);
-          }
-        }
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) Dl[mt] = mfma_bf16(AT[mt][kk], XB[kk], Dl[mt]);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) H.db[kk][l] = pack_b(Dl[2 * kk], Dl[2 * kk + 1]);
         // state update: S^T <- gam_last S^T + K^T diag(dec) Dl
@@ -821,23 +935,21 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
         for (int mt = 0; mt < 4; ++mt) {
           const f32x4 dc = *reinterpret_cast<const f32x4*>(Gd.dec + 32 * (mt >> 1) + 8 * g + 4 * (mt & 1));
 #pragma unroll
-          for (int i = 0; i < 4; ++i) Dl[mt][i] *= dc[i];
+          for (int i2 = 0; i2 < 4; ++i2) Dl[mt][i2] *= dc[i2];
         }
         const bf16x8 DTB[2] = {pack_b(Dl[0], Dl[1]), pack_b(Dl[2], Dl[3])};
         const float gL = Gd.gam[kC - 1];
 #pragma unroll
+        for (int t = 0; t < 8; ++t) ST[t] *= gL;
+#pragma unroll
         for (int t = 0; t < 8; ++t) {
-          ST[t] *= gL;
           const int row = prow(t, r);
 #pragma unroll
           for (int kk = 0; kk < 2; ++kk) {
-            const int p = (4 * kk + g) ^ swz(row);
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(S.KT + row * 128 + 16 * p);
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(S.KT + row * 128 + 16 * ((4 * kk + g) ^ swz(row)));
             ST[t] = mfma_bf16(a, DTB[kk], ST[t]);
           }
         }
-#pragma unroll
-        for (int e = 0; e < 16; ++e) vcur[e] = vnext[e];
       }
       barrier_lds();
     }
@@ -902,7 +1014,11 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
     O[2] = mfma_bf16(op.mf[3], DB[1], O[2]);
     O[3] = mfma_bf16(op.mf[4], DB[0], O[3]);
     O[3] = mfma_bf16(op.mf[5], DB[1], O[3]);
-    bf16* st = sm.ost[s];
+    // O rows are natural tokens 16mt + 4g + i; this lane owns value row dv0 + r.
+    // The hand-off slot just read is free until the chain wave refills it two
+    // iterations later, so it stages O for 16-byte stores.
+    wave_lds_fence();
+    bf16* st = reinterpret_cast<bf16*>(&sm.hand[c & 1][s]);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -911,13 +1027,11 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int pc = l + 64 * j, t = pc >> 1, half = pc & 1;
-      if (t < op.L) {
-        const uint4 val = *reinterpret_cast<const uint4*>(st + t * 16 + 8 * half);
+      const uint4 val = *reinterpret_cast<const uint4*>(st + t * 16 + 8 * half);
+      if (t < op.L)
         *reinterpret_cast<uint4*>(o + (size_t)(op.tok0 + t) * hv_stride + (size_t)h * kD + dv0 +
                                   8 * half) = val;
-      }
     }
-    wave_lds_fence();
   };
   // Iteration i emits chunk i-1 and then refills the same register set with
   // chunk i+1, so each set is loaded about one and a half iterations before
