@@ -668,49 +668,62 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
 
 // ---------------------------------------------------------------- split scan (bf16)
 // The bf16 scan with the work of each 16-row value slice split between two
-// waves and the chunk operands brought in by a third:
+// waves and all chunk operands brought into LDS by two more:
 //
 //  * chain wave (one per slice): the serial part only.  P = K S^T, X, Dl =
 //    Tt X, the state update; it hands S^T (as the B fragments it built for P)
 //    and Dl to the output wave through LDS.  40 MFMAs per chunk.
-//  * output wave (one per slice), one chunk behind: O = diag(gam) Q S^T + M Dl
-//    with its Q and M fragments loaded straight from global memory into
-//    registers one chunk ahead.  22 MFMAs per chunk.
-//  * producer wave: copies K, K^T, Tt, gam and dec of chunk c+2 from global
-//    memory straight into LDS (global_load_lds_dwordx4, no registers) while
-//    chunk c is computed; three LDS slots rotate.
+//  * output wave (one per slice), one chunk behind: O = diag(gam) Q S^T + M Dl.
+//    22 MFMAs per chunk.
+//  * two producer waves: copy K^T, Tt, V, gam, dec of chunk c+2 and Q, M of
+//    chunk c from global memory straight into LDS rings
+//    (global_load_lds_dwordx4: no registers, no VALU) while chunk c is
+//    computed.
+//
+// K is kept in LDS only as K^T.  The A fragments of P = K S^T (rows = tokens,
+// K slots = d_k) are read from K^T with ds_read_b64_tr_b16, which transposes
+// 16-bit elements across each group of 16 lanes: input lane p reads four
+// tokens of K^T row dk(p/4) starting at token base + 8 (p%4), and output lane m
+// receives element m%4 of input lanes m/4, m/4+4, m/4+8, m/4+12, i.e.
+// K[token(m)][dk(0..3)].  This halves the bytes each CU moves per chunk.
 //
 // Token and d_k order.  An accumulator tile pair holds, per lane group g, rows
 // {4g..4g+3} and {16+4g..16+4g+3} of a 32-row block; used as a B fragment these
 // are the K slots.  Inside each 32-row block the library stores logical row
 // x at physical position prow(x) = 8*((x%16)/4) + 4*(x/16) + x%4, so that the 8
 // K slots of lane group g are the 8 consecutive physical rows 8g..8g+7 and
-// every A fragment is a single 16-byte LDS read.  The permutation is applied to
-// tokens (rows of P, X, Dl) and to d_k (rows of S^T); it is undone where the
-// state is loaded and stored.  LDS rows are XOR-swizzled in 16-byte pieces
-// (swz) so the 16 gathered rows of an A fragment hit distinct banks.
+// every A fragment is one 16-byte LDS read (or two transposed 8-byte reads).
+// The permutation is applied to tokens (rows of P, X, Dl) and to d_k (rows of
+// S^T); it is undone where the state is loaded and stored.  LDS rows are
+// XOR-swizzled in 16-byte pieces (swz) so the 16 gathered rows of an A
+// fragment hit distinct banks.
 namespace split {
 constexpr int kSlices = 2;                   // 16-row value slices per workgroup
 constexpr int kRows = 16 * kSlices;          // value rows per workgroup
 constexpr int kNsl = kD / kRows;             // workgroups per value head
 constexpr int kWaves = 2 * kSlices + 2;      // chain x2, output x2, producer x2
-constexpr int kSlots = 3;
-constexpr int kKB = kC * kD * 2;             // K tile, bytes
-constexpr int kKTB = kD * kC * 2;            // K^T tile
+constexpr int kSlots = 3;                    // chain operands: chunks c, c+1, c+2
+constexpr int kQmSlots = 2;                  // output operands: chunks c-1, c
+constexpr int kGdSlots = 4;                  // gam/dec: chunks c-1 .. c+2
+constexpr int kKTB = kD * kC * 2;            // K^T tile, bytes
 constexpr int kTB = kC * kC * 2;             // Tt tile
 constexpr int kVB = kC * kRows * 2;          // V tile of the workgroup's value rows
-// Copy ops per chunk of the two producer waves (each keeps two chunks in
-// flight, within the 63 outstanding vector-memory ops a wave can count).
-constexpr int kDmaOps0 = kKB / 1024 + kVB / 1024 + 2;    // K, V, gam, dec
-constexpr int kDmaOps1 = kKTB / 1024 + kTB / 1024;        // K^T, Tt
-static_assert(2 * kDmaOps0 <= 63 && 2 * kDmaOps1 <= 63, "vmcnt range");
+constexpr int kQB = kC * kD * 2;             // Q tile
+constexpr int kMB = kC * kC * 2;             // M tile
+// Copy ops of each producer per chunk; each keeps at most 63 in flight.
+constexpr int kOpsA = kTB / 1024 + kVB / 1024 + 2;      // Tt, V, gam, dec   (chunk c+2)
+constexpr int kOpsQM = kQB / 1024 + kMB / 1024;         // Q, M             (chunk c)
+constexpr int kOpsKT = kKTB / 1024;                     // K^T              (chunk c+2)
+static_assert(2 * kOpsA + kOpsQM <= 63 && 2 * kOpsKT <= 63, "vmcnt range");
 
-constexpr int kGdSlots = 4;                  // gam/dec ring: chunks c-1 .. c+2 live
 struct Slot {
-  alignas(16) uint8_t K[kKB];
-  alignas(16) uint8_t KT[kKTB];
-  alignas(16) uint8_t T[kTB];
+  alignas(16) uint8_t KT[kKTB];              // [128 d_k][64 tokens], 128-byte rows
+  alignas(16) uint8_t T[kTB];                // [64][64], 128-byte rows
   alignas(16) uint8_t V[kVB];                // [64 tokens][32 value rows], 64-byte rows
+};
+struct QmSlot {
+  alignas(16) uint8_t Q[kQB];                // [64 tokens][128 d_k], 256-byte rows
+  alignas(16) uint8_t M[kMB];                // [64][64], 128-byte rows
 };
 struct GateSlot {
   alignas(16) float gam[kC];
@@ -722,11 +735,12 @@ struct Hand {
 };
 struct Smem {
   Slot slot[kSlots];
+  QmSlot qm[kQmSlots];
   GateSlot gd[kGdSlots];
   Hand hand[2][kSlices];
 };
 
-// row x (0..31 within a 32-row block, tile t2 = x / 16, r = x % 16) -> physical
+// logical row r of 16-row tile t -> physical row (see above)
 __device__ __forceinline__ int prow(int t, int r) {
   return 32 * (t >> 1) + 8 * (r >> 2) + 4 * (t & 1) + (r & 3);
 }
@@ -736,6 +750,8 @@ __device__ __forceinline__ int swz(int row) { return (row & 3) | ((row >> 1) & 4
 __device__ __forceinline__ int vswz(int tok) { return (tok >> 3) & 3; }
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
   __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_dst, 16, 0, 0);
@@ -743,10 +759,16 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
 __device__ __forceinline__ void dma4(const void* src, void* lds_dst) {
   __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_dst, 4, 0, 0);
 }
+__device__ __forceinline__ s16x4 lds_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+}
 
 __device__ __forceinline__ void barrier_lds() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
+
+// Copies of a [rows][bytes_per_row] tile of 16-byte pieces with XOR swizzle:
+// instruction `it` fills LDS bytes [1024 it, 1024 it + 1024).
 }  // namespace split
 
 __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
@@ -755,6 +777,7 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
     ChunkMap cm, int Hqk, int Hv, int G) {
   using namespace split;
   __shared__ Smem sm;
+  (void)k;
 
   const int nlin = Hv * kNsl;
   int lin = blockIdx.x;
@@ -786,65 +809,98 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
   if (w >= 2 * kSlices) {
     // ------------------------------------------------------------ producers
     const int pw = w - 2 * kSlices;
-    auto issue = [&](int c) {
+    // Tt, V, gam, dec of chunk c into ring slots (c % 3, c % 4).
+    auto issue_a = [&](int c) {
       const int cid = cid0 + c;
       int tok0, L;
       chunk_of(cm, cid, tok0, L);
       Slot& S = sm.slot[c % kSlots];
-      if (pw == 0) {
-        const bf16* kbase = k + (size_t)tok0 * qk_stride + (size_t)gq * kD;
+      const bf16* tb = ws.Tt + ((size_t)cid * Hv + h) * kC * kC;
 #pragma unroll
-        for (int it = 0; it < kKB / 1024; ++it) {
-          const int row = 4 * it + (l >> 4), p = (l & 15) ^ swz(row);
-          dma16(kbase + (size_t)min(row, L - 1) * qk_stride + 8 * p, S.K + 1024 * it);
-        }
-        const bf16* vbase = v + (size_t)tok0 * hv_stride + (size_t)h * kD + dvb;
+      for (int it = 0; it < kTB / 1024; ++it) {
+        const int row = 8 * it + (l >> 3), p = (l & 7) ^ swz(row);
+        dma16(tb + row * kC + 8 * p, S.T + 1024 * it);
+      }
+      const bf16* vbase = v + (size_t)tok0 * hv_stride + (size_t)h * kD + dvb;
 #pragma unroll
-        for (int it = 0; it < kVB / 1024; ++it) {
-          const int row = 16 * it + (l >> 2), p = (l & 3) ^ vswz(row);
-          dma16(vbase + (size_t)min(row, L - 1) * hv_stride + 8 * p, S.V + 1024 * it);
-        }
-        GateSlot& Gd = sm.gd[c % kGdSlots];
-        dma4(ws.gam + ((size_t)cid * Hv + h) * kC + l, Gd.gam);
-        dma4(ws.dec + ((size_t)cid * Hv + h) * kC + l, Gd.dec);
-      } else {
-        const bf16* ktb = ws.KT + ((size_t)cid * Hqk + gq) * kD * kC;
+      for (int it = 0; it < kVB / 1024; ++it) {
+        const int row = 16 * it + (l >> 2), p = (l & 3) ^ vswz(row);
+        dma16(vbase + (size_t)min(row, L - 1) * hv_stride + 8 * p, S.V + 1024 * it);
+      }
+      GateSlot& Gd = sm.gd[c % kGdSlots];
+      dma4(ws.gam + ((size_t)cid * Hv + h) * kC + l, Gd.gam);
+      dma4(ws.dec + ((size_t)cid * Hv + h) * kC + l, Gd.dec);
+    };
+    // Q, M of chunk c into qm slot c % 2.
+    auto issue_qm = [&](int c) {
+      const int cid = cid0 + c;
+      int tok0, L;
+      chunk_of(cm, cid, tok0, L);
+      QmSlot& Qs = sm.qm[c % kQmSlots];
+      const bf16* qbase = q + (size_t)tok0 * qk_stride + (size_t)gq * kD;
 #pragma unroll
-        for (int it = 0; it < kKTB / 1024; ++it) {
-          const int row = 8 * it + (l >> 3), p = (l & 7) ^ swz(row);
-          dma16(ktb + row * kC + 8 * p, S.KT + 1024 * it);
-        }
-        const bf16* tb = ws.Tt + ((size_t)cid * Hv + h) * kC * kC;
+      for (int it = 0; it < kQB / 1024; ++it) {
+        const int row = 4 * it + (l >> 4), p = (l & 15) ^ swz(row);
+        dma16(qbase + (size_t)min(row, L - 1) * qk_stride + 8 * p, Qs.Q + 1024 * it);
+      }
+      const bf16* mb = ws.M + ((size_t)cid * Hv + h) * kC * kC;
 #pragma unroll
-        for (int it = 0; it < kTB / 1024; ++it) {
-          const int row = 8 * it + (l >> 3), p = (l & 7) ^ swz(row);
-          dma16(tb + row * kC + 8 * p, S.T + 1024 * it);
-        }
+      for (int it = 0; it < kMB / 1024; ++it) {
+        const int row = 8 * it + (l >> 3), p = (l & 7) ^ swz(row);
+        dma16(mb + row * kC + 8 * p, Qs.M + 1024 * it);
       }
     };
-    // Wait until only the copies of the newest chunk are outstanding.
-    auto wait_all_but_last = [&]() {
-      if (pw == 0)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaOps0) : "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaOps1) : "memory");
+    // K^T of chunk c into slot c % 3.
+    auto issue_kt = [&](int c) {
+      const int cid = cid0 + c;
+      Slot& S = sm.slot[c % kSlots];
+      const bf16* ktb = ws.KT + ((size_t)cid * Hqk + gq) * kD * kC;
+#pragma unroll
+      for (int it = 0; it < kKTB / 1024; ++it) {
+        const int row = 8 * it + (l >> 3), p = (l & 7) ^ swz(row);
+        dma16(ktb + row * kC + 8 * p, S.KT + 1024 * it);
+      }
     };
-    if (nch > 0) issue(0);
-    if (nch > 1) {
-      issue(1);
-      wait_all_but_last();
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    barrier_lds();
-    for (int i = 0; i <= nch; ++i) {
-      if (i + 2 < nch) {
-        issue(i + 2);
-        wait_all_but_last();
+    // Chunk c's chain operands must be in LDS by the barrier that ends
+    // iteration c-1, its Q and M by the one that ends iteration c.  Each
+    // producer waits until only its newest chain-operand copies are pending.
+    if (pw == 0) {
+      if (nch > 0) issue_a(0);
+      if (nch > 1) {
+        issue_a(1);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kOpsA) : "memory");
       } else {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
       barrier_lds();
+      for (int i = 0; i <= nch; ++i) {
+        if (i < nch) issue_qm(i);
+        if (i + 2 < nch) {
+          issue_a(i + 2);
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kOpsA) : "memory");
+        } else {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        barrier_lds();
+      }
+    } else {
+      if (nch > 0) issue_kt(0);
+      if (nch > 1) {
+        issue_kt(1);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kOpsKT) : "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      barrier_lds();
+      for (int i = 0; i <= nch; ++i) {
+        if (i + 2 < nch) {
+          issue_kt(i + 2);
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kOpsKT) : "memory");
+        } else {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        barrier_lds();
+      }
     }
     return;
   }
@@ -866,14 +922,21 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
         const Slot& S = sm.slot[i % kSlots];
         const GateSlot& Gd = sm.gd[i % kGdSlots];
         Hand& H = sm.hand[i & 1][s];
-        // A fragments of P = K S^T, all issued before the first MFMA.
+        // A fragments of P = K S^T from K^T by transposed reads: this lane, as
+        // input lane r of group g, reads 4 tokens of K^T row
+        // 32kk + 8g + r/4 (+4) starting at token 32(mt/2) + 8(r%4) + 4(mt%2).
         bf16x8 AK[4][4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-          const int row = prow(mt, r);
+          const int t0 = 32 * (mt >> 1) + 8 * (r & 3) + 4 * (mt & 1);
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk)
-            AK[mt][kk] = *reinterpret_cast<const bf16x8*>(S.K + row * 256 + 16 * ((4 * kk + g) ^ swz(row)));
+          for (int kk = 0; kk < 4; ++kk) {
+            const int d0 = 32 * kk + 8 * g + (r >> 2), d1 = d0 + 4;
+            const s16x4 lo = lds_tr16(S.KT + d0 * 128 + 16 * ((t0 >> 3) ^ swz(d0)) + 2 * (t0 & 7));
+            const s16x4 hi = lds_tr16(S.KT + d1 * 128 + 16 * ((t0 >> 3) ^ swz(d1)) + 2 * (t0 & 7));
+            const s16x4 lh[2] = {lo, hi};
+            AK[mt][kk] = *reinterpret_cast<const bf16x8*>(lh);
+          }
         }
         bf16x8 SB[4];
 #pragma unroll
@@ -889,7 +952,7 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
         for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt) P[mt] = mfma_bf16(AK[mt][kk], SB[kk], P[mt]);
-        // Tt fragments and this lane's V values (tokens 32(mt/2) + 8g + 4(mt%2) + i)
+        // Tt fragments
         bf16x8 AT[4][2];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
@@ -905,19 +968,14 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
         const int col = 16 * s + r;                   // value row within the workgroup
         const bf16* vl = reinterpret_cast<const bf16*>(S.V) + 8 * g * kRows +
                          8 * ((col >> 3) ^ g) + (col & 7);
-        float vv[4][4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int i2 = 0; i2 < 4; ++i2)
-            vv[mt][i2] = (float)vl[(32 * (mt >> 1) + 4 * (mt & 1) + i2) * kRows];
         // X = V - diag(gam) P
         f32x4 X[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           const f32x4 gm = *reinterpret_cast<const f32x4*>(Gd.gam + 32 * (mt >> 1) + 8 * g + 4 * (mt & 1));
 #pragma unroll
-          for (int i2 = 0; i2 < 4; ++i2) X[mt][i2] = vv[mt][i2] - gm[i2] * P[mt][i2];
+          for (int i2 = 0; i2 < 4; ++i2)
+            X[mt][i2] = (float)vl[(32 * (mt >> 1) + 4 * (mt & 1) + i2) * kRows] - gm[i2] * P[mt][i2];
         }
         const bf16x8 XB[2] = {pack_b(X[0], X[1]), pack_b(X[2], X[3])};
         // Dl = Tt X
@@ -962,91 +1020,64 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
   }
 
   // -------------------------------------------------------------- output wave
+  // Chunk c's O at iteration c+1: Q and M from the qm ring, S^T and Dl B
+  // fragments from the chain wave's hand-off slot, gam from the gate ring.
   const int s = w - kSlices, dv0 = dvb + 16 * s;
-  // Operands of one chunk in registers: Q fragments (natural token rows 16mt + r,
-  // K slots d_k 32kk + 8g + j) and M fragments (K slots tokens 32kk + 8g + j;
-  // the upper half of rows 0..31 is zero and skipped).  gam comes from the LDS
-  // gate ring.
-  struct Ops {
-    bf16x8 qf[4][4];
-    bf16x8 mf[6];
-    int tok0, L;
-  };
-  auto load_ops = [&](int c, Ops& op) {
-    const int cid = cid0 + c;
-    chunk_of(cm, cid, op.tok0, op.L);
-    const bf16* qb = q + (size_t)op.tok0 * qk_stride + (size_t)gq * kD + 8 * g;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const bf16* qr = qb + (size_t)min(16 * mt + r, op.L - 1) * qk_stride;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) op.qf[mt][kk] = *reinterpret_cast<const bf16x8*>(qr + 32 * kk);
-    }
-    const bf16* mb = ws.M + ((size_t)cid * Hv + h) * kC * kC + 8 * g;
-    op.mf[0] = *reinterpret_cast<const bf16x8*>(mb + (0 + r) * kC);
-    op.mf[1] = *reinterpret_cast<const bf16x8*>(mb + (16 + r) * kC);
-    op.mf[2] = *reinterpret_cast<const bf16x8*>(mb + (32 + r) * kC);
-    op.mf[3] = *reinterpret_cast<const bf16x8*>(mb + (32 + r) * kC + 32);
-    op.mf[4] = *reinterpret_cast<const bf16x8*>(mb + (48 + r) * kC);
-    op.mf[5] = *reinterpret_cast<const bf16x8*>(mb + (48 + r) * kC + 32);
-  };
-  auto emit = [&](int c, const Ops& op) {
-    const Hand& H = sm.hand[c & 1][s];
-    const GateSlot& Gd = sm.gd[c % kGdSlots];
-    bf16x8 SB[4], DB[2];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) SB[kk] = H.sb[kk][l];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) DB[kk] = H.db[kk][l];
-    f32x4 O[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      O[mt] = zero4();
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) O[mt] = mfma_bf16(op.qf[mt][kk], SB[kk], O[mt]);
-      const f32x4 gm = *reinterpret_cast<const f32x4*>(Gd.gam + 16 * mt + 4 * g);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) O[mt][i] *= gm[i];
-    }
-    O[0] = mfma_bf16(op.mf[0], DB[0], O[0]);
-    O[1] = mfma_bf16(op.mf[1], DB[0], O[1]);
-    O[2] = mfma_bf16(op.mf[2], DB[0], O[2]);
-    O[2] = mfma_bf16(op.mf[3], DB[1], O[2]);
-    O[3] = mfma_bf16(op.mf[4], DB[0], O[3]);
-    O[3] = mfma_bf16(op.mf[5], DB[1], O[3]);
-    // O rows are natural tokens 16mt + 4g + i; this lane owns value row dv0 + r.
-    // The hand-off slot just read is free until the chain wave refills it two
-    // iterations later, so it stages O for 16-byte stores.
-    wave_lds_fence();
-    bf16* st = reinterpret_cast<bf16*>(&sm.hand[c & 1][s]);
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st[(16 * mt + 4 * g + i) * 16 + r] = (bf16)O[mt][i];
-    wave_lds_fence();
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int pc = l + 64 * j, t = pc >> 1, half = pc & 1;
-      const uint4 val = *reinterpret_cast<const uint4*>(st + t * 16 + 8 * half);
-      if (t < op.L)
-        *reinterpret_cast<uint4*>(o + (size_t)(op.tok0 + t) * hv_stride + (size_t)h * kD + dv0 +
-                                  8 * half) = val;
-    }
-  };
-  // Iteration i emits chunk i-1 and then refills the same register set with
-  // chunk i+1, so each set is loaded about one and a half iterations before
-  // use.  Even chunks use set A, odd chunks set B; every role executes
-  // exactly nch + 1 loop barriers after the prologue barrier.
-  Ops opA, opB;
-  if (nch > 0) load_ops(0, opA);
   barrier_lds();
-  for (int i = 0; i <= nch; i += 2) {
-    if (i >= 1) emit(i - 1, opB);
-    if (i + 1 < nch) load_ops(i + 1, opB);
-    barrier_lds();
-    if (i + 1 > nch) break;
-    emit(i, opA);
-    if (i + 2 < nch) load_ops(i + 2, opA);
+  for (int i = 0; i <= nch; ++i) {
+    if (i >= 1) {
+      const int c = i - 1;
+      int tok0, L;
+      chunk_of(cm, cid0 + c, tok0, L);
+      const QmSlot& Qs = sm.qm[c % kQmSlots];
+      const Hand& H = sm.hand[c & 1][s];
+      const GateSlot& Gd = sm.gd[c % kGdSlots];
+      bf16x8 SB[4], DB[2];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) SB[kk] = H.sb[kk][l];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) DB[kk] = H.db[kk][l];
+      f32x4 O[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int row = 16 * mt + r;
+        O[mt] = zero4();
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(Qs.Q + row * 256 + 16 * ((4 * kk + g) ^ swz(row)));
+          O[mt] = mfma_bf16(a, SB[kk], O[mt]);
+        }
+        const f32x4 gm = *reinterpret_cast<const f32x4*>(Gd.gam + 16 * mt + 4 * g);
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) O[mt][i2] *= gm[i2];
+        // M is zero right of the diagonal: rows 0..31 need only the first
+        // 32 columns.
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          if (kk == 1 && mt < 2) continue;
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(Qs.M + row * 128 + 16 * ((4 * kk + g) ^ swz(row)));
+          O[mt] = mfma_bf16(a, DB[kk], O[mt]);
+        }
+      }
+      // O rows are natural tokens 16mt + 4g + i; this lane owns value row
+      // dv0 + r.  The hand-off slot just read is free until the chain wave
+      // refills it two iterations later, so it stages O for 16-byte stores.
+      wave_lds_fence();
+      bf16* st = reinterpret_cast<bf16*>(&sm.hand[c & 1][s]);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) st[(16 * mt + 4 * g + i2) * 16 + r] = (bf16)O[mt][i2];
+      wave_lds_fence();
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int pc = l + 64 * j, t = pc >> 1, half = pc & 1;
+        const uint4 val = *reinterpret_cast<const uint4*>(st + t * 16 + 8 * half);
+        if (t < L)
+          *reinterpret_cast<uint4*>(o + (size_t)(tok0 + t) * hv_stride + (size_t)h * kD + dv0 +
+                                    8 * half) = val;
+      }
+    }
     barrier_lds();
   }
 }
