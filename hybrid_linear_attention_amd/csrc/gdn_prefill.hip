@@ -961,21 +961,34 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
           for (int kk = 0; kk < 2; ++kk)
             AT[mt][kk] = *reinterpret_cast<const bf16x8*>(S.T + row * 128 + 16 * ((4 * kk + g) ^ swz(row)));
         }
-        // V at tokens 32(mt/2) + 8g + 4(mt%2) + i: the swizzle term vswz(token)
-        // is g for all of them, so the reads are fixed offsets from one base.
+        bf16x8 AKT[8][2];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int row = prow(t, r);
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk)
+            AKT[t][kk] = *reinterpret_cast<const bf16x8*>(S.KT + row * 128 + 16 * ((4 * kk + g) ^ swz(row)));
+        }
+        // V of this lane's value row at its tokens 32(mt/2) + 8g + 4(mt%2) + i,
+        // by transposed reads: as input lane r of group g this lane reads 4
+        // value rows (16s + 4(r%4) ..+3) of token 32(mt/2) + 8g + 4(mt%2) + r/4.
         // Rows beyond L hold a copy of the last token; they only meet the zero
         // columns of Tt, so they need no masking.
-        const int col = 16 * s + r;                   // value row within the workgroup
-        const bf16* vl = reinterpret_cast<const bf16*>(S.V) + 8 * g * kRows +
-                         8 * ((col >> 3) ^ g) + (col & 7);
+        s16x4 vt[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const int tok = 32 * (mt >> 1) + 8 * g + 4 * (mt & 1) + (r >> 2);
+          const int col = 16 * s + 4 * (r & 3);
+          vt[mt] = lds_tr16(S.V + tok * (2 * kRows) + 16 * ((col >> 3) ^ vswz(tok)) + 2 * (col & 7));
+        }
         // X = V - diag(gam) P
         f32x4 X[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           const f32x4 gm = *reinterpret_cast<const f32x4*>(Gd.gam + 32 * (mt >> 1) + 8 * g + 4 * (mt & 1));
+          const bf16* v4 = reinterpret_cast<const bf16*>(&vt[mt]);
 #pragma unroll
-          for (int i2 = 0; i2 < 4; ++i2)
-            X[mt][i2] = (float)vl[(32 * (mt >> 1) + 4 * (mt & 1) + i2) * kRows] - gm[i2] * P[mt][i2];
+          for (int i2 = 0; i2 < 4; ++i2) X[mt][i2] = (float)v4[i2] - gm[i2] * P[mt][i2];
         }
         const bf16x8 XB[2] = {pack_b(X[0], X[1]), pack_b(X[2], X[3])};
         // Dl = Tt X
@@ -1000,14 +1013,9 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
 #pragma unroll
         for (int t = 0; t < 8; ++t) ST[t] *= gL;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int row = prow(t, r);
+        for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(S.KT + row * 128 + 16 * ((4 * kk + g) ^ swz(row)));
-            ST[t] = mfma_bf16(a, DTB[kk], ST[t]);
-          }
-        }
+          for (int t = 0; t < 8; ++t) ST[t] = mfma_bf16(AKT[t][kk], DTB[kk], ST[t]);
       }
       barrier_lds();
     }
