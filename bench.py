@@ -19,6 +19,7 @@ Rates:
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -51,6 +52,43 @@ def scan_flops(T, B=1):
 
 def decode_state_bytes(B):
     return 2 * B * HV * D * D * 4
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_bytes_prefill_T8192_decode_B64.md")
+
+
+def counted_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary (calibrated against a plain copy), or None
+    when there is no such line or the kernel's source has changed since the
+    counters were taken."""
+    try:
+        lines = open(TRAFFIC_FILE).read().splitlines()
+    except OSError:
+        return None
+    for ln in lines:
+        f = ln.split()
+        if len(f) == 5 and f[0] == "traffic" and f[1] == kernel:
+            src = os.path.join(ROOT, "hybrid_linear_attention_amd", "csrc", f[2])
+            try:
+                h = hashlib.sha256(open(src, "rb").read()).hexdigest()
+            except OSError:
+                return None
+            return int(f[4]) if h == f[3] else None
+    return None
+
+
+def scan_bytes(T, B=1):
+    """Algorithmic bytes of one scan launch (bf16): it reads q, v, the
+    workspace (Tt and M: 64 x 64 bf16 per chunk and value head; K^T: 128 x 64
+    bf16 per chunk and query/key head; two fp32 gate vectors of 64 per chunk and
+    value head) and writes o and the fp32 final state."""
+    nc = B * ((T + C - 1) // C)
+    tok = B * T
+    rd = tok * HQK * D * 2 + tok * HV * D * 2 + nc * (HV * 2 * C * C * 2 + HQK * D * C * 2 + HV * 2 * C * 4)
+    wr = tok * HV * D * 2 + B * HV * D * D * 4
+    return rd + wr
 
 
 def log(*a):
@@ -113,19 +151,25 @@ def timed_decode(gdn, B, steps, warmup, dtype=torch.bfloat16):
     return dict(step_ms=ms, gbs=gbs)
 
 
-def cpu_baseline(inp, T_sample):
-    """The float64 oracle, untuned, on a bounded sample of the same workload:
-    the first T_sample tokens of every value head."""
+def cpu_baseline(inp, T_sample, min_seconds=10.0, max_calls=64):
+    """The float64 oracle, untuned, on the same workload: the first T_sample
+    tokens of every value head, called repeatedly until about min_seconds of
+    CPU work have run (each call is independent; the rate is tokens over the
+    summed wall time)."""
     import oracle
     oracle.build(force=False)
     sl = {k: inp[k][:, :T_sample].cpu() for k in ("q", "k", "v", "alpha", "beta")}
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-    t0 = time.perf_counter()
-    oracle.prefill(sl["q"], sl["k"], sl["v"], sl["alpha"], sl["beta"], None)
-    dt = time.perf_counter() - t0
-    return dict(value=T_sample / dt, unit="tokens/s", cores=threads, kind="oracle",
-                sample="first %d of 8192 tokens, all 48 value heads, batch 1, float64 "
-                       "sequential recurrence (%.1f s)" % (T_sample, dt))
+    calls, dt = 0, 0.0
+    while calls < max_calls and dt < min_seconds:
+        t0 = time.perf_counter()
+        oracle.prefill(sl["q"], sl["k"], sl["v"], sl["alpha"], sl["beta"], None)
+        dt += time.perf_counter() - t0
+        calls += 1
+    return dict(value=calls * T_sample / dt, unit="tokens/s", cores=threads, kind="oracle",
+                sample="%d calls on the first %d of 8192 tokens, all 48 value heads, batch 1, "
+                       "float64 sequential recurrence, OpenMP over heads (%.1f s)"
+                       % (calls, T_sample, dt))
 
 
 def main():
@@ -174,6 +218,11 @@ def main():
     log("decode B=64: %d steps" % args.decode_steps)
     dec = timed_decode(gdn, 64, args.decode_steps, 16)
     log("decode step %.4f ms, %.1f GB/s" % (dec["step_ms"], dec["gbs"]))
+    # 64 x 48 x 128 x 128 fp32 (192 MiB) fits in the 256 MB last-level cache;
+    # 256 sequences (768 MiB) do not, which shows the rate that DRAM sustains.
+    log("decode B=256 (state larger than the last-level cache): 64 steps")
+    dec256 = timed_decode(gdn, 256, 64, 8)
+    log("decode B=256 step %.4f ms, %.1f GB/s" % (dec256["step_ms"], dec256["gbs"]))
 
     out = {
         "metric": "GDN prefill tokens/s @T=8192 (% MFMA peak) + decode state GB/s (% HBM peak)",
@@ -199,14 +248,18 @@ def main():
                      "achieved": scan_tflops if dominant == "scan" else None,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": (scan_tflops / PEAK_BF16_TFLOPS) if dominant == "scan" else None,
-                     "traffic": None},
+                     "traffic": counted_traffic("scan_split_kernel") if dominant == "scan" else None,
+                     "algorithmic_bytes": scan_bytes(T),
+                     "hbm_gbs": scan_bytes(T) / (pre["scan_ms"] * 1e-3) / 1e9},
         "decode": {"metric": "decode state GB/s", "value": dec["gbs"], "unit": "GB/s",
                    "ms_per_step": dec["step_ms"], "steps": args.decode_steps,
                    "workload": "64 sequences x 1 token, fp32 state [64,48,128,128] in place, "
                                "bf16 q/k/v",
                    "roofline": {"bound": "hbm", "achieved": dec["gbs"], "peak": PEAK_HBM_GBS,
                                 "unit": "GB/s", "frac": dec["gbs"] / PEAK_HBM_GBS,
-                                "traffic": None}},
+                                "traffic": counted_traffic("decode_step_kernel")},
+                   "dram_diagnostic_B256": {"ms_per_step": dec256["step_ms"], "gbs": dec256["gbs"],
+                                            "frac": dec256["gbs"] / PEAK_HBM_GBS}},
     }
     if args.extended:
         log("extended: T=262144")

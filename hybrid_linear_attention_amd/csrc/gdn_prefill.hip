@@ -88,17 +88,16 @@ constexpr int kLdT = 68;   // LDS row stride of 64-wide fp32/bf16 tiles
 template <typename E>
 struct PrepSmem {
   static constexpr int LDK = 136;   // K/Q row stride: rows 16-byte aligned for b128 reads
+  static constexpr int NB = 3;      // value heads whose A matrices are resident at once
   union {
     struct {
       E Ks[kC * LDK];
       E Qs[kC * LDK];
     } in;
-    float buf[4][kC * kLdT];        // per-wave A -> T buffers (after the Grams)
+    float buf[NB][kC * kLdT];       // per value head: A, then (I + A)^-1 in place
   } u;
-  float gram[kC * kLdT];            // K K^T
-  float qkg[kC * kLdT];             // Q K^T
-  float gate[4][kC];
-  float bet[4][kC];
+  float gate[NB][kC];               // G2 (base-2 log-decay prefix) per head
+  float bet[NB][kC];
 };
 
 // acc = A[arow0.., acol0..] (16x16) * B[brow0.., bcol0..] (16x16), both fp32 in LDS.
@@ -112,12 +111,28 @@ __device__ __forceinline__ f32x4 mm16_lds(const float* A, int arow0, int acol0,
   return acc;
 }
 
+// One workgroup per (chunk, query/key head), four waves.
+//  1. K and Q of the chunk are staged in LDS; wave w computes the Gram tiles
+//     with A = K rows 16w..16w+15 against B = K and Q rows of each 16-token
+//     block nt:  KK[w][nt](m, n) = k_{16w+m} . k_{16nt+n},  KQ[w][nt](m, n) =
+//     k_{16w+m} . q_{16nt+n}.  In the accumulator layout lane (n, g) holds
+//     m = 4g..4g+3, so for token i = 16nt + n it holds four consecutive
+//     columns j = 16w + 4g.. of row i of K K^T (symmetric) and of Q K^T:
+//     rows of A and M are written straight from registers.
+//  2. K^T is written for the scan.
+//  3. Per batch of up to three value heads: gates (one wave per head), then
+//     every wave writes its column block of A (to LDS) and M (to global) for
+//     each head of the batch, then one wave per head solves (I + A)^-1 in
+//     place and writes Tt.
+// LDS is 53,760 bytes for bf16 (three workgroups share a CU) and 71,168 for
+// fp32 (two).
 template <typename E>
-__global__ __launch_bounds__(256) void prepare_kernel(
+__global__ __launch_bounds__(256, sizeof(E) == 2 ? 3 : 2) void prepare_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const float* __restrict__ alpha,
     const float* __restrict__ beta, Work<E> ws, ChunkMap cm, int Hqk, int Hv, int G) {
   constexpr bool BF = sizeof(E) == 2;
   constexpr int LDK = PrepSmem<E>::LDK;
+  constexpr int NB = PrepSmem<E>::NB;
   constexpr int EPV = 16 / sizeof(E);            // elements per 16-byte piece
   __shared__ PrepSmem<E> sm;
 
@@ -128,10 +143,10 @@ __global__ __launch_bounds__(256) void prepare_kernel(
   if (L <= 0) return;                            // unused varlen table slot
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
 
-  // Gates of the value head this wave will solve first (issued before the
-  // K/Q loads so both latencies overlap).
+  // Gates of the first head batch (issued before the K/Q loads so both
+  // latencies overlap): wave w < min(G, NB) owns value head gq*G + w.
   float al0 = 1.f, bl0 = 0.f;
-  if (w < G && l < L) {
+  if (w < min(G, NB) && l < L) {
     const size_t gi = (size_t)(tok0 + l) * Hv + gq * G + w;
     al0 = alpha[gi];
     bl0 = beta[gi];
@@ -157,22 +172,20 @@ __global__ __launch_bounds__(256) void prepare_kernel(
   }
   __syncthreads();
 
-  // Gram matrices: wave w computes rows 16w..16w+15 of K K^T and Q K^T.
-  f32x4 kk[4], qk[4];
+  f32x4 kk[4], kq[4];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) { kk[nt] = zero4(); qk[nt] = zero4(); }
+  for (int nt = 0; nt < 4; ++nt) { kk[nt] = zero4(); kq[nt] = zero4(); }
   if constexpr (BF) {
     const bf16* Ks = reinterpret_cast<const bf16*>(sm.u.in.Ks);
     const bf16* Qs = reinterpret_cast<const bf16*>(sm.u.in.Qs);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const bf16x8 ak = lds_row8_bf16(Ks, LDK, 16 * w + r, 32 * ks);
-      const bf16x8 aq = lds_row8_bf16(Qs, LDK, 16 * w + r, 32 * ks);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const bf16x8 b = lds_row8_bf16(Ks, LDK, 16 * nt + r, 32 * ks);
-        kk[nt] = mfma_bf16(ak, b, kk[nt]);
-        qk[nt] = mfma_bf16(aq, b, qk[nt]);
+        if (nt < w) continue;                    // tiles above the diagonal are masked
+        kk[nt] = mfma_bf16(ak, lds_row8_bf16(Ks, LDK, 16 * nt + r, 32 * ks), kk[nt]);
+        kq[nt] = mfma_bf16(ak, lds_row8_bf16(Qs, LDK, 16 * nt + r, 32 * ks), kq[nt]);
       }
     }
   } else {
@@ -180,23 +193,14 @@ __global__ __launch_bounds__(256) void prepare_kernel(
     const float* Qs = reinterpret_cast<const float*>(sm.u.in.Qs);
     for (int s = 0; s < kD / 4; ++s) {
       const float ak = Ks[(16 * w + r) * LDK + 4 * s + g];
-      const float aq = Qs[(16 * w + r) * LDK + 4 * s + g];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const float b = Ks[(16 * nt + r) * LDK + 4 * s + g];
-        kk[nt] = mfma_f32(ak, b, kk[nt]);
-        qk[nt] = mfma_f32(aq, b, qk[nt]);
+        if (nt < w) continue;
+        kk[nt] = mfma_f32(ak, Ks[(16 * nt + r) * LDK + 4 * s + g], kk[nt]);
+        kq[nt] = mfma_f32(ak, Qs[(16 * nt + r) * LDK + 4 * s + g], kq[nt]);
       }
     }
   }
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 16 * w + 4 * g + i, col = 16 * nt + r;
-      sm.gram[row * kLdT + col] = kk[nt][i];
-      sm.qkg[row * kLdT + col] = qk[nt][i];
-    }
   if constexpr (BF) {
     // K^T of the chunk for the scan's state update, [128 d_k][64 tokens]:
     // each thread writes 16-byte pieces (8 tokens of one d_k column).
@@ -211,143 +215,144 @@ __global__ __launch_bounds__(256) void prepare_kernel(
       *reinterpret_cast<bf16x8*>(kt + dk * kC + 8 * tb) = col;
     }
   }
-  __syncthreads();   // K/Q tiles are dead from here on; buf[] reuses them
 
-  // One wave per value head of this query/key group.
-  float* A = sm.u.buf[w];
-  for (int rr = w; rr < G; rr += 4) {
-    const int h = gq * G + rr;
-    float al = al0, bl = bl0;
-    if (rr >= 4) {
-      const size_t gi = (size_t)(tok0 + l) * Hv + h;
-      al = (l < L) ? alpha[gi] : 1.f;
-      bl = (l < L) ? beta[gi] : 0.f;
+  for (int hb = 0; hb < G; hb += NB) {
+    const int nb = min(NB, G - hb);
+    // Gates: G2_t = sum_{j<=t} log2(alpha_j) over the chunk, one wave per head.
+    if (w < nb) {
+      const int h = gq * G + hb + w;
+      float al = al0, bl = bl0;
+      if (hb > 0) {
+        const size_t gi = (size_t)(tok0 + l) * Hv + h;
+        al = (l < L) ? alpha[gi] : 1.f;
+        bl = (l < L) ? beta[gi] : 0.f;
+      }
+      const float Gl = wave_inclusive_sum(hw_log2(al));
+      const float Glast = __shfl(Gl, kC - 1, 64);
+      ws.gam[((size_t)cid * Hv + h) * kC + l] = hw_exp2(Gl);
+      ws.dec[((size_t)cid * Hv + h) * kC + l] = hw_exp2(Glast - Gl);
+      sm.gate[w][l] = Gl;
+      sm.bet[w][l] = bl;
     }
-    const float Gl = wave_inclusive_sum(hw_log2(al));
-    const float Glast = __shfl(Gl, kC - 1, 64);
-    ws.gam[((size_t)cid * Hv + h) * kC + l] = hw_exp2(Gl);
-    ws.dec[((size_t)cid * Hv + h) * kC + l] = hw_exp2(Glast - Gl);
-    sm.gate[w][l] = Gl;
-    sm.bet[w][l] = bl;
-    wave_lds_fence();
+    __syncthreads();   // gates visible; K/Q tiles (first batch) or the previous
+                       // batch's buffers are dead from here on
 
-    // A[i][j] = beta_i exp(G_i - G_j) (k_i . k_j) for j < i, and the output
-    // mask M[i][j] = exp(G_i - G_j) (q_i . k_j) for j <= i.  Lane = (8-column
-    // block cb, row group rg); rows rg, rg + 8, ...
-    E* mo = ws.M + ((size_t)cid * Hv + h) * kC * kC;
-    {
-      const int cb = l & 7, rg = l >> 3;
-      float gj[8];
+    // A[i][j] = beta_i 2^(G2_i - G2_j) (k_i . k_j) for j < i, and the output
+    // mask M[i][j] = 2^(G2_i - G2_j) (q_i . k_j) for j <= i; zero elsewhere.
+    // This wave: columns j = 16w + 4g .. +3 of rows i = 16nt + r.
+    for (int hh = 0; hh < nb; ++hh) {
+      const int h = gq * G + hb + hh;
+      float* A = sm.u.buf[hh];
+      E* mo = ws.M + ((size_t)cid * Hv + h) * kC * kC;
+      const f32x4 gj = *reinterpret_cast<const f32x4*>(&sm.gate[hh][16 * w + 4 * g]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) gj[e] = sm.gate[w][8 * cb + e];
+      for (int nt = 0; nt < 4; ++nt) {
+        const int i = 16 * nt + r;
+        float a4[4], m4[4];
+        if (nt < w) {
 #pragma unroll
-      for (int i0 = 0; i0 < 8; ++i0) {
-        const int i = 8 * i0 + rg;
-        const float gi_ = sm.gate[w][i], bi = sm.bet[w][i];
-        const f32x4 k0 = *reinterpret_cast<const f32x4*>(sm.gram + i * kLdT + 8 * cb);
-        const f32x4 k1 = *reinterpret_cast<const f32x4*>(sm.gram + i * kLdT + 8 * cb + 4);
-        const f32x4 q0 = *reinterpret_cast<const f32x4*>(sm.qkg + i * kLdT + 8 * cb);
-        const f32x4 q1 = *reinterpret_cast<const f32x4*>(sm.qkg + i * kLdT + 8 * cb + 4);
-        const float kk8[8] = {k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
-        const float qk8[8] = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
-        float a8[8];
-        E m8[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int j = 8 * cb + e;
-          const float dg = (j <= i) ? hw_exp2(gi_ - gj[e]) : 0.f;
-          a8[e] = (j < i) ? bi * dg * kk8[e] : 0.f;
-          m8[e] = from_f32<E>(dg * qk8[e]);
-        }
-        *reinterpret_cast<f32x4*>(A + i * kLdT + 8 * cb) = f32x4{a8[0], a8[1], a8[2], a8[3]};
-        *reinterpret_cast<f32x4*>(A + i * kLdT + 8 * cb + 4) = f32x4{a8[4], a8[5], a8[6], a8[7]};
-        if constexpr (BF) {
-          bf16x8 mv;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) mv[e] = m8[e];
-          *reinterpret_cast<bf16x8*>(mo + i * kC + 8 * cb) = mv;
+          for (int e = 0; e < 4; ++e) { a4[e] = 0.f; m4[e] = 0.f; }
         } else {
-          *reinterpret_cast<f32x4*>(mo + i * kC + 8 * cb) = f32x4{m8[0], m8[1], m8[2], m8[3]};
-          *reinterpret_cast<f32x4*>(mo + i * kC + 8 * cb + 4) = f32x4{m8[4], m8[5], m8[6], m8[7]};
+          const float gi_ = sm.gate[hh][i], bi = sm.bet[hh][i];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = 16 * w + 4 * g + e;
+            const float dg = (j <= i) ? hw_exp2(gi_ - gj[e]) : 0.f;
+            a4[e] = (j < i) ? bi * dg * kk[nt][e] : 0.f;
+            m4[e] = dg * kq[nt][e];
+          }
         }
-      }
-    }
-    wave_lds_fence();
-
-    // Diagonal 16x16 blocks of (I + A)^-1 by forward substitution:
-    // lane = (block bb, column c).
-    {
-      const int bb = l >> 4, c = l & 15;
-      const float* Ab = A + (16 * bb) * kLdT + 16 * bb;
-      float x[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float acc = (i == c) ? 1.f : 0.f;
-#pragma unroll
-        for (int j = 0; j < i; ++j) acc -= Ab[i * kLdT + j] * x[j];
-        x[i] = acc;
-      }
-      wave_lds_fence();
-      float* Tb = A + (16 * bb) * kLdT + 16 * bb;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) Tb[i * kLdT + c] = x[i];
-      wave_lds_fence();
-    }
-
-    // Off-diagonal blocks, block row by block row:
-    //   T_ij = -T_ii * sum_{k=j}^{i-1} A_ik T_kj
-#pragma unroll
-    for (int ib = 1; ib < 4; ++ib) {
-      f32x4 Y[3];
-#pragma unroll
-      for (int jb = 0; jb < ib; ++jb) {
-        Y[jb] = zero4();
-        for (int kb = jb; kb < ib; ++kb)
-          Y[jb] = mm16_lds(A, 16 * ib, 16 * kb, A, 16 * kb, 16 * jb, Y[jb]);
-      }
-      f32x4 Z[3];
-#pragma unroll
-      for (int jb = 0; jb < ib; ++jb) {
-        Z[jb] = zero4();
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          Z[jb] = mfma_f32(A[(16 * ib + r) * kLdT + 16 * ib + 4 * g + s], Y[jb][s], Z[jb]);
-      }
-      wave_lds_fence();
-#pragma unroll
-      for (int jb = 0; jb < ib; ++jb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) A[(16 * ib + 4 * g + i) * kLdT + 16 * jb + r] = -Z[jb][i];
-      wave_lds_fence();
-    }
-
-    // Tt = T diag(beta): lane = (8-column block, row group), 16-byte stores.
-    E* tt = ws.Tt + ((size_t)cid * Hv + h) * kC * kC;
-    {
-      const int cb = l & 7, rg = l >> 3;
-      float bj[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) bj[e] = sm.bet[w][8 * cb + e];
-#pragma unroll
-      for (int i0 = 0; i0 < 8; ++i0) {
-        const int i = 8 * i0 + rg;
-        const f32x4 t0 = *reinterpret_cast<const f32x4*>(A + i * kLdT + 8 * cb);
-        const f32x4 t1 = *reinterpret_cast<const f32x4*>(A + i * kLdT + 8 * cb + 4);
-        const float t8[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+        *reinterpret_cast<f32x4*>(A + i * kLdT + 16 * w + 4 * g) = f32x4{a4[0], a4[1], a4[2], a4[3]};
         if constexpr (BF) {
-          bf16x8 tv;
+          bf16x4 mv;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) tv[e] = (bf16)(t8[e] * bj[e]);
-          *reinterpret_cast<bf16x8*>(tt + i * kC + 8 * cb) = tv;
+          for (int e = 0; e < 4; ++e) mv[e] = (bf16)m4[e];
+          *reinterpret_cast<bf16x4*>(mo + i * kC + 16 * w + 4 * g) = mv;
         } else {
-          *reinterpret_cast<f32x4*>(tt + i * kC + 8 * cb) =
-              f32x4{t8[0] * bj[0], t8[1] * bj[1], t8[2] * bj[2], t8[3] * bj[3]};
-          *reinterpret_cast<f32x4*>(tt + i * kC + 8 * cb + 4) =
-              f32x4{t8[4] * bj[4], t8[5] * bj[5], t8[6] * bj[6], t8[7] * bj[7]};
+          *reinterpret_cast<f32x4*>(mo + i * kC + 16 * w + 4 * g) = f32x4{m4[0], m4[1], m4[2], m4[3]};
         }
       }
     }
-    wave_lds_fence();
+    __syncthreads();
+
+    // One wave per value head of the batch: (I + A)^-1 in place, then Tt.
+    if (w < nb) {
+      const int h = gq * G + hb + w;
+      float* A = sm.u.buf[w];
+      // Diagonal 16x16 blocks by forward substitution: lane = (block bb, column c).
+      {
+        const int bb = l >> 4, c = l & 15;
+        const float* Ab = A + (16 * bb) * kLdT + 16 * bb;
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float acc = (i == c) ? 1.f : 0.f;
+#pragma unroll
+          for (int j = 0; j < i; ++j) acc -= Ab[i * kLdT + j] * x[j];
+          x[i] = acc;
+        }
+        wave_lds_fence();
+        float* Tb = A + (16 * bb) * kLdT + 16 * bb;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) Tb[i * kLdT + c] = x[i];
+        wave_lds_fence();
+      }
+
+      // Off-diagonal blocks, block row by block row:
+      //   T_ij = -T_ii * sum_{k=j}^{i-1} A_ik T_kj
+#pragma unroll
+      for (int ib = 1; ib < 4; ++ib) {
+        f32x4 Y[3];
+#pragma unroll
+        for (int jb = 0; jb < ib; ++jb) {
+          Y[jb] = zero4();
+          for (int kb = jb; kb < ib; ++kb)
+            Y[jb] = mm16_lds(A, 16 * ib, 16 * kb, A, 16 * kb, 16 * jb, Y[jb]);
+        }
+        f32x4 Z[3];
+#pragma unroll
+        for (int jb = 0; jb < ib; ++jb) {
+          Z[jb] = zero4();
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            Z[jb] = mfma_f32(A[(16 * ib + r) * kLdT + 16 * ib + 4 * g + s], Y[jb][s], Z[jb]);
+        }
+        wave_lds_fence();
+#pragma unroll
+        for (int jb = 0; jb < ib; ++jb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) A[(16 * ib + 4 * g + i) * kLdT + 16 * jb + r] = -Z[jb][i];
+        wave_lds_fence();
+      }
+
+      // Tt = T diag(beta): lane = (8-column block, row group), 16-byte stores.
+      E* tt = ws.Tt + ((size_t)cid * Hv + h) * kC * kC;
+      {
+        const int cb = l & 7, rg = l >> 3;
+        float bj[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bj[e] = sm.bet[w][8 * cb + e];
+#pragma unroll
+        for (int i0 = 0; i0 < 8; ++i0) {
+          const int i = 8 * i0 + rg;
+          const f32x4 t0 = *reinterpret_cast<const f32x4*>(A + i * kLdT + 8 * cb);
+          const f32x4 t1 = *reinterpret_cast<const f32x4*>(A + i * kLdT + 8 * cb + 4);
+          const float t8[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+          if constexpr (BF) {
+            bf16x8 tv;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) tv[e] = (bf16)(t8[e] * bj[e]);
+            *reinterpret_cast<bf16x8*>(tt + i * kC + 8 * cb) = tv;
+          } else {
+            *reinterpret_cast<f32x4*>(tt + i * kC + 8 * cb) =
+                f32x4{t8[0] * bj[0], t8[1] * bj[1], t8[2] * bj[2], t8[3] * bj[3]};
+            *reinterpret_cast<f32x4*>(tt + i * kC + 8 * cb + 4) =
+                f32x4{t8[4] * bj[4], t8[5] * bj[5], t8[6] * bj[6], t8[7] * bj[7]};
+          }
+        }
+      }
+    }
+    if (hb + NB < G) __syncthreads();   // the next batch rewrites gates and buffers
   }
 }
 
