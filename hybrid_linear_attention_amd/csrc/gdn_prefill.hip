@@ -27,15 +27,18 @@
 //    by fp32 MFMA).  Writes Tt, the masked output matrix M and G to the
 //    workspace.
 //  * scan     (grid: value-row slices x value heads x sequences) - the serial
-//    chain.  Each wave owns 16 value rows of one head's state and keeps them,
-//    transposed (S^T, d_k x 16), in fp32 MFMA accumulators for the whole
+//    chain.  Each chain wave owns 16 value rows of one head's state and keeps
+//    them, transposed (S^T, d_k x 16), in fp32 MFMA accumulators for the whole
 //    sequence.  Per chunk every product feeds the next one straight from
 //    registers: the accumulator tiles of S^T, X and Dl are the B operands of the
 //    following MFMAs (see gdn_device.hpp for the K order that makes this work),
-//    so only the shared chunk operands (K, K^T, Q, Tt, M, V) go through LDS;
-//    those are fetched into registers one chunk ahead.
+//    so only the shared chunk operands (K^T, Q, Tt, M, V) go through LDS.
 //    Rows of the state never interact, so the value rows split across waves
-//    and workgroups with no communication at all.
+//    and workgroups with no communication at all.  Two versions: the bf16
+//    scan (scan_split_kernel: chain, output and copy work on separate waves,
+//    operands copied straight into LDS) and a generic one (scan_kernel: fp32
+//    inputs, and the gated RMSNorm epilogue), which stages operands through
+//    registers one chunk ahead.
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
@@ -678,8 +681,9 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
 //  * chain wave (one per slice): the serial part only.  P = K S^T, X, Dl =
 //    Tt X, the state update; it hands S^T (as the B fragments it built for P)
 //    and Dl to the output wave through LDS.  40 MFMAs per chunk.
-//  * output wave (one per slice), one chunk behind: O = diag(gam) Q S^T + M Dl.
-//    22 MFMAs per chunk.
+//  * one output wave for both slices, one chunk behind: O = diag(gam) Q S^T +
+//    M Dl.  Each Q and M fragment read from LDS serves both slices: 44 MFMAs
+//    per chunk.
 //  * two producer waves: copy K^T, Tt, V, gam, dec of chunk c+2 and Q, M of
 //    chunk c from global memory straight into LDS rings
 //    (global_load_lds_dwordx4: no registers, no VALU) while chunk c is
@@ -706,7 +710,7 @@ namespace split {
 constexpr int kSlices = 2;                   // 16-row value slices per workgroup
 constexpr int kRows = 16 * kSlices;          // value rows per workgroup
 constexpr int kNsl = kD / kRows;             // workgroups per value head
-constexpr int kWaves = 2 * kSlices + 2;      // chain x2, output x2, producer x2
+constexpr int kWaves = kSlices + 3;          // chain x2, output, producer x2
 constexpr int kSlots = 3;                    // chain operands: chunks c, c+1, c+2
 constexpr int kQmSlots = 2;                  // output operands: chunks c-1, c
 constexpr int kGdSlots = 4;                  // gam/dec: chunks c-1 .. c+2
@@ -811,9 +815,9 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
   const size_t hv_stride = (size_t)Hv * kD;         // elements between tokens of v / o
   const size_t qk_stride = (size_t)Hqk * kD;
 
-  if (w >= 2 * kSlices) {
+  if (w >= kSlices + 1) {
     // ------------------------------------------------------------ producers
-    const int pw = w - 2 * kSlices;
+    const int pw = w - kSlices - 1;
     // Tt, V, gam, dec of chunk c into ring slots (c % 3, c % 4).
     auto issue_a = [&](int c) {
       const int cid = cid0 + c;
@@ -1033,9 +1037,7 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
   }
 
   // -------------------------------------------------------------- output wave
-  // Chunk c's O at iteration c+1: Q and M from the qm ring, S^T and Dl B
-  // fragments from the chain wave's hand-off slot, gam from the gate ring.
-  const int s = w - kSlices, dv0 = dvb + 16 * s;
+  // Chunk c's O at iteration c+1 for both value slices.
   barrier_lds();
   for (int i = 0; i <= nch; ++i) {
     if (i >= 1) {
@@ -1043,52 +1045,61 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
       int tok0, L;
       chunk_of(cm, cid0 + c, tok0, L);
       const QmSlot& Qs = sm.qm[c % kQmSlots];
-      const Hand& H = sm.hand[c & 1][s];
       const GateSlot& Gd = sm.gd[c % kGdSlots];
-      bf16x8 SB[4], DB[2];
+      bf16x8 SB[kSlices][4], DB[kSlices][2];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) SB[kk] = H.sb[kk][l];
+      for (int s = 0; s < kSlices; ++s) {
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) DB[kk] = H.db[kk][l];
-      f32x4 O[4];
+        for (int kk = 0; kk < 4; ++kk) SB[s][kk] = sm.hand[c & 1][s].sb[kk][l];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) DB[s][kk] = sm.hand[c & 1][s].db[kk][l];
+      }
+      f32x4 O[kSlices][4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const int row = 16 * mt + r;
-        O[mt] = zero4();
+#pragma unroll
+        for (int s = 0; s < kSlices; ++s) O[s][mt] = zero4();
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(Qs.Q + row * 256 + 16 * ((4 * kk + g) ^ swz(row)));
-          O[mt] = mfma_bf16(a, SB[kk], O[mt]);
+#pragma unroll
+          for (int s = 0; s < kSlices; ++s) O[s][mt] = mfma_bf16(a, SB[s][kk], O[s][mt]);
         }
         const f32x4 gm = *reinterpret_cast<const f32x4*>(Gd.gam + 16 * mt + 4 * g);
 #pragma unroll
-        for (int i2 = 0; i2 < 4; ++i2) O[mt][i2] *= gm[i2];
-        // M is zero right of the diagonal: rows 0..31 need only the first
-        // 32 columns.
+        for (int s = 0; s < kSlices; ++s)
+#pragma unroll
+          for (int i2 = 0; i2 < 4; ++i2) O[s][mt][i2] *= gm[i2];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
           if (kk == 1 && mt < 2) continue;
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(Qs.M + row * 128 + 16 * ((4 * kk + g) ^ swz(row)));
-          O[mt] = mfma_bf16(a, DB[kk], O[mt]);
+#pragma unroll
+          for (int s = 0; s < kSlices; ++s) O[s][mt] = mfma_bf16(a, DB[s][kk], O[s][mt]);
         }
       }
-      // O rows are natural tokens 16mt + 4g + i; this lane owns value row
-      // dv0 + r.  The hand-off slot just read is free until the chain wave
-      // refills it two iterations later, so it stages O for 16-byte stores.
-      wave_lds_fence();
-      bf16* st = reinterpret_cast<bf16*>(&sm.hand[c & 1][s]);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i2 = 0; i2 < 4; ++i2) st[(16 * mt + 4 * g + i2) * 16 + r] = (bf16)O[mt][i2];
       wave_lds_fence();
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int pc = l + 64 * j, t = pc >> 1, half = pc & 1;
-        const uint4 val = *reinterpret_cast<const uint4*>(st + t * 16 + 8 * half);
-        if (t < L)
-          *reinterpret_cast<uint4*>(o + (size_t)(tok0 + t) * hv_stride + (size_t)h * kD + dv0 +
-                                    8 * half) = val;
+      for (int s = 0; s < kSlices; ++s) {
+        bf16* st = reinterpret_cast<bf16*>(&sm.hand[c & 1][s]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i2 = 0; i2 < 4; ++i2) st[(16 * mt + 4 * g + i2) * 16 + r] = (bf16)O[s][mt][i2];
+      }
+      wave_lds_fence();
+#pragma unroll
+      for (int s = 0; s < kSlices; ++s) {
+        const bf16* st = reinterpret_cast<const bf16*>(&sm.hand[c & 1][s]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int pc = l + 64 * j, t = pc >> 1, half = pc & 1;
+          const uint4 val = *reinterpret_cast<const uint4*>(st + t * 16 + 8 * half);
+          if (t < L)
+            *reinterpret_cast<uint4*>(o + (size_t)(tok0 + t) * hv_stride + (size_t)h * kD + dvb +
+                                      16 * s + 8 * half) = val;
+        }
       }
     }
     barrier_lds();
