@@ -33,6 +33,8 @@ Functions
 ---------
 prefill(q, k, v, alpha, beta, h0=None)       -> (o, ht)     C, OpenMP over (b, h)
 decode_step(q, k, v, alpha, beta, state)     -> (o, state') C
+decode_step_bf16_state(...), prefill_bf16_state(...)   states stored in bf16
+round_bf16(x)                                -> x rounded to bfloat16 (RNE)
 varlen(q, k, v, alpha, beta, cu_seqlens, ...)-> (y, ht)     C per sequence + epilogue
 gate_rmsnorm(o, gate, weight, eps)           -> y           NumPy float64
 np_prefill(q, k, v, alpha, beta, h0=None)    -> (o, ht)     NumPy twin (tiny sizes)
@@ -148,6 +150,47 @@ def decode_step(q, k, v, alpha, beta, state, inplace=False):
     if rc != 0:
         raise ValueError("oracle_gdn_decode_step failed (%d)" % rc)
     return o, st
+
+
+# bfloat16: 1 sign bit, 8 exponent bits, 7 fraction bits (8 significant
+# bits), the exponent range of float32.
+_BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
+_BF16_MIN_EXP = -133          # spacing of the subnormals: 2^-126 * 2^-7
+
+
+def round_bf16(x) -> np.ndarray:
+    """Round float64 values once to the nearest bfloat16 value, ties to even.
+
+    Returns float64 values that are exactly representable in bfloat16.  For
+    |x| in [2^(e-1), 2^e) the bfloat16 spacing is 2^(e-8) (8 significant
+    bits), never finer than the subnormal spacing 2^-133; results beyond the
+    largest finite value (2 - 2^-7) 2^127 become infinite with the sign of x.
+    Infinities and NaNs pass through."""
+    x = _f64(x)
+    _, e = np.frexp(np.abs(x))
+    q = np.ldexp(1.0, np.maximum(e - 8, _BF16_MIN_EXP))
+    with np.errstate(invalid="ignore"):
+        r = np.rint(x / q) * q
+    r = np.where(np.abs(r) > _BF16_MAX, np.copysign(np.inf, x), r)
+    return np.where(np.isfinite(x), r, x)
+
+
+def decode_step_bf16_state(q, k, v, alpha, beta, state):
+    """One decode step with the state stored in bfloat16 (the footprint the
+    pages count in BF16): the stored state is widened exactly, advanced in
+    float64 by ``decode_step``, and the new state is rounded once to
+    bfloat16.  Returns ``(o, new_state)``, both float64; ``new_state`` holds
+    bfloat16 values."""
+    o, st = decode_step(q, k, v, alpha, beta, state)
+    return o, round_bf16(st)
+
+
+def prefill_bf16_state(q, k, v, alpha, beta, h0=None):
+    """``prefill`` with the carried states stored in bfloat16: h0 (bfloat16
+    values) is widened exactly and the final state is rounded once to
+    bfloat16.  The recurrence inside the call runs in float64."""
+    o, ht = prefill(q, k, v, alpha, beta, h0)
+    return o, round_bf16(ht)
 
 
 def gate_rmsnorm(o, gate, weight=None, eps=1e-6):

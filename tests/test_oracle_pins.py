@@ -333,6 +333,64 @@ def test_varlen_equals_separate_sequences(oracle_mod):
     np.testing.assert_array_equal(ht[1], h0[1])      # empty sequence passes h0
 
 
+def test_round_bf16_pins():
+    """bfloat16 rounding, pinned against the hardware conversion (torch's
+    float32 -> bfloat16 is round-to-nearest-even) on float32 values, and by
+    hand on ties, binade edges, subnormals and overflow."""
+    import torch
+    r = rng(17)
+    x32 = np.concatenate([r.standard_normal(20000) * 10.0 ** r.integers(-30, 30, 20000),
+                          r.standard_normal(1000) * 1e-40]).astype(np.float32)
+    ref = torch.from_numpy(x32).to(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(oracle.round_bf16(x32.astype(np.float64)), ref)
+    one = 1.0
+    ulp = 2.0 ** -7                                    # spacing in [1, 2)
+    cases = {
+        one + ulp / 2: one,                            # tie, 1.0 is even
+        one + 3 * ulp / 2: one + 2 * ulp,              # tie, rounds up to even
+        one + ulp / 2 + 2.0 ** -30: one + ulp,         # just above a tie
+        2.0 - ulp / 4: 2.0,                            # carries into the next binade
+        -(one + ulp / 2): -one,
+        0.0: 0.0,
+        2.0 ** -133: 2.0 ** -133,                      # smallest subnormal
+        2.0 ** -134: 0.0,                              # tie with 0: even
+        3 * 2.0 ** -135: 2.0 ** -133,                  # above the tie
+        (2.0 - 2.0 ** -7) * 2.0 ** 127: (2.0 - 2.0 ** -7) * 2.0 ** 127,
+        (2.0 - 2.0 ** -9) * 2.0 ** 127: np.inf,        # rounds past the largest value
+    }
+    got = oracle.round_bf16(np.array(list(cases.keys())))
+    np.testing.assert_array_equal(got, np.array(list(cases.values())))
+    assert np.isnan(oracle.round_bf16(np.array([np.nan]))[0])
+    # idempotent, and the double rounding through float32 is not what it does
+    x = r.standard_normal(1000)
+    np.testing.assert_array_equal(oracle.round_bf16(oracle.round_bf16(x)), oracle.round_bf16(x))
+    t = 1.0 + 2.0 ** -8 + 2.0 ** -40            # just above a bf16 tie, below float32 resolution
+    assert oracle.round_bf16(np.array([t]))[0] == 1.0 + 2.0 ** -7
+    assert torch.tensor([t], dtype=torch.float64).float().to(torch.bfloat16).item() == 1.0
+
+
+def test_bf16_state_variants(oracle_mod):
+    """The bf16-state oracle is the float64 step followed by one rounding."""
+    import torch
+    r = rng(19)
+    B, Hqk, Hv, D = 2, 2, 6, 16
+    st = torch.from_numpy(r.standard_normal((B, Hv, D, D)) * 0.1).to(torch.bfloat16)
+    q = unit(r.standard_normal((B, Hqk, D))); k = unit(r.standard_normal((B, Hqk, D))); v = r.standard_normal((B, Hv, D))
+    a = np.exp(-0.05 * r.random((B, Hv))); be = r.random((B, Hv))
+    o, s1 = oracle.decode_step_bf16_state(q, k, v, a, be, st)
+    o_ref, s_ref = oracle.decode_step(q, k, v, a, be, st.double().numpy())
+    np.testing.assert_array_equal(o, o_ref)
+    np.testing.assert_array_equal(s1, oracle.round_bf16(s_ref))
+    assert np.array_equal(torch.from_numpy(s1).to(torch.bfloat16).double().numpy(), s1)
+    T = 5
+    qs = unit(r.standard_normal((1, T, Hqk, D))); ks = unit(r.standard_normal((1, T, Hqk, D))); vs = r.standard_normal((1, T, Hv, D))
+    al = np.exp(-0.05 * r.random((1, T, Hv))); bs = r.random((1, T, Hv))
+    op, hp = oracle.prefill_bf16_state(qs, ks, vs, al, bs, st[:1])
+    op_ref, hp_ref = oracle.prefill(qs, ks, vs, al, bs, st[:1].double().numpy())
+    np.testing.assert_array_equal(op, op_ref)
+    np.testing.assert_array_equal(hp, oracle.round_bf16(hp_ref))
+
+
 def test_gate_rmsnorm_pins():
     r = rng(13)
     D = 128
