@@ -124,9 +124,9 @@ def timed_prefill(gdn, inp, steps, warmup):
     return dict(step_ms=step, prepare_ms=prep, scan_ms=scan, wall_s=wall)
 
 
-def timed_decode(gdn, B, steps, warmup, dtype=torch.bfloat16):
+def timed_decode(gdn, B, steps, warmup, dtype=torch.bfloat16, state_dtype=torch.float32):
     dev = "cuda:0"
-    state = synth.decode_state(B, 1002, 0.02).to(dev)
+    state = synth.decode_state(B, 1002, 0.02).to(state_dtype).to(dev)
     sets = [{k: v.to(dev) for k, v in synth.decode_step_inputs(B, s, dtype, seed=1002).items()}
             for s in range(4)]
     o = torch.empty((B, HV, D), dtype=dtype, device=dev)
@@ -147,8 +147,9 @@ def timed_decode(gdn, B, steps, warmup, dtype=torch.bfloat16):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    gbs = decode_state_bytes(B) / (ms * 1e-3) / 1e9
-    return dict(step_ms=ms, gbs=gbs)
+    nbytes = decode_state_bytes(B) * state.element_size() // 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return dict(step_ms=ms, gbs=gbs, state_bytes=nbytes)
 
 
 def cpu_baseline(inp, T_sample, min_seconds=10.0, max_calls=64):
@@ -223,6 +224,9 @@ def main():
     log("decode B=256 (state larger than the last-level cache): 64 steps")
     dec256 = timed_decode(gdn, 256, 64, 8)
     log("decode B=256 step %.4f ms, %.1f GB/s" % (dec256["step_ms"], dec256["gbs"]))
+    log("decode B=64 with the state stored in bf16: %d steps" % args.decode_steps)
+    decb = timed_decode(gdn, 64, args.decode_steps, 16, state_dtype=torch.bfloat16)
+    log("decode bf16-state step %.4f ms, %.1f GB/s" % (decb["step_ms"], decb["gbs"]))
 
     out = {
         "metric": "GDN prefill tokens/s @T=8192 (% MFMA peak) + decode state GB/s (% HBM peak)",
@@ -259,7 +263,11 @@ def main():
                                 "unit": "GB/s", "frac": dec["gbs"] / PEAK_HBM_GBS,
                                 "traffic": counted_traffic("decode_step_kernel")},
                    "dram_diagnostic_B256": {"ms_per_step": dec256["step_ms"], "gbs": dec256["gbs"],
-                                            "frac": dec256["gbs"] / PEAK_HBM_GBS}},
+                                            "frac": dec256["gbs"] / PEAK_HBM_GBS},
+                   "bf16_state": {"ms_per_step": decb["step_ms"], "gbs": decb["gbs"],
+                                  "frac": decb["gbs"] / PEAK_HBM_GBS,
+                                  "state_bytes_per_step": decb["state_bytes"],
+                                  "sequences_per_s": 64 / (decb["step_ms"] * 1e-3)}},
     }
     if args.extended:
         log("extended: T=262144")

@@ -90,12 +90,13 @@ gdn_status fail_hip(hipError_t e) {
 }
 
 // Checks shared by the packed and fixed-length prefill.  ntok = all tokens,
-// nseq = number of states.
+// nseq = number of states, ses = bytes per state element (4: float32, 2: bf16).
 gdn_status check_prefill(const void* q, const void* k, const void* v, const float* alpha,
-                         const float* beta, const float* h0, const void* o, const float* ht,
+                         const float* beta, const void* h0, const void* o, const void* ht,
                          const void* gate, const float* norm_w, const void* cu, int64_t cu_len,
                          int64_t ntok, int64_t nseq, int64_t H_qk, int64_t H_v, gdn_dtype dt,
-                         const void* workspace, size_t workspace_bytes, size_t need) {
+                         const void* workspace, size_t workspace_bytes, size_t need,
+                         int64_t ses) {
   const int64_t es = (int64_t)esize(dt);
   const int64_t D = gdn::kD;
   if (ntok > 0 && (!q || !k || !v || !alpha || !beta || !o)) return GDN_ERR_NULL;
@@ -111,7 +112,7 @@ gdn_status check_prefill(const void* q, const void* k, const void* v, const floa
   const Range rq = span(q, ntok * H_qk * D * es), rk = span(k, ntok * H_qk * D * es);
   const Range rv = span(v, ntok * H_v * D * es), ro = span(o, ntok * H_v * D * es);
   const Range ra = span(alpha, ntok * H_v * 4), rb = span(beta, ntok * H_v * 4);
-  const Range rh0 = span(h0, nseq * H_v * D * D * 4), rht = span(ht, nseq * H_v * D * D * 4);
+  const Range rh0 = span(h0, nseq * H_v * D * D * ses), rht = span(ht, nseq * H_v * D * D * ses);
   const Range rg = span(gate, gate ? ntok * H_v * D * es : 0);
   const Range rw = span(norm_w, norm_w ? D * 4 : 0);
   const Range rcu = span(cu, cu ? cu_len * 4 : 0);
@@ -131,9 +132,10 @@ gdn_status check_prefill(const void* q, const void* k, const void* v, const floa
 enum Phase { kPrepare = 1, kScan = 2, kBoth = 3 };
 
 gdn_status prefill_fixed(const void* q, const void* k, const void* v, const float* alpha,
-                         const float* beta, const float* h0, void* o, float* ht, int32_t B,
+                         const float* beta, const void* h0, void* o, void* ht, int32_t B,
                          int32_t T, int32_t H_qk, int32_t H_v, int32_t D, gdn_dtype dt,
-                         void* workspace, size_t workspace_bytes, void* stream, int phase) {
+                         void* workspace, size_t workspace_bytes, void* stream, int phase,
+                         bool state_bf16) {
   gdn_status s = check_dims(H_qk, H_v, D, dt);
   if (s != GDN_OK) return s;
   if (B < 0 || T < 0) return GDN_ERR_SHAPE;
@@ -144,7 +146,8 @@ gdn_status prefill_fixed(const void* q, const void* k, const void* v, const floa
   const WsLayout L = ws_layout(nc, H_qk, H_v, dt, -1);
   const size_t need = nc > 0 ? L.total : 0;
   s = check_prefill(q, k, v, alpha, beta, h0, o, ht, nullptr, nullptr, nullptr, 0,
-                    (int64_t)B * T, B, H_qk, H_v, dt, workspace, workspace_bytes, need);
+                    (int64_t)B * T, B, H_qk, H_v, dt, workspace, workspace_bytes, need,
+                    state_bf16 ? 2 : 4);
   if (s != GDN_OK) return s;
 
   gdn::PrefillLaunch a{};
@@ -161,6 +164,7 @@ gdn_status prefill_fixed(const void* q, const void* k, const void* v, const floa
   a.nc_launch = (int)nc;
   a.Hqk = H_qk; a.Hv = H_v;
   a.bf16_io = dt == GDN_BF16;
+  a.state_bf16 = state_bf16;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if ((phase & kPrepare) && nc > 0) {
     s = fail_hip(gdn::launch_prepare(a, st));
@@ -216,7 +220,7 @@ gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v, cons
                                gdn_dtype dt, void* workspace, size_t workspace_bytes,
                                void* stream) {
   return prefill_fixed(q, k, v, alpha, beta, h0, o, ht, B, T, H_qk, H_v, D, dt, workspace,
-                       workspace_bytes, stream, kBoth);
+                       workspace_bytes, stream, kBoth, false);
 }
 
 gdn_status gdn_prefill_prepare(const void* q, const void* k, const void* v, const float* alpha,
@@ -225,7 +229,7 @@ gdn_status gdn_prefill_prepare(const void* q, const void* k, const void* v, cons
                                gdn_dtype dt, void* workspace, size_t workspace_bytes,
                                void* stream) {
   return prefill_fixed(q, k, v, alpha, beta, h0, o, ht, B, T, H_qk, H_v, D, dt, workspace,
-                       workspace_bytes, stream, kPrepare);
+                       workspace_bytes, stream, kPrepare, false);
 }
 
 gdn_status gdn_prefill_scan(const void* q, const void* k, const void* v, const float* alpha,
@@ -233,12 +237,22 @@ gdn_status gdn_prefill_scan(const void* q, const void* k, const void* v, const f
                             int32_t T, int32_t H_qk, int32_t H_v, int32_t D, gdn_dtype dt,
                             void* workspace, size_t workspace_bytes, void* stream) {
   return prefill_fixed(q, k, v, alpha, beta, h0, o, ht, B, T, H_qk, H_v, D, dt, workspace,
-                       workspace_bytes, stream, kScan);
+                       workspace_bytes, stream, kScan, false);
 }
 
-gdn_status gdn_decode_step(const void* q, const void* k, const void* v, const float* alpha,
-                           const float* beta, float* state, void* o, int32_t B, int32_t H_qk,
-                           int32_t H_v, int32_t D, gdn_dtype dt, void* stream) {
+gdn_status gdn_prefill_chunked_bf16_state(const void* q, const void* k, const void* v,
+                                          const float* alpha, const float* beta, const void* h0,
+                                          void* o, void* ht, int32_t B, int32_t T, int32_t H_qk,
+                                          int32_t H_v, int32_t D, gdn_dtype dt, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  return prefill_fixed(q, k, v, alpha, beta, h0, o, ht, B, T, H_qk, H_v, D, dt, workspace,
+                       workspace_bytes, stream, kBoth, true);
+}
+
+namespace {
+gdn_status decode_common(const void* q, const void* k, const void* v, const float* alpha,
+                         const float* beta, void* state, void* o, int32_t B, int32_t H_qk,
+                         int32_t H_v, int32_t D, gdn_dtype dt, void* stream, bool state_bf16) {
   gdn_status s = check_dims(H_qk, H_v, D, dt);
   if (s != GDN_OK) return s;
   if (B < 0) return GDN_ERR_SHAPE;
@@ -253,13 +267,28 @@ gdn_status gdn_decode_step(const void* q, const void* k, const void* v, const fl
   const Range rq = span(q, B * H_qk * Dl * es), rk = span(k, B * H_qk * Dl * es);
   const Range rv = span(v, B * H_v * Dl * es), ro = span(o, B * H_v * Dl * es);
   const Range ra = span(alpha, B * H_v * 4), rb = span(beta, B * H_v * 4);
-  const Range rs = span(state, (int64_t)B * H_v * Dl * Dl * 4);
+  const Range rs = span(state, (int64_t)B * H_v * Dl * Dl * (state_bf16 ? 2 : 4));
   const Range ins[] = {rq, rk, rv, ra, rb};
   for (const Range& in : ins)
     if (overlap(ro, in) || overlap(rs, in)) return GDN_ERR_ALIAS;
   if (overlap(ro, rs)) return GDN_ERR_ALIAS;
   return fail_hip(gdn::launch_decode_step(q, k, v, alpha, beta, state, o, B, H_qk, H_v,
-                                          dt == GDN_BF16, static_cast<hipStream_t>(stream)));
+                                          dt == GDN_BF16, state_bf16,
+                                          static_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+gdn_status gdn_decode_step(const void* q, const void* k, const void* v, const float* alpha,
+                           const float* beta, float* state, void* o, int32_t B, int32_t H_qk,
+                           int32_t H_v, int32_t D, gdn_dtype dt, void* stream) {
+  return decode_common(q, k, v, alpha, beta, state, o, B, H_qk, H_v, D, dt, stream, false);
+}
+
+gdn_status gdn_decode_step_bf16_state(const void* q, const void* k, const void* v,
+                                      const float* alpha, const float* beta, void* state,
+                                      void* o, int32_t B, int32_t H_qk, int32_t H_v, int32_t D,
+                                      gdn_dtype dt, void* stream) {
+  return decode_common(q, k, v, alpha, beta, state, o, B, H_qk, H_v, D, dt, stream, true);
 }
 
 gdn_status gdn_prefill_varlen(const void* q, const void* k, const void* v, const float* alpha,
@@ -279,7 +308,7 @@ gdn_status gdn_prefill_varlen(const void* q, const void* k, const void* v, const
   if (nc > (int64_t(1) << 30)) return GDN_ERR_UNSUPPORTED;
   const WsLayout L = ws_layout(nc, H_qk, H_v, dt, N);
   s = check_prefill(q, k, v, alpha, beta, h0, o, ht, gate, norm_weight, cu_seqlens, N + 1,
-                    T_tot, N, H_qk, H_v, dt, workspace, workspace_bytes, L.total);
+                    T_tot, N, H_qk, H_v, dt, workspace, workspace_bytes, L.total, 4);
   if (s != GDN_OK) return s;
 
   char* ws = static_cast<char*>(workspace);
@@ -294,6 +323,7 @@ gdn_status gdn_prefill_varlen(const void* q, const void* k, const void* v, const
   a.gam = reinterpret_cast<float*>(ws + L.gam);
   a.dec = reinterpret_cast<float*>(ws + L.dec);
   a.cm = gdn::ChunkMap{tab, seq_off, 0, 0, (int)nc};
+  a.state_bf16 = false;
   a.nseq = N;
   a.nc_launch = (int)nc;
   a.Hqk = H_qk; a.Hv = H_v;

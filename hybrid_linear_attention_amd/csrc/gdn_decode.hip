@@ -112,20 +112,116 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   }
 }
 
+// The same step with the state stored as bfloat16 (the footprint the pages
+// count in BF16): 32 KiB per (sequence, value head) read and written, the
+// arithmetic in fp32, the new row rounded to nearest even.  Each lane owns two
+// runs of 8 columns (8*l8 + 64*i .. +7), so every access is 16 bytes and the 8
+// lanes of a row cover it in two 128-byte segments.
+template <typename E>
+__global__ __launch_bounds__(256) void decode_step_bs_kernel(
+    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
+    const float* __restrict__ alpha, const float* __restrict__ beta,
+    bf16* __restrict__ state, E* __restrict__ o, int Hqk, int Hv, int G) {
+  const int bh = blockIdx.x;
+  const int b = bh / Hv, h = bh - (bh / Hv) * Hv;
+  const int gq = h / G;
+  const int tid = threadIdx.x;
+  const int l8 = tid & 7;
+  const int rg = tid >> 3;
+
+  const E* qp = q + ((size_t)b * Hqk + gq) * kD;
+  const E* kp = k + ((size_t)b * Hqk + gq) * kD;
+  bf16* S = state + (size_t)bh * kD * kD;
+
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 s[4][2];
+#pragma unroll
+  for (int p = 0; p < 4; ++p)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      s[p][i] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(S + (rg + 32 * p) * kD + 8 * l8 + 64 * i));
+
+  float kr[2][8], qr[2][8];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const f32x4 k0 = load4<E>(kp + 8 * l8 + 64 * i), k1 = load4<E>(kp + 8 * l8 + 64 * i + 4);
+    const f32x4 q0 = load4<E>(qp + 8 * l8 + 64 * i), q1 = load4<E>(qp + 8 * l8 + 64 * i + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      kr[i][j] = k0[j]; kr[i][4 + j] = k1[j];
+      qr[i][j] = q0[j]; qr[i][4 + j] = q1[j];
+    }
+  }
+  const float a = alpha[bh], be = beta[bh];
+  float vr[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) vr[p] = to_f32(v[(size_t)bh * kD + rg + 32 * p]);
+
+  float kq = 0.f;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) kq += kr[i][j] * qr[i][j];
+  kq = sum8(kq);
+
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    float sf[2][8];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const bf16x8 sv = *reinterpret_cast<const bf16x8*>(&s[p][i]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sf[i][j] = (float)sv[j];
+    }
+    float u = 0.f, pq = 0.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        u += sf[i][j] * kr[i][j];
+        pq += sf[i][j] * qr[i][j];
+      }
+    u = sum8(u);
+    pq = sum8(pq);
+    const float d = be * (vr[p] - a * u);
+    const int row = rg + 32 * p;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      bf16x8 n;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) n[j] = (bf16)(a * sf[i][j] + d * kr[i][j]);
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(&n),
+                                  reinterpret_cast<u32x4*>(S + row * kD + 8 * l8 + 64 * i));
+    }
+    if (l8 == 0) o[(size_t)bh * kD + row] = from_f32<E>(a * pq + d * kq);
+  }
+}
+
 hipError_t launch_decode_step(const void* q, const void* k, const void* v,
-                              const float* alpha, const float* beta, float* state,
-                              void* o, int B, int Hqk, int Hv, bool bf16_io,
+                              const float* alpha, const float* beta, void* state,
+                              void* o, int B, int Hqk, int Hv, bool bf16_io, bool state_bf16,
                               hipStream_t stream) {
   const int G = Hv / Hqk;
   dim3 grid((unsigned)(B * Hv)), block(256);
-  if (bf16_io)
+  if (state_bf16) {
+    if (bf16_io)
+      hipLaunchKernelGGL(decode_step_bs_kernel<bf16>, grid, block, 0, stream,
+                         (const bf16*)q, (const bf16*)k, (const bf16*)v, alpha, beta,
+                         (bf16*)state, (bf16*)o, Hqk, Hv, G);
+    else
+      hipLaunchKernelGGL(decode_step_bs_kernel<float>, grid, block, 0, stream,
+                         (const float*)q, (const float*)k, (const float*)v, alpha, beta,
+                         (bf16*)state, (float*)o, Hqk, Hv, G);
+  } else if (bf16_io) {
     hipLaunchKernelGGL(decode_step_kernel<bf16>, grid, block, 0, stream,
                        (const bf16*)q, (const bf16*)k, (const bf16*)v, alpha, beta,
-                       state, (bf16*)o, Hqk, Hv, G);
-  else
+                       (float*)state, (bf16*)o, Hqk, Hv, G);
+  } else {
     hipLaunchKernelGGL(decode_step_kernel<float>, grid, block, 0, stream,
                        (const float*)q, (const float*)k, (const float*)v, alpha,
-                       beta, state, (float*)o, Hqk, Hv, G);
+                       beta, (float*)state, (float*)o, Hqk, Hv, G);
+  }
   return hipGetLastError();
 }
 

@@ -34,6 +34,25 @@ template <typename E> __device__ __forceinline__ E from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // RNE
 
+// Four consecutive elements of a carried state (h0 / ht), stored as float32
+// or, when `as_bf16` is set, as bfloat16 (converted with round to nearest even).
+__device__ __forceinline__ f32x4 load_state4(const void* base, size_t idx, bool as_bf16) {
+  if (as_bf16) {
+    const bf16x4 v = *reinterpret_cast<const bf16x4*>(static_cast<const bf16*>(base) + idx);
+    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+  }
+  return *reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + idx);
+}
+__device__ __forceinline__ void store_state4(void* base, size_t idx, const f32x4& x, bool as_bf16) {
+  if (as_bf16) {
+    bf16x4 v;
+    v[0] = (bf16)x[0]; v[1] = (bf16)x[1]; v[2] = (bf16)x[2]; v[3] = (bf16)x[3];
+    *reinterpret_cast<bf16x4*>(static_cast<bf16*>(base) + idx) = v;
+  } else {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(base) + idx) = x;
+  }
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 

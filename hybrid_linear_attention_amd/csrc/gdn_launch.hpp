@@ -16,9 +16,10 @@ struct ChunkMap {
 
 struct PrefillLaunch {
   const void *q, *k, *v;
-  const float *alpha, *beta, *h0;
+  const float *alpha, *beta;
+  const void* h0;          // [nseq][Hv][128][128], float32 or bfloat16 (state_bf16)
   void* o;
-  float* ht;
+  void* ht;
   const void* gate;        // null: plain output; else fused RMSNorm * sigmoid(gate)
   const float* norm_w;
   float norm_eps;
@@ -27,6 +28,7 @@ struct PrefillLaunch {
   ChunkMap cm;
   int nseq, nc_launch, Hqk, Hv;
   bool bf16_io;
+  bool state_bf16;         // h0 / ht stored as bfloat16
 };
 
 hipError_t launch_prepare(const PrefillLaunch& a, hipStream_t st);
@@ -34,7 +36,7 @@ hipError_t launch_scan(const PrefillLaunch& a, hipStream_t st);
 hipError_t launch_varlen_table(const int32_t* cu, int N, int T_tot, int nc_max, int32_t* tab,
                                int32_t* seq_off, hipStream_t st);
 hipError_t launch_decode_step(const void* q, const void* k, const void* v, const float* alpha,
-                              const float* beta, float* state, void* o, int B, int Hqk, int Hv,
-                              bool bf16_io, hipStream_t stream);
+                              const float* beta, void* state, void* o, int B, int Hqk, int Hv,
+                              bool bf16_io, bool state_bf16, hipStream_t stream);
 
 }  // namespace gdn

@@ -379,7 +379,7 @@ struct ScanSmem {
 template <typename E, int NW, bool GATED>
 __global__ __launch_bounds__(64 * NW) void scan_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
-    const float* __restrict__ h0, E* __restrict__ o, float* __restrict__ ht,
+    const void* __restrict__ h0, E* __restrict__ o, void* __restrict__ ht, bool sbf,
     const E* __restrict__ gate, const float* __restrict__ norm_w, float norm_eps,
     Work<E> ws, ChunkMap cm, int Hqk, int Hv, int G) {
   using Sm = ScanSmem<E, NW, GATED>;
@@ -422,10 +422,10 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
   // S[dv0 + r][16t + 4g + i].
   f32x4 ST[8];
   {
-    const float* hp = h0 ? h0 + (((size_t)seq * Hv + h) * kD + dv0 + r) * kD : nullptr;
+    const size_t hrow = (((size_t)seq * Hv + h) * kD + dv0 + r) * kD;
 #pragma unroll
     for (int t = 0; t < 8; ++t)
-      ST[t] = hp ? *reinterpret_cast<const f32x4*>(hp + 16 * t + 4 * g) : zero4();
+      ST[t] = h0 ? load_state4(h0, hrow + 16 * t + 4 * g, sbf) : zero4();
   }
 
   // Chunk operands are fetched into registers one chunk ahead (issued right
@@ -668,9 +668,9 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
   if (nch > 0) write_out(ptok0, pL);
 
   if (ht) {
-    float* hp = ht + (((size_t)seq * Hv + h) * kD + dv0 + r) * kD;
+    const size_t hrow = (((size_t)seq * Hv + h) * kD + dv0 + r) * kD;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) *reinterpret_cast<f32x4*>(hp + 16 * t + 4 * g) = ST[t];
+    for (int t = 0; t < 8; ++t) store_state4(ht, hrow + 16 * t + 4 * g, ST[t], sbf);
   }
 }
 
@@ -782,7 +782,7 @@ __device__ __forceinline__ void barrier_lds() {
 
 __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const float* __restrict__ h0, bf16* __restrict__ o, float* __restrict__ ht, Work<bf16> ws,
+    const void* __restrict__ h0, bf16* __restrict__ o, void* __restrict__ ht, bool sbf, Work<bf16> ws,
     ChunkMap cm, int Hqk, int Hv, int G) {
   using namespace split;
   __shared__ Smem sm;
@@ -920,10 +920,10 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
     // S^T accumulator tiles: ST[t][i] = S[dv0 + r][prow(t, 4g + i)].
     f32x4 ST[8];
     {
-      const float* hp = h0 ? h0 + (((size_t)seq * Hv + h) * kD + dv0 + r) * kD : nullptr;
+      const size_t hrow = (((size_t)seq * Hv + h) * kD + dv0 + r) * kD;
 #pragma unroll
       for (int t = 0; t < 8; ++t)
-        ST[t] = hp ? *reinterpret_cast<const f32x4*>(hp + prow(t, 4 * g)) : zero4();
+        ST[t] = h0 ? load_state4(h0, hrow + prow(t, 4 * g), sbf) : zero4();
     }
     barrier_lds();
     for (int i = 0; i <= nch; ++i) {
@@ -1029,9 +1029,9 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
       barrier_lds();
     }
     if (ht) {
-      float* hp = ht + (((size_t)seq * Hv + h) * kD + dv0 + r) * kD;
+      const size_t hrow = (((size_t)seq * Hv + h) * kD + dv0 + r) * kD;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) *reinterpret_cast<f32x4*>(hp + prow(t, 4 * g)) = ST[t];
+      for (int t = 0; t < 8; ++t) store_state4(ht, hrow + prow(t, 4 * g), ST[t], sbf);
     }
     return;
   }
@@ -1173,7 +1173,7 @@ static hipError_t launch_scan_t(const PrefillLaunch& a, hipStream_t st) {
   if ((a.Hqk & 7) == 0) nlin = ((nlin + 7) / 8) * 8;
   dim3 grid((unsigned)nlin, (unsigned)a.nseq), block(64 * NW);
   hipLaunchKernelGGL((scan_kernel<E, NW, GATED>), grid, block, 0, st, (const E*)a.q,
-                     (const E*)a.k, (const E*)a.v, a.h0, (E*)a.o, a.ht, (const E*)a.gate,
+                     (const E*)a.k, (const E*)a.v, a.h0, (E*)a.o, a.ht, a.state_bf16, (const E*)a.gate,
                      a.norm_w, a.norm_eps, ws, a.cm, a.Hqk, a.Hv, a.Hv / a.Hqk);
   return hipGetLastError();
 }
@@ -1189,7 +1189,7 @@ static hipError_t launch_scan_split(const PrefillLaunch& a, hipStream_t st) {
   if ((a.Hqk & 7) == 0) nlin = ((nlin + 7) / 8) * 8;
   dim3 grid((unsigned)nlin, (unsigned)a.nseq), block(64 * split::kWaves);
   hipLaunchKernelGGL(scan_split_kernel, grid, block, 0, st, (const bf16*)a.q, (const bf16*)a.k,
-                     (const bf16*)a.v, a.h0, (bf16*)a.o, a.ht, ws, a.cm, a.Hqk, a.Hv,
+                     (const bf16*)a.v, a.h0, (bf16*)a.o, a.ht, a.state_bf16, ws, a.cm, a.Hqk, a.Hv,
                      a.Hv / a.Hqk);
   return hipGetLastError();
 }

@@ -40,7 +40,8 @@ def _load():
     lib = ctypes.CDLL(LIB_PATH)
     vp, sz, i32, f32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_float
     pre = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int, vp, sz, vp]
-    for name in ("gdn_prefill_chunked", "gdn_prefill_prepare", "gdn_prefill_scan"):
+    for name in ("gdn_prefill_chunked", "gdn_prefill_prepare", "gdn_prefill_scan",
+                 "gdn_prefill_chunked_bf16_state"):
         fn = getattr(lib, name)
         fn.argtypes = pre
         fn.restype = ctypes.c_int
@@ -51,6 +52,8 @@ def _load():
     lib.gdn_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                     ctypes.c_int, vp]
     lib.gdn_decode_step.restype = ctypes.c_int
+    lib.gdn_decode_step_bf16_state.argtypes = lib.gdn_decode_step.argtypes
+    lib.gdn_decode_step_bf16_state.restype = ctypes.c_int
     lib.gdn_prefill_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp,
                                        f32, i32, i32, i32, ctypes.c_int, vp, sz, vp]
     lib.gdn_prefill_varlen.restype = ctypes.c_int
@@ -140,7 +143,8 @@ def _workspace(nbytes, device, workspace):
 
 
 # ---------------------------------------------------------------- prefill
-def _prefill_args(q, k, v, alpha, beta, h0, o, ht, output_final_state, workspace):
+def _prefill_args(q, k, v, alpha, beta, h0, o, ht, output_final_state, workspace,
+                  state_dtype=torch.float32):
     _req(q, "q", ndim=4)
     dtype, dev = q.dtype, q.device
     B, T, H_qk, D = q.shape
@@ -154,15 +158,15 @@ def _prefill_args(q, k, v, alpha, beta, h0, o, ht, output_final_state, workspace
         _req(t, name, torch.float32, 3, dev)
         if tuple(t.shape) != (B, T, H_v):
             raise ValueError("%s must be [B,T,Hv]" % name)
-    _req(h0, "h0", torch.float32, 4, dev)
+    _req(h0, "h0", state_dtype, 4, dev)
     if h0 is not None and tuple(h0.shape) != (B, H_v, D, D):
         raise ValueError("h0 must be [B,Hv,D,D]")
     if o is None:
         o = torch.empty((B, T, H_v, D), dtype=dtype, device=dev)
     _req(o, "o", dtype, 4, dev)
     if ht is None and output_final_state:
-        ht = torch.empty((B, H_v, D, D), dtype=torch.float32, device=dev)
-    _req(ht, "ht", torch.float32, 4, dev)
+        ht = torch.empty((B, H_v, D, D), dtype=state_dtype, device=dev)
+    _req(ht, "ht", state_dtype, 4, dev)
     nbytes = prefill_workspace_bytes(B, T, H_qk, H_v, D, dtype)
     ws = _workspace(nbytes, dev, workspace)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(h0), _ptr(o), _ptr(ht),
@@ -171,13 +175,23 @@ def _prefill_args(q, k, v, alpha, beta, h0, o, ht, output_final_state, workspace
 
 
 def prefill_chunked(q, k, v, alpha, beta, h0=None, *, o=None, ht=None,
-                    output_final_state=True, workspace=None):
+                    output_final_state=True, workspace=None, state_dtype=None):
     """Chunked prefill of B equal-length sequences (gdn_prefill_chunked).
     q, k [B,T,Hqk,128]; v [B,T,Hv,128] (bf16 or fp32); alpha, beta [B,T,Hv]
-    fp32; h0 [B,Hv,128,128] fp32 or None.  Returns (o, ht)."""
+    fp32; h0 [B,Hv,128,128] or None.  States (h0, ht) are fp32, or bf16
+    (gdn_prefill_chunked_bf16_state) when ``state_dtype`` is torch.bfloat16;
+    by default the dtype of h0, else of ht, else fp32.  Returns (o, ht)."""
+    if state_dtype is None:
+        state_dtype = h0.dtype if h0 is not None else (ht.dtype if ht is not None
+                                                       else torch.float32)
+    if state_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("state_dtype must be torch.float32 or torch.bfloat16")
     args, o, ht, _ = _prefill_args(q, k, v, alpha, beta, h0, o, ht, output_final_state,
-                                   workspace)
-    _check(lib.gdn_prefill_chunked(*args), "gdn_prefill_chunked")
+                                   workspace, state_dtype)
+    if state_dtype == torch.bfloat16:
+        _check(lib.gdn_prefill_chunked_bf16_state(*args), "gdn_prefill_chunked_bf16_state")
+    else:
+        _check(lib.gdn_prefill_chunked(*args), "gdn_prefill_chunked")
     return o, ht
 
 
@@ -197,8 +211,9 @@ def prefill_scan(q, k, v, alpha, beta, h0, o, ht, workspace):
 
 # ---------------------------------------------------------------- decode
 def decode_step(q, k, v, alpha, beta, state, *, o=None):
-    """One token per sequence (gdn_decode_step); ``state`` [B,Hv,128,128]
-    fp32 is updated in place.  Returns o [B,Hv,128]."""
+    """One token per sequence; ``state`` [B,Hv,128,128] is updated in place:
+    fp32 (gdn_decode_step) or bf16 (gdn_decode_step_bf16_state).  Returns
+    o [B,Hv,128]."""
     _req(q, "q", ndim=3)
     dtype, dev = q.dtype, q.device
     B, H_qk, D = q.shape
@@ -211,14 +226,17 @@ def decode_step(q, k, v, alpha, beta, state, *, o=None):
         _req(t, name, torch.float32, 2, dev)
         if tuple(t.shape) != (B, H_v):
             raise ValueError("%s must be [B,Hv]" % name)
-    _req(state, "state", torch.float32, 4, dev)
+    if not isinstance(state, torch.Tensor) or state.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("state must be a float32 or bfloat16 tensor")
+    _req(state, "state", state.dtype, 4, dev)
     if tuple(state.shape) != (B, H_v, D, D):
         raise ValueError("state must be [B,Hv,D,D]")
     if o is None:
         o = torch.empty((B, H_v, D), dtype=dtype, device=dev)
     _req(o, "o", dtype, 3, dev)
-    rc = lib.gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state),
-                             _ptr(o), B, H_qk, H_v, D, _dt(q), _stream(dev))
+    fn = lib.gdn_decode_step if state.dtype == torch.float32 else lib.gdn_decode_step_bf16_state
+    rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state),
+            _ptr(o), B, H_qk, H_v, D, _dt(q), _stream(dev))
     _check(rc, "gdn_decode_step")
     return o
 

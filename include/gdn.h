@@ -142,6 +142,41 @@ gdn_status gdn_decode_step(const void *q, const void *k, const void *v,
                            int32_t D, gdn_dtype dt, void *stream);
 
 /*
+ * States stored as bfloat16.  The pages count the recurrent-state footprint
+ * at BF16 (page "Qwen3.8 Explained: 27B Multimodal, 2.4T MoE, and the VRAM
+ * Math", section "The architecture detail that matters for VRAM": a constant
+ * overhead of tens of megabytes over the 48 DeltaNet layers).  These calls
+ * take and return the state in bfloat16; all arithmetic stays fp32, and a
+ * state is rounded to bfloat16 (nearest even) only where it is stored.
+ *
+ * gdn_decode_step_bf16_state: as gdn_decode_step with
+ *   state  [B, H_v, D, D]   bfloat16, read and overwritten with S_t
+ * which halves the bytes the step moves.  Same errors and aliasing rules.
+ */
+gdn_status gdn_decode_step_bf16_state(const void *q, const void *k,
+                                      const void *v, const float *alpha,
+                                      const float *beta, void *state, void *o,
+                                      int32_t B, int32_t H_qk, int32_t H_v,
+                                      int32_t D, gdn_dtype dt, void *stream);
+
+/*
+ * gdn_prefill_chunked_bf16_state: as gdn_prefill_chunked with
+ *   h0     [B, H_v, D, D]   bfloat16 initial state, or NULL for zeros
+ *   ht     [B, H_v, D, D]   bfloat16 final state, or NULL; may be exactly h0
+ * (the carry between a prefill and the decode steps that follow it).  The
+ * state inside the call is fp32; only h0 and ht are bfloat16.  Uses the same
+ * workspace size as gdn_prefill_chunked.
+ */
+gdn_status gdn_prefill_chunked_bf16_state(const void *q, const void *k,
+                                          const void *v, const float *alpha,
+                                          const float *beta, const void *h0,
+                                          void *o, void *ht, int32_t B,
+                                          int32_t T, int32_t H_qk, int32_t H_v,
+                                          int32_t D, gdn_dtype dt,
+                                          void *workspace,
+                                          size_t workspace_bytes, void *stream);
+
+/*
  * gdn_prefill_varlen - N sequences of different lengths packed along the
  * token axis (several concurrent sequences, as a serving engine batches them:
  * page "Inside Qwen3.8-27B ...", section "Serving Qwen3.8-27B: Recipes for

@@ -145,6 +145,35 @@ def test_decode_validation(lib, kw, code):
     assert decode_call(lib, **kw) == code
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=64), EUNSUP),
+    (dict(state=None), ENULL),
+    (dict(state=addr(5, 8)), EALIGN),
+    (dict(o=addr(5, 256)), EALIAS),           # o inside the bf16 state
+    (dict(o=addr(5, 64 * 48 * 128 * 128 * 2 - 16)), EALIAS),   # o in the bf16 state's last bytes
+])
+def test_decode_bf16_state_validation(lib, kw, code):
+    args = dict(q=addr(0), k=addr(1), v=addr(2), alpha=addr(3), beta=addr(4), state=addr(5),
+                o=addr(6), B=64, Hqk=16, Hv=48, D=128, dt=BF16, stream=None)
+    args.update(kw)
+    rc = lib.gdn_decode_step_bf16_state(args["q"], args["k"], args["v"], args["alpha"],
+                                        args["beta"], args["state"], args["o"], args["B"],
+                                        args["Hqk"], args["Hv"], args["D"], args["dt"],
+                                        args["stream"])
+    assert rc == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=64), EUNSUP),
+    (dict(ht=addr(7, 4)), EALIGN),
+    (dict(ht=addr(5, 1024)), EALIAS),         # ht overlaps h0 without being h0
+    (dict(o=addr(5, 48 * 128 * 128 * 2 - 16)), EALIAS),   # o in h0's last bytes (bf16)
+    (dict(ws=None), EWS),
+])
+def test_prefill_bf16_state_validation(lib, kw, code):
+    assert prefill_call(lib, "gdn_prefill_chunked_bf16_state", **kw) == code
+
+
 def test_decode_empty_batch_is_a_no_op(lib):
     assert decode_call(lib, B=0) == OK
 

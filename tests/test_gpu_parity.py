@@ -220,6 +220,99 @@ def test_decode_steps_equal_fp32_prefill(gdn):
     assert rel(st, ht_p.cpu().double().numpy()) <= 1e-5
 
 
+# ------------------------------------------------------------------ bf16 state storage
+def _bf16(x64):
+    """float64 array holding bfloat16 values -> bfloat16 tensor (exact)."""
+    return torch.from_numpy(np.asarray(x64, dtype=np.float64)).float().to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+def test_decode_bf16_state_small(gdn, dtype):
+    B, steps = 5, 6
+    say("decode_bf16_state_small", dtype)
+    st = synth.decode_state(B, seed=31, std=0.05).to(torch.bfloat16).to(DEV)
+    ref = st.cpu().double().numpy().copy()
+    worst = 0.0
+    for s in range(steps):
+        d = synth.decode_step_inputs(B, s, dtype, seed=31)
+        dd = to_dev(d)
+        o = gdn.decode_step(dd["q"], dd["k"], dd["v"], dd["alpha"], dd["beta"], st)
+        o_ref, ref = oracle.decode_step_bf16_state(d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                                                   ref)
+        torch.cuda.synchronize()
+        worst = max(worst, rel(o, o_ref))
+    worst = max(worst, rel(st, ref))
+    say("  worst rel %.3e" % worst)
+    assert st.dtype == torch.bfloat16 and worst <= 2e-2
+
+
+def test_decode_bf16_state_64x64(gdn):
+    """The decode workload's batch (64 sequences) with the state in bf16, for
+    64 steps (each oracle step rounds 50 M state elements on the host)."""
+    B, steps = 64, 64
+    st = synth.decode_state(B, 1002, 0.02).to(torch.bfloat16)
+    ref = st.double().numpy().copy()
+    st = st.to(DEV)
+    worst = 0.0
+    t0 = time.time()
+    for s in range(steps):
+        d = synth.decode_step_inputs(B, s, torch.bfloat16, seed=1002)
+        dd = to_dev(d)
+        o = gdn.decode_step(dd["q"], dd["k"], dd["v"], dd["alpha"], dd["beta"], st)
+        o_ref, ref = oracle.decode_step_bf16_state(d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                                                   ref)
+        worst = max(worst, rel(o, o_ref))
+        if s % 16 == 0:
+            say("  bf16-state decode step %d worst %.3e (%.1fs)" % (s, worst, time.time() - t0))
+    worst = max(worst, rel(st, ref))
+    say("decode bf16 state 64x64 worst rel %.3e" % worst)
+    assert worst <= 2e-2
+
+
+@pytest.mark.parametrize("T", [0, 64, 150], ids=["T0", "T64", "T150"])
+def test_prefill_bf16_state(gdn, T):
+    inp = synth.prefill_inputs(2, T, torch.bfloat16, seed=33, h0_std=0.05)
+    h0 = inp["h0"].to(torch.bfloat16)
+    d = to_dev(inp)
+    o, ht = gdn.prefill_chunked(d["q"], d["k"], d["v"], d["alpha"], d["beta"], h0.to(DEV))
+    torch.cuda.synchronize()
+    assert ht.dtype == torch.bfloat16
+    if T == 0:
+        assert torch.equal(ht.cpu(), h0)                 # passes the state through exactly
+        return
+    o_ref, ht_ref = oracle.prefill_bf16_state(inp["q"], inp["k"], inp["v"], inp["alpha"],
+                                              inp["beta"], h0)
+    eo, eh = rel(o, o_ref), rel(ht, ht_ref)
+    say("prefill bf16 state T=%d rel o %.3e ht %.3e" % (T, eo, eh))
+    assert eo <= 2e-2 and eh <= 2e-2
+    # the same call with the final state written over h0
+    hin = h0.to(DEV)
+    o2, ht2 = gdn.prefill_chunked(d["q"], d["k"], d["v"], d["alpha"], d["beta"], hin, ht=hin)
+    torch.cuda.synchronize()
+    assert ht2.data_ptr() == hin.data_ptr()
+    assert torch.equal(o2, o) and torch.equal(ht2, ht)
+
+
+def test_bf16_state_prefill_then_decode(gdn):
+    """Carry in bf16: a prefill's final state continues in decode steps."""
+    T, steps = 130, 8
+    inp = synth.prefill_inputs(1, T, torch.bfloat16, seed=34, h0_std=0.02)
+    h0 = inp["h0"].to(torch.bfloat16)
+    d = to_dev(inp)
+    _, st = gdn.prefill_chunked(d["q"], d["k"], d["v"], d["alpha"], d["beta"], h0.to(DEV))
+    _, ref = oracle.prefill_bf16_state(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], h0)
+    worst = rel(st, ref)
+    for s in range(steps):
+        dd = synth.decode_step_inputs(1, s, torch.bfloat16, seed=34)
+        o = gdn.decode_step(*(dd[x].to(DEV) for x in ("q", "k", "v", "alpha", "beta")), st)
+        o_ref, ref = oracle.decode_step_bf16_state(dd["q"], dd["k"], dd["v"], dd["alpha"],
+                                                   dd["beta"], ref)
+        worst = max(worst, rel(o, o_ref))
+    worst = max(worst, rel(st, ref))
+    say("bf16 carry prefill -> decode worst rel %.3e" % worst)
+    assert worst <= 2e-2
+
+
 # ------------------------------------------------------------------ varlen
 @pytest.mark.parametrize("gated", [False, True], ids=["plain", "gated"])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
