@@ -35,6 +35,8 @@ prefill(q, k, v, alpha, beta, h0=None)       -> (o, ht)     C, OpenMP over (b, h
 decode_step(q, k, v, alpha, beta, state)     -> (o, state') C
 decode_step_bf16_state(...), prefill_bf16_state(...)   states stored in bf16
 round_bf16(x)                                -> x rounded to bfloat16 (RNE)
+decode_verify(q, k, v, alpha, beta, state)   -> o of n draft tokens, state unchanged
+decode_commit(k, v, alpha, beta, state, m)   -> state advanced by m[b] accepted tokens
 varlen(q, k, v, alpha, beta, cu_seqlens, ...)-> (y, ht)     C per sequence + epilogue
 gate_rmsnorm(o, gate, weight, eps)           -> y           NumPy float64
 np_prefill(q, k, v, alpha, beta, h0=None)    -> (o, ht)     NumPy twin (tiny sizes)
@@ -150,6 +152,37 @@ def decode_step(q, k, v, alpha, beta, state, inplace=False):
     if rc != 0:
         raise ValueError("oracle_gdn_decode_step failed (%d)" % rc)
     return o, st
+
+
+def decode_verify(q, k, v, alpha, beta, state):
+    """Outputs for n draft tokens per sequence, starting from ``state``,
+    without changing it (the verify pass of speculative decoding with drafted
+    tokens, as the MTP heads on page "Inside Qwen3.8-27B ...", section
+    "Multi-Token Prediction (MTP)", produce them).  q, k ``[B,n,Hqk,D]``;
+    v ``[B,n,Hv,D]``; alpha, beta ``[B,n,Hv]``; state ``[B,Hv,D,D]``.
+    Returns o ``[B,n,Hv,D]``: token t's output is S_t q_t with S_t the state
+    after draft tokens 0..t, i.e. the prefill of the n tokens from state."""
+    o, _ = prefill(q, k, v, alpha, beta, state)
+    return o
+
+
+def decode_commit(k, v, alpha, beta, state, n_accept):
+    """Advance ``state`` by the first ``n_accept[b]`` draft tokens of each
+    sequence b (the accepted prefix; values are clipped to [0, n]).  Returns
+    the new state; the input is not modified."""
+    k, v, alpha, beta = (_f64(x) for x in (k, v, alpha, beta))
+    st = _f64(state).copy()
+    B, n = k.shape[:2]
+    acc = np.clip(np.asarray(n_accept, dtype=np.int64).reshape(B), 0, n)
+    for b in range(B):
+        m = int(acc[b])
+        if m == 0:
+            continue
+        sl = slice(b, b + 1)
+        zq = np.zeros_like(k[sl, :m])
+        _, ht = prefill(zq, k[sl, :m], v[sl, :m], alpha[sl, :m], beta[sl, :m], st[sl])
+        st[b] = ht[0]
+    return st
 
 
 # bfloat16: 1 sign bit, 8 exponent bits, 7 fraction bits (8 significant

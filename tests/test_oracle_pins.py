@@ -391,6 +391,34 @@ def test_bf16_state_variants(oracle_mod):
     np.testing.assert_array_equal(hp, oracle.round_bf16(hp_ref))
 
 
+def test_verify_commit_pins(oracle_mod):
+    """Speculative decoding glue: verify of n tokens equals n sequential
+    decode steps on a copy; commit of m tokens equals m decode steps; the
+    state is advanced only by commit; per-sequence acceptance counts."""
+    r = rng(23)
+    B, n, Hqk, Hv, D = 3, 3, 2, 4, 16
+    q = unit(r.standard_normal((B, n, Hqk, D))); k = unit(r.standard_normal((B, n, Hqk, D)))
+    v = r.standard_normal((B, n, Hv, D))
+    a = np.exp(-0.05 * r.random((B, n, Hv))); be = r.random((B, n, Hv))
+    st = r.standard_normal((B, Hv, D, D)) * 0.1
+    st0 = st.copy()
+    o = oracle.decode_verify(q, k, v, a, be, st)
+    np.testing.assert_array_equal(st, st0)
+    ref = st.copy()
+    for t in range(n):
+        ot, ref = oracle.decode_step(q[:, t], k[:, t], v[:, t], a[:, t], be[:, t], ref)
+        np.testing.assert_allclose(o[:, t], ot, rtol=1e-12, atol=1e-14)
+        s_t = oracle.decode_commit(k, v, a, be, st, [t + 1] * B)
+        np.testing.assert_allclose(s_t, ref, rtol=1e-12, atol=1e-14)
+    m = [0, 2, 5]                                     # 5 is clipped to n
+    s_m = oracle.decode_commit(k, v, a, be, st, m)
+    np.testing.assert_array_equal(s_m[0], st[0])
+    _, s2 = oracle.decode_step(q[1:2, 0], k[1:2, 0], v[1:2, 0], a[1:2, 0], be[1:2, 0], st[1:2])
+    _, s2 = oracle.decode_step(q[1:2, 1], k[1:2, 1], v[1:2, 1], a[1:2, 1], be[1:2, 1], s2)
+    np.testing.assert_allclose(s_m[1], s2[0], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(s_m[2], ref[2], rtol=1e-12, atol=1e-14)
+
+
 def test_gate_rmsnorm_pins():
     r = rng(13)
     D = 128
