@@ -152,6 +152,36 @@ def timed_decode(gdn, B, steps, warmup, dtype=torch.bfloat16, state_dtype=torch.
     return dict(step_ms=ms, gbs=gbs, state_bytes=nbytes)
 
 
+def timed_speculative(gdn, B, n, rounds, warmup):
+    """Verify of n drafted tokens then commit of all of them, per round: the
+    state is read by verify and read + written by commit."""
+    dev = "cuda:0"
+    state = synth.decode_state(B, 1002, 0.02).to(dev)
+    d = {k: v.to(dev) for k, v in synth.prefill_inputs(B, n, torch.bfloat16, seed=77).items()
+         if v is not None}
+    acc = torch.full((B,), n, dtype=torch.int32, device=dev)
+    o = torch.empty((B, n, HV, D), dtype=torch.bfloat16, device=dev)
+
+    def rnd():
+        gdn.decode_verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], state, o=o)
+        gdn.decode_commit(d["k"], d["v"], d["alpha"], d["beta"], state, acc)
+
+    for _ in range(warmup):
+        rnd()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(rounds):
+        rnd()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / rounds
+    nbytes = 3 * decode_state_bytes(B) // 2
+    return dict(ms=ms, gbs=nbytes / (ms * 1e-3) / 1e9, tokens_per_s=B * n / (ms * 1e-3))
+
+
 def cpu_baseline(inp, T_sample, min_seconds=10.0, max_calls=64):
     """The float64 oracle, untuned, on the same workload: the first T_sample
     tokens of every value head, called repeatedly until about min_seconds of
@@ -227,6 +257,9 @@ def main():
     log("decode B=64 with the state stored in bf16: %d steps" % args.decode_steps)
     decb = timed_decode(gdn, 64, args.decode_steps, 16, state_dtype=torch.bfloat16)
     log("decode bf16-state step %.4f ms, %.1f GB/s" % (decb["step_ms"], decb["gbs"]))
+    spec = timed_speculative(gdn, 64, 3, 64, 8)
+    log("speculative verify + commit of 3 tokens x 64 sequences: %.4f ms, %.1f GB/s"
+        % (spec["ms"], spec["gbs"]))
 
     out = {
         "metric": "GDN prefill tokens/s @T=8192 (% MFMA peak) + decode state GB/s (% HBM peak)",
@@ -267,7 +300,12 @@ def main():
                    "bf16_state": {"ms_per_step": decb["step_ms"], "gbs": decb["gbs"],
                                   "frac": decb["gbs"] / PEAK_HBM_GBS,
                                   "state_bytes_per_step": decb["state_bytes"],
-                                  "sequences_per_s": 64 / (decb["step_ms"] * 1e-3)}},
+                                  "sequences_per_s": 64 / (decb["step_ms"] * 1e-3)},
+                   "speculative_n3": {"ms_per_round": spec["ms"], "state_gbs": spec["gbs"],
+                                      "frac": spec["gbs"] / PEAK_HBM_GBS,
+                                      "tokens_per_s_all_accepted": spec["tokens_per_s"],
+                                      "workload": "64 sequences, verify of 3 drafted tokens then "
+                                                  "commit of all 3, fp32 state"}},
     }
     if args.extended:
         log("extended: T=262144")

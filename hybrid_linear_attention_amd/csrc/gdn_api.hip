@@ -291,6 +291,59 @@ gdn_status gdn_decode_step_bf16_state(const void* q, const void* k, const void* 
   return decode_common(q, k, v, alpha, beta, state, o, B, H_qk, H_v, D, dt, stream, true);
 }
 
+gdn_status gdn_decode_verify(const void* q, const void* k, const void* v, const float* alpha,
+                             const float* beta, const float* state, void* o, int32_t B,
+                             int32_t n, int32_t H_qk, int32_t H_v, int32_t D, gdn_dtype dt,
+                             void* stream) {
+  gdn_status s = check_dims(H_qk, H_v, D, dt);
+  if (s != GDN_OK) return s;
+  if (B < 0 || n < 1) return GDN_ERR_SHAPE;
+  if (n > gdn::kMaxDraft) return GDN_ERR_UNSUPPORTED;
+  if (B == 0) return GDN_OK;
+  if (!q || !k || !v || !alpha || !beta || !state || !o) return GDN_ERR_NULL;
+  if ((int64_t)B * H_v > (int64_t(1) << 30)) return GDN_ERR_UNSUPPORTED;
+  const int64_t es = (int64_t)esize(dt), Dl = gdn::kD, Bn = (int64_t)B * n;
+  const void* p16[] = {q, k, v, o, state};
+  for (const void* p : p16)
+    if (!aligned(p, 16)) return GDN_ERR_ALIGN;
+  if (!aligned(alpha, 4) || !aligned(beta, 4)) return GDN_ERR_ALIGN;
+  const Range ro = span(o, Bn * H_v * Dl * es);
+  const Range ins[] = {span(q, Bn * H_qk * Dl * es), span(k, Bn * H_qk * Dl * es),
+                       span(v, Bn * H_v * Dl * es), span(alpha, Bn * H_v * 4),
+                       span(beta, Bn * H_v * 4), span(state, (int64_t)B * H_v * Dl * Dl * 4)};
+  for (const Range& in : ins)
+    if (overlap(ro, in)) return GDN_ERR_ALIAS;
+  return fail_hip(gdn::launch_decode_multi(q, k, v, alpha, beta, const_cast<float*>(state),
+                                           nullptr, o, B, n, H_qk, H_v, dt == GDN_BF16, true,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_decode_commit(const void* k, const void* v, const float* alpha, const float* beta,
+                             float* state, const int32_t* n_accept, int32_t B, int32_t n,
+                             int32_t H_qk, int32_t H_v, int32_t D, gdn_dtype dt, void* stream) {
+  gdn_status s = check_dims(H_qk, H_v, D, dt);
+  if (s != GDN_OK) return s;
+  if (B < 0 || n < 1) return GDN_ERR_SHAPE;
+  if (n > gdn::kMaxDraft) return GDN_ERR_UNSUPPORTED;
+  if (B == 0) return GDN_OK;
+  if (!k || !v || !alpha || !beta || !state || !n_accept) return GDN_ERR_NULL;
+  if ((int64_t)B * H_v > (int64_t(1) << 30)) return GDN_ERR_UNSUPPORTED;
+  const int64_t es = (int64_t)esize(dt), Dl = gdn::kD, Bn = (int64_t)B * n;
+  const void* p16[] = {k, v, state};
+  for (const void* p : p16)
+    if (!aligned(p, 16)) return GDN_ERR_ALIGN;
+  if (!aligned(alpha, 4) || !aligned(beta, 4) || !aligned(n_accept, 4)) return GDN_ERR_ALIGN;
+  const Range rs = span(state, (int64_t)B * H_v * Dl * Dl * 4);
+  const Range ins[] = {span(k, Bn * H_qk * Dl * es), span(v, Bn * H_v * Dl * es),
+                       span(alpha, Bn * H_v * 4), span(beta, Bn * H_v * 4),
+                       span(n_accept, (int64_t)B * 4)};
+  for (const Range& in : ins)
+    if (overlap(rs, in)) return GDN_ERR_ALIAS;
+  return fail_hip(gdn::launch_decode_multi(nullptr, k, v, alpha, beta, state, n_accept, nullptr,
+                                           B, n, H_qk, H_v, dt == GDN_BF16, false,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 gdn_status gdn_prefill_varlen(const void* q, const void* k, const void* v, const float* alpha,
                               const float* beta, const int32_t* cu_seqlens, int32_t N,
                               int32_t T_tot, const float* h0, void* o, float* ht,

@@ -198,6 +198,122 @@ __global__ __launch_bounds__(256) void decode_step_bs_kernel(
   }
 }
 
+// Speculative decoding with n drafted tokens per sequence (the MTP heads of
+// page "Inside Qwen3.8-27B ...", section "Multi-Token Prediction (MTP)",
+// draft tokens t+1 and t+2).  VERIFY: outputs of all n tokens from the state,
+// which is read but not written.  COMMIT: the state advanced in place by the
+// first m = clamp(n_accept[b], 0, n) tokens; q and o are not used.  The n
+// tokens' q, k, v, alpha, beta are first staged in LDS (as float32) so their
+// loads overlap the state's; then every thread applies the n steps to its 4
+// rows in registers, exactly as decode_step_kernel does for one.
+template <typename E, bool VERIFY>
+__global__ __launch_bounds__(256) void decode_multi_kernel(
+    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
+    const float* __restrict__ alpha, const float* __restrict__ beta, float* __restrict__ state,
+    const int32_t* __restrict__ n_accept, E* __restrict__ o, int n, int Hqk, int Hv, int G) {
+  __shared__ float sk[kMaxDraft][kD], sq[kMaxDraft][kD], sv[kMaxDraft][kD];
+  __shared__ float sa[kMaxDraft], sbt[kMaxDraft];
+  const int bh = blockIdx.x;
+  const int b = bh / Hv, h = bh - (bh / Hv) * Hv;
+  const int gq = h / G;
+  const int tid = threadIdx.x;
+  const int l8 = tid & 7;
+  const int rg = tid >> 3;
+  const int m = VERIFY ? n : min(max(n_accept[b], 0), n);
+  float* S = state + (size_t)bh * kD * kD;
+
+  f32x4 s[4][4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      s[p][i] = *reinterpret_cast<const f32x4*>(S + (rg + 32 * p) * kD + 4 * l8 + 32 * i);
+
+  for (int e = tid; e < m * kD; e += 256) {
+    const int t = e / kD, c = e - (e / kD) * kD;
+    const size_t tk = ((size_t)b * n + t) * Hqk + gq, tv = ((size_t)b * n + t) * Hv + h;
+    sk[t][c] = to_f32(k[tk * kD + c]);
+    if (VERIFY) sq[t][c] = to_f32(q[tk * kD + c]);
+    sv[t][c] = to_f32(v[tv * kD + c]);
+    if (c == 0) {
+      sa[t] = alpha[tv];
+      sbt[t] = beta[tv];
+    }
+  }
+  __syncthreads();
+
+  for (int t = 0; t < m; ++t) {
+    f32x4 kr[4], qr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kr[i] = *reinterpret_cast<const f32x4*>(&sk[t][4 * l8 + 32 * i]);
+      if (VERIFY) qr[i] = *reinterpret_cast<const f32x4*>(&sq[t][4 * l8 + 32 * i]);
+    }
+    const float a = sa[t], be = sbt[t];
+    float kq = 0.f;
+    if (VERIFY) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kq += dot4(kr[i], qr[i]);
+      kq = sum8(kq);
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int row = rg + 32 * p;
+      float u = 0.f, pq = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u += dot4(s[p][i], kr[i]);
+        if (VERIFY) pq += dot4(s[p][i], qr[i]);
+      }
+      u = sum8(u);
+      const float d = be * (sv[t][row] - a * u);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s[p][i][j] = a * s[p][i][j] + d * kr[i][j];
+      if (VERIFY) {
+        pq = sum8(pq);
+        if (l8 == 0) o[(((size_t)b * n + t) * Hv + h) * kD + row] = from_f32<E>(a * pq + d * kq);
+      }
+    }
+  }
+  if (!VERIFY && m > 0) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<f32x4*>(S + (rg + 32 * p) * kD + 4 * l8 + 32 * i) = s[p][i];
+  }
+}
+
+hipError_t launch_decode_multi(const void* q, const void* k, const void* v, const float* alpha,
+                               const float* beta, float* state, const int32_t* n_accept,
+                               void* o, int B, int n, int Hqk, int Hv, bool bf16_io,
+                               bool verify, hipStream_t stream) {
+  const int G = Hv / Hqk;
+  dim3 grid((unsigned)(B * Hv)), block(256);
+  if (bf16_io) {
+    if (verify)
+      hipLaunchKernelGGL((decode_multi_kernel<bf16, true>), grid, block, 0, stream,
+                         (const bf16*)q, (const bf16*)k, (const bf16*)v, alpha, beta, state,
+                         n_accept, (bf16*)o, n, Hqk, Hv, G);
+    else
+      hipLaunchKernelGGL((decode_multi_kernel<bf16, false>), grid, block, 0, stream,
+                         (const bf16*)q, (const bf16*)k, (const bf16*)v, alpha, beta, state,
+                         n_accept, (bf16*)o, n, Hqk, Hv, G);
+  } else {
+    if (verify)
+      hipLaunchKernelGGL((decode_multi_kernel<float, true>), grid, block, 0, stream,
+                         (const float*)q, (const float*)k, (const float*)v, alpha, beta, state,
+                         n_accept, (float*)o, n, Hqk, Hv, G);
+    else
+      hipLaunchKernelGGL((decode_multi_kernel<float, false>), grid, block, 0, stream,
+                         (const float*)q, (const float*)k, (const float*)v, alpha, beta, state,
+                         n_accept, (float*)o, n, Hqk, Hv, G);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_decode_step(const void* q, const void* k, const void* v,
                               const float* alpha, const float* beta, void* state,
                               void* o, int B, int Hqk, int Hv, bool bf16_io, bool state_bf16,

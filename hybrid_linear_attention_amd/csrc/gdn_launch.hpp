@@ -35,6 +35,13 @@ hipError_t launch_prepare(const PrefillLaunch& a, hipStream_t st);
 hipError_t launch_scan(const PrefillLaunch& a, hipStream_t st);
 hipError_t launch_varlen_table(const int32_t* cu, int N, int T_tot, int nc_max, int32_t* tab,
                                int32_t* seq_off, hipStream_t st);
+// Most drafted tokens a verify or commit call takes per sequence.
+constexpr int kMaxDraft = 8;
+
+hipError_t launch_decode_multi(const void* q, const void* k, const void* v, const float* alpha,
+                               const float* beta, float* state, const int32_t* n_accept,
+                               void* o, int B, int n, int Hqk, int Hv, bool bf16_io,
+                               bool verify, hipStream_t stream);
 hipError_t launch_decode_step(const void* q, const void* k, const void* v, const float* alpha,
                               const float* beta, void* state, void* o, int B, int Hqk, int Hv,
                               bool bf16_io, bool state_bf16, hipStream_t stream);

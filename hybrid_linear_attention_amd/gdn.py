@@ -54,6 +54,12 @@ def _load():
     lib.gdn_decode_step.restype = ctypes.c_int
     lib.gdn_decode_step_bf16_state.argtypes = lib.gdn_decode_step.argtypes
     lib.gdn_decode_step_bf16_state.restype = ctypes.c_int
+    lib.gdn_decode_verify.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                      ctypes.c_int, vp]
+    lib.gdn_decode_verify.restype = ctypes.c_int
+    lib.gdn_decode_commit.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                      ctypes.c_int, vp]
+    lib.gdn_decode_commit.restype = ctypes.c_int
     lib.gdn_prefill_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp,
                                        f32, i32, i32, i32, ctypes.c_int, vp, sz, vp]
     lib.gdn_prefill_varlen.restype = ctypes.c_int
@@ -239,6 +245,54 @@ def decode_step(q, k, v, alpha, beta, state, *, o=None):
             _ptr(o), B, H_qk, H_v, D, _dt(q), _stream(dev))
     _check(rc, "gdn_decode_step")
     return o
+
+
+def _multi_args(k, v, alpha, beta, state):
+    _req(k, "k", ndim=4)
+    dtype, dev = k.dtype, k.device
+    B, n, H_qk, D = k.shape
+    _req(v, "v", dtype, 4, dev)
+    H_v = v.shape[2]
+    if tuple(v.shape) != (B, n, H_v, D):
+        raise ValueError("k [B,n,Hqk,D] and v [B,n,Hv,D] disagree")
+    for name, t in (("alpha", alpha), ("beta", beta)):
+        _req(t, name, torch.float32, 3, dev)
+        if tuple(t.shape) != (B, n, H_v):
+            raise ValueError("%s must be [B,n,Hv]" % name)
+    _req(state, "state", torch.float32, 4, dev)
+    if tuple(state.shape) != (B, H_v, D, D):
+        raise ValueError("state must be [B,Hv,D,D]")
+    return dtype, dev, B, n, H_qk, H_v, D
+
+
+def decode_verify(q, k, v, alpha, beta, state, *, o=None):
+    """Outputs of n drafted tokens per sequence from ``state`` (not modified)
+    (gdn_decode_verify).  q, k [B,n,Hqk,128]; v [B,n,Hv,128]; alpha, beta
+    [B,n,Hv] fp32; state [B,Hv,128,128] fp32.  Returns o [B,n,Hv,128]."""
+    dtype, dev, B, n, H_qk, H_v, D = _multi_args(k, v, alpha, beta, state)
+    _req(q, "q", dtype, 4, dev)
+    if tuple(q.shape) != tuple(k.shape):
+        raise ValueError("q and k must have the same shape")
+    if o is None:
+        o = torch.empty((B, n, H_v, D), dtype=dtype, device=dev)
+    _req(o, "o", dtype, 4, dev)
+    _check(lib.gdn_decode_verify(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                 _ptr(state), _ptr(o), B, n, H_qk, H_v, D, _dt(k), _stream(dev)),
+           "gdn_decode_verify")
+    return o
+
+
+def decode_commit(k, v, alpha, beta, state, n_accept):
+    """Advance ``state`` in place by the first n_accept[b] drafted tokens of
+    each sequence (gdn_decode_commit); n_accept is an int32 tensor [B] on the
+    device."""
+    dtype, dev, B, n, H_qk, H_v, D = _multi_args(k, v, alpha, beta, state)
+    _req(n_accept, "n_accept", torch.int32, 1, dev)
+    if n_accept.shape[0] != B:
+        raise ValueError("n_accept must be [B]")
+    _check(lib.gdn_decode_commit(_ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state),
+                                 _ptr(n_accept), B, n, H_qk, H_v, D, _dt(k), _stream(dev)),
+           "gdn_decode_commit")
 
 
 # ---------------------------------------------------------------- varlen

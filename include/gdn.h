@@ -177,6 +177,42 @@ gdn_status gdn_prefill_chunked_bf16_state(const void *q, const void *k,
                                           size_t workspace_bytes, void *stream);
 
 /*
+ * Speculative decoding with drafted tokens (page "Inside Qwen3.8-27B ...",
+ * section "Multi-Token Prediction (MTP)": extra heads draft the next tokens,
+ * which the model then verifies).  For n drafted tokens per sequence
+ * (1 <= n <= 8):
+ *
+ * gdn_decode_verify: the outputs of all n tokens, token t's output being
+ * S_t q_t with S_t the state after tokens 0..t, computed from `state`,
+ * which is only read.
+ *   q, k   [B, n, H_qk, D]  dt
+ *   v      [B, n, H_v, D]   dt
+ *   alpha, beta [B, n, H_v] float32
+ *   state  [B, H_v, D, D]   float32, not modified
+ *   o      [B, n, H_v, D]   dt
+ *
+ * gdn_decode_commit: advances `state` in place by the first
+ * min(max(n_accept[b], 0), n) tokens of sequence b, the accepted prefix (0:
+ * unchanged).  n_accept is an int32 DEVICE array [B], so the count decided on
+ * the device needs no host round trip.  k, v, alpha, beta as for verify.
+ *
+ * Verify then commit is the rollback of a rejected draft: the state is never
+ * advanced past the accepted prefix, and no snapshot is kept.  Verify reads
+ * the state once, and commit reads and writes it once, whatever n is.
+ * n > 8 returns GDN_ERR_UNSUPPORTED.
+ */
+gdn_status gdn_decode_verify(const void *q, const void *k, const void *v,
+                             const float *alpha, const float *beta,
+                             const float *state, void *o, int32_t B, int32_t n,
+                             int32_t H_qk, int32_t H_v, int32_t D, gdn_dtype dt,
+                             void *stream);
+gdn_status gdn_decode_commit(const void *k, const void *v, const float *alpha,
+                             const float *beta, float *state,
+                             const int32_t *n_accept, int32_t B, int32_t n,
+                             int32_t H_qk, int32_t H_v, int32_t D, gdn_dtype dt,
+                             void *stream);
+
+/*
  * gdn_prefill_varlen - N sequences of different lengths packed along the
  * token axis (several concurrent sequences, as a serving engine batches them:
  * page "Inside Qwen3.8-27B ...", section "Serving Qwen3.8-27B: Recipes for

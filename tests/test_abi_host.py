@@ -174,6 +174,42 @@ def test_prefill_bf16_state_validation(lib, kw, code):
     assert prefill_call(lib, "gdn_prefill_chunked_bf16_state", **kw) == code
 
 
+def multi_call(lib, verify=True, **kw):
+    args = dict(q=addr(0), k=addr(1), v=addr(2), alpha=addr(3), beta=addr(4), state=addr(5),
+                o=addr(6), acc=addr(7), B=64, n=3, Hqk=16, Hv=48, D=128, dt=BF16, stream=None)
+    args.update(kw)
+    if verify:
+        return lib.gdn_decode_verify(args["q"], args["k"], args["v"], args["alpha"], args["beta"],
+                                     args["state"], args["o"], args["B"], args["n"], args["Hqk"],
+                                     args["Hv"], args["D"], args["dt"], args["stream"])
+    return lib.gdn_decode_commit(args["k"], args["v"], args["alpha"], args["beta"], args["state"],
+                                 args["acc"], args["B"], args["n"], args["Hqk"], args["Hv"],
+                                 args["D"], args["dt"], args["stream"])
+
+
+@pytest.mark.parametrize("verify", [True, False], ids=["verify", "commit"])
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=0), ESHAPE),
+    (dict(n=9), EUNSUP),
+    (dict(B=-1), ESHAPE),
+    (dict(D=64), EUNSUP),
+    (dict(state=None), ENULL),
+    (dict(k=addr(1, 8)), EALIGN),
+    (dict(beta=addr(4, 2)), EALIGN),
+])
+def test_verify_commit_validation(lib, verify, kw, code):
+    assert multi_call(lib, verify, **kw) == code
+
+
+def test_verify_commit_aliasing(lib):
+    assert multi_call(lib, True, o=addr(5, 4096)) == EALIAS        # o inside the state
+    assert multi_call(lib, True, o=addr(0, 64)) == EALIAS          # o inside q
+    assert multi_call(lib, False, state=addr(2, 0)) == EALIAS      # state is v
+    assert multi_call(lib, False, acc=None) == ENULL
+    assert multi_call(lib, False, acc=addr(7, 2)) == EALIGN
+    assert multi_call(lib, True, B=0) == OK and multi_call(lib, False, B=0) == OK
+
+
 def test_decode_empty_batch_is_a_no_op(lib):
     assert decode_call(lib, B=0) == OK
 

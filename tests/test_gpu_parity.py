@@ -313,6 +313,62 @@ def test_bf16_state_prefill_then_decode(gdn):
     assert worst <= 2e-2
 
 
+# ------------------------------------------------------------------ speculative decoding
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+def test_verify_commit_small(gdn, dtype):
+    B, n = 6, 3
+    d = synth.prefill_inputs(B, n, dtype, seed=41)
+    st = synth.decode_state(B, seed=41, std=0.05)
+    dd = to_dev(d)
+    sd = st.to(DEV)
+    o = gdn.decode_verify(dd["q"], dd["k"], dd["v"], dd["alpha"], dd["beta"], sd)
+    torch.cuda.synchronize()
+    assert torch.equal(sd.cpu(), st)                  # verify leaves the state alone
+    o_ref = oracle.decode_verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], st)
+    eo = rel(o, o_ref)
+    acc = torch.tensor([0, 1, 2, 3, 7, -2], dtype=torch.int32)   # 7 and -2 are clamped
+    gdn.decode_commit(dd["k"], dd["v"], dd["alpha"], dd["beta"], sd, acc.to(DEV))
+    torch.cuda.synchronize()
+    s_ref = oracle.decode_commit(d["k"], d["v"], d["alpha"], d["beta"], st, acc.numpy())
+    es = rel(sd, s_ref)
+    assert torch.equal(sd[0].cpu(), st[0]) and torch.equal(sd[5].cpu(), st[5])
+    # after committing m tokens, verifying the rest reproduces the first verify
+    m = 1
+    s1 = st.to(DEV)
+    gdn.decode_commit(dd["k"], dd["v"], dd["alpha"], dd["beta"], s1,
+                      torch.full((B,), m, dtype=torch.int32, device=DEV))
+    rest = {x: dd[x][:, m:].contiguous() for x in ("q", "k", "v", "alpha", "beta")}
+    o2 = gdn.decode_verify(rest["q"], rest["k"], rest["v"], rest["alpha"], rest["beta"], s1)
+    torch.cuda.synchronize()
+    ec = rel(o2, o[:, m:].cpu().double().numpy())
+    say("verify/commit %s rel o %.3e state %.3e consistency %.3e" % (dtype, eo, es, ec))
+    tol = TOL[dtype]
+    assert eo <= tol and es <= tol and ec <= tol
+
+
+def test_verify_commit_rounds(gdn):
+    """64 sequences, drafts of 3 tokens (two MTP drafts plus the next token),
+    16 rounds of verify + commit with seeded acceptance counts."""
+    B, n, rounds = 64, 3, 16
+    st = synth.decode_state(B, 1002, 0.02)
+    ref = st.double().numpy().copy()
+    sd = st.to(DEV)
+    gen = torch.Generator().manual_seed(4242)
+    worst = 0.0
+    for rd in range(rounds):
+        d = synth.prefill_inputs(B, n, torch.bfloat16, seed=5000 + rd)
+        dd = to_dev(d)
+        o = gdn.decode_verify(dd["q"], dd["k"], dd["v"], dd["alpha"], dd["beta"], sd)
+        acc = torch.randint(0, n + 1, (B,), generator=gen, dtype=torch.int32)
+        gdn.decode_commit(dd["k"], dd["v"], dd["alpha"], dd["beta"], sd, acc.to(DEV))
+        o_ref = oracle.decode_verify(d["q"], d["k"], d["v"], d["alpha"], d["beta"], ref)
+        ref = oracle.decode_commit(d["k"], d["v"], d["alpha"], d["beta"], ref, acc.numpy())
+        worst = max(worst, rel(o, o_ref))
+    worst = max(worst, rel(sd, ref))
+    say("verify/commit 64 x 16 rounds worst rel %.3e" % worst)
+    assert worst <= 2e-2
+
+
 # ------------------------------------------------------------------ varlen
 @pytest.mark.parametrize("gated", [False, True], ids=["plain", "gated"])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
