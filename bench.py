@@ -316,6 +316,32 @@ def main():
                                "tokens_per_s": 262144 / (r3["step_ms"] * 1e-3),
                                "tflops_algorithmic": prefill_flops(262144) / (r3["step_ms"] * 1e-3) / 1e12}
         del inp3
+        log("extended: packed varlen batch with the gated RMSNorm epilogue")
+        inp4 = {k: (v.to("cuda") if isinstance(v, torch.Tensor) else v)
+                for k, v in synth.config_inputs(4).items()}
+        T4 = int(inp4["cu_seqlens"][-1].item())
+        res = {}
+        for gated in (False, True):
+            vargs = (inp4["q"], inp4["k"], inp4["v"], inp4["alpha"], inp4["beta"],
+                    inp4["cu_seqlens"], inp4["h0"])
+            kw = dict(gate=inp4["gate"]) if gated else {}
+            for _ in range(1):
+                gdn.prefill_varlen(*vargs, **kw)
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(3):
+                gdn.prefill_varlen(*vargs, **kw)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 3
+            res["gated" if gated else "plain"] = {"ms": ms, "tokens_per_s": T4 / (ms * 1e-3)}
+            log("varlen %s: %.3f ms, %.1f M tokens/s" % ("gated" if gated else "plain", ms,
+                                                         T4 / ms / 1e3))
+        out["varlen_8_sequences"] = dict(tokens=T4, lengths=[int(x) for x in inp4["lengths"]],
+                                         **res)
+        del inp4
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) on %d tokens" % args.cpu_tokens)
         out["cpu_baseline"] = cpu_baseline(inp_cpu, args.cpu_tokens)

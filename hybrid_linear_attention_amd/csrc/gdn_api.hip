@@ -161,6 +161,7 @@ gdn_status prefill_fixed(const void* q, const void* k, const void* v, const floa
   a.dec = ws ? reinterpret_cast<float*>(ws + L.dec) : nullptr;
   a.cm = gdn::ChunkMap{nullptr, nullptr, T, (int)Nc, (int)nc};
   a.nseq = B;
+  a.ntok = (int64_t)B * T;
   a.nc_launch = (int)nc;
   a.Hqk = H_qk; a.Hv = H_v;
   a.bf16_io = dt == GDN_BF16;
@@ -378,6 +379,7 @@ gdn_status gdn_prefill_varlen(const void* q, const void* k, const void* v, const
   a.cm = gdn::ChunkMap{tab, seq_off, 0, 0, (int)nc};
   a.state_bf16 = false;
   a.nseq = N;
+  a.ntok = T_tot;
   a.nc_launch = (int)nc;
   a.Hqk = H_qk; a.Hv = H_v;
   a.bf16_io = dt == GDN_BF16;

@@ -27,6 +27,7 @@ struct PrefillLaunch {
   float *gam, *dec;
   ChunkMap cm;
   int nseq, nc_launch, Hqk, Hv;
+  int64_t ntok;            // all tokens of the call (B * T, or T_tot)
   bool bf16_io;
   bool state_bf16;         // h0 / ht stored as bfloat16
 };

@@ -1153,6 +1153,42 @@ __global__ __launch_bounds__(256) void varlen_table_kernel(const int32_t* __rest
   }
 }
 
+// ---------------------------------------------------------------- gated output
+// In place on a bf16 output o [rows = tokens x value heads][128]:
+//   y = o / sqrt(mean_d(o^2) + eps) * w * sigmoid(gate)
+// (RMS normalisation over the head dim, then the sigmoid output gate).  The
+// bf16 scan leaves each head's 128 channels spread over four workgroups, so
+// this runs as its own bandwidth-bound pass: 16 lanes per row, 8 channels
+// (16 bytes) each, 16 rows per workgroup, sums of squares by xor shuffles
+// inside the 16-lane group.
+__global__ __launch_bounds__(256) void gate_norm_kernel(bf16* __restrict__ o,
+                                                        const bf16* __restrict__ gate,
+                                                        const float* __restrict__ w, float eps,
+                                                        int64_t nrows) {
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  if (row >= nrows) return;                        // whole 16-lane groups leave together
+  const int c = (threadIdx.x & 15) * 8;
+  const bf16x8 ov = *reinterpret_cast<const bf16x8*>(o + row * kD + c);
+  const bf16x8 gv = *reinterpret_cast<const bf16x8*>(gate + row * kD + c);
+  float x[8], ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    x[j] = (float)ov[j];
+    ss += x[j] * x[j];
+  }
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) ss += __shfl_xor(ss, off, 16);
+  const float rs = 1.f / sqrtf(ss * (1.f / kD) + eps);
+  bf16x8 yv;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float wj = w ? w[c + j] : 1.f;
+    const float sg = 1.f / (1.f + __expf(-(float)gv[j]));
+    yv[j] = (bf16)(x[j] * rs * wj * sg);
+  }
+  *reinterpret_cast<bf16x8*>(o + row * kD + c) = yv;
+}
+
 // ---------------------------------------------------------------- launchers
 template <typename E>
 static hipError_t launch_prepare_t(const PrefillLaunch& a, hipStream_t st) {
@@ -1195,9 +1231,14 @@ static hipError_t launch_scan_split(const PrefillLaunch& a, hipStream_t st) {
 }
 
 hipError_t launch_scan(const PrefillLaunch& a, hipStream_t st) {
-  if (a.gate)
-    return a.bf16_io ? launch_scan_t<bf16, 8, true>(a, st) : launch_scan_t<float, 8, true>(a, st);
-  return a.bf16_io ? launch_scan_split(a, st) : launch_scan_t<float, 4, false>(a, st);
+  if (!a.bf16_io)
+    return a.gate ? launch_scan_t<float, 8, true>(a, st) : launch_scan_t<float, 4, false>(a, st);
+  hipError_t e = launch_scan_split(a, st);
+  if (e != hipSuccess || !a.gate || a.ntok == 0) return e;
+  const int64_t nrows = a.ntok * a.Hv;
+  hipLaunchKernelGGL(gate_norm_kernel, dim3((unsigned)((nrows + 15) / 16)), dim3(256), 0, st,
+                     (bf16*)a.o, (const bf16*)a.gate, a.norm_w, a.norm_eps, nrows);
+  return hipGetLastError();
 }
 
 hipError_t launch_varlen_table(const int32_t* cu, int N, int T_tot, int nc_max, int32_t* tab,
