@@ -41,12 +41,12 @@ size_t esize(gdn_dtype dt) { return dt == GDN_BF16 ? 2 : 4; }
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Workspace layout: Tt [nc][Hv][64][64], M [nc][Hv][64][64] and
-// K^T [nc][Hqk][128][64] (element type), gam and dec [nc][Hv][64] fp32, then
+// Workspace layout: Tt [nc][Hv][64][64] and M [nc][Hv][64][64] (element
+// type), gam and dec [nc][Hv][64] fp32, then
 // for varlen the chunk table [nc][2] and the per-sequence chunk offsets [N+1]
 // (int32).
 struct WsLayout {
-  size_t tt, m, kt, gam, dec, tab, seq, total;
+  size_t tt, m, gam, dec, tab, seq, total;
 };
 
 WsLayout ws_layout(int64_t nc, int64_t Hqk, int64_t Hv, gdn_dtype dt, int64_t nseq_varlen) {
@@ -57,8 +57,6 @@ WsLayout ws_layout(int64_t nc, int64_t Hqk, int64_t Hv, gdn_dtype dt, int64_t ns
   off += round256((size_t)nc * Hv * gdn::kC * gdn::kC * es);
   w.m = off;
   off += round256((size_t)nc * Hv * gdn::kC * gdn::kC * es);
-  w.kt = off;
-  off += round256((size_t)nc * Hqk * gdn::kD * gdn::kC * es);
   w.gam = off;
   off += round256((size_t)nc * Hv * gdn::kC * sizeof(float));
   w.dec = off;
@@ -156,7 +154,6 @@ gdn_status prefill_fixed(const void* q, const void* k, const void* v, const floa
   char* ws = static_cast<char*>(workspace);
   a.Tt = ws ? ws + L.tt : nullptr;
   a.M = ws ? ws + L.m : nullptr;
-  a.KT = ws ? ws + L.kt : nullptr;
   a.gam = ws ? reinterpret_cast<float*>(ws + L.gam) : nullptr;
   a.dec = ws ? reinterpret_cast<float*>(ws + L.dec) : nullptr;
   a.cm = gdn::ChunkMap{nullptr, nullptr, T, (int)Nc, (int)nc};
@@ -373,7 +370,6 @@ gdn_status gdn_prefill_varlen(const void* q, const void* k, const void* v, const
   a.gate = gate; a.norm_w = norm_weight; a.norm_eps = norm_eps;
   a.Tt = ws + L.tt;
   a.M = ws + L.m;
-  a.KT = ws + L.kt;
   a.gam = reinterpret_cast<float*>(ws + L.gam);
   a.dec = reinterpret_cast<float*>(ws + L.dec);
   a.cm = gdn::ChunkMap{tab, seq_off, 0, 0, (int)nc};

@@ -23,7 +23,7 @@ struct PrefillLaunch {
   const void* gate;        // null: plain output; else fused RMSNorm * sigmoid(gate)
   const float* norm_w;
   float norm_eps;
-  void *Tt, *M, *KT;       // workspace regions
+  void *Tt, *M;            // workspace regions
   float *gam, *dec;
   ChunkMap cm;
   int nseq, nc_launch, Hqk, Hv;

@@ -50,7 +50,6 @@ template <typename E>
 struct Work {
   E* Tt;       // [nc][Hv][64][64]   (I + A)^-1 diag(beta)
   E* M;        // [nc][Hv][64][64]   (Q K^T * exp(G_i - G_j)) on and below the diagonal
-  E* KT;       // [nc][Hqk][128][64] K^T of the chunk (bf16 path only)
   float* gam;  // [nc][Hv][64]       exp(G_t)
   float* dec;  // [nc][Hv][64]       exp(G_last - G_t)
 };
@@ -204,21 +203,6 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 3 : 2) void prepare_kernel(
       }
     }
   }
-  if constexpr (BF) {
-    // K^T of the chunk for the scan's state update, [128 d_k][64 tokens]:
-    // each thread writes 16-byte pieces (8 tokens of one d_k column).
-    const bf16* Ks = reinterpret_cast<const bf16*>(sm.u.in.Ks);
-    bf16* kt = reinterpret_cast<bf16*>(ws.KT) + ((size_t)cid * Hqk + gq) * kD * kC;
-#pragma unroll
-    for (int it = 0; it < kD * kC / 8 / 256; ++it) {
-      const int p = tid + 256 * it, dk = p >> 3, tb = p & 7;
-      bf16x8 col;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) col[e] = Ks[(8 * tb + e) * LDK + dk];
-      *reinterpret_cast<bf16x8*>(kt + dk * kC + 8 * tb) = col;
-    }
-  }
-
   for (int hb = 0; hb < G; hb += NB) {
     const int nb = min(NB, G - hb);
     // Gates: G2_t = sum_{j<=t} log2(alpha_j) over the chunk, one wave per head.
@@ -684,17 +668,18 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
 //  * one output wave for both slices, one chunk behind: O = diag(gam) Q S^T +
 //    M Dl.  Each Q and M fragment read from LDS serves both slices: 44 MFMAs
 //    per chunk.
-//  * two producer waves: copy K^T, Tt, V, gam, dec of chunk c+2 and Q, M of
+//  * two producer waves: copy K, Tt, V, gam, dec of chunk c+2 and Q, M of
 //    chunk c from global memory straight into LDS rings
 //    (global_load_lds_dwordx4: no registers, no VALU) while chunk c is
-//    computed.
+//    computed.  K comes straight from the input tensor.
 //
-// K is kept in LDS only as K^T.  The A fragments of P = K S^T (rows = tokens,
-// K slots = d_k) are read from K^T with ds_read_b64_tr_b16, which transposes
-// 16-bit elements across each group of 16 lanes: input lane p reads four
-// tokens of K^T row dk(p/4) starting at token base + 8 (p%4), and output lane m
-// receives element m%4 of input lanes m/4, m/4+4, m/4+8, m/4+12, i.e.
-// K[token(m)][dk(0..3)].  This halves the bytes each CU moves per chunk.
+// K is staged once per chunk, as it is stored ([64 tokens][128 d_k]).  The A
+// fragments of P = K S^T (rows = tokens, K slots = d_k) are 16-byte reads of
+// it; those of the state update K^T Dl (rows = d_k, K slots = tokens) come
+// from the same tile through ds_read_b64_tr_b16, which transposes 16-bit
+// elements across each group of 16 lanes: input lane p reads four d_k of
+// token base + p/4, and output lane m receives element m%4 of input lanes
+// m/4, m/4+4, m/4+8, m/4+12, i.e. four tokens of d_k row(m).
 //
 // Token and d_k order.  An accumulator tile pair holds, per lane group g, rows
 // {4g..4g+3} and {16+4g..16+4g+3} of a 32-row block; used as a B fragment these
@@ -704,8 +689,9 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
 // every A fragment is one 16-byte LDS read (or two transposed 8-byte reads).
 // The permutation is applied to tokens (rows of P, X, Dl) and to d_k (rows of
 // S^T); it is undone where the state is loaded and stored.  LDS rows are
-// XOR-swizzled in 16-byte pieces (swz) so the 16 gathered rows of an A
-// fragment hit distinct banks.
+// XOR-swizzled in 16-byte pieces (swz for 128-byte rows, ksw for the K tile's
+// 256-byte rows) so that every 16-lane pass of an A fragment read hits
+// distinct banks.
 namespace split {
 constexpr int kSlices = 2;                   // 16-row value slices per workgroup
 constexpr int kRows = 16 * kSlices;          // value rows per workgroup
@@ -714,7 +700,7 @@ constexpr int kWaves = kSlices + 3;          // chain x2, output, producer x2
 constexpr int kSlots = 3;                    // chain operands: chunks c, c+1, c+2
 constexpr int kQmSlots = 2;                  // output operands: chunks c-1, c
 constexpr int kGdSlots = 4;                  // gam/dec: chunks c-1 .. c+2
-constexpr int kKTB = kD * kC * 2;            // K^T tile, bytes
+constexpr int kKTB = kD * kC * 2;            // K tile, bytes
 constexpr int kTB = kC * kC * 2;             // Tt tile
 constexpr int kVB = kC * kRows * 2;          // V tile of the workgroup's value rows
 constexpr int kQB = kC * kD * 2;             // Q tile
@@ -722,11 +708,11 @@ constexpr int kMB = kC * kC * 2;             // M tile
 // Copy ops of each producer per chunk; each keeps at most 63 in flight.
 constexpr int kOpsA = kTB / 1024 + kVB / 1024 + 2;      // Tt, V, gam, dec   (chunk c+2)
 constexpr int kOpsQM = kQB / 1024 + kMB / 1024;         // Q, M             (chunk c)
-constexpr int kOpsKT = kKTB / 1024;                     // K^T              (chunk c+2)
+constexpr int kOpsKT = kKTB / 1024;                     // K                (chunk c+2)
 static_assert(2 * kOpsA + kOpsQM <= 63 && 2 * kOpsKT <= 63, "vmcnt range");
 
 struct Slot {
-  alignas(16) uint8_t KT[kKTB];              // [128 d_k][64 tokens], 128-byte rows
+  alignas(16) uint8_t K[kKTB];               // [64 tokens][128 d_k], 256-byte rows
   alignas(16) uint8_t T[kTB];                // [64][64], 128-byte rows
   alignas(16) uint8_t V[kVB];                // [64 tokens][32 value rows], 64-byte rows
 };
@@ -754,6 +740,9 @@ __device__ __forceinline__ int prow(int t, int r) {
   return 32 * (t >> 1) + 8 * (r >> 2) + 4 * (t & 1) + (r & 3);
 }
 __device__ __forceinline__ int swz(int row) { return (row & 3) | ((row >> 1) & 4); }
+// K tile rows are 16 pieces: rows prow(mt, 0..15) (plain reads) and the four
+// tokens base + 0..3 of a transposed read both land on 16 distinct pieces.
+__device__ __forceinline__ int ksw(int row) { return ((row & 3) << 2) | ((row >> 3) & 3); }
 // V tile rows are 4 pieces of 16 bytes; a chain wave reads 8 consecutive tokens
 // 8 apart per lane group, so the piece order is rotated by (token / 8) % 4.
 __device__ __forceinline__ int vswz(int tok) { return (tok >> 3) & 3; }
@@ -786,7 +775,6 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
     ChunkMap cm, int Hqk, int Hv, int G) {
   using namespace split;
   __shared__ Smem sm;
-  (void)k;
 
   const int nlin = Hv * kNsl;
   int lin = blockIdx.x;
@@ -859,15 +847,19 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
         dma16(mb + row * kC + 8 * p, Qs.M + 1024 * it);
       }
     };
-    // K^T of chunk c into slot c % 3.
+    // K of chunk c into slot c % 3, from the input: 4 tokens per copy, rows
+    // beyond L repeat the last token (they meet zero Tt columns and zero
+    // decay-scaled Dl rows).
     auto issue_kt = [&](int c) {
       const int cid = cid0 + c;
+      int tok0, L;
+      chunk_of(cm, cid, tok0, L);
       Slot& S = sm.slot[c % kSlots];
-      const bf16* ktb = ws.KT + ((size_t)cid * Hqk + gq) * kD * kC;
+      const bf16* kbase = k + (size_t)tok0 * qk_stride + (size_t)gq * kD;
 #pragma unroll
       for (int it = 0; it < kKTB / 1024; ++it) {
-        const int row = 8 * it + (l >> 3), p = (l & 7) ^ swz(row);
-        dma16(ktb + row * kC + 8 * p, S.KT + 1024 * it);
+        const int row = 4 * it + (l >> 4), p = (l & 15) ^ ksw(row);
+        dma16(kbase + (size_t)min(row, L - 1) * qk_stride + 8 * p, S.K + 1024 * it);
       }
     };
     // Chunk c's chain operands must be in LDS by the barrier that ends
@@ -931,21 +923,15 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
         const Slot& S = sm.slot[i % kSlots];
         const GateSlot& Gd = sm.gd[i % kGdSlots];
         Hand& H = sm.hand[i & 1][s];
-        // A fragments of P = K S^T from K^T by transposed reads: this lane, as
-        // input lane r of group g, reads 4 tokens of K^T row
-        // 32kk + 8g + r/4 (+4) starting at token 32(mt/2) + 8(r%4) + 4(mt%2).
+        // A fragments of P = K S^T: row prow(mt, r) of the K tile, d_k
+        // 32kk + 8g .. +7.
         bf16x8 AK[4][4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-          const int t0 = 32 * (mt >> 1) + 8 * (r & 3) + 4 * (mt & 1);
+          const int row = prow(mt, r);
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            const int d0 = 32 * kk + 8 * g + (r >> 2), d1 = d0 + 4;
-            const s16x4 lo = lds_tr16(S.KT + d0 * 128 + 16 * ((t0 >> 3) ^ swz(d0)) + 2 * (t0 & 7));
-            const s16x4 hi = lds_tr16(S.KT + d1 * 128 + 16 * ((t0 >> 3) ^ swz(d1)) + 2 * (t0 & 7));
-            const s16x4 lh[2] = {lo, hi};
-            AK[mt][kk] = *reinterpret_cast<const bf16x8*>(lh);
-          }
+          for (int kk = 0; kk < 4; ++kk)
+            AK[mt][kk] = *reinterpret_cast<const bf16x8*>(S.K + row * 256 + 16 * ((4 * kk + g) ^ ksw(row)));
         }
         bf16x8 SB[4];
 #pragma unroll
@@ -970,13 +956,22 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
           for (int kk = 0; kk < 2; ++kk)
             AT[mt][kk] = *reinterpret_cast<const bf16x8*>(S.T + row * 128 + 16 * ((4 * kk + g) ^ swz(row)));
         }
+        // A fragments of the update K^T Dl (rows d_k prow(t, .), K slots
+        // tokens 32kk + 8g .. +7) by transposed reads: as input lane r of
+        // group g this lane reads d_k 32(t/2) + 8(r%4) + 4(t%2) .. +3 of
+        // token 32kk + 8g + r/4 (and of the token 4 later).
         bf16x8 AKT[8][2];
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-          const int row = prow(t, r);
+          const int dk = 32 * (t >> 1) + 8 * (r & 3) + 4 * (t & 1);
 #pragma unroll
-          for (int kk = 0; kk < 2; ++kk)
-            AKT[t][kk] = *reinterpret_cast<const bf16x8*>(S.KT + row * 128 + 16 * ((4 * kk + g) ^ swz(row)));
+          for (int kk = 0; kk < 2; ++kk) {
+            const int t0 = 32 * kk + 8 * g + (r >> 2), t1 = t0 + 4;
+            const s16x4 lo = lds_tr16(S.K + t0 * 256 + 16 * ((dk >> 3) ^ ksw(t0)) + 2 * (dk & 7));
+            const s16x4 hi = lds_tr16(S.K + t1 * 256 + 16 * ((dk >> 3) ^ ksw(t1)) + 2 * (dk & 7));
+            const s16x4 lh[2] = {lo, hi};
+            AKT[t][kk] = *reinterpret_cast<const bf16x8*>(lh);
+          }
         }
         // V of this lane's value row at its tokens 32(mt/2) + 8g + 4(mt%2) + i,
         // by transposed reads: as input lane r of group g this lane reads 4
@@ -1193,7 +1188,7 @@ __global__ __launch_bounds__(256) void gate_norm_kernel(bf16* __restrict__ o,
 template <typename E>
 static hipError_t launch_prepare_t(const PrefillLaunch& a, hipStream_t st) {
   if (a.nc_launch <= 0) return hipSuccess;
-  Work<E> ws{(E*)a.Tt, (E*)a.M, (E*)a.KT, a.gam, a.dec};
+  Work<E> ws{(E*)a.Tt, (E*)a.M, a.gam, a.dec};
   dim3 grid((unsigned)a.nc_launch, (unsigned)a.Hqk), block(256);
   hipLaunchKernelGGL(prepare_kernel<E>, grid, block, 0, st, (const E*)a.q, (const E*)a.k,
                      a.alpha, a.beta, ws, a.cm, a.Hqk, a.Hv, a.Hv / a.Hqk);
@@ -1203,7 +1198,7 @@ static hipError_t launch_prepare_t(const PrefillLaunch& a, hipStream_t st) {
 template <typename E, int NW, bool GATED>
 static hipError_t launch_scan_t(const PrefillLaunch& a, hipStream_t st) {
   if (a.nseq <= 0) return hipSuccess;
-  Work<E> ws{(E*)a.Tt, (E*)a.M, (E*)a.KT, a.gam, a.dec};
+  Work<E> ws{(E*)a.Tt, (E*)a.M, a.gam, a.dec};
   constexpr int NSL = kD / (16 * NW);
   int nlin = a.Hv * NSL;
   if ((a.Hqk & 7) == 0) nlin = ((nlin + 7) / 8) * 8;
@@ -1220,7 +1215,7 @@ hipError_t launch_prepare(const PrefillLaunch& a, hipStream_t st) {
 
 static hipError_t launch_scan_split(const PrefillLaunch& a, hipStream_t st) {
   if (a.nseq <= 0) return hipSuccess;
-  Work<bf16> ws{(bf16*)a.Tt, (bf16*)a.M, (bf16*)a.KT, a.gam, a.dec};
+  Work<bf16> ws{(bf16*)a.Tt, (bf16*)a.M, a.gam, a.dec};
   int nlin = a.Hv * split::kNsl;
   if ((a.Hqk & 7) == 0) nlin = ((nlin + 7) / 8) * 8;
   dim3 grid((unsigned)nlin, (unsigned)a.nseq), block(64 * split::kWaves);

@@ -57,9 +57,9 @@ def test_status_strings(gdn):
 
 
 def test_workspace_sizes(gdn):
-    # per chunk: Tt and M (48 x 64 x 64 elements each), K^T (16 x 128 x 64),
-    # gam and dec (48 x 64 fp32 each)
-    per_chunk_bf16 = 2 * 48 * 4096 * 2 + 16 * 128 * 64 * 2 + 2 * 48 * 64 * 4
+    # per chunk: Tt and M (48 x 64 x 64 elements each), gam and dec (48 x 64
+    # fp32 each)
+    per_chunk_bf16 = 2 * 48 * 4096 * 2 + 2 * 48 * 64 * 4
     assert gdn.prefill_workspace_bytes(1, 0, 16, 48) == 0
     w1 = gdn.prefill_workspace_bytes(1, 64, 16, 48)
     w2 = gdn.prefill_workspace_bytes(1, 128, 16, 48)
