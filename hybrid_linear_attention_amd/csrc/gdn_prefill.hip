@@ -48,7 +48,9 @@ namespace gdn {
 
 template <typename E>
 struct Work {
-  E* Tt;       // [nc][Hv][64][64]   (I + A)^-1 diag(beta)
+  E* Tt;       // [nc][Hv][64][64]   (I + A)^-1 diag(beta).  bf16: the zero block
+               //                    rows 0..31 x columns 32..63 (also of M) is not
+               //                    written; the scan copies it but never reads it
   E* M;        // [nc][Hv][64][64]   (Q K^T * exp(G_i - G_j)) on and below the diagonal
   float* gam;  // [nc][Hv][64]       exp(G_t)
   float* dec;  // [nc][Hv][64]       exp(G_last - G_t)
@@ -254,7 +256,8 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 3 : 2) void prepare_kernel(
           bf16x4 mv;
 #pragma unroll
           for (int e = 0; e < 4; ++e) mv[e] = (bf16)m4[e];
-          *reinterpret_cast<bf16x4*>(mo + i * kC + 16 * w + 4 * g) = mv;
+          // The bf16 scan never reads the zero block rows 0..31 x columns 32..63.
+          if (i >= 32 || w < 2) *reinterpret_cast<bf16x4*>(mo + i * kC + 16 * w + 4 * g) = mv;
         } else {
           *reinterpret_cast<f32x4*>(mo + i * kC + 16 * w + 4 * g) = f32x4{m4[0], m4[1], m4[2], m4[3]};
         }
@@ -329,7 +332,7 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 3 : 2) void prepare_kernel(
             bf16x8 tv;
 #pragma unroll
             for (int e = 0; e < 8; ++e) tv[e] = (bf16)(t8[e] * bj[e]);
-            *reinterpret_cast<bf16x8*>(tt + i * kC + 8 * cb) = tv;
+            if (i >= 32 || cb < 4) *reinterpret_cast<bf16x8*>(tt + i * kC + 8 * cb) = tv;
           } else {
             *reinterpret_cast<f32x4*>(tt + i * kC + 8 * cb) =
                 f32x4{t8[0] * bj[0], t8[1] * bj[1], t8[2] * bj[2], t8[3] * bj[3]};
@@ -995,14 +998,16 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
           for (int i2 = 0; i2 < 4; ++i2) X[mt][i2] = (float)v4[i2] - gm[i2] * P[mt][i2];
         }
         const bf16x8 XB[2] = {pack_b(X[0], X[1]), pack_b(X[2], X[3])};
-        // Dl = Tt X
+        // Dl = Tt X.  Tt is lower triangular: tiles mt < 2 (rows 0..31) have
+        // nothing in columns 32..63.
         f32x4 Dl[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) Dl[mt] = zero4();
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt) Dl[mt] = mfma_bf16(AT[mt][kk], XB[kk], Dl[mt]);
+          for (int mt = 0; mt < 4; ++mt)
+            if (kk == 0 || mt >= 2) Dl[mt] = mfma_bf16(AT[mt][kk], XB[kk], Dl[mt]);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) H.db[kk][l] = pack_b(Dl[2 * kk], Dl[2 * kk + 1]);
         // state update: S^T <- gam_last S^T + K^T diag(dec) Dl
