@@ -33,6 +33,8 @@ Functions
 ---------
 prefill(q, k, v, alpha, beta, h0=None)       -> (o, ht)     C, OpenMP over (b, h)
 decode_step(q, k, v, alpha, beta, state)     -> (o, state') C
+prefill_backward(q, k, v, alpha, beta, do, h0, dht)
+                                             -> (dq, dk, dv, dalpha, dbeta, dh0)  C
 decode_step_bf16_state(...), prefill_bf16_state(...)   states stored in bf16
 round_bf16(x)                                -> x rounded to bfloat16 (RNE)
 decode_verify(q, k, v, alpha, beta, state)   -> o of n draft tokens, state unchanged
@@ -88,6 +90,8 @@ def _load():
             lib.oracle_gdn_decode_step.argtypes = [dp, dp, dp, dp, dp, dp, dp,
                                                    i64, i64, i64, i64]
             lib.oracle_gdn_decode_step.restype = ctypes.c_int
+            lib.oracle_gdn_backward.argtypes = [dp] * 14 + [i64] * 5
+            lib.oracle_gdn_backward.restype = ctypes.c_int
             _lib = lib
     return _lib
 
@@ -129,6 +133,42 @@ def prefill(q, k, v, alpha, beta, h0=None):
     if rc != 0:
         raise ValueError("oracle_gdn_prefill failed (%d)" % rc)
     return o, ht
+
+
+def prefill_backward(q, k, v, alpha, beta, do, h0=None, dht=None):
+    """Gradients of ``L = sum <do, o> + <dht, ht>`` with respect to every
+    input of :func:`prefill` (the training pass of the same recurrence, page
+    "Inside Qwen3.8-27B ...", note under "The Role of Periodic Gated
+    Attention").  The chain rule is applied token by token in reverse, in
+    float64; the derivation is written out in ``gdn_oracle.c``.
+
+    do ``[B,T,Hv,D]``; dht ``[B,Hv,D,D]`` or None (zero).  Returns float64
+    ``dq, dk [B,T,Hqk,D]`` (summed over the value heads of each group),
+    ``dv [B,T,Hv,D]``, ``dalpha, dbeta [B,T,Hv]`` and ``dh0 [B,Hv,D,D]``.
+    """
+    q, k, v, alpha, beta, do = (_f64(x) for x in (q, k, v, alpha, beta, do))
+    B, T, Hqk, D = q.shape
+    Hv = v.shape[2]
+    assert k.shape == q.shape and v.shape == (B, T, Hv, D) and do.shape == v.shape
+    assert alpha.shape == (B, T, Hv) and beta.shape == (B, T, Hv)
+    h0a = None if h0 is None else _f64(h0)
+    dhta = None if dht is None else _f64(dht)
+    for s in (h0a, dhta):
+        if s is not None:
+            assert s.shape == (B, Hv, D, D)
+    dq = np.zeros((B, T, Hqk, D))
+    dk = np.zeros((B, T, Hqk, D))
+    dv = np.zeros((B, T, Hv, D))
+    da = np.zeros((B, T, Hv))
+    db = np.zeros((B, T, Hv))
+    dh0 = np.zeros((B, Hv, D, D))
+    rc = _load().oracle_gdn_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(h0a), _ptr(do),
+        _ptr(dhta), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(da), _ptr(db), _ptr(dh0),
+        B, T, Hqk, Hv, D)
+    if rc != 0:
+        raise ValueError("oracle_gdn_backward failed (%d)" % rc)
+    return dq, dk, dv, da, db, dh0
 
 
 def decode_step(q, k, v, alpha, beta, state, inplace=False):

@@ -119,3 +119,139 @@ int oracle_gdn_decode_step(const double *q, const double *k, const double *v,
     return oracle_gdn_prefill(q, k, v, alpha, beta, state, o, state, B, 1, Hqk,
                               Hv, D);
 }
+
+/*
+ * Gradients of the prefill (page "Inside Qwen3.8-27B ...", note under "The
+ * Role of Periodic Gated Attention": training runs the same recurrence as
+ * prefill, so its backward pass is the derivative of that recurrence).
+ *
+ * The scalar loss whose gradients are returned is
+ *     L = sum_t <dout_t, o_t> + <dht, S_T>
+ * i.e. dout is dL/do and dht is dL/dS_T (NULL = zero).  Written per step with
+ * u_t = S_{t-1} k_t and d_t = beta_t (v_t - alpha_t u_t), so that
+ * S_t = alpha_t S_{t-1} + d_t k_t^T, the chain rule gives, walking t from T
+ * down to 1 with G = dL/dS_t (which first takes in dout_t q_t^T):
+ *     dq_t     = S_t^T dout_t
+ *     e        = G k_t                               (dL/dd_t)
+ *     dv_t     = beta_t e
+ *     dbeta_t  = e . (v_t - alpha_t u_t)
+ *     dalpha_t = <G, S_{t-1}> - beta_t (e . u_t)
+ *     f        = -alpha_t beta_t e                   (dL/du_t)
+ *     dk_t     = G^T d_t + S_{t-1}^T f
+ *     dL/dS_{t-1} = alpha_t G + f k_t^T
+ * and dh0 = dL/dS_0.  dq and dk of a query/key head are the sums over the
+ * value heads that share it, added in increasing value-head order.
+ *
+ * Layouts as for oracle_gdn_prefill; dout, dv [B,T,Hv,D]; dq, dk [B,T,Hqk,D];
+ * dalpha, dbeta [B,T,Hv]; dht, dh0 [B,Hv,D,D] (dht, h0 and dh0 may be NULL).
+ * The forward states S_0..S_T of one value head are kept in memory
+ * ((T+1) D^2 doubles per worker).  Returns 0, -1 (sizes) or -2 (memory).
+ */
+int oracle_gdn_backward(const double *q, const double *k, const double *v,
+                        const double *alpha, const double *beta,
+                        const double *h0, const double *dout, const double *dht,
+                        double *dq, double *dk, double *dv, double *dalpha,
+                        double *dbeta, double *dh0,
+                        int64_t B, int64_t T, int64_t Hqk, int64_t Hv, int64_t D)
+{
+    if (B < 0 || T < 0 || Hqk <= 0 || Hv <= 0 || D <= 0 || Hv % Hqk != 0)
+        return -1;
+    const int64_t G = Hv / Hqk, DD = D * D;
+    const int64_t qs = Hqk * D, vs = Hv * D;
+    int bad = 0;
+    memset(dq, 0, (size_t)(B * T * Hqk * D) * sizeof(double));
+    memset(dk, 0, (size_t)(B * T * Hqk * D) * sizeof(double));
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bg = 0; bg < B * Hqk; ++bg) {
+        const int64_t b = bg / Hqk, g = bg % Hqk;
+        double *S = (double *)malloc((size_t)((T + 1) * DD) * sizeof(double));
+        double *Gm = (double *)malloc((size_t)DD * sizeof(double));
+        double *u = (double *)malloc((size_t)(4 * D) * sizeof(double));
+        if (!S || !Gm || !u) {
+#pragma omp atomic write
+            bad = 1;
+            free(S); free(Gm); free(u);
+            continue;
+        }
+        double *d = u + D, *e = u + 2 * D, *f = u + 3 * D;
+        const double *qg = q + b * T * qs + g * D, *kg = k + b * T * qs + g * D;
+        double *dqg = dq + b * T * qs + g * D, *dkg = dk + b * T * qs + g * D;
+        for (int64_t h = g * G; h < (g + 1) * G; ++h) {
+            const double *vh = v + b * T * vs + h * D;
+            const double *dh = dout + b * T * vs + h * D;
+            const double *ah = alpha + b * T * Hv + h, *bh = beta + b * T * Hv + h;
+            double *dvh = dv + b * T * vs + h * D;
+            /* forward, keeping every state: S + t*DD is S_t */
+            if (h0)
+                memcpy(S, h0 + (b * Hv + h) * DD, (size_t)DD * sizeof(double));
+            else
+                memset(S, 0, (size_t)DD * sizeof(double));
+            for (int64_t t = 0; t < T; ++t) {
+                const double *P = S + t * DD;
+                double *N = S + (t + 1) * DD;
+                const double *kt = kg + t * qs, *vt = vh + t * vs;
+                const double a = ah[t * Hv], be = bh[t * Hv];
+                for (int64_t i = 0; i < D; ++i) {
+                    double ui = 0.0;
+                    for (int64_t j = 0; j < D; ++j)
+                        ui += P[i * D + j] * kt[j];
+                    const double di = be * (vt[i] - a * ui);
+                    for (int64_t j = 0; j < D; ++j)
+                        N[i * D + j] = a * P[i * D + j] + di * kt[j];
+                }
+            }
+            /* backward */
+            if (dht)
+                memcpy(Gm, dht + (b * Hv + h) * DD, (size_t)DD * sizeof(double));
+            else
+                memset(Gm, 0, (size_t)DD * sizeof(double));
+            for (int64_t t = T - 1; t >= 0; --t) {
+                const double *P = S + t * DD, *N = S + (t + 1) * DD;
+                const double *qt = qg + t * qs, *kt = kg + t * qs;
+                const double *vt = vh + t * vs, *dot = dh + t * vs;
+                const double a = ah[t * Hv], be = bh[t * Hv];
+                double *dqt = dqg + t * qs, *dkt = dkg + t * qs;
+                for (int64_t i = 0; i < D; ++i)
+                    for (int64_t j = 0; j < D; ++j)
+                        Gm[i * D + j] += dot[i] * qt[j];
+                for (int64_t j = 0; j < D; ++j) {
+                    double s = 0.0;
+                    for (int64_t i = 0; i < D; ++i)
+                        s += N[i * D + j] * dot[i];
+                    dqt[j] += s;
+                }
+                double db = 0.0, eu = 0.0, gp = 0.0;
+                for (int64_t i = 0; i < D; ++i) {
+                    double ui = 0.0, ei = 0.0;
+                    for (int64_t j = 0; j < D; ++j) {
+                        ui += P[i * D + j] * kt[j];
+                        ei += Gm[i * D + j] * kt[j];
+                        gp += Gm[i * D + j] * P[i * D + j];
+                    }
+                    u[i] = ui;
+                    e[i] = ei;
+                    d[i] = be * (vt[i] - a * ui);
+                    f[i] = -a * be * ei;
+                    dvh[t * vs + i] = be * ei;
+                    db += ei * (vt[i] - a * ui);
+                    eu += ei * ui;
+                }
+                dbeta[(b * T + t) * Hv + h] = db;
+                dalpha[(b * T + t) * Hv + h] = gp - be * eu;
+                for (int64_t j = 0; j < D; ++j) {
+                    double s = 0.0;
+                    for (int64_t i = 0; i < D; ++i)
+                        s += Gm[i * D + j] * d[i] + P[i * D + j] * f[i];
+                    dkt[j] += s;
+                }
+                for (int64_t i = 0; i < D; ++i)
+                    for (int64_t j = 0; j < D; ++j)
+                        Gm[i * D + j] = a * Gm[i * D + j] + f[i] * kt[j];
+            }
+            if (dh0)
+                memcpy(dh0 + (b * Hv + h) * DD, Gm, (size_t)DD * sizeof(double));
+        }
+        free(S); free(Gm); free(u);
+    }
+    return bad ? -2 : 0;
+}

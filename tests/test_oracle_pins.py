@@ -23,6 +23,11 @@ head map                     value head h reads query/key head h // (Hv/Hqk)
 contraction bound            ||S_t|| <= alpha_t ||S_{t-1}|| + beta_t ||v_t||
                              for unit keys and beta in [0, 1]
 empty sequence               T = 0 passes the state through
+backward: finite differences every gradient of the backward oracle equals the
+                             central difference of the forward oracle
+backward: autograd           reverse-mode AD (torch, float64) of a plain loop
+backward: identity           beta=0, alpha=1 closed forms of all six gradients
+backward: chunked            the chunked backward derivation agrees (1e-12)
 ===========================  ==================================================
 
 ``test_mutants_are_caught`` runs every pin against deliberately broken copies
@@ -519,3 +524,109 @@ def test_synth_inputs_deterministic_and_normalised():
     x = -np.log(a["alpha"].double().numpy()) / 0.05       # softplus of N(0,1)
     z = np.log(np.expm1(x))                                 # back to N(0,1)
     assert scipy.stats.kstest(z.ravel(), "norm").pvalue > 1e-4
+
+
+# ------------------------------------------------------------- backward pins
+# The oracle's backward (oracle.prefill_backward) is the chain rule applied by
+# hand to the sequential recurrence.  It is pinned by (1) central finite
+# differences of the forward oracle on every input element, (2) reverse-mode
+# automatic differentiation (torch, float64) of a plain forward loop, (3) the
+# closed form of the identity case beta=0, alpha=1, and (4) the chunked
+# backward derivation reaching the same gradients.
+
+def _bwd_inputs(seed, B, T, Hqk, Hv, D):
+    r = rng(seed)
+    q, k, v, alpha, beta, s0 = rand_inputs(r, B, T, Hqk, Hv, D)
+    do = r.standard_normal((B, T, Hv, D))
+    dht = r.standard_normal((B, Hv, D, D))
+    return q, k, v, alpha, beta, s0, do, dht
+
+
+def test_backward_finite_differences(oracle_mod):
+    q, k, v, a, b, s0, do, dht = _bwd_inputs(41, 2, 5, 2, 6, 4)
+    grads = oracle.prefill_backward(q, k, v, a, b, do, s0, dht)
+    ins = [q, k, v, a, b, s0]
+
+    def loss(args):
+        o, ht = oracle.prefill(*args)
+        return float(np.sum(o * do) + np.sum(ht * dht))
+
+    eps = 1e-6
+    for n, (x, gx) in enumerate(zip(ins, [grads[0], grads[1], grads[2],
+                                          grads[3], grads[4], grads[5]])):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp = [y.copy() for y in ins]
+            xm = [y.copy() for y in ins]
+            xp[n][idx] += eps
+            xm[n][idx] -= eps
+            fd[idx] = (loss(xp) - loss(xm)) / (2 * eps)
+        err = np.abs(fd - gx).max() / np.abs(fd).max()
+        assert err < 1e-7, (n, err)
+
+
+def test_backward_matches_autograd(oracle_mod):
+    torch = pytest.importorskip("torch")
+    q, k, v, a, b, s0, do, dht = _bwd_inputs(42, 1, 70, 2, 6, 8)
+    t = [torch.tensor(x, dtype=torch.float64, requires_grad=True)
+         for x in (q, k, v, a, b, s0)]
+    tq, tk, tv, ta, tb, ts = t
+    B, T, Hqk, D = q.shape
+    Hv = v.shape[2]
+    loss = 0.0
+    for h in range(Hv):
+        g = h // (Hv // Hqk)
+        S = ts[0, h]
+        for i in range(T):
+            kt = tk[0, i, g]
+            S = ta[0, i, h] * (S - tb[0, i, h] * torch.outer(S @ kt, kt)) \
+                + tb[0, i, h] * torch.outer(tv[0, i, h], kt)
+            loss = loss + torch.dot(S @ tq[0, i, g], torch.tensor(do[0, i, h]))
+        loss = loss + torch.sum(S * torch.tensor(dht[0, h]))
+    loss.backward()
+    mine = oracle.prefill_backward(q, k, v, a, b, do, s0, dht)
+    for x, gx in zip(t, mine):
+        ref = x.grad.numpy()
+        assert np.abs(ref - gx).max() <= 1e-11 * max(1.0, np.abs(ref).max())
+
+
+def test_backward_identity_closed_form(oracle_mod):
+    # beta = 0, alpha = 1: S_t = S_0 for every t, so with
+    # G_t = dht + sum_{s >= t} do_s q_s^T:
+    #   dq_t = sum_h S_0^T do_t,  dk = dv = 0,  dh0 = G_1,
+    #   dalpha_t = <G_t, S_0>,  dbeta_t = (G_t k_t) . (v_t - S_0 k_t)
+    q, k, v, a, b, s0, do, dht = _bwd_inputs(43, 1, 7, 2, 6, 5)
+    a = np.ones_like(a)
+    b = np.zeros_like(b)
+    dq, dk, dv, da, db, dh0 = oracle.prefill_backward(q, k, v, a, b, do, s0, dht)
+    assert np.all(dk == 0) and np.all(dv == 0)
+    T, Hv = q.shape[1], v.shape[2]
+    for h in range(Hv):
+        g = h // 3
+        Gm = dht[0, h].copy()
+        for t in range(T - 1, -1, -1):
+            Gm += np.outer(do[0, t, h], q[0, t, g])
+            assert np.isclose(da[0, t, h], np.sum(Gm * s0[0, h]), rtol=1e-12)
+            ref_b = (Gm @ k[0, t, g]) @ (v[0, t, h] - s0[0, h] @ k[0, t, g])
+            assert np.isclose(db[0, t, h], ref_b, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(dh0[0, h], Gm, rtol=1e-12, atol=1e-12)
+    for t in range(T):
+        for g in range(2):
+            ref = sum(s0[0, h].T @ do[0, t, h] for h in range(3 * g, 3 * g + 3))
+            np.testing.assert_allclose(dq[0, t, g], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_backward_empty_sequence(oracle_mod):
+    q, k, v, a, b, s0, do, dht = _bwd_inputs(44, 1, 0, 2, 6, 4)
+    dq, dk, dv, da, db, dh0 = oracle.prefill_backward(q, k, v, a, b, do, s0, dht)
+    assert dq.shape == (1, 0, 2, 4) and da.shape == (1, 0, 6)
+    np.testing.assert_array_equal(dh0, dht)
+
+
+@pytest.mark.parametrize("C", [1, 16, 64])
+def test_chunked_backward_equals_sequential(oracle_mod, C):
+    q, k, v, a, b, s0, do, dht = _bwd_inputs(45, 1, 150, 2, 6, 16)
+    seq = oracle.prefill_backward(q, k, v, a, b, do, s0, dht)
+    chk = chunked_form.chunked_backward(q, k, v, a, b, do, s0, dht, C=C)
+    for x, y in zip(seq, chk):
+        assert np.linalg.norm(x - y) <= 1e-12 * np.linalg.norm(x)
