@@ -387,4 +387,114 @@ gdn_status gdn_prefill_varlen(const void* q, const void* k, const void* v, const
   return fail_hip(gdn::launch_scan(a, st));
 }
 
+namespace {
+// Backward workspace: the forward layout (its Tt region holding (I + A)^-1),
+// then the state entering every chunk and the gradient of the state leaving
+// every chunk, [nc][Hv][128][128] each in the element type.
+struct BwdLayout {
+  WsLayout f;
+  size_t s, ds, total;
+};
+BwdLayout bwd_layout(int64_t nc, int64_t Hqk, int64_t Hv, gdn_dtype dt) {
+  BwdLayout b{};
+  b.f = ws_layout(nc, Hqk, Hv, dt, -1);
+  const size_t st = round256((size_t)nc * Hv * gdn::kD * gdn::kD * esize(dt));
+  b.s = b.f.total;
+  b.ds = b.s + st;
+  b.total = b.ds + st;
+  return b;
+}
+}  // namespace
+
+size_t gdn_prefill_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H_qk, int32_t H_v,
+                                       int32_t D, gdn_dtype dt) {
+  if (check_dims(H_qk, H_v, D, dt) != GDN_OK || B < 0 || T < 0) return 0;
+  const int64_t nc = (int64_t)B * (((int64_t)T + gdn::kC - 1) / gdn::kC);
+  if (nc == 0) return 0;
+  return bwd_layout(nc, H_qk, H_v, dt).total;
+}
+
+gdn_status gdn_prefill_chunked_bwd(const void* q, const void* k, const void* v,
+                                   const float* alpha, const float* beta, const float* h0,
+                                   const void* dout, const float* dht, void* dq, void* dk,
+                                   void* dv, float* dalpha, float* dbeta, float* dh0, int32_t B,
+                                   int32_t T, int32_t H_qk, int32_t H_v, int32_t D,
+                                   gdn_dtype dt, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  gdn_status s = check_dims(H_qk, H_v, D, dt);
+  if (s != GDN_OK) return s;
+  if (B < 0 || T < 0) return GDN_ERR_SHAPE;
+  if (B > 65535) return GDN_ERR_UNSUPPORTED;
+  const int64_t Nc = ((int64_t)T + gdn::kC - 1) / gdn::kC;
+  const int64_t nc = (int64_t)B * Nc;
+  if (nc > (int64_t(1) << 30) || nc * H_v * gdn::kD * gdn::kD > kMaxElems)
+    return GDN_ERR_UNSUPPORTED;
+  const int64_t ntok = (int64_t)B * T;
+  if (ntok > 0 && (!q || !k || !v || !alpha || !beta || !dout || !dq || !dk || !dv ||
+                   !dalpha || !dbeta))
+    return GDN_ERR_NULL;
+  if (ntok * H_v * gdn::kD > kMaxElems || (int64_t)B * H_v * gdn::kD * gdn::kD > kMaxElems)
+    return GDN_ERR_UNSUPPORTED;
+  const BwdLayout Lw = bwd_layout(nc, H_qk, H_v, dt);
+  const size_t need = nc > 0 ? Lw.total : 0;
+  if (need > 0 && !workspace) return GDN_ERR_WORKSPACE;
+  if (workspace_bytes < need) return GDN_ERR_WORKSPACE;
+  const void* p16[] = {q, k, v, dout, dq, dk, dv, h0, dht, dh0, workspace};
+  for (const void* p : p16)
+    if (!aligned(p, 16)) return GDN_ERR_ALIGN;
+  const void* p4[] = {alpha, beta, dalpha, dbeta};
+  for (const void* p : p4)
+    if (!aligned(p, 4)) return GDN_ERR_ALIGN;
+  const int64_t es = (int64_t)esize(dt), Dl = gdn::kD, SB = (int64_t)B * H_v * Dl * Dl * 4;
+  const Range ins[] = {span(q, ntok * H_qk * Dl * es), span(k, ntok * H_qk * Dl * es),
+                       span(v, ntok * H_v * Dl * es),  span(dout, ntok * H_v * Dl * es),
+                       span(alpha, ntok * H_v * 4),    span(beta, ntok * H_v * 4),
+                       span(h0, SB),                   span(dht, SB)};
+  const Range outs[] = {span(dq, ntok * H_qk * Dl * es), span(dk, ntok * H_qk * Dl * es),
+                        span(dv, ntok * H_v * Dl * es),  span(dalpha, ntok * H_v * 4),
+                        span(dbeta, ntok * H_v * 4),     span(dh0, SB),
+                        span(workspace, (int64_t)need)};
+  // outputs overlap neither an input nor each other
+  for (size_t a = 0; a < sizeof(outs) / sizeof(outs[0]); ++a) {
+    for (const Range& in : ins)
+      if (overlap(outs[a], in)) return GDN_ERR_ALIAS;
+    for (size_t c = a + 1; c < sizeof(outs) / sizeof(outs[0]); ++c)
+      if (overlap(outs[a], outs[c])) return GDN_ERR_ALIAS;
+  }
+
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (nc > 0) {
+    gdn::PrefillLaunch a{};
+    a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta;
+    a.Tt = ws + Lw.f.tt;
+    a.M = ws + Lw.f.m;
+    a.gam = reinterpret_cast<float*>(ws + Lw.f.gam);
+    a.dec = reinterpret_cast<float*>(ws + Lw.f.dec);
+    a.cm = gdn::ChunkMap{nullptr, nullptr, T, (int)Nc, (int)nc};
+    a.nseq = B;
+    a.ntok = ntok;
+    a.nc_launch = (int)nc;
+    a.Hqk = H_qk; a.Hv = H_v;
+    a.bf16_io = dt == GDN_BF16;
+    a.solve_only = true;
+    s = fail_hip(gdn::launch_prepare(a, st));
+    if (s != GDN_OK) return s;
+  }
+  if (B == 0 || (nc == 0 && !dh0)) return GDN_OK;
+  gdn::BackwardLaunch bl{};
+  bl.q = q; bl.k = k; bl.v = v; bl.dout = dout; bl.alpha = alpha; bl.beta = beta;
+  bl.h0 = h0; bl.dht = dht;
+  bl.dq = dq; bl.dk = dk; bl.dv = dv; bl.dalpha = dalpha; bl.dbeta = dbeta; bl.dh0 = dh0;
+  bl.N = ws ? ws + Lw.f.tt : nullptr;
+  bl.M = ws ? ws + Lw.f.m : nullptr;
+  bl.S = ws ? ws + Lw.s : nullptr;
+  bl.dS = ws ? ws + Lw.ds : nullptr;
+  bl.gam = ws ? reinterpret_cast<float*>(ws + Lw.f.gam) : nullptr;
+  bl.dec = ws ? reinterpret_cast<float*>(ws + Lw.f.dec) : nullptr;
+  bl.B = B; bl.T = T; bl.Nc = (int)Nc; bl.Hqk = H_qk; bl.Hv = H_v;
+  bl.bf16_io = dt == GDN_BF16;
+  return fail_hip(gdn::launch_backward(bl, st));
+}
+
 }  // extern "C"

@@ -1,0 +1,856 @@
+// Backward pass of the chunked gated delta rule on gfx950.
+//
+// The page "Inside Qwen3.8-27B: Hybrid DeltaNet Architecture, 256k Context,
+// and 24GB Local Serving" (note under "The Role of Periodic Gated Attention")
+// says training runs the same block-parallel form as prefill.  Its gradients
+// follow from the chunk relations of the forward pass (one chunk, L <= 64
+// tokens, incoming state S0, G = prefix of ln alpha, gamma = exp G,
+// Gam_ij = exp(G_i - G_j) for j <= i, dec_i = Gam_{L-1,i}):
+//
+//     A  = strict_lower(diag(beta) (K K^T * Gam)),   N = (I + A)^-1
+//     X  = V - diag(gamma) K S0^T,    Dl = N diag(beta) X
+//     O  = diag(gamma) Q S0^T + M Dl,              M = (Q K^T * Gam) incl. diagonal
+//     S' = gamma_{L-1} S0 + Dl^T diag(dec) K
+//
+// Given dO = dL/dO and dS' = dL/dS', the chain rule gives
+//
+//     dDl = M^T dO + diag(dec) K dS'^T,      Y = N^T dDl,     dV = diag(beta) Y
+//     dS0 = gamma_{L-1} dS' + (diag(gamma) Q)^T dO - (diag(gamma) K)^T diag(beta) Y
+//     dM  = tril(dO Dl^T),   dA = -strict_lower(Y Dl^T),   Wa = diag(beta) (dA * Gam)
+//     dQ  = diag(gamma) dO S0 + (dM * Gam) K
+//     dK  = -diag(gamma beta) Y S0 + diag(dec) Dl dS' + (dM * Gam)^T Q + (Wa + Wa^T) K
+//     dbeta_i = Y_i . X_i + sum_j dA_ij Gam_ij (k_i . k_j)
+//     dG_i = q_i . (gamma_i (dO S0)_i) - gamma_i beta_i Y_i . (K S0^T)_i - w_i
+//            + rowsum_i(P) - colsum_i(P),   P = dM * M + dA * A,
+//            w_i = dec_i Dl_i . (K dS'^T)_i;   dG_{L-1} += sum_i w_i + gamma_{L-1} <dS', S0>
+//     dalpha_j = (sum_{i >= j} dG_i) / alpha_j
+//
+// Kernels, launched in this order on one stream:
+//  1. prepare (the forward's, with solve_only): N and M per (chunk, value head).
+//  2. fwd_states: the forward state chain again, storing the state entering
+//     every chunk (element type of the inputs) instead of outputs.
+//  3. bwd_chain: dL/dS carried from the last chunk to the first, storing the
+//     gradient of the state leaving every chunk; dh0 at the end.  Value rows
+//     never interact in either chain, so rows split across waves and
+//     workgroups as in the forward scan.
+//  4. bwd_grad: one workgroup per (chunk, query/key head), fully parallel.  It
+//     walks the value heads of its group and accumulates dq and dk for the
+//     group in registers, so no atomics and no reduction pass are needed.
+#include "gdn_device.hpp"
+#include "gdn_launch.hpp"
+
+namespace gdn {
+namespace bwd {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// ------------------------------------------------------------ fragments
+// A fragment holds the K slots one lane supplies to an MFMA: 8 bf16 (one
+// 16x16x32 instruction) or 4 fp32 (four 16x16x4 instructions).  Slot j of
+// lane group g is K offset kslot(g, j) inside a K block of KB.
+template <typename E> struct FragOf;
+template <> struct FragOf<bf16> { typedef bf16x8 T; static constexpr int KB = 32; };
+template <> struct FragOf<float> { typedef f32x4 T; static constexpr int KB = 16; };
+template <typename E> using Fr = typename FragOf<E>::T;
+
+template <typename E> __device__ __forceinline__ int kslot(int g, int j) {
+  if constexpr (sizeof(E) == 2) return j < 4 ? 4 * g + j : 12 + 4 * g + j;
+  else return 4 * g + j;
+}
+template <typename E> constexpr int kSlotsOf = sizeof(E) == 2 ? 8 : 4;
+
+__device__ __forceinline__ f32x4 mma(f32x4 c, const bf16x8& a, const bf16x8& b) {
+  return mfma_bf16(a, b, c);
+}
+__device__ __forceinline__ f32x4 mma(f32x4 c, const f32x4& a, const f32x4& b) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) c = mfma_f32(a[s], b[s], c);
+  return c;
+}
+
+// Fragment from accumulator tiles whose rows are the K index (tile t covers
+// K rows 16t .. 16t+15): a product's result used as the next product's B
+// operand (or, transposed, as its A operand) without leaving registers.
+template <typename E> __device__ __forceinline__ Fr<E> acc_frag(const f32x4* t, int kb) {
+  if constexpr (sizeof(E) == 2) return pack_b(t[2 * kb], t[2 * kb + 1]);
+  else return t[kb];
+}
+
+template <typename E> __device__ __forceinline__ void frag_zero(Fr<E>& f, int j) {
+  if constexpr (sizeof(E) == 2) f[j] = (bf16)0.f;
+  else f[j] = 0.f;
+}
+
+__device__ __forceinline__ bf16x4 as_bf16x4(s16x4 v) {
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+// Row-major matrix of W columns in LDS.  bf16: unpadded rows with 8-byte
+// units XOR-swizzled so that both fragment reads below hit every bank once per
+// pass; fp32: rows padded by 4 floats.
+template <typename E, int W>
+struct Lds {
+  static constexpr bool BF = sizeof(E) == 2;
+  static constexpr int LD = BF ? W : W + 4;
+  static constexpr int size(int rows) { return rows * LD; }
+  E* p;
+  __device__ static int at(int row, int col) {
+    if constexpr (BF) {
+      constexpr int rpl = 128 / W, nb = W / 16;
+      return row * W + ((((col >> 2) ^ (((row / rpl) % nb) << 2))) << 2) + (col & 3);
+    } else {
+      return row * LD + col;
+    }
+  }
+  __device__ E& operator()(int row, int col) const { return p[at(row, col)]; }
+  __device__ float get(int row, int col) const { return to_f32(p[at(row, col)]); }
+  // Lane index along rows: slot j = element (row, k0 + kslot(g, j)).
+  __device__ Fr<E> rm(int row, int k0) const {
+    const int g = lane_id() >> 4;
+    if constexpr (BF) {
+      const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p + at(row, k0 + 4 * g));
+      const bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + at(row, k0 + 16 + 4 * g));
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    } else {
+      return *reinterpret_cast<const f32x4*>(p + row * LD + k0 + 4 * g);
+    }
+  }
+  // Lane index along columns (col = 16-aligned base + lane % 16): slot j =
+  // element (k0 + kslot(g, j), col).  bf16 uses ds_read_b64_tr_b16: input lane
+  // r of a 16-lane group reads four columns base + 4(r%4) .. +3 of row
+  // k0 + 4g + r/4, and output lane m receives column base + m of those rows.
+  __device__ Fr<E> cm(int col, int k0) const {
+    const int l = lane_id(), r = l & 15, g = l >> 4;
+    if constexpr (BF) {
+      const int c0 = col - r + 4 * (r & 3);
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(p + at(k0 + 4 * g + (r >> 2), c0)));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(p + at(k0 + 16 + 4 * g + (r >> 2), c0)));
+      return __builtin_shufflevector(as_bf16x4(lo), as_bf16x4(hi), 0, 1, 2, 3, 4, 5, 6, 7);
+    } else {
+      f32x4 f;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) f[s] = p[(k0 + 4 * g + s) * LD + col];
+      return f;
+    }
+  }
+};
+
+// Row-major matrix in global memory with `rows` valid rows (reads beyond them
+// return zero: the tail of the last chunk).
+template <typename E>
+struct Glb {
+  const E* p;
+  int64_t ld;
+  int rows;
+  __device__ float get(int row, int col) const {
+    return row < rows ? to_f32(p[row * ld + col]) : 0.f;
+  }
+  __device__ Fr<E> rm(int row, int k0) const {
+    const int g = lane_id() >> 4;
+    Fr<E> f;
+#pragma unroll
+    for (int j = 0; j < kSlotsOf<E>; ++j)
+      f[j] = row < rows ? p[row * ld + k0 + kslot<E>(g, j)] : (E)0.f;
+    return f;
+  }
+  __device__ Fr<E> cm(int col, int k0) const {
+    const int g = lane_id() >> 4;
+    Fr<E> f;
+#pragma unroll
+    for (int j = 0; j < kSlotsOf<E>; ++j) {
+      const int row = k0 + kslot<E>(g, j);
+      f[j] = row < rows ? p[row * ld + col] : (E)0.f;
+    }
+    return f;
+  }
+};
+
+// Copies rows [0, rows) of a global row-major matrix (row stride ld elements,
+// W columns) into an LDS matrix, zero-filling rows [rows, R).  All NT threads
+// take part; 16-byte pieces.
+template <typename E, int W, int R, int NT>
+__device__ __forceinline__ void stage(Lds<E, W> dst, const E* src, int64_t ld, int rows) {
+  constexpr int EP = 16 / sizeof(E);
+  constexpr int PPR = W / EP;
+  constexpr int NP = R * PPR;
+  static_assert(NP % NT == 0, "pieces per thread");
+  uint4 buf[NP / NT];
+#pragma unroll
+  for (int it = 0; it < NP / NT; ++it) {
+    const int pc = threadIdx.x + NT * it, row = pc / PPR, c = (pc % PPR) * EP;
+    buf[it] = row < rows ? *reinterpret_cast<const uint4*>(src + row * ld + c)
+                         : uint4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int it = 0; it < NP / NT; ++it) {
+    const int pc = threadIdx.x + NT * it, row = pc / PPR, c = (pc % PPR) * EP;
+    if constexpr (sizeof(E) == 2) {
+      // two 8-byte units; the swizzle keeps each 16-byte piece contiguous
+      *reinterpret_cast<uint4*>(&dst(row, c)) = buf[it];
+    } else {
+      *reinterpret_cast<uint4*>(&dst(row, c)) = buf[it];
+    }
+  }
+}
+
+// Sum over the 16 lanes of a lane group (same g).
+__device__ __forceinline__ float sum16(float x) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+template <typename E>
+__device__ __forceinline__ void store4(E* p, const f32x4& x) {
+  if constexpr (sizeof(E) == 2) {
+    bf16x4 v;
+    v[0] = (bf16)x[0]; v[1] = (bf16)x[1]; v[2] = (bf16)x[2]; v[3] = (bf16)x[3];
+    *reinterpret_cast<bf16x4*>(p) = v;
+  } else {
+    *reinterpret_cast<f32x4*>(p) = x;
+  }
+}
+
+// ------------------------------------------------------------ chains
+// Both chains: one workgroup of NW waves per (value-row slice, value head,
+// sequence); wave w owns value rows dv0 .. dv0+15 (dv0 = 16 (NW slice + w)) and
+// keeps them transposed (d_k x 16, eight accumulator tiles) for the whole
+// sequence, so that the tiles are directly the B operand of K S^T.  Per chunk
+// the shared operands are staged in LDS by the whole workgroup.
+template <typename E, int NW>
+struct ChainSmem {
+  static constexpr int R = 16 * NW;
+  E K[Lds<E, 128>::size(kC)];
+  E Q[Lds<E, 128>::size(kC)];            // gamma-scaled Q (bwd_chain only)
+  E V[Lds<E, R>::size(kC)];              // V (fwd) or dO (bwd) of the slice's rows
+  E N[Lds<E, 64>::size(kC)];
+  E M[Lds<E, 64>::size(kC)];             // bwd_chain only
+  float gm[kC], dc[kC], bt[kC];
+};
+
+template <typename E, int NW>
+__global__ __launch_bounds__(64 * NW) void fwd_states_kernel(
+    const E* __restrict__ k, const E* __restrict__ v, const float* __restrict__ beta,
+    const float* __restrict__ h0, const E* __restrict__ Nw, const float* __restrict__ gam,
+    const float* __restrict__ dec, E* __restrict__ Sc, int T, int Nc, int Hqk, int Hv) {
+  constexpr int R = 16 * NW, KB = FragOf<E>::KB, NT = 64 * NW;
+  __shared__ ChainSmem<E, NW> sm;
+  const Lds<E, 128> Ks{sm.K};
+  const Lds<E, R> Vs{sm.V};
+  const Lds<E, 64> Ns{sm.N};
+  const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
+  const int h = blockIdx.y, b = blockIdx.z, gq = h / (Hv / Hqk);
+  const int rbase = R * blockIdx.x, dv0 = rbase + 16 * w;
+
+  f32x4 ST[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+    ST[t] = h0 ? *reinterpret_cast<const f32x4*>(
+                     h0 + (((size_t)b * Hv + h) * kD + dv0 + r) * kD + 16 * t + 4 * g)
+               : zero4();
+
+  for (int j = 0; j < Nc; ++j) {
+    const int cid = b * Nc + j, L = min(kC, T - kC * j);
+    const size_t tok0 = (size_t)b * T + (size_t)kC * j;
+    const size_t hc = (size_t)cid * Hv + h;
+    E* sdst = Sc + (hc * kD + dv0 + r) * kD;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) store4(sdst + 16 * t + 4 * g, ST[t]);
+
+    __syncthreads();
+    stage<E, 128, kC, NT>(Ks, k + (tok0 * Hqk + gq) * kD, (int64_t)Hqk * kD, L);
+    stage<E, R, kC, NT>(Vs, v + (tok0 * Hv + h) * kD + rbase, (int64_t)Hv * kD, L);
+    stage<E, 64, kC, NT>(Ns, Nw + hc * kC * kC, kC, kC);
+    if (threadIdx.x < kC) {
+      const int t = threadIdx.x;
+      sm.gm[t] = gam[hc * kC + t];
+      sm.dc[t] = dec[hc * kC + t];
+      sm.bt[t] = t < L ? beta[(tok0 + t) * Hv + h] : 0.f;
+    }
+    __syncthreads();
+
+    // X = V - diag(gamma) K S^T (rows: tokens), times beta
+    f32x4 XB[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x4 u = zero4();
+#pragma unroll
+      for (int kb = 0; kb < kD / KB; ++kb) u = mma(u, Ks.rm(16 * mt + r, KB * kb), acc_frag<E>(ST, kb));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = 16 * mt + 4 * g + i;
+        XB[mt][i] = sm.bt[tok] * (Vs.get(tok, 16 * w + r) - sm.gm[tok] * u[i]);
+      }
+    }
+    // Dl = N (beta X), then diag(dec) Dl
+    f32x4 DD[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x4 d = zero4();
+#pragma unroll
+      for (int kb = 0; kb < kC / KB; ++kb) d = mma(d, Ns.rm(16 * mt + r, KB * kb), acc_frag<E>(XB, kb));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) DD[mt][i] = sm.dc[16 * mt + 4 * g + i] * d[i];
+    }
+    // S^T <- gamma_last S^T + K^T diag(dec) Dl
+    const float gl = sm.gm[kC - 1];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      f32x4 a = ST[t] * gl;
+#pragma unroll
+      for (int kb = 0; kb < kC / KB; ++kb) a = mma(a, Ks.cm(16 * t + r, KB * kb), acc_frag<E>(DD, kb));
+      ST[t] = a;
+    }
+  }
+}
+
+template <typename E, int NW>
+__global__ __launch_bounds__(64 * NW) void bwd_chain_kernel(
+    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ dout,
+    const float* __restrict__ beta, const float* __restrict__ dht, float* __restrict__ dh0,
+    const E* __restrict__ Nw, const E* __restrict__ Mw, const float* __restrict__ gam,
+    const float* __restrict__ dec, E* __restrict__ dSc, int T, int Nc, int Hqk, int Hv) {
+  constexpr int R = 16 * NW, KB = FragOf<E>::KB, NT = 64 * NW;
+  __shared__ ChainSmem<E, NW> sm;
+  const Lds<E, 128> Ks{sm.K}, Qs{sm.Q};
+  const Lds<E, R> Os{sm.V};
+  const Lds<E, 64> Ns{sm.N}, Ms{sm.M};
+  const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
+  const int h = blockIdx.y, b = blockIdx.z, gq = h / (Hv / Hqk);
+  const int rbase = R * blockIdx.x, dv0 = rbase + 16 * w;
+  constexpr int EP = 16 / sizeof(E);
+
+  // dS^T tiles: DT[t][i] = dL/dS [dv0 + r][16t + 4g + i]
+  f32x4 DT[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+    DT[t] = dht ? *reinterpret_cast<const f32x4*>(
+                      dht + (((size_t)b * Hv + h) * kD + dv0 + r) * kD + 16 * t + 4 * g)
+                : zero4();
+
+  for (int j = Nc - 1; j >= 0; --j) {
+    const int cid = b * Nc + j, L = min(kC, T - kC * j);
+    const size_t tok0 = (size_t)b * T + (size_t)kC * j;
+    const size_t hc = (size_t)cid * Hv + h;
+    E* ddst = dSc + (hc * kD + dv0 + r) * kD;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) store4(ddst + 16 * t + 4 * g, DT[t]);
+
+    __syncthreads();
+    if (threadIdx.x < kC) {
+      const int t = threadIdx.x;
+      sm.gm[t] = gam[hc * kC + t];
+      sm.dc[t] = dec[hc * kC + t];
+      sm.bt[t] = t < L ? beta[(tok0 + t) * Hv + h] : 0.f;
+    }
+    stage<E, 128, kC, NT>(Ks, k + (tok0 * Hqk + gq) * kD, (int64_t)Hqk * kD, L);
+    stage<E, R, kC, NT>(Os, dout + (tok0 * Hv + h) * kD + rbase, (int64_t)Hv * kD, L);
+    stage<E, 64, kC, NT>(Ns, Nw + hc * kC * kC, kC, kC);
+    stage<E, 64, kC, NT>(Ms, Mw + hc * kC * kC, kC, kC);
+    // gamma-scaled Q rows
+    {
+      constexpr int PPR = kD / EP, NP = kC * PPR;
+      const float* gsrc = gam + hc * kC;
+      for (int pc = threadIdx.x; pc < NP; pc += NT) {
+        const int row = pc / PPR, c = (pc % PPR) * EP;
+        const float gr = gsrc[row];
+        union { uint4 u; E e[EP]; } raw, out;
+        raw.u = row < L ? *reinterpret_cast<const uint4*>(q + ((tok0 + row) * Hqk + gq) * kD + c)
+                        : uint4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int x = 0; x < EP; ++x) out.e[x] = from_f32<E>(gr * to_f32(raw.e[x]));
+        *reinterpret_cast<uint4*>(&Qs(row, c)) = out.u;
+      }
+    }
+    __syncthreads();
+
+    // dDl = M^T dO + diag(dec) K dS^T    (rows: tokens, column: this lane's dv)
+    f32x4 dD[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x4 p = zero4(), m = zero4();
+#pragma unroll
+      for (int kb = 0; kb < kD / KB; ++kb) p = mma(p, Ks.rm(16 * mt + r, KB * kb), acc_frag<E>(DT, kb));
+#pragma unroll
+      for (int kb = 0; kb < kC / KB; ++kb)
+        m = mma(m, Ms.cm(16 * mt + r, KB * kb), Os.cm(16 * w + r, KB * kb));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dD[mt][i] = m[i] + sm.dc[16 * mt + 4 * g + i] * p[i];
+    }
+    // Y = N^T dDl;  Z = -gamma beta Y
+    f32x4 Z[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x4 y = zero4();
+#pragma unroll
+      for (int kb = 0; kb < kC / KB; ++kb) y = mma(y, Ns.cm(16 * mt + r, KB * kb), acc_frag<E>(dD, kb));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = 16 * mt + 4 * g + i;
+        Z[mt][i] = -sm.gm[tok] * sm.bt[tok] * y[i];
+      }
+    }
+    // dS^T <- gamma_last dS^T + (gamma Q)^T dO + K^T Z
+    const float gl = sm.gm[kC - 1];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      f32x4 a = DT[t] * gl;
+#pragma unroll
+      for (int kb = 0; kb < kC / KB; ++kb) {
+        a = mma(a, Qs.cm(16 * t + r, KB * kb), Os.cm(16 * w + r, KB * kb));
+        a = mma(a, Ks.cm(16 * t + r, KB * kb), acc_frag<E>(Z, kb));
+      }
+      DT[t] = a;
+    }
+  }
+  if (dh0) {
+    float* dst = dh0 + (((size_t)b * Hv + h) * kD + dv0 + r) * kD;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) *reinterpret_cast<f32x4*>(dst + 16 * t + 4 * g) = DT[t];
+  }
+}
+
+// ------------------------------------------------------------ per-chunk gradients
+// One workgroup of 8 waves per (chunk, query/key head).  Per value head of the
+// group:
+//  phase 1   wave w owns value columns 16w..16w+15 of X, Dl, dDl, Y (rows:
+//            tokens); writes dv, and Dl and Y to LDS.
+//  phase 1.5 the 64x64 products dO Dl^T and Y Dl^T, two 16x16 tiles per wave,
+//            turned into dM * Gam and Wa (stored together in one 64x64
+//            matrix E: dM * Gam on and below the diagonal, Wa transposed
+//            above it) and the gate and beta row/column sums.
+//  phase 2   wave w owns key columns 16w..16w+15 of dq and dk (rows: tokens),
+//            accumulated over the group's value heads in registers.
+// bf16 stages every operand in LDS (about 157 KB); fp32 reads the inputs from
+// global memory (L2) and keeps only the intermediates Dl, Y, E in LDS.
+constexpr int kGW = 8;  // waves
+
+template <typename E>
+struct GradSmem {
+  static constexpr bool BF = sizeof(E) == 2;
+  // bf16 only (fp32 reads these from global memory)
+  E K[BF ? Lds<E, 128>::size(kC) : 1];
+  E Q[BF ? Lds<E, 128>::size(kC) : 1];
+  E S0[BF ? Lds<E, 128>::size(kD) : 1];
+  E dS[BF ? Lds<E, 128>::size(kD) : 1];
+  E dO[BF ? Lds<E, 128>::size(kC) : 1];
+  union {
+    E V[BF ? Lds<E, 128>::size(kC) : 1];    // phase 1 input (bf16)
+    E Dl[Lds<E, 128>::size(kC)];            // phase 1 output
+  } u1;
+  union {
+    struct {
+      E N[BF ? Lds<E, 64>::size(kC) : 1];
+      E M[BF ? Lds<E, 64>::size(kC) : 1];
+    } nm;                                    // phase 1 inputs (bf16)
+    E Y[Lds<E, 128>::size(kC)];             // phase 1 output
+  } u2;
+  union {
+    float part[kGW][3][kC];                 // phase 1 per-wave row sums
+    E Em[Lds<E, 64>::size(kC)];             // phase 1.5 output
+  } u3;
+  float ss[kGW];                            // per-wave <dS', S0>
+  float rowp[4][kC], colp[4][kC], rowb[4][kC];
+  float pa[kGW][kC];
+  float fin[3][kC];                         // gate, beta, w
+  float G2[kC], gm[kC], dc[kC], bt[kC], al[kC];
+};
+
+template <typename E>
+__global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
+    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
+    const E* __restrict__ dout, const float* __restrict__ alpha, const float* __restrict__ beta,
+    const E* __restrict__ Nw, const E* __restrict__ Mw, const E* __restrict__ Sc,
+    const E* __restrict__ dSc, E* __restrict__ dq, E* __restrict__ dk, E* __restrict__ dv,
+    float* __restrict__ dalpha, float* __restrict__ dbeta, int T, int Nc, int Hqk, int Hv) {
+  constexpr bool BF = sizeof(E) == 2;
+  constexpr int KB = FragOf<E>::KB, NT = 64 * kGW, NS = kSlotsOf<E>;
+  __shared__ GradSmem<E> sm;
+  const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
+  const int cid = blockIdx.x, gq = blockIdx.y, G = Hv / Hqk;
+  const int b = cid / Nc, j = cid - b * Nc, L = min(kC, T - kC * j);
+  const size_t tok0 = (size_t)b * T + (size_t)kC * j;
+
+  const Lds<E, 128> Dls{sm.u1.Dl}, Ys{sm.u2.Y};
+  const Lds<E, 64> Es{sm.u3.Em};
+  const E* kg = k + (tok0 * Hqk + gq) * kD;
+  const E* qg = q + (tok0 * Hqk + gq) * kD;
+
+  auto mK = [&]() {
+    if constexpr (BF) return Lds<E, 128>{sm.K};
+    else return Glb<E>{kg, (int64_t)Hqk * kD, L};
+  }();
+  auto mQ = [&]() {
+    if constexpr (BF) return Lds<E, 128>{sm.Q};
+    else return Glb<E>{qg, (int64_t)Hqk * kD, L};
+  }();
+  if constexpr (BF) {
+    stage<E, 128, kC, NT>(Lds<E, 128>{sm.K}, kg, (int64_t)Hqk * kD, L);
+    stage<E, 128, kC, NT>(Lds<E, 128>{sm.Q}, qg, (int64_t)Hqk * kD, L);
+    __syncthreads();
+  }
+
+  // This wave's two 64x64 tiles (ti, tj), and K K^T / Q K^T on them.
+  int ti[2], tj[2];
+  f32x4 KK[2], QK[2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int t = 2 * w + x;
+    ti[x] = t >> 2;
+    tj[x] = t & 3;
+    KK[x] = zero4();
+    QK[x] = zero4();
+    if (tj[x] <= ti[x]) {
+#pragma unroll
+      for (int kb = 0; kb < kD / KB; ++kb) {
+        const Fr<E> bk = mK.rm(16 * tj[x] + r, KB * kb);
+        KK[x] = mma(KK[x], mK.rm(16 * ti[x] + r, KB * kb), bk);
+        QK[x] = mma(QK[x], mQ.rm(16 * ti[x] + r, KB * kb), bk);
+      }
+    }
+  }
+
+  f32x4 dQ[4], dK[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) { dQ[mt] = zero4(); dK[mt] = zero4(); }
+
+  for (int hh = 0; hh < G; ++hh) {
+    const int h = gq * G + hh;
+    const size_t hc = (size_t)cid * Hv + h;
+    const E* vh = v + (tok0 * Hv + h) * kD;
+    const E* oh = dout + (tok0 * Hv + h) * kD;
+    auto mS0 = [&]() {
+      if constexpr (BF) return Lds<E, 128>{sm.S0};
+      else return Glb<E>{Sc + hc * kD * kD, kD, kD};
+    }();
+    auto mdS = [&]() {
+      if constexpr (BF) return Lds<E, 128>{sm.dS};
+      else return Glb<E>{dSc + hc * kD * kD, kD, kD};
+    }();
+    auto mO = [&]() {
+      if constexpr (BF) return Lds<E, 128>{sm.dO};
+      else return Glb<E>{oh, (int64_t)Hv * kD, L};
+    }();
+    auto mV = [&]() {
+      if constexpr (BF) return Lds<E, 128>{sm.u1.V};
+      else return Glb<E>{vh, (int64_t)Hv * kD, L};
+    }();
+    auto mN = [&]() {
+      if constexpr (BF) return Lds<E, 64>{sm.u2.nm.N};
+      else return Glb<E>{Nw + hc * kC * kC, kC, kC};
+    }();
+    auto mM = [&]() {
+      if constexpr (BF) return Lds<E, 64>{sm.u2.nm.M};
+      else return Glb<E>{Mw + hc * kC * kC, kC, kC};
+    }();
+
+    // ---- stage
+    if constexpr (BF) {
+      stage<E, 128, kD, NT>(Lds<E, 128>{sm.S0}, Sc + hc * kD * kD, kD, kD);
+      stage<E, 128, kD, NT>(Lds<E, 128>{sm.dS}, dSc + hc * kD * kD, kD, kD);
+      stage<E, 128, kC, NT>(Lds<E, 128>{sm.dO}, oh, (int64_t)Hv * kD, L);
+      stage<E, 128, kC, NT>(Lds<E, 128>{sm.u1.V}, vh, (int64_t)Hv * kD, L);
+      stage<E, 64, kC, NT>(Lds<E, 64>{sm.u2.nm.N}, Nw + hc * kC * kC, kC, kC);
+      stage<E, 64, kC, NT>(Lds<E, 64>{sm.u2.nm.M}, Mw + hc * kC * kC, kC, kC);
+    }
+    if (w == 0) {
+      const float a = l < L ? alpha[(tok0 + l) * Hv + h] : 1.f;
+      const float G2 = wave_inclusive_sum(hw_log2(a));
+      const float Glast = __shfl(G2, kC - 1, 64);
+      sm.G2[l] = G2;
+      sm.gm[l] = hw_exp2(G2);
+      sm.dc[l] = hw_exp2(Glast - G2);
+      sm.bt[l] = l < L ? beta[(tok0 + l) * Hv + h] : 0.f;
+      sm.al[l] = a;
+    }
+    __syncthreads();
+
+    // ---- phase 1: this wave's value columns c = 16w + r
+    const int c = 16 * w + r;
+    float ssl = 0.f;
+    f32x4 KS[4], X[4], Dl[4], dD[4], Y[4];
+    {
+      f32x4 KdS[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) { KS[mt] = zero4(); KdS[mt] = zero4(); }
+#pragma unroll
+      for (int kb = 0; kb < kD / KB; ++kb) {
+        const Fr<E> s0 = mS0.rm(c, KB * kb), ds = mdS.rm(c, KB * kb);
+#pragma unroll
+        for (int e = 0; e < NS; ++e) ssl += (float)s0[e] * (float)ds[e];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const Fr<E> ak = mK.rm(16 * mt + r, KB * kb);
+          KS[mt] = mma(KS[mt], ak, s0);
+          KdS[mt] = mma(KdS[mt], ak, ds);
+        }
+      }
+      f32x4 XB[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tok = 16 * mt + 4 * g + i;
+          X[mt][i] = mV.get(tok, c) - sm.gm[tok] * KS[mt][i];
+          XB[mt][i] = sm.bt[tok] * X[mt][i];
+        }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        f32x4 d = zero4(), m = zero4();
+#pragma unroll
+        for (int kb = 0; kb < kC / KB; ++kb) {
+          d = mma(d, mN.rm(16 * mt + r, KB * kb), acc_frag<E>(XB, kb));
+          m = mma(m, mM.cm(16 * mt + r, KB * kb), mO.cm(c, KB * kb));
+        }
+        Dl[mt] = d;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dD[mt][i] = m[i] + sm.dc[16 * mt + 4 * g + i] * KdS[mt][i];
+      }
+      // w_i partial: dec_i Dl_i . (K dS'^T)_i over this wave's columns
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) KdS[mt][i] = sum16(Dl[mt][i] * KdS[mt][i]);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        f32x4 y = zero4();
+#pragma unroll
+        for (int kb = 0; kb < kC / KB; ++kb) y = mma(y, mN.cm(16 * mt + r, KB * kb), acc_frag<E>(dD, kb));
+        Y[mt] = y;
+      }
+      __syncthreads();   // every wave is done with V, N, M (their LDS is reused)
+      E* dvh = dv + (tok0 * Hv + h) * kD;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tok = 16 * mt + 4 * g + i;
+          Dls(tok, c) = from_f32<E>(Dl[mt][i]);
+          Ys(tok, c) = from_f32<E>(Y[mt][i]);
+          if (tok < L) dvh[(size_t)tok * Hv * kD + c] = from_f32<E>(sm.bt[tok] * Y[mt][i]);
+          const float pb = sum16(Y[mt][i] * X[mt][i]);
+          const float pg = sum16(Y[mt][i] * KS[mt][i]);
+          if (r == 0) {
+            sm.u3.part[w][0][tok] = pb;
+            sm.u3.part[w][1][tok] = -sm.gm[tok] * sm.bt[tok] * pg;
+            sm.u3.part[w][2][tok] = sm.dc[tok] * KdS[mt][i];
+          }
+        }
+      ssl = wave_sum(ssl);
+      if (l == 0) sm.ss[w] = ssl;
+    }
+    __syncthreads();
+
+    // ---- reduce the phase 1 partials (fixed order)
+    if (threadIdx.x < 3 * kC) {
+      const int qn = threadIdx.x / kC, t = threadIdx.x % kC;
+      float s = 0.f;
+#pragma unroll
+      for (int x = 0; x < kGW; ++x) s += sm.u3.part[x][qn][t];
+      sm.fin[qn == 0 ? 1 : (qn == 1 ? 0 : 2)][t] = s;
+    }
+    // ---- phase 1.5: dO Dl^T and Y Dl^T on this wave's tiles
+    f32x4 OD[2], YD[2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      OD[x] = zero4();
+      YD[x] = zero4();
+      if (tj[x] <= ti[x]) {
+#pragma unroll
+        for (int kb = 0; kb < kD / KB; ++kb) {
+          const Fr<E> bd = Dls.rm(16 * tj[x] + r, KB * kb);
+          OD[x] = mma(OD[x], mO.rm(16 * ti[x] + r, KB * kb), bd);
+          YD[x] = mma(YD[x], Ys.rm(16 * ti[x] + r, KB * kb), bd);
+        }
+      }
+    }
+    __syncthreads();   // partials consumed; E may overwrite them
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      if (tj[x] > ti[x]) continue;
+      const int jj = 16 * tj[x] + r;
+      float colsum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ii = 16 * ti[x] + 4 * g + i;
+        const float gam_ = jj <= ii ? hw_exp2(sm.G2[ii] - sm.G2[jj]) : 0.f;
+        const float dMG = jj <= ii ? OD[x][i] * gam_ : 0.f;
+        const float dAG = jj < ii ? -YD[x][i] * gam_ : 0.f;
+        const float wa = sm.bt[ii] * dAG;
+        const float P = dMG * QK[x][i] + wa * KK[x][i];
+        // every location of E has exactly one writer: (ii, jj) on and below
+        // the diagonal, its mirror (jj, ii) above it
+        if (jj <= ii) Es(ii, jj) = from_f32<E>(dMG);
+        if (jj < ii) Es(jj, ii) = from_f32<E>(wa);
+        const float rs = sum16(P), rb = sum16(dAG * KK[x][i]);
+        if (r == 0) {
+          sm.rowp[tj[x]][ii] = rs;
+          sm.rowb[tj[x]][ii] = rb;
+        }
+        colsum += P;
+      }
+      colsum += __shfl_xor(colsum, 16, 64);
+      colsum += __shfl_xor(colsum, 32, 64);
+      if (g == 0) sm.colp[ti[x]][jj] = colsum;
+    }
+    __syncthreads();
+
+    // ---- phase 2: this wave's key columns c
+    if (w == 0) {
+      const int t = l, tt = t >> 4;
+      float rs = 0.f, rb = 0.f, cs = 0.f;
+      for (int x = 0; x <= tt; ++x) { rs += sm.rowp[x][t]; rb += sm.rowb[x][t]; }
+      for (int x = tt; x < 4; ++x) cs += sm.colp[x][t];
+      sm.fin[0][t] += rs - cs;
+      sm.fin[1][t] += rb;
+    }
+    {
+      f32x4 T1[4], T2[4], T3[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) { T1[mt] = zero4(); T2[mt] = zero4(); T3[mt] = zero4(); }
+#pragma unroll
+      for (int kb = 0; kb < kD / KB; ++kb) {
+        const Fr<E> s0 = mS0.cm(c, KB * kb), ds = mdS.cm(c, KB * kb);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          T1[mt] = mma(T1[mt], mO.rm(16 * mt + r, KB * kb), s0);
+          T2[mt] = mma(T2[mt], Ys.rm(16 * mt + r, KB * kb), s0);
+          T3[mt] = mma(T3[mt], Dls.rm(16 * mt + r, KB * kb), ds);
+        }
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tok = 16 * mt + 4 * g + i;
+          const float g1 = sm.gm[tok] * T1[mt][i];
+          dQ[mt][i] += g1;
+          dK[mt][i] += sm.dc[tok] * T3[mt][i] - sm.gm[tok] * sm.bt[tok] * T2[mt][i];
+          const float pa = sum16(mQ.get(tok, c) * g1);
+          if (r == 0) sm.pa[w][tok] = pa;
+        }
+      // (dM * Gam) K into dq; (dM * Gam)^T Q and (Wa + Wa^T) K into dk
+#pragma unroll
+      for (int kb = 0; kb < kC / KB; ++kb) {
+        const Fr<E> bk = mK.cm(c, KB * kb), bq = mQ.cm(c, KB * kb);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const int row = 16 * mt + r;
+          Fr<E> e_rm = Es.rm(row, KB * kb), e_cm = Es.cm(row, KB * kb);
+          Fr<E> lowr = e_rm, lowt = e_cm, sym;
+#pragma unroll
+          for (int e = 0; e < NS; ++e) {
+            const int kk = KB * kb + kslot<E>(g, e);
+            if (kk > row) frag_zero<E>(lowr, e);
+            if (kk < row) frag_zero<E>(lowt, e);
+            sym[e] = kk > row ? e_rm[e] : e_cm[e];
+            if (kk == row) frag_zero<E>(sym, e);
+          }
+          dQ[mt] = mma(dQ[mt], lowr, bk);
+          dK[mt] = mma(dK[mt], lowt, bq);
+          dK[mt] = mma(dK[mt], sym, bk);
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- gates and beta for this head (wave 0, lane = token)
+    if (w == 0) {
+      const int t = l;
+      float pa = 0.f, fw = sm.fin[2][t];
+#pragma unroll
+      for (int x = 0; x < kGW; ++x) pa += sm.pa[x][t];
+      float ss = 0.f;
+#pragma unroll
+      for (int x = 0; x < kGW; ++x) ss += sm.ss[x];
+      const float wsum = wave_sum(t < L ? fw : 0.f);
+      float dG = t < L ? pa + sm.fin[0][t] - fw : 0.f;
+      if (t == L - 1) dG += wsum + sm.gm[t] * ss;
+      // reverse inclusive prefix: sum over i >= t
+      const float tot = wave_sum(dG);
+      const float incl = wave_inclusive_sum(dG);
+      const float dlog = tot - incl + dG;
+      if (t < L) {
+        const size_t gi = (tok0 + t) * Hv + h;
+        dalpha[gi] = dlog / sm.al[t];
+        dbeta[gi] = sm.fin[1][t];
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- dq, dk of the group
+  E* dqg = dq + (tok0 * Hqk + gq) * kD;
+  E* dkg = dk + (tok0 * Hqk + gq) * kD;
+  const int c = 16 * w + r;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tok = 16 * mt + 4 * g + i;
+      if (tok < L) {
+        dqg[(size_t)tok * Hqk * kD + c] = from_f32<E>(dQ[mt][i]);
+        dkg[(size_t)tok * Hqk * kD + c] = from_f32<E>(dK[mt][i]);
+      }
+    }
+}
+
+}  // namespace bwd
+
+hipError_t launch_backward(const BackwardLaunch& a, hipStream_t st) {
+  using namespace bwd;
+  constexpr int NW = 2;
+  const dim3 gchain(kD / (16 * NW), a.Hv, a.B);
+  if (a.bf16_io) {
+    typedef bf16 E;
+    if (a.Nc > 0) {
+      hipLaunchKernelGGL((fwd_states_kernel<E, NW>), gchain, dim3(64 * NW), 0, st, (const E*)a.k,
+                         (const E*)a.v, a.beta, a.h0, (const E*)a.N, a.gam, a.dec, (E*)a.S,
+                         a.T, a.Nc, a.Hqk, a.Hv);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((bwd_chain_kernel<E, NW>), gchain, dim3(64 * NW), 0, st, (const E*)a.q,
+                       (const E*)a.k, (const E*)a.dout, a.beta, a.dht, a.dh0, (const E*)a.N,
+                       (const E*)a.M, a.gam, a.dec, (E*)a.dS, a.T, a.Nc, a.Hqk, a.Hv);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.Nc == 0) return e;
+    hipLaunchKernelGGL((bwd_grad_kernel<E>), dim3(a.B * a.Nc, a.Hqk), dim3(64 * kGW), 0, st,
+                       (const E*)a.q, (const E*)a.k, (const E*)a.v, (const E*)a.dout, a.alpha,
+                       a.beta, (const E*)a.N, (const E*)a.M, (const E*)a.S, (const E*)a.dS,
+                       (E*)a.dq, (E*)a.dk, (E*)a.dv, a.dalpha, a.dbeta, a.T, a.Nc, a.Hqk, a.Hv);
+    return hipGetLastError();
+  } else {
+    typedef float E;
+    if (a.Nc > 0) {
+      hipLaunchKernelGGL((fwd_states_kernel<E, NW>), gchain, dim3(64 * NW), 0, st, (const E*)a.k,
+                         (const E*)a.v, a.beta, a.h0, (const E*)a.N, a.gam, a.dec, (E*)a.S,
+                         a.T, a.Nc, a.Hqk, a.Hv);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((bwd_chain_kernel<E, NW>), gchain, dim3(64 * NW), 0, st, (const E*)a.q,
+                       (const E*)a.k, (const E*)a.dout, a.beta, a.dht, a.dh0, (const E*)a.N,
+                       (const E*)a.M, a.gam, a.dec, (E*)a.dS, a.T, a.Nc, a.Hqk, a.Hv);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.Nc == 0) return e;
+    hipLaunchKernelGGL((bwd_grad_kernel<E>), dim3(a.B * a.Nc, a.Hqk), dim3(64 * kGW), 0, st,
+                       (const E*)a.q, (const E*)a.k, (const E*)a.v, (const E*)a.dout, a.alpha,
+                       a.beta, (const E*)a.N, (const E*)a.M, (const E*)a.S, (const E*)a.dS,
+                       (E*)a.dq, (E*)a.dk, (E*)a.dv, a.dalpha, a.dbeta, a.T, a.Nc, a.Hqk, a.Hv);
+    return hipGetLastError();
+  }
+}
+
+}  // namespace gdn

@@ -30,7 +30,23 @@ struct PrefillLaunch {
   int64_t ntok;            // all tokens of the call (B * T, or T_tot)
   bool bf16_io;
   bool state_bf16;         // h0 / ht stored as bfloat16
+  bool solve_only;         // prepare for the backward pass: Tt <- (I + A)^-1, all blocks
 };
+
+// Backward pass of a fixed-length prefill (B sequences of T tokens).
+struct BackwardLaunch {
+  const void *q, *k, *v, *dout;
+  const float *alpha, *beta;
+  const float *h0, *dht;   // [B][Hv][128][128] float32, or null (zeros)
+  void *dq, *dk, *dv;
+  float *dalpha, *dbeta;
+  float* dh0;              // or null (not written)
+  void *N, *M, *S, *dS;    // workspace: prepare's solve and mask, chunk states, state grads
+  float *gam, *dec;
+  int B, T, Nc, Hqk, Hv;
+  bool bf16_io;
+};
+hipError_t launch_backward(const BackwardLaunch& a, hipStream_t st);
 
 hipError_t launch_prepare(const PrefillLaunch& a, hipStream_t st);
 hipError_t launch_scan(const PrefillLaunch& a, hipStream_t st);

@@ -25,7 +25,8 @@
 //    H_v/H_qk value heads that read it), gate prefix G, and the triangular
 //    solve in fp32 (16x16 diagonal blocks by substitution, off-diagonal blocks
 //    by fp32 MFMA).  Writes Tt, the masked output matrix M and G to the
-//    workspace.
+//    workspace.  For the backward pass (solve_only) it writes (I + A)^-1
+//    without the diag(beta) factor, and every block of it and of M.
 //  * scan     (grid: value-row slices x value heads x sequences) - the serial
 //    chain.  Each chain wave owns 16 value rows of one head's state and keeps
 //    them, transposed (S^T, d_k x 16), in fp32 MFMA accumulators for the whole
@@ -133,7 +134,8 @@ __device__ __forceinline__ f32x4 mm16_lds(const float* A, int arow0, int acol0,
 template <typename E>
 __global__ __launch_bounds__(256, sizeof(E) == 2 ? 3 : 2) void prepare_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const float* __restrict__ alpha,
-    const float* __restrict__ beta, Work<E> ws, ChunkMap cm, int Hqk, int Hv, int G) {
+    const float* __restrict__ beta, Work<E> ws, ChunkMap cm, int Hqk, int Hv, int G,
+    bool solve_only) {
   constexpr bool BF = sizeof(E) == 2;
   constexpr int LDK = PrepSmem<E>::LDK;
   constexpr int NB = PrepSmem<E>::NB;
@@ -257,7 +259,8 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 3 : 2) void prepare_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) mv[e] = (bf16)m4[e];
           // The bf16 scan never reads the zero block rows 0..31 x columns 32..63.
-          if (i >= 32 || w < 2) *reinterpret_cast<bf16x4*>(mo + i * kC + 16 * w + 4 * g) = mv;
+          if (i >= 32 || w < 2 || solve_only)
+            *reinterpret_cast<bf16x4*>(mo + i * kC + 16 * w + 4 * g) = mv;
         } else {
           *reinterpret_cast<f32x4*>(mo + i * kC + 16 * w + 4 * g) = f32x4{m4[0], m4[1], m4[2], m4[3]};
         }
@@ -321,7 +324,7 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 3 : 2) void prepare_kernel(
         const int cb = l & 7, rg = l >> 3;
         float bj[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) bj[e] = sm.bet[w][8 * cb + e];
+        for (int e = 0; e < 8; ++e) bj[e] = solve_only ? 1.f : sm.bet[w][8 * cb + e];
 #pragma unroll
         for (int i0 = 0; i0 < 8; ++i0) {
           const int i = 8 * i0 + rg;
@@ -332,7 +335,8 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 3 : 2) void prepare_kernel(
             bf16x8 tv;
 #pragma unroll
             for (int e = 0; e < 8; ++e) tv[e] = (bf16)(t8[e] * bj[e]);
-            if (i >= 32 || cb < 4) *reinterpret_cast<bf16x8*>(tt + i * kC + 8 * cb) = tv;
+            if (i >= 32 || cb < 4 || solve_only)
+              *reinterpret_cast<bf16x8*>(tt + i * kC + 8 * cb) = tv;
           } else {
             *reinterpret_cast<f32x4*>(tt + i * kC + 8 * cb) =
                 f32x4{t8[0] * bj[0], t8[1] * bj[1], t8[2] * bj[2], t8[3] * bj[3]};
@@ -1196,7 +1200,7 @@ static hipError_t launch_prepare_t(const PrefillLaunch& a, hipStream_t st) {
   Work<E> ws{(E*)a.Tt, (E*)a.M, a.gam, a.dec};
   dim3 grid((unsigned)a.nc_launch, (unsigned)a.Hqk), block(256);
   hipLaunchKernelGGL(prepare_kernel<E>, grid, block, 0, st, (const E*)a.q, (const E*)a.k,
-                     a.alpha, a.beta, ws, a.cm, a.Hqk, a.Hv, a.Hv / a.Hqk);
+                     a.alpha, a.beta, ws, a.cm, a.Hqk, a.Hv, a.Hv / a.Hqk, a.solve_only);
   return hipGetLastError();
 }
 

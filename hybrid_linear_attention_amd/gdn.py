@@ -63,6 +63,10 @@ def _load():
     lib.gdn_prefill_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp,
                                        f32, i32, i32, i32, ctypes.c_int, vp, sz, vp]
     lib.gdn_prefill_varlen.restype = ctypes.c_int
+    lib.gdn_prefill_chunked_bwd.argtypes = [vp] * 14 + [i32] * 5 + [ctypes.c_int, vp, sz, vp]
+    lib.gdn_prefill_chunked_bwd.restype = ctypes.c_int
+    lib.gdn_prefill_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int]
+    lib.gdn_prefill_bwd_workspace_bytes.restype = sz
     lib.gdn_status_str.argtypes = [ctypes.c_int]
     lib.gdn_status_str.restype = ctypes.c_char_p
     lib.gdn_last_hip_error.argtypes = []
@@ -199,6 +203,61 @@ def prefill_chunked(q, k, v, alpha, beta, h0=None, *, o=None, ht=None,
     else:
         _check(lib.gdn_prefill_chunked(*args), "gdn_prefill_chunked")
     return o, ht
+
+
+def prefill_bwd_workspace_bytes(B, T, H_qk, H_v, D=HEAD_DIM, dtype=torch.bfloat16) -> int:
+    dt = GDN_BF16 if dtype == torch.bfloat16 else GDN_F32
+    return int(lib.gdn_prefill_bwd_workspace_bytes(B, T, H_qk, H_v, D, dt))
+
+
+def prefill_backward(q, k, v, alpha, beta, do, h0=None, dht=None, *, grads=None,
+                     want_dh0=True, workspace=None):
+    """Gradients of a chunked prefill (gdn_prefill_chunked_bwd) for
+    ``L = sum <do, o> + <dht, ht>``.  Inputs as for :func:`prefill_chunked`
+    plus do [B,T,Hv,128] (dtype of q) and dht [B,Hv,128,128] fp32 or None.
+    Returns ``(dq, dk, dv, dalpha, dbeta, dh0)``; dq/dk/dv in the dtype of q,
+    dalpha/dbeta/dh0 fp32 (dh0 None unless ``want_dh0``).  ``grads`` may hold
+    preallocated outputs in that order."""
+    _req(q, "q", ndim=4)
+    dtype, dev = q.dtype, q.device
+    B, T, H_qk, D = q.shape
+    _req(k, "k", dtype, 4, dev)
+    _req(v, "v", dtype, 4, dev)
+    _req(do, "do", dtype, 4, dev)
+    H_v = v.shape[2]
+    if (tuple(k.shape) != (B, T, H_qk, D) or tuple(v.shape) != (B, T, H_v, D)
+            or tuple(do.shape) != (B, T, H_v, D)):
+        raise ValueError("q/k [B,T,Hqk,D], v/do [B,T,Hv,D] disagree")
+    for name, t in (("alpha", alpha), ("beta", beta)):
+        _req(t, name, torch.float32, 3, dev)
+        if tuple(t.shape) != (B, T, H_v):
+            raise ValueError("%s must be [B,T,Hv]" % name)
+    for name, t in (("h0", h0), ("dht", dht)):
+        _req(t, name, torch.float32, 4, dev)
+        if t is not None and tuple(t.shape) != (B, H_v, D, D):
+            raise ValueError("%s must be [B,Hv,D,D]" % name)
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
+                 torch.empty_like(alpha), torch.empty_like(beta),
+                 torch.empty((B, H_v, D, D), dtype=torch.float32, device=dev)
+                 if want_dh0 else None)
+    dq, dk, dv, da, db, dh0 = grads
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _req(t, name, dtype, 4, dev)
+        if t.shape != ref.shape:
+            raise ValueError("%s must have the shape of its input" % name)
+    for name, t in (("dalpha", da), ("dbeta", db)):
+        _req(t, name, torch.float32, 3, dev)
+        if tuple(t.shape) != (B, T, H_v):
+            raise ValueError("%s must be [B,T,Hv]" % name)
+    _req(dh0, "dh0", torch.float32, 4, dev)
+    nbytes = prefill_bwd_workspace_bytes(B, T, H_qk, H_v, D, dtype)
+    ws = _workspace(nbytes, dev, workspace)
+    _check(lib.gdn_prefill_chunked_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(h0), _ptr(do), _ptr(dht),
+        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(da), _ptr(db), _ptr(dh0),
+        B, T, H_qk, H_v, D, _dt(q), _ptr(ws), nbytes, _stream(dev)), "gdn_prefill_chunked_bwd")
+    return dq, dk, dv, da, db, dh0
 
 
 def prefill_prepare(q, k, v, alpha, beta, h0, o, ht, workspace):

@@ -253,6 +253,44 @@ gdn_status gdn_prefill_varlen(const void *q, const void *k, const void *v,
 size_t gdn_varlen_workspace_bytes(int32_t N, int32_t T_tot, int32_t H_qk,
                                   int32_t H_v, int32_t D, gdn_dtype dt);
 
+/*
+ * gdn_prefill_chunked_bwd - gradients of gdn_prefill_chunked (training runs
+ * the same block-parallel form as prefill: page "Inside Qwen3.8-27B ...", the
+ * note under "The Role of Periodic Gated Attention").  For the scalar
+ *     L = sum_t <dout_t, o_t> + <dht, S_T>
+ * it returns dL/dq, dL/dk, dL/dv, dL/dalpha, dL/dbeta and dL/dh0.
+ *
+ *   q, k, v, alpha, beta, h0   the forward call's inputs (same layouts; h0
+ *                              may be NULL for a zero initial state)
+ *   dout   [B, T, H_v, D]   dt        dL/do
+ *   dht    [B, H_v, D, D]   float32   dL/dS_T, or NULL (zero)
+ *   dq, dk [B, T, H_qk, D]  dt        summed over the value heads sharing
+ *                                     each query/key head
+ *   dv     [B, T, H_v, D]   dt
+ *   dalpha, dbeta [B, T, H_v] float32
+ *   dh0    [B, H_v, D, D]   float32   or NULL (not written)
+ *   workspace  at least gdn_prefill_bwd_workspace_bytes(...) bytes; it holds
+ *              the state entering every chunk and the gradient of the state
+ *              leaving every chunk (element type dt), so it grows with T.
+ * The forward states are recomputed from the inputs (nothing is kept from the
+ * forward call).  Outputs must not overlap inputs, each other or the
+ * workspace.  Arithmetic: dt operands on the matrix units, fp32 accumulation
+ * and fp32 carried state gradient.  T = 0 gives dh0 = dht (or zeros).
+ */
+gdn_status gdn_prefill_chunked_bwd(const void *q, const void *k, const void *v,
+                                   const float *alpha, const float *beta,
+                                   const float *h0, const void *dout,
+                                   const float *dht, void *dq, void *dk,
+                                   void *dv, float *dalpha, float *dbeta,
+                                   float *dh0, int32_t B, int32_t T,
+                                   int32_t H_qk, int32_t H_v, int32_t D,
+                                   gdn_dtype dt, void *workspace,
+                                   size_t workspace_bytes, void *stream);
+
+/* Workspace bytes for gdn_prefill_chunked_bwd (0 on unsupported arguments). */
+size_t gdn_prefill_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H_qk,
+                                       int32_t H_v, int32_t D, gdn_dtype dt);
+
 /* Human-readable name of a status code (static string). */
 const char *gdn_status_str(gdn_status s);
 

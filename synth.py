@@ -26,6 +26,10 @@ in float32, in this order):
 
 Decode: the carried state is drawn from ``seed``; the per-step tensors of
 step s come from seed + 7919 * (s + 1).
+
+Backward: after the prefill draws above, from the same generator, the
+upstream gradient of the outputs do ~ N(0, 1) in the working dtype, then (when
+asked for) the upstream gradient of the final state dht ~ N(0, std^2) fp32.
 """
 from __future__ import annotations
 
@@ -84,6 +88,17 @@ def prefill_inputs(B, T, dtype=torch.bfloat16, seed=0, h0_std=0.0,
     ``[B,T,Hv]`` fp32; h0 ``[B,Hv,Dh,Dh]`` fp32 or None."""
     gen = torch.Generator().manual_seed(seed)
     return _draw(gen, (B, T), Hqk, Hv, Dh, dtype, (B, Hv, Dh, Dh), h0_std, False)
+
+
+def backward_inputs(B, T, dtype=torch.bfloat16, seed=0, h0_std=0.0, dht_std=0.0,
+                    Hqk=H_QK, Hv=H_V, Dh=D):
+    """:func:`prefill_inputs` plus ``do [B,T,Hv,Dh]`` (dtype) and ``dht
+    [B,Hv,Dh,Dh]`` fp32 or None."""
+    gen = torch.Generator().manual_seed(seed)
+    d = _draw(gen, (B, T), Hqk, Hv, Dh, dtype, (B, Hv, Dh, Dh), h0_std, False)
+    d["do"] = _normal(gen, (B, T, Hv, Dh)).to(dtype).contiguous()
+    d["dht"] = (_normal(gen, (B, Hv, Dh, Dh)) * dht_std).contiguous() if dht_std else None
+    return d
 
 
 def varlen_lengths(N, lo, hi, seed):

@@ -496,3 +496,75 @@ def test_config4_varlen_sampled_heads(gdn):
             eh = rel(ht[n, h], ht_ref[n, i])
             assert ey <= 2e-2 and eh <= 2e-2, (n, h, ey, eh)
     say("config4 ok")
+
+
+# ------------------------------------------------------------------ backward
+GRAD_NAMES = ("dq", "dk", "dv", "dalpha", "dbeta", "dh0")
+
+
+def run_backward(gdn, inp):
+    d = to_dev(inp)
+    g = gdn.prefill_backward(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["do"],
+                             d["h0"], d["dht"])
+    torch.cuda.synchronize()
+    return g
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+@pytest.mark.parametrize("B,T,h0std,dhtstd", [(1, 64, 0.0, 0.0), (1, 200, 0.02, 0.02),
+                                              (2, 130, 0.02, 0.0), (1, 1, 0.02, 0.02),
+                                              (3, 63, 0.0, 0.02), (1, 321, 0.5, 0.1)])
+def test_backward_small(gdn, dtype, B, T, h0std, dhtstd):
+    say("backward_small", dtype, B, T, h0std, dhtstd)
+    inp = synth.backward_inputs(B, T, dtype, seed=11 + T + B, h0_std=h0std, dht_std=dhtstd)
+    got = run_backward(gdn, inp)
+    ref = oracle.prefill_backward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"],
+                                  inp["do"], inp["h0"], inp["dht"])
+    errs = [rel(x, y) for x, y in zip(got, ref)]
+    say("  rel " + " ".join("%s %.3e" % (n, e) for n, e in zip(GRAD_NAMES, errs)))
+    for n, e in zip(GRAD_NAMES, errs):
+        assert e <= TOL[dtype], (n, e)
+
+
+def test_backward_T0(gdn):
+    inp = synth.backward_inputs(2, 0, torch.bfloat16, seed=5, h0_std=0.1, dht_std=0.1)
+    got = run_backward(gdn, inp)
+    assert got[0].shape == (2, 0, 16, 128)
+    assert torch.equal(got[5].cpu(), inp["dht"])
+    inp["dht"] = None
+    got = run_backward(gdn, inp)
+    assert torch.count_nonzero(got[5]).item() == 0
+
+
+def test_backward_deterministic(gdn):
+    inp = synth.backward_inputs(1, 300, torch.bfloat16, seed=9, h0_std=0.02, dht_std=0.02)
+    g1 = run_backward(gdn, inp)
+    g2 = run_backward(gdn, inp)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+def test_backward_T8192_sampled_groups(gdn):
+    # the training shape of the prefill workload: whole call on the GPU, two
+    # query/key groups (their three value heads each) checked against the oracle
+    inp = synth.backward_inputs(1, 8192, torch.bfloat16, seed=1011, h0_std=0.02,
+                                dht_std=0.02)
+    got = run_backward(gdn, inp)
+    say("backward T=8192 done on GPU")
+    for gq in (0, 15):
+        heads = [3 * gq, 3 * gq + 1, 3 * gq + 2]
+        sub = oracle.subset_heads(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"],
+                                  inp["h0"], heads, 16, 48)
+        do_s = inp["do"][:, :, heads]
+        dht_s = inp["dht"][:, heads]
+        t0 = time.time()
+        # one query/key head shared by the three value heads, as in the call
+        ref = oracle.prefill_backward(sub[0][:, :, :1], sub[1][:, :, :1], sub[2], sub[3],
+                                      sub[4], do_s, sub[5], dht_s)
+        say("  oracle group %d %.1fs" % (gq, time.time() - t0))
+        mine = (got[0][:, :, gq:gq + 1], got[1][:, :, gq:gq + 1], got[2][:, :, heads],
+                got[3][:, :, heads], got[4][:, :, heads], got[5][:, heads])
+        errs = [rel(x, y) for x, y in zip(mine, ref)]
+        say("  group %d rel " % gq + " ".join("%s %.3e" % (n, e) for n, e in zip(GRAD_NAMES, errs)))
+        for n, e in zip(GRAD_NAMES, errs):
+            assert e <= 2e-2, (gq, n, e)
