@@ -388,18 +388,19 @@ gdn_status gdn_prefill_varlen(const void* q, const void* k, const void* v, const
 }
 
 namespace {
-// Backward workspace: the forward layout (its Tt region holding (I + A)^-1),
-// then the state entering every chunk and the gradient of the state leaving
-// every chunk, [nc][Hv][128][128] each in the element type.
+// Backward workspace: the forward layout, then N = (I + A)^-1 [nc][Hv][64][64],
+// the state entering every chunk and the gradient of the state leaving every
+// chunk ([nc][Hv][128][128] each), all in the element type.
 struct BwdLayout {
   WsLayout f;
-  size_t s, ds, total;
+  size_t n, s, ds, total;
 };
 BwdLayout bwd_layout(int64_t nc, int64_t Hqk, int64_t Hv, gdn_dtype dt) {
   BwdLayout b{};
   b.f = ws_layout(nc, Hqk, Hv, dt, -1);
   const size_t st = round256((size_t)nc * Hv * gdn::kD * gdn::kD * esize(dt));
-  b.s = b.f.total;
+  b.n = b.f.total;
+  b.s = b.n + round256((size_t)nc * Hv * gdn::kC * gdn::kC * esize(dt));
   b.ds = b.s + st;
   b.total = b.ds + st;
   return b;
@@ -478,15 +479,24 @@ gdn_status gdn_prefill_chunked_bwd(const void* q, const void* k, const void* v,
     a.Hqk = H_qk; a.Hv = H_v;
     a.bf16_io = dt == GDN_BF16;
     a.solve_only = true;
+    a.N = ws + Lw.n;
     s = fail_hip(gdn::launch_prepare(a, st));
     if (s != GDN_OK) return s;
+    if (a.bf16_io) {
+      // the forward scan, outputs off, writing the state entering every chunk
+      a.h0 = h0;
+      a.states = ws + Lw.s;
+      s = fail_hip(gdn::launch_scan(a, st));
+      if (s != GDN_OK) return s;
+    }
   }
   if (B == 0 || (nc == 0 && !dh0)) return GDN_OK;
   gdn::BackwardLaunch bl{};
   bl.q = q; bl.k = k; bl.v = v; bl.dout = dout; bl.alpha = alpha; bl.beta = beta;
   bl.h0 = h0; bl.dht = dht;
   bl.dq = dq; bl.dk = dk; bl.dv = dv; bl.dalpha = dalpha; bl.dbeta = dbeta; bl.dh0 = dh0;
-  bl.N = ws ? ws + Lw.f.tt : nullptr;
+  bl.N = ws ? ws + Lw.n : nullptr;
+  bl.states_ready = dt == GDN_BF16;
   bl.M = ws ? ws + Lw.f.m : nullptr;
   bl.S = ws ? ws + Lw.s : nullptr;
   bl.dS = ws ? ws + Lw.ds : nullptr;

@@ -27,8 +27,9 @@
 //
 // Kernels, launched in this order on one stream:
 //  1. prepare (the forward's, with solve_only): N and M per (chunk, value head).
-//  2. fwd_states: the forward state chain again, storing the state entering
-//     every chunk (element type of the inputs) instead of outputs.
+//  2. the forward state chain again, storing the state entering every chunk
+//     (element type of the inputs) instead of outputs: bf16 uses the forward
+//     scan itself with its outputs off, fp32 the fwd_states kernel below.
 //  3. bwd_chain: dL/dS carried from the last chunk to the first, storing the
 //     gradient of the state leaving every chunk; dh0 at the end.  Value rows
 //     never interact in either chain, so rows split across waves and
@@ -89,6 +90,20 @@ __device__ __forceinline__ bf16x4 as_bf16x4(s16x4 v) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
+// A lane's position in the MFMA fragment layouts (r = lane % 16, g = lane / 16).
+struct Lane {
+  int r, g;
+};
+__device__ __forceinline__ Lane lane_here() { return Lane{lane_id() & 15, lane_id() >> 4}; }
+// The same, hidden from the optimiser: fragment addresses derived from it are
+// recomputed where they are used instead of being hoisted out of a loop and
+// kept live (or spilled) across it.
+__device__ __forceinline__ Lane lane_opaque() {
+  int l = lane_id();
+  asm volatile("" : "+v"(l));
+  return Lane{l & 15, l >> 4};
+}
+
 // Row-major matrix of W columns in LDS.  bf16: unpadded rows with 8-byte
 // units XOR-swizzled so that both fragment reads below hit every bank once per
 // pass; fp32: rows padded by 4 floats.
@@ -109,8 +124,9 @@ struct Lds {
   __device__ E& operator()(int row, int col) const { return p[at(row, col)]; }
   __device__ float get(int row, int col) const { return to_f32(p[at(row, col)]); }
   // Lane index along rows: slot j = element (row, k0 + kslot(g, j)).
-  __device__ Fr<E> rm(int row, int k0) const {
-    const int g = lane_id() >> 4;
+  __device__ Fr<E> rm(int row, int k0) const { return rm(row, k0, lane_here()); }
+  __device__ Fr<E> rm(int row, int k0, const Lane& ln) const {
+    const int g = ln.g;
     if constexpr (BF) {
       const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p + at(row, k0 + 4 * g));
       const bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + at(row, k0 + 16 + 4 * g));
@@ -123,8 +139,9 @@ struct Lds {
   // element (k0 + kslot(g, j), col).  bf16 uses ds_read_b64_tr_b16: input lane
   // r of a 16-lane group reads four columns base + 4(r%4) .. +3 of row
   // k0 + 4g + r/4, and output lane m receives column base + m of those rows.
-  __device__ Fr<E> cm(int col, int k0) const {
-    const int l = lane_id(), r = l & 15, g = l >> 4;
+  __device__ Fr<E> cm(int col, int k0) const { return cm(col, k0, lane_here()); }
+  __device__ Fr<E> cm(int col, int k0, const Lane& ln) const {
+    const int r = ln.r, g = ln.g;
     if constexpr (BF) {
       const int c0 = col - r + 4 * (r & 3);
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -151,16 +168,18 @@ struct Glb {
   __device__ float get(int row, int col) const {
     return row < rows ? to_f32(p[row * ld + col]) : 0.f;
   }
-  __device__ Fr<E> rm(int row, int k0) const {
-    const int g = lane_id() >> 4;
+  __device__ Fr<E> rm(int row, int k0) const { return rm(row, k0, lane_here()); }
+  __device__ Fr<E> rm(int row, int k0, const Lane& ln) const {
+    const int g = ln.g;
     Fr<E> f;
 #pragma unroll
     for (int j = 0; j < kSlotsOf<E>; ++j)
       f[j] = row < rows ? p[row * ld + k0 + kslot<E>(g, j)] : (E)0.f;
     return f;
   }
-  __device__ Fr<E> cm(int col, int k0) const {
-    const int g = lane_id() >> 4;
+  __device__ Fr<E> cm(int col, int k0) const { return cm(col, k0, lane_here()); }
+  __device__ Fr<E> cm(int col, int k0, const Lane& ln) const {
+    const int g = ln.g;
     Fr<E> f;
 #pragma unroll
     for (int j = 0; j < kSlotsOf<E>; ++j) {
@@ -421,6 +440,162 @@ __global__ __launch_bounds__(64 * NW) void bwd_chain_kernel(
   }
 }
 
+// bf16 reverse chain with operands copied straight into LDS
+// (global_load_lds_dwordx4: no registers, no VALU), double-buffered: the copies
+// of chunk j-1 are in flight while chunk j is computed.  Copy instruction `it`
+// of a tile fills LDS bytes [1024 it, 1024 it + 1024); lane l's 16 bytes are
+// the piece of the swizzled layout at that position, so each lane reads the
+// global piece the swizzle puts there.  Rows beyond the chunk's length repeat
+// its last token: such tokens get a zero gamma wherever they could reach the
+// state gradient (the gamma-scaled dO and the beta-scaled Y), and the mask
+// matrix M, written by prepare from zero rows, is zero there.
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_dst, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_dst, 4, 0, 0);
+}
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+__device__ __forceinline__ void wait_copies() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// 64 rows (rows >= L repeat row L-1) of a bf16 matrix with W columns into the
+// Lds<bf16, W> layout at dst; wave w of nw issues copies w, w + nw, ...
+template <int W>
+__device__ __forceinline__ void copy_rows(const bf16* src, int64_t ld, int L, bf16* dst, int w,
+                                          int nw) {
+  constexpr int RPK = 1024 / (2 * W), NIT = kC / RPK;
+  constexpr int rpl = 128 / W, nb = W / 16;
+  const int l = lane_id();
+  const int rin = (16 * l) / (2 * W), pp = ((16 * l) % (2 * W)) / 16;
+  for (int it = w; it < NIT; it += nw) {
+    const int row = it * RPK + rin;
+    const int lp = pp ^ (((row / rpl) % nb) << 1);
+    dma16(src + (int64_t)min(row, L - 1) * ld + 8 * lp, reinterpret_cast<char*>(dst) + 1024 * it);
+  }
+}
+
+template <int NW>
+struct ChainDmaBuf {
+  static constexpr int R = 16 * NW;
+  bf16 K[kC * kD];
+  bf16 Q[kC * kD];
+  bf16 O[kC * R];
+  bf16 N[kC * kC];
+  bf16 M[kC * kC];
+  float gm[kC], dc[kC], bt[kC];
+};
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void bwd_chain_bf16_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ dout,
+    const float* __restrict__ beta, const float* __restrict__ dht, float* __restrict__ dh0,
+    const bf16* __restrict__ Nw, const bf16* __restrict__ Mw, const float* __restrict__ gam,
+    const float* __restrict__ dec, bf16* __restrict__ dSc, int T, int Nc, int Hqk, int Hv) {
+  typedef bf16 E;
+  constexpr int R = 16 * NW, KB = 32;
+  __shared__ ChainDmaBuf<NW> buf[2];
+  const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
+  const int h = blockIdx.y, b = blockIdx.z, gq = h / (Hv / Hqk);
+  const int rbase = R * blockIdx.x, dv0 = rbase + 16 * w;
+
+  auto issue = [&](int j) {
+    ChainDmaBuf<NW>& B_ = buf[j & 1];
+    const int cid = b * Nc + j, L = min(kC, T - kC * j);
+    const size_t tok0 = (size_t)b * T + (size_t)kC * j;
+    const size_t hc = (size_t)cid * Hv + h;
+    copy_rows<128>(k + (tok0 * Hqk + gq) * kD, (int64_t)Hqk * kD, L, B_.K, w, NW);
+    copy_rows<128>(q + (tok0 * Hqk + gq) * kD, (int64_t)Hqk * kD, L, B_.Q, w, NW);
+    copy_rows<R>(dout + (tok0 * Hv + h) * kD + rbase, (int64_t)Hv * kD, L, B_.O, w, NW);
+    copy_rows<64>(Nw + hc * kC * kC, kC, kC, B_.N, w, NW);
+    copy_rows<64>(Mw + hc * kC * kC, kC, kC, B_.M, w, NW);
+    if (w == 0) dma4(gam + hc * kC + l, B_.gm);
+    if (w == NW - 1) dma4(dec + hc * kC + l, B_.dc);
+    if (w == (NW > 2 ? 1 : 0)) dma4(beta + (tok0 + min(l, L - 1)) * Hv + h, B_.bt);
+  };
+
+  f32x4 DT[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+    DT[t] = dht ? *reinterpret_cast<const f32x4*>(
+                      dht + (((size_t)b * Hv + h) * kD + dv0 + r) * kD + 16 * t + 4 * g)
+                : zero4();
+  if (Nc > 0) issue(Nc - 1);
+  wait_copies();
+  barrier_lds();
+
+  for (int j = Nc - 1; j >= 0; --j) {
+    const int cid = b * Nc + j, L = min(kC, T - kC * j);
+    const size_t hc = (size_t)cid * Hv + h;
+    E* ddst = dSc + (hc * kD + dv0 + r) * kD;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) store4(ddst + 16 * t + 4 * g, DT[t]);
+    if (j > 0) issue(j - 1);
+
+    const ChainDmaBuf<NW>& B_ = buf[j & 1];
+    const Lds<E, 128> Ks{const_cast<E*>(B_.K)}, Qs{const_cast<E*>(B_.Q)};
+    const Lds<E, R> Os{const_cast<E*>(B_.O)};
+    const Lds<E, 64> Ns{const_cast<E*>(B_.N)}, Ms{const_cast<E*>(B_.M)};
+
+    // dO fragments (B operand, K = tokens), plain and gamma-scaled (masked)
+    bf16x8 OB[2], OG[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      OB[kb] = Os.cm(16 * w + r, KB * kb);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int tok = KB * kb + kslot<E>(g, e);
+        OG[kb][e] = (bf16)(tok < L ? B_.gm[tok] * (float)OB[kb][e] : 0.f);
+      }
+    }
+    f32x4 dD[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x4 p = zero4(), m = zero4();
+#pragma unroll
+      for (int kb = 0; kb < kD / KB; ++kb) p = mma(p, Ks.rm(16 * mt + r, KB * kb), acc_frag<E>(DT, kb));
+#pragma unroll
+      for (int kb = 0; kb < kC / KB; ++kb) m = mma(m, Ms.cm(16 * mt + r, KB * kb), OB[kb]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dD[mt][i] = m[i] + B_.dc[16 * mt + 4 * g + i] * p[i];
+    }
+    f32x4 Z[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x4 y = zero4();
+#pragma unroll
+      for (int kb = 0; kb < kC / KB; ++kb) y = mma(y, Ns.cm(16 * mt + r, KB * kb), acc_frag<E>(dD, kb));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = 16 * mt + 4 * g + i;
+        Z[mt][i] = tok < L ? -B_.gm[tok] * B_.bt[tok] * y[i] : 0.f;
+      }
+    }
+    const float gl = B_.gm[kC - 1];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      f32x4 a = DT[t] * gl;
+#pragma unroll
+      for (int kb = 0; kb < kC / KB; ++kb) {
+        a = mma(a, Qs.cm(16 * t + r, KB * kb), OG[kb]);
+        a = mma(a, Ks.cm(16 * t + r, KB * kb), acc_frag<E>(Z, kb));
+      }
+      DT[t] = a;
+    }
+    wait_copies();
+    barrier_lds();
+  }
+  if (dh0) {
+    float* dst = dh0 + (((size_t)b * Hv + h) * kD + dv0 + r) * kD;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) *reinterpret_cast<f32x4*>(dst + 16 * t + 4 * g) = DT[t];
+  }
+}
+
 // ------------------------------------------------------------ per-chunk gradients
 // One workgroup of 8 waves per (chunk, query/key head).  Per value head of the
 // group:
@@ -527,6 +702,8 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
 
   for (int hh = 0; hh < G; ++hh) {
     const int h = gq * G + hh;
+    const Lane ln = lane_opaque();
+    const int r = ln.r, g = ln.g;
     const size_t hc = (size_t)cid * Hv + h;
     const E* vh = v + (tok0 * Hv + h) * kD;
     const E* oh = dout + (tok0 * Hv + h) * kD;
@@ -578,57 +755,78 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
 
     // ---- phase 1: this wave's value columns c = 16w + r
     const int c = 16 * w + r;
-    float ssl = 0.f;
-    f32x4 KS[4], X[4], Dl[4], dD[4], Y[4];
     {
-      f32x4 KdS[4];
+      float ssl = 0.f;
+      f32x4 X[4], Dl[4], dD[4], Y[4];
+      {
+        f32x4 XB[4];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) { KS[mt] = zero4(); KdS[mt] = zero4(); }
+        for (int mt = 0; mt < 4; ++mt) X[mt] = zero4();
 #pragma unroll
-      for (int kb = 0; kb < kD / KB; ++kb) {
-        const Fr<E> s0 = mS0.rm(c, KB * kb), ds = mdS.rm(c, KB * kb);
+        for (int kb = 0; kb < kD / KB; ++kb) {
+          const Fr<E> s0 = mS0.rm(c, KB * kb, ln), ds = mdS.rm(c, KB * kb, ln);
 #pragma unroll
-        for (int e = 0; e < NS; ++e) ssl += (float)s0[e] * (float)ds[e];
+          for (int e = 0; e < NS; ++e) ssl += (float)s0[e] * (float)ds[e];
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) X[mt] = mma(X[mt], mK.rm(16 * mt + r, KB * kb, ln), s0);
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int tok = 16 * mt + 4 * g + i;
+            X[mt][i] = mV.get(tok, c) - sm.gm[tok] * X[mt][i];   // V - gamma K S0^T
+            XB[mt][i] = sm.bt[tok] * X[mt][i];
+          }
+        // Dl = N (beta X)
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-          const Fr<E> ak = mK.rm(16 * mt + r, KB * kb);
-          KS[mt] = mma(KS[mt], ak, s0);
-          KdS[mt] = mma(KdS[mt], ak, ds);
+          f32x4 d = zero4();
+#pragma unroll
+          for (int kb = 0; kb < kC / KB; ++kb) d = mma(d, mN.rm(16 * mt + r, KB * kb, ln), acc_frag<E>(XB, kb));
+          Dl[mt] = d;
         }
       }
-      f32x4 XB[4];
+      // dDl = M^T dO + diag(dec) K dS'^T, one token tile at a time; w_i partial
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        f32x4 kds = zero4(), m = zero4();
+#pragma unroll
+        for (int kb = 0; kb < kD / KB; ++kb)
+          kds = mma(kds, mK.rm(16 * mt + r, KB * kb, ln), mdS.rm(c, KB * kb, ln));
+#pragma unroll
+        for (int kb = 0; kb < kC / KB; ++kb) m = mma(m, mM.cm(16 * mt + r, KB * kb, ln), mO.cm(c, KB * kb, ln));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tok = 16 * mt + 4 * g + i;
+          dD[mt][i] = m[i] + sm.dc[tok] * kds[i];
+          const float pw = sum16(Dl[mt][i] * kds[i]);
+          if (r == 0) sm.u3.part[w][2][tok] = sm.dc[tok] * pw;
+        }
+      }
+      // Y = N^T dDl
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        f32x4 y = zero4();
+#pragma unroll
+        for (int kb = 0; kb < kC / KB; ++kb) y = mma(y, mN.cm(16 * mt + r, KB * kb, ln), acc_frag<E>(dD, kb));
+        Y[mt] = y;
+      }
+      // beta and gate partials: Y.X and -gamma beta Y.(K S0^T) = -beta Y.(V - X)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int tok = 16 * mt + 4 * g + i;
-          X[mt][i] = mV.get(tok, c) - sm.gm[tok] * KS[mt][i];
-          XB[mt][i] = sm.bt[tok] * X[mt][i];
+          const float pb = sum16(Y[mt][i] * X[mt][i]);
+          const float pg = sum16(Y[mt][i] * (mV.get(tok, c) - X[mt][i]));
+          if (r == 0) {
+            sm.u3.part[w][0][tok] = pb;
+            sm.u3.part[w][1][tok] = -sm.bt[tok] * pg;
+          }
         }
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        f32x4 d = zero4(), m = zero4();
-#pragma unroll
-        for (int kb = 0; kb < kC / KB; ++kb) {
-          d = mma(d, mN.rm(16 * mt + r, KB * kb), acc_frag<E>(XB, kb));
-          m = mma(m, mM.cm(16 * mt + r, KB * kb), mO.cm(c, KB * kb));
-        }
-        Dl[mt] = d;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dD[mt][i] = m[i] + sm.dc[16 * mt + 4 * g + i] * KdS[mt][i];
-      }
-      // w_i partial: dec_i Dl_i . (K dS'^T)_i over this wave's columns
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) KdS[mt][i] = sum16(Dl[mt][i] * KdS[mt][i]);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        f32x4 y = zero4();
-#pragma unroll
-        for (int kb = 0; kb < kC / KB; ++kb) y = mma(y, mN.cm(16 * mt + r, KB * kb), acc_frag<E>(dD, kb));
-        Y[mt] = y;
-      }
+      ssl = wave_sum(ssl);
+      if (l == 0) sm.ss[w] = ssl;
       __syncthreads();   // every wave is done with V, N, M (their LDS is reused)
       E* dvh = dv + (tok0 * Hv + h) * kD;
 #pragma unroll
@@ -639,16 +837,7 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
           Dls(tok, c) = from_f32<E>(Dl[mt][i]);
           Ys(tok, c) = from_f32<E>(Y[mt][i]);
           if (tok < L) dvh[(size_t)tok * Hv * kD + c] = from_f32<E>(sm.bt[tok] * Y[mt][i]);
-          const float pb = sum16(Y[mt][i] * X[mt][i]);
-          const float pg = sum16(Y[mt][i] * KS[mt][i]);
-          if (r == 0) {
-            sm.u3.part[w][0][tok] = pb;
-            sm.u3.part[w][1][tok] = -sm.gm[tok] * sm.bt[tok] * pg;
-            sm.u3.part[w][2][tok] = sm.dc[tok] * KdS[mt][i];
-          }
         }
-      ssl = wave_sum(ssl);
-      if (l == 0) sm.ss[w] = ssl;
     }
     __syncthreads();
 
@@ -669,9 +858,9 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
       if (tj[x] <= ti[x]) {
 #pragma unroll
         for (int kb = 0; kb < kD / KB; ++kb) {
-          const Fr<E> bd = Dls.rm(16 * tj[x] + r, KB * kb);
-          OD[x] = mma(OD[x], mO.rm(16 * ti[x] + r, KB * kb), bd);
-          YD[x] = mma(YD[x], Ys.rm(16 * ti[x] + r, KB * kb), bd);
+          const Fr<E> bd = Dls.rm(16 * tj[x] + r, KB * kb, ln);
+          OD[x] = mma(OD[x], mO.rm(16 * ti[x] + r, KB * kb, ln), bd);
+          YD[x] = mma(YD[x], Ys.rm(16 * ti[x] + r, KB * kb, ln), bd);
         }
       }
     }
@@ -716,38 +905,71 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
       sm.fin[1][t] += rb;
     }
     {
-      f32x4 T1[4], T2[4], T3[4];
+      // gamma dO S0 into dq (and the gate's q . dq partial)
+      {
+        f32x4 T1[4];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) { T1[mt] = zero4(); T2[mt] = zero4(); T3[mt] = zero4(); }
+        for (int mt = 0; mt < 4; ++mt) T1[mt] = zero4();
 #pragma unroll
-      for (int kb = 0; kb < kD / KB; ++kb) {
-        const Fr<E> s0 = mS0.cm(c, KB * kb), ds = mdS.cm(c, KB * kb);
+        for (int kb = 0; kb < kD / KB; ++kb) {
+          const Fr<E> s0 = mS0.cm(c, KB * kb, ln);
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          T1[mt] = mma(T1[mt], mO.rm(16 * mt + r, KB * kb), s0);
-          T2[mt] = mma(T2[mt], Ys.rm(16 * mt + r, KB * kb), s0);
-          T3[mt] = mma(T3[mt], Dls.rm(16 * mt + r, KB * kb), ds);
+          for (int mt = 0; mt < 4; ++mt) T1[mt] = mma(T1[mt], mO.rm(16 * mt + r, KB * kb, ln), s0);
         }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int tok = 16 * mt + 4 * g + i;
+            const float g1 = sm.gm[tok] * T1[mt][i];
+            dQ[mt][i] += g1;
+            const float pa = sum16(mQ.get(tok, c) * g1);
+            if (r == 0) sm.pa[w][tok] = pa;
+          }
       }
+      // -gamma beta Y S0 into dk
+      {
+        f32x4 T2[4];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 4; ++mt) T2[mt] = zero4();
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tok = 16 * mt + 4 * g + i;
-          const float g1 = sm.gm[tok] * T1[mt][i];
-          dQ[mt][i] += g1;
-          dK[mt][i] += sm.dc[tok] * T3[mt][i] - sm.gm[tok] * sm.bt[tok] * T2[mt][i];
-          const float pa = sum16(mQ.get(tok, c) * g1);
-          if (r == 0) sm.pa[w][tok] = pa;
+        for (int kb = 0; kb < kD / KB; ++kb) {
+          const Fr<E> s0 = mS0.cm(c, KB * kb, ln);
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) T2[mt] = mma(T2[mt], Ys.rm(16 * mt + r, KB * kb, ln), s0);
         }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int tok = 16 * mt + 4 * g + i;
+            dK[mt][i] -= sm.gm[tok] * sm.bt[tok] * T2[mt][i];
+          }
+      }
+      // diag(dec) Dl dS' into dk
+      {
+        f32x4 T3[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) T3[mt] = zero4();
+#pragma unroll
+        for (int kb = 0; kb < kD / KB; ++kb) {
+          const Fr<E> ds = mdS.cm(c, KB * kb, ln);
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) T3[mt] = mma(T3[mt], Dls.rm(16 * mt + r, KB * kb, ln), ds);
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dK[mt][i] += sm.dc[16 * mt + 4 * g + i] * T3[mt][i];
+      }
       // (dM * Gam) K into dq; (dM * Gam)^T Q and (Wa + Wa^T) K into dk
 #pragma unroll
       for (int kb = 0; kb < kC / KB; ++kb) {
-        const Fr<E> bk = mK.cm(c, KB * kb), bq = mQ.cm(c, KB * kb);
+        const Fr<E> bk = mK.cm(c, KB * kb, ln), bq = mQ.cm(c, KB * kb, ln);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           const int row = 16 * mt + r;
-          Fr<E> e_rm = Es.rm(row, KB * kb), e_cm = Es.cm(row, KB * kb);
+          Fr<E> e_rm = Es.rm(row, KB * kb, ln), e_cm = Es.cm(row, KB * kb, ln);
           Fr<E> lowr = e_rm, lowt = e_cm, sym;
 #pragma unroll
           for (int e = 0; e < NS; ++e) {
@@ -814,16 +1036,18 @@ hipError_t launch_backward(const BackwardLaunch& a, hipStream_t st) {
   const dim3 gchain(kD / (16 * NW), a.Hv, a.B);
   if (a.bf16_io) {
     typedef bf16 E;
-    if (a.Nc > 0) {
+    if (a.Nc > 0 && !a.states_ready) {
       hipLaunchKernelGGL((fwd_states_kernel<E, NW>), gchain, dim3(64 * NW), 0, st, (const E*)a.k,
                          (const E*)a.v, a.beta, a.h0, (const E*)a.N, a.gam, a.dec, (E*)a.S,
                          a.T, a.Nc, a.Hqk, a.Hv);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((bwd_chain_kernel<E, NW>), gchain, dim3(64 * NW), 0, st, (const E*)a.q,
-                       (const E*)a.k, (const E*)a.dout, a.beta, a.dht, a.dh0, (const E*)a.N,
-                       (const E*)a.M, a.gam, a.dec, (E*)a.dS, a.T, a.Nc, a.Hqk, a.Hv);
+    constexpr int NWB = 2;
+    hipLaunchKernelGGL((bwd_chain_bf16_kernel<NWB>), dim3(kD / (16 * NWB), a.Hv, a.B),
+                       dim3(64 * NWB), 0, st, (const E*)a.q, (const E*)a.k, (const E*)a.dout,
+                       a.beta, a.dht, a.dh0, (const E*)a.N, (const E*)a.M, a.gam, a.dec,
+                       (E*)a.dS, a.T, a.Nc, a.Hqk, a.Hv);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.Nc == 0) return e;
     hipLaunchKernelGGL((bwd_grad_kernel<E>), dim3(a.B * a.Nc, a.Hqk), dim3(64 * kGW), 0, st,

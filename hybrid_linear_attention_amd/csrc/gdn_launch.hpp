@@ -30,7 +30,9 @@ struct PrefillLaunch {
   int64_t ntok;            // all tokens of the call (B * T, or T_tot)
   bool bf16_io;
   bool state_bf16;         // h0 / ht stored as bfloat16
-  bool solve_only;         // prepare for the backward pass: Tt <- (I + A)^-1, all blocks
+  bool solve_only;         // prepare for the backward pass: also N = (I + A)^-1, all blocks
+  void* N;                 // solve_only: where N goes
+  void* states;            // bf16 scan: state entering every chunk (backward pass), or null
 };
 
 // Backward pass of a fixed-length prefill (B sequences of T tokens).
@@ -45,6 +47,7 @@ struct BackwardLaunch {
   float *gam, *dec;
   int B, T, Nc, Hqk, Hv;
   bool bf16_io;
+  bool states_ready;       // S already written (by the bf16 forward scan)
 };
 hipError_t launch_backward(const BackwardLaunch& a, hipStream_t st);
 

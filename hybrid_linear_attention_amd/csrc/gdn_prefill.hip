@@ -25,8 +25,8 @@
 //    H_v/H_qk value heads that read it), gate prefix G, and the triangular
 //    solve in fp32 (16x16 diagonal blocks by substitution, off-diagonal blocks
 //    by fp32 MFMA).  Writes Tt, the masked output matrix M and G to the
-//    workspace.  For the backward pass (solve_only) it writes (I + A)^-1
-//    without the diag(beta) factor, and every block of it and of M.
+//    workspace.  For the backward pass (solve_only) it also writes N =
+//    (I + A)^-1 without the diag(beta) factor, and every block of N and M.
 //  * scan     (grid: value-row slices x value heads x sequences) - the serial
 //    chain.  Each chain wave owns 16 value rows of one head's state and keeps
 //    them, transposed (S^T, d_k x 16), in fp32 MFMA accumulators for the whole
@@ -55,6 +55,7 @@ struct Work {
   E* M;        // [nc][Hv][64][64]   (Q K^T * exp(G_i - G_j)) on and below the diagonal
   float* gam;  // [nc][Hv][64]       exp(G_t)
   float* dec;  // [nc][Hv][64]       exp(G_last - G_t)
+  E* N;        // [nc][Hv][64][64]   (I + A)^-1, every block (backward pass only; else null)
 };
 
 // Gates are kept in base 2 so that the hardware v_exp_f32 / v_log_f32 apply
@@ -324,7 +325,8 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 3 : 2) void prepare_kernel(
         const int cb = l & 7, rg = l >> 3;
         float bj[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) bj[e] = solve_only ? 1.f : sm.bet[w][8 * cb + e];
+        for (int e = 0; e < 8; ++e) bj[e] = sm.bet[w][8 * cb + e];
+        E* nn = solve_only ? ws.N + ((size_t)cid * Hv + h) * kC * kC : nullptr;
 #pragma unroll
         for (int i0 = 0; i0 < 8; ++i0) {
           const int i = 8 * i0 + rg;
@@ -335,13 +337,21 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 3 : 2) void prepare_kernel(
             bf16x8 tv;
 #pragma unroll
             for (int e = 0; e < 8; ++e) tv[e] = (bf16)(t8[e] * bj[e]);
-            if (i >= 32 || cb < 4 || solve_only)
-              *reinterpret_cast<bf16x8*>(tt + i * kC + 8 * cb) = tv;
+            if (i >= 32 || cb < 4) *reinterpret_cast<bf16x8*>(tt + i * kC + 8 * cb) = tv;
+            if (nn) {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) tv[e] = (bf16)t8[e];
+              *reinterpret_cast<bf16x8*>(nn + i * kC + 8 * cb) = tv;
+            }
           } else {
             *reinterpret_cast<f32x4*>(tt + i * kC + 8 * cb) =
                 f32x4{t8[0] * bj[0], t8[1] * bj[1], t8[2] * bj[2], t8[3] * bj[3]};
             *reinterpret_cast<f32x4*>(tt + i * kC + 8 * cb + 4) =
                 f32x4{t8[4] * bj[4], t8[5] * bj[5], t8[6] * bj[6], t8[7] * bj[7]};
+            if (nn) {
+              *reinterpret_cast<f32x4*>(nn + i * kC + 8 * cb) = f32x4{t8[0], t8[1], t8[2], t8[3]};
+              *reinterpret_cast<f32x4*>(nn + i * kC + 8 * cb + 4) = f32x4{t8[4], t8[5], t8[6], t8[7]};
+            }
           }
         }
       }
@@ -779,7 +789,7 @@ __device__ __forceinline__ void barrier_lds() {
 __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const void* __restrict__ h0, bf16* __restrict__ o, void* __restrict__ ht, bool sbf, Work<bf16> ws,
-    ChunkMap cm, int Hqk, int Hv, int G) {
+    ChunkMap cm, int Hqk, int Hv, int G, bf16* __restrict__ states) {
   using namespace split;
   __shared__ Smem sm;
 
@@ -927,6 +937,12 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
     barrier_lds();
     for (int i = 0; i <= nch; ++i) {
       if (i < nch) {
+        if (states) {
+          // the state entering chunk i, for the backward pass
+          const size_t srow = (((size_t)(cid0 + i) * Hv + h) * kD + dv0 + r) * kD;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) store_state4(states, srow + prow(t, 4 * g), ST[t], true);
+        }
         const Slot& S = sm.slot[i % kSlots];
         const GateSlot& Gd = sm.gd[i % kGdSlots];
         Hand& H = sm.hand[i & 1][s];
@@ -1041,10 +1057,11 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
   }
 
   // -------------------------------------------------------------- output wave
-  // Chunk c's O at iteration c+1 for both value slices.
+  // Chunk c's O at iteration c+1 for both value slices (no outputs when o is
+  // null: the state-checkpoint pass of the backward).
   barrier_lds();
   for (int i = 0; i <= nch; ++i) {
-    if (i >= 1) {
+    if (i >= 1 && o) {
       const int c = i - 1;
       int tok0, L;
       chunk_of(cm, cid0 + c, tok0, L);
@@ -1197,7 +1214,7 @@ __global__ __launch_bounds__(256) void gate_norm_kernel(bf16* __restrict__ o,
 template <typename E>
 static hipError_t launch_prepare_t(const PrefillLaunch& a, hipStream_t st) {
   if (a.nc_launch <= 0) return hipSuccess;
-  Work<E> ws{(E*)a.Tt, (E*)a.M, a.gam, a.dec};
+  Work<E> ws{(E*)a.Tt, (E*)a.M, a.gam, a.dec, (E*)a.N};
   dim3 grid((unsigned)a.nc_launch, (unsigned)a.Hqk), block(256);
   hipLaunchKernelGGL(prepare_kernel<E>, grid, block, 0, st, (const E*)a.q, (const E*)a.k,
                      a.alpha, a.beta, ws, a.cm, a.Hqk, a.Hv, a.Hv / a.Hqk, a.solve_only);
@@ -1207,7 +1224,7 @@ static hipError_t launch_prepare_t(const PrefillLaunch& a, hipStream_t st) {
 template <typename E, int NW, bool GATED>
 static hipError_t launch_scan_t(const PrefillLaunch& a, hipStream_t st) {
   if (a.nseq <= 0) return hipSuccess;
-  Work<E> ws{(E*)a.Tt, (E*)a.M, a.gam, a.dec};
+  Work<E> ws{(E*)a.Tt, (E*)a.M, a.gam, a.dec, nullptr};
   constexpr int NSL = kD / (16 * NW);
   int nlin = a.Hv * NSL;
   if ((a.Hqk & 7) == 0) nlin = ((nlin + 7) / 8) * 8;
@@ -1224,13 +1241,13 @@ hipError_t launch_prepare(const PrefillLaunch& a, hipStream_t st) {
 
 static hipError_t launch_scan_split(const PrefillLaunch& a, hipStream_t st) {
   if (a.nseq <= 0) return hipSuccess;
-  Work<bf16> ws{(bf16*)a.Tt, (bf16*)a.M, a.gam, a.dec};
+  Work<bf16> ws{(bf16*)a.Tt, (bf16*)a.M, a.gam, a.dec, nullptr};
   int nlin = a.Hv * split::kNsl;
   if ((a.Hqk & 7) == 0) nlin = ((nlin + 7) / 8) * 8;
   dim3 grid((unsigned)nlin, (unsigned)a.nseq), block(64 * split::kWaves);
   hipLaunchKernelGGL(scan_split_kernel, grid, block, 0, st, (const bf16*)a.q, (const bf16*)a.k,
                      (const bf16*)a.v, a.h0, (bf16*)a.o, a.ht, a.state_bf16, ws, a.cm, a.Hqk, a.Hv,
-                     a.Hv / a.Hqk);
+                     a.Hv / a.Hqk, (bf16*)a.states);
   return hipGetLastError();
 }
 
