@@ -50,6 +50,22 @@ def scan_flops(T, B=1):
     return nc * HV * (6 * C * D * D + 4 * C * C * D)
 
 
+def backward_flops(T, B=1):
+    """Algorithmic FLOPs of one backward call (gdn_prefill_chunked_bwd), per
+    chunk and value head: the state-checkpoint pass 4Cd^2 + 2C^2d, the reverse
+    state-gradient chain 6Cd^2 + 4C^2d, the per-chunk gradients 10Cd^2 +
+    16C^2d, the in-chunk solve C^3/3; per chunk and query/key head the Gram
+    matrices of prepare and of the gradient kernel, 8C^2d."""
+    nc = B * ((T + C - 1) // C)
+    return nc * (HV * (20 * C * D * D + 22 * C * C * D + C ** 3 / 3) + HQK * 8 * C * C * D)
+
+
+def grad_kernel_flops(T, B=1):
+    """Algorithmic FLOPs of the per-chunk gradient kernel per launch."""
+    nc = B * ((T + C - 1) // C)
+    return nc * HV * (10 * C * D * D + 16 * C * C * D)
+
+
 def decode_state_bytes(B):
     return 2 * B * HV * D * D * 4
 
@@ -182,6 +198,31 @@ def timed_speculative(gdn, B, n, rounds, warmup):
     return dict(ms=ms, gbs=nbytes / (ms * 1e-3) / 1e9, tokens_per_s=B * n / (ms * 1e-3))
 
 
+def timed_backward(gdn, T, steps, warmup):
+    """One backward call of the T-token bf16 training shape (zero initial
+    state, no final-state gradient), inputs and workspace resident."""
+    d = {k: (v.to("cuda") if isinstance(v, torch.Tensor) else v)
+         for k, v in synth.backward_inputs(1, T, torch.bfloat16, seed=1011).items()}
+    ws = torch.empty(gdn.prefill_bwd_workspace_bytes(1, T, HQK, HV, D, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+    args = (d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["do"], None, None)
+    g = gdn.prefill_backward(*args, workspace=ws)
+    for _ in range(warmup):
+        gdn.prefill_backward(*args, grads=g, workspace=ws)
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        gdn.prefill_backward(*args, grads=g, workspace=ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return dict(ms=ms, tokens_per_s=T / (ms * 1e-3),
+                tflops=backward_flops(T) / (ms * 1e-3) / 1e12)
+
+
 def cpu_baseline(inp, T_sample, min_seconds=10.0, max_calls=64):
     """The float64 oracle, untuned, on the same workload: the first T_sample
     tokens of every value head, called repeatedly until about min_seconds of
@@ -261,6 +302,11 @@ def main():
     log("speculative verify + commit of 3 tokens x 64 sequences: %.4f ms, %.1f GB/s"
         % (spec["ms"], spec["gbs"]))
 
+    log("backward T=%d (training shape): 20 calls" % T)
+    bwd = timed_backward(gdn, T, 20, 3)
+    log("backward %.3f ms, %.2f M tokens/s, %.1f TFLOP/s" %
+        (bwd["ms"], bwd["tokens_per_s"] / 1e6, bwd["tflops"]))
+
     out = {
         "metric": "GDN prefill tokens/s @T=8192 (% MFMA peak) + decode state GB/s (% HBM peak)",
         "value": tok_s,
@@ -307,6 +353,13 @@ def main():
                                       "workload": "64 sequences, verify of 3 drafted tokens then "
                                                   "commit of all 3, fp32 state"}},
     }
+    out["backward"] = {
+        "workload": "gradients of the T=8192 prefill (dq, dk, dv, dalpha, dbeta, dh0), bf16, "
+                    "zero initial state, upstream gradient of o only",
+        "ms_per_call": bwd["ms"], "tokens_per_s": bwd["tokens_per_s"],
+        "tflops_algorithmic": bwd["tflops"], "frac_bf16_mfma_peak": bwd["tflops"] / PEAK_BF16_TFLOPS,
+        "gflop_per_call": backward_flops(T) / 1e9,
+        "grad_kernel_gflop_per_launch": grad_kernel_flops(T) / 1e9}
     if args.extended:
         log("extended: T=262144")
         inp3 = {k: (v.to("cuda") if isinstance(v, torch.Tensor) else v)

@@ -81,6 +81,16 @@ template <typename E> __device__ __forceinline__ Fr<E> acc_frag(const f32x4* t, 
   else return t[kb];
 }
 
+// Position of the 16-row tile mt against the K block kb of a 64x64
+// triangular operand: wholly above the diagonal (every K index > every row) or
+// wholly below it (every K index < every row).
+template <typename E> constexpr bool blk_above(int mt, int kb) {
+  return FragOf<E>::KB * kb > 16 * mt + 15;
+}
+template <typename E> constexpr bool blk_below(int mt, int kb) {
+  return FragOf<E>::KB * kb + FragOf<E>::KB - 1 < 16 * mt;
+}
+
 template <typename E> __device__ __forceinline__ void frag_zero(Fr<E>& f, int j) {
   if constexpr (sizeof(E) == 2) f[j] = (bf16)0.f;
   else f[j] = 0.f;
@@ -218,10 +228,18 @@ __device__ __forceinline__ void stage(Lds<E, W> dst, const E* src, int64_t ld, i
   }
 }
 
-// Sum over the 16 lanes of a lane group (same g).
+// Sum over the 16 lanes of a lane group (same g): four DPP row rotations
+// (VALU only; every lane of the row ends with the full sum).
+template <int N>
+__device__ __forceinline__ float row_ror(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                               0x120 + N, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float sum16(float x) {
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) x += __shfl_xor(x, o, 64);
+  x += row_ror<8>(x);
+  x += row_ror<4>(x);
+  x += row_ror<2>(x);
+  x += row_ror<1>(x);
   return x;
 }
 __device__ __forceinline__ float wave_sum(float x) {
@@ -463,12 +481,13 @@ __device__ __forceinline__ void wait_copies() {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// 64 rows (rows >= L repeat row L-1) of a bf16 matrix with W columns into the
-// Lds<bf16, W> layout at dst; wave w of nw issues copies w, w + nw, ...
-template <int W>
+// ROWS rows (rows >= L repeat row L-1) of a bf16 matrix with W columns into the
+// Lds<bf16, W> layout at dst; wave w of nw issues copies w, w + nw, ...  (w
+// must be wave-uniform: the LDS destination goes through M0).
+template <int W, int ROWS = kC>
 __device__ __forceinline__ void copy_rows(const bf16* src, int64_t ld, int L, bf16* dst, int w,
                                           int nw) {
-  constexpr int RPK = 1024 / (2 * W), NIT = kC / RPK;
+  constexpr int RPK = 1024 / (2 * W), NIT = ROWS / RPK;
   constexpr int rpl = 128 / W, nb = W / 16;
   const int l = lane_id();
   const int rin = (16 * l) / (2 * W), pp = ((16 * l) % (2 * W)) / 16;
@@ -499,7 +518,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chain_bf16_kernel(
   typedef bf16 E;
   constexpr int R = 16 * NW, KB = 32;
   __shared__ ChainDmaBuf<NW> buf[2];
-  const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(wave_id()), l = lane_id(), r = l & 15, g = l >> 4;
   const int h = blockIdx.y, b = blockIdx.z, gq = h / (Hv / Hqk);
   const int rbase = R * blockIdx.x, dv0 = rbase + 16 * w;
 
@@ -559,7 +578,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_chain_bf16_kernel(
 #pragma unroll
       for (int kb = 0; kb < kD / KB; ++kb) p = mma(p, Ks.rm(16 * mt + r, KB * kb), acc_frag<E>(DT, kb));
 #pragma unroll
-      for (int kb = 0; kb < kC / KB; ++kb) m = mma(m, Ms.cm(16 * mt + r, KB * kb), OB[kb]);
+      for (int kb = 0; kb < kC / KB; ++kb)
+        if (!blk_below<E>(mt, kb)) m = mma(m, Ms.cm(16 * mt + r, KB * kb), OB[kb]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) dD[mt][i] = m[i] + B_.dc[16 * mt + 4 * g + i] * p[i];
     }
@@ -568,7 +588,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_chain_bf16_kernel(
     for (int mt = 0; mt < 4; ++mt) {
       f32x4 y = zero4();
 #pragma unroll
-      for (int kb = 0; kb < kC / KB; ++kb) y = mma(y, Ns.cm(16 * mt + r, KB * kb), acc_frag<E>(dD, kb));
+      for (int kb = 0; kb < kC / KB; ++kb)
+        if (!blk_below<E>(mt, kb)) y = mma(y, Ns.cm(16 * mt + r, KB * kb), acc_frag<E>(dD, kb));
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tok = 16 * mt + 4 * g + i;
@@ -676,24 +697,12 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
     __syncthreads();
   }
 
-  // This wave's two 64x64 tiles (ti, tj), and K K^T / Q K^T on them.
+  // This wave's two 64x64 tiles (ti, tj) of the phase-1.5 products.
   int ti[2], tj[2];
-  f32x4 KK[2], QK[2];
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
-    const int t = 2 * w + x;
-    ti[x] = t >> 2;
-    tj[x] = t & 3;
-    KK[x] = zero4();
-    QK[x] = zero4();
-    if (tj[x] <= ti[x]) {
-#pragma unroll
-      for (int kb = 0; kb < kD / KB; ++kb) {
-        const Fr<E> bk = mK.rm(16 * tj[x] + r, KB * kb);
-        KK[x] = mma(KK[x], mK.rm(16 * ti[x] + r, KB * kb), bk);
-        QK[x] = mma(QK[x], mQ.rm(16 * ti[x] + r, KB * kb), bk);
-      }
-    }
+    ti[x] = (2 * w + x) >> 2;
+    tj[x] = (2 * w + x) & 3;
   }
 
   f32x4 dQ[4], dK[4];
@@ -732,14 +741,17 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
       else return Glb<E>{Mw + hc * kC * kC, kC, kC};
     }();
 
-    // ---- stage
+    // ---- stage (bf16: copied straight into LDS.  Rows of dO and V beyond L
+    // repeat the last token; they only ever meet zero rows of K and Q, zero
+    // beta and the identity rows of N, so nothing they touch is stored.)
     if constexpr (BF) {
-      stage<E, 128, kD, NT>(Lds<E, 128>{sm.S0}, Sc + hc * kD * kD, kD, kD);
-      stage<E, 128, kD, NT>(Lds<E, 128>{sm.dS}, dSc + hc * kD * kD, kD, kD);
-      stage<E, 128, kC, NT>(Lds<E, 128>{sm.dO}, oh, (int64_t)Hv * kD, L);
-      stage<E, 128, kC, NT>(Lds<E, 128>{sm.u1.V}, vh, (int64_t)Hv * kD, L);
-      stage<E, 64, kC, NT>(Lds<E, 64>{sm.u2.nm.N}, Nw + hc * kC * kC, kC, kC);
-      stage<E, 64, kC, NT>(Lds<E, 64>{sm.u2.nm.M}, Mw + hc * kC * kC, kC, kC);
+      const int wu = __builtin_amdgcn_readfirstlane(w);
+      copy_rows<128, kD>(Sc + hc * kD * kD, kD, kD, sm.S0, wu, kGW);
+      copy_rows<128, kD>(dSc + hc * kD * kD, kD, kD, sm.dS, wu, kGW);
+      copy_rows<128>(oh, (int64_t)Hv * kD, L, sm.dO, wu, kGW);
+      copy_rows<128>(vh, (int64_t)Hv * kD, L, sm.u1.V, wu, kGW);
+      copy_rows<64>(Nw + hc * kC * kC, kC, kC, sm.u2.nm.N, wu, kGW);
+      copy_rows<64>(Mw + hc * kC * kC, kC, kC, sm.u2.nm.M, wu, kGW);
     }
     if (w == 0) {
       const float a = l < L ? alpha[(tok0 + l) * Hv + h] : 1.f;
@@ -751,6 +763,7 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
       sm.bt[l] = l < L ? beta[(tok0 + l) * Hv + h] : 0.f;
       sm.al[l] = a;
     }
+    if constexpr (BF) wait_copies();
     __syncthreads();
 
     // ---- phase 1: this wave's value columns c = 16w + r
@@ -783,7 +796,8 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
         for (int mt = 0; mt < 4; ++mt) {
           f32x4 d = zero4();
 #pragma unroll
-          for (int kb = 0; kb < kC / KB; ++kb) d = mma(d, mN.rm(16 * mt + r, KB * kb, ln), acc_frag<E>(XB, kb));
+          for (int kb = 0; kb < kC / KB; ++kb)
+            if (!blk_above<E>(mt, kb)) d = mma(d, mN.rm(16 * mt + r, KB * kb, ln), acc_frag<E>(XB, kb));
           Dl[mt] = d;
         }
       }
@@ -795,7 +809,8 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
         for (int kb = 0; kb < kD / KB; ++kb)
           kds = mma(kds, mK.rm(16 * mt + r, KB * kb, ln), mdS.rm(c, KB * kb, ln));
 #pragma unroll
-        for (int kb = 0; kb < kC / KB; ++kb) m = mma(m, mM.cm(16 * mt + r, KB * kb, ln), mO.cm(c, KB * kb, ln));
+        for (int kb = 0; kb < kC / KB; ++kb)
+          if (!blk_below<E>(mt, kb)) m = mma(m, mM.cm(16 * mt + r, KB * kb, ln), mO.cm(c, KB * kb, ln));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int tok = 16 * mt + 4 * g + i;
@@ -809,7 +824,8 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
       for (int mt = 0; mt < 4; ++mt) {
         f32x4 y = zero4();
 #pragma unroll
-        for (int kb = 0; kb < kC / KB; ++kb) y = mma(y, mN.cm(16 * mt + r, KB * kb, ln), acc_frag<E>(dD, kb));
+        for (int kb = 0; kb < kC / KB; ++kb)
+          if (!blk_below<E>(mt, kb)) y = mma(y, mN.cm(16 * mt + r, KB * kb, ln), acc_frag<E>(dD, kb));
         Y[mt] = y;
       }
       // beta and gate partials: Y.X and -gamma beta Y.(K S0^T) = -beta Y.(V - X)
@@ -849,18 +865,25 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
       for (int x = 0; x < kGW; ++x) s += sm.u3.part[x][qn][t];
       sm.fin[qn == 0 ? 1 : (qn == 1 ? 0 : 2)][t] = s;
     }
-    // ---- phase 1.5: dO Dl^T and Y Dl^T on this wave's tiles
-    f32x4 OD[2], YD[2];
+    // ---- phase 1.5: dO Dl^T and Y Dl^T on this wave's tiles, with K K^T
+    // and Q K^T on the same tiles (recomputed per head: cheaper than keeping
+    // them live)
+    f32x4 OD[2], YD[2], KK[2], QK[2];
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
       OD[x] = zero4();
       YD[x] = zero4();
+      KK[x] = zero4();
+      QK[x] = zero4();
       if (tj[x] <= ti[x]) {
 #pragma unroll
         for (int kb = 0; kb < kD / KB; ++kb) {
           const Fr<E> bd = Dls.rm(16 * tj[x] + r, KB * kb, ln);
           OD[x] = mma(OD[x], mO.rm(16 * ti[x] + r, KB * kb, ln), bd);
           YD[x] = mma(YD[x], Ys.rm(16 * ti[x] + r, KB * kb, ln), bd);
+          const Fr<E> bk = mK.rm(16 * tj[x] + r, KB * kb, ln);
+          KK[x] = mma(KK[x], mK.rm(16 * ti[x] + r, KB * kb, ln), bk);
+          QK[x] = mma(QK[x], mQ.rm(16 * ti[x] + r, KB * kb, ln), bk);
         }
       }
     }
@@ -969,19 +992,29 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           const int row = 16 * mt + r;
-          Fr<E> e_rm = Es.rm(row, KB * kb, ln), e_cm = Es.cm(row, KB * kb, ln);
-          Fr<E> lowr = e_rm, lowt = e_cm, sym;
+          if (blk_below<E>(mt, kb)) {          // every K index below the row
+            const Fr<E> e_rm = Es.rm(row, KB * kb, ln), e_cm = Es.cm(row, KB * kb, ln);
+            dQ[mt] = mma(dQ[mt], e_rm, bk);
+            dK[mt] = mma(dK[mt], e_cm, bk);
+          } else if (blk_above<E>(mt, kb)) {   // every K index above the row
+            const Fr<E> e_rm = Es.rm(row, KB * kb, ln), e_cm = Es.cm(row, KB * kb, ln);
+            dK[mt] = mma(dK[mt], e_cm, bq);
+            dK[mt] = mma(dK[mt], e_rm, bk);
+          } else {
+            const Fr<E> e_rm = Es.rm(row, KB * kb, ln), e_cm = Es.cm(row, KB * kb, ln);
+            Fr<E> lowr = e_rm, lowt = e_cm, sym;
 #pragma unroll
-          for (int e = 0; e < NS; ++e) {
-            const int kk = KB * kb + kslot<E>(g, e);
-            if (kk > row) frag_zero<E>(lowr, e);
-            if (kk < row) frag_zero<E>(lowt, e);
-            sym[e] = kk > row ? e_rm[e] : e_cm[e];
-            if (kk == row) frag_zero<E>(sym, e);
+            for (int e = 0; e < NS; ++e) {
+              const int kk = KB * kb + kslot<E>(g, e);
+              if (kk > row) frag_zero<E>(lowr, e);
+              if (kk < row) frag_zero<E>(lowt, e);
+              sym[e] = kk > row ? e_rm[e] : e_cm[e];
+              if (kk == row) frag_zero<E>(sym, e);
+            }
+            dQ[mt] = mma(dQ[mt], lowr, bk);
+            dK[mt] = mma(dK[mt], lowt, bq);
+            dK[mt] = mma(dK[mt], sym, bk);
           }
-          dQ[mt] = mma(dQ[mt], lowr, bk);
-          dK[mt] = mma(dK[mt], lowt, bq);
-          dK[mt] = mma(dK[mt], sym, bk);
         }
       }
     }

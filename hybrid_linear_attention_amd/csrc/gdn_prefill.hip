@@ -132,11 +132,10 @@ __device__ __forceinline__ f32x4 mm16_lds(const float* A, int arow0, int acol0,
 //     place and writes Tt.
 // LDS is 53,760 bytes for bf16 (three workgroups share a CU) and 71,168 for
 // fp32 (two).
-template <typename E>
+template <typename E, bool solve_only>
 __global__ __launch_bounds__(256, sizeof(E) == 2 ? 3 : 2) void prepare_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const float* __restrict__ alpha,
-    const float* __restrict__ beta, Work<E> ws, ChunkMap cm, int Hqk, int Hv, int G,
-    bool solve_only) {
+    const float* __restrict__ beta, Work<E> ws, ChunkMap cm, int Hqk, int Hv, int G) {
   constexpr bool BF = sizeof(E) == 2;
   constexpr int LDK = PrepSmem<E>::LDK;
   constexpr int NB = PrepSmem<E>::NB;
@@ -786,6 +785,7 @@ __device__ __forceinline__ void barrier_lds() {
 // instruction `it` fills LDS bytes [1024 it, 1024 it + 1024).
 }  // namespace split
 
+template <bool CKPT>
 __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const void* __restrict__ h0, bf16* __restrict__ o, void* __restrict__ ht, bool sbf, Work<bf16> ws,
@@ -937,7 +937,7 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
     barrier_lds();
     for (int i = 0; i <= nch; ++i) {
       if (i < nch) {
-        if (states) {
+        if constexpr (CKPT) {
           // the state entering chunk i, for the backward pass
           const size_t srow = (((size_t)(cid0 + i) * Hv + h) * kD + dv0 + r) * kD;
 #pragma unroll
@@ -1057,11 +1057,11 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
   }
 
   // -------------------------------------------------------------- output wave
-  // Chunk c's O at iteration c+1 for both value slices (no outputs when o is
-  // null: the state-checkpoint pass of the backward).
+  // Chunk c's O at iteration c+1 for both value slices (no outputs in the
+  // state-checkpoint pass of the backward).
   barrier_lds();
   for (int i = 0; i <= nch; ++i) {
-    if (i >= 1 && o) {
+    if (i >= 1 && !CKPT) {
       const int c = i - 1;
       int tok0, L;
       chunk_of(cm, cid0 + c, tok0, L);
@@ -1216,8 +1216,12 @@ static hipError_t launch_prepare_t(const PrefillLaunch& a, hipStream_t st) {
   if (a.nc_launch <= 0) return hipSuccess;
   Work<E> ws{(E*)a.Tt, (E*)a.M, a.gam, a.dec, (E*)a.N};
   dim3 grid((unsigned)a.nc_launch, (unsigned)a.Hqk), block(256);
-  hipLaunchKernelGGL(prepare_kernel<E>, grid, block, 0, st, (const E*)a.q, (const E*)a.k,
-                     a.alpha, a.beta, ws, a.cm, a.Hqk, a.Hv, a.Hv / a.Hqk, a.solve_only);
+  if (a.solve_only)
+    hipLaunchKernelGGL((prepare_kernel<E, true>), grid, block, 0, st, (const E*)a.q,
+                       (const E*)a.k, a.alpha, a.beta, ws, a.cm, a.Hqk, a.Hv, a.Hv / a.Hqk);
+  else
+    hipLaunchKernelGGL((prepare_kernel<E, false>), grid, block, 0, st, (const E*)a.q,
+                       (const E*)a.k, a.alpha, a.beta, ws, a.cm, a.Hqk, a.Hv, a.Hv / a.Hqk);
   return hipGetLastError();
 }
 
@@ -1245,9 +1249,14 @@ static hipError_t launch_scan_split(const PrefillLaunch& a, hipStream_t st) {
   int nlin = a.Hv * split::kNsl;
   if ((a.Hqk & 7) == 0) nlin = ((nlin + 7) / 8) * 8;
   dim3 grid((unsigned)nlin, (unsigned)a.nseq), block(64 * split::kWaves);
-  hipLaunchKernelGGL(scan_split_kernel, grid, block, 0, st, (const bf16*)a.q, (const bf16*)a.k,
-                     (const bf16*)a.v, a.h0, (bf16*)a.o, a.ht, a.state_bf16, ws, a.cm, a.Hqk, a.Hv,
-                     a.Hv / a.Hqk, (bf16*)a.states);
+  if (a.states)
+    hipLaunchKernelGGL(scan_split_kernel<true>, grid, block, 0, st, (const bf16*)a.q,
+                       (const bf16*)a.k, (const bf16*)a.v, a.h0, (bf16*)a.o, a.ht, a.state_bf16, ws,
+                       a.cm, a.Hqk, a.Hv, a.Hv / a.Hqk, (bf16*)a.states);
+  else
+    hipLaunchKernelGGL(scan_split_kernel<false>, grid, block, 0, st, (const bf16*)a.q,
+                       (const bf16*)a.k, (const bf16*)a.v, a.h0, (bf16*)a.o, a.ht, a.state_bf16, ws,
+                       a.cm, a.Hqk, a.Hv, a.Hv / a.Hqk, nullptr);
   return hipGetLastError();
 }
 

@@ -260,3 +260,50 @@ def test_binding_rejects_bad_tensors(gdn):
     with pytest.raises(ValueError):
         gdn.decode_step(torch.zeros(2, 16, 128), torch.zeros(2, 16, 128), torch.zeros(2, 48, 128),
                         torch.zeros(2, 48), torch.zeros(2, 48), torch.zeros(2, 48, 128, 64))
+
+
+def bwd_call(lib, **kw):
+    args = dict(q=addr(0), k=addr(1), v=addr(2), alpha=addr(3), beta=addr(4), h0=addr(5),
+                do=addr(6), dht=addr(7), dq=addr(8), dk=addr(9), dv=addr(10), da=addr(11),
+                db=addr(12), dh0=addr(13), B=1, T=128, Hqk=16, Hv=48, D=128, dt=BF16,
+                ws=addr(14), ws_bytes=1 << 40, stream=None)
+    args.update(kw)
+    a = args
+    return lib.gdn_prefill_chunked_bwd(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["h0"],
+                                       a["do"], a["dht"], a["dq"], a["dk"], a["dv"], a["da"],
+                                       a["db"], a["dh0"], a["B"], a["T"], a["Hqk"], a["Hv"],
+                                       a["D"], a["dt"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=64), EUNSUP),
+    (dict(dt=7), EUNSUP),
+    (dict(Hv=47), ESHAPE),
+    (dict(T=-1), ESHAPE),
+    (dict(do=None), ENULL),
+    (dict(dq=None), ENULL),
+    (dict(db=None), ENULL),
+    (dict(ws=None), EWS),
+    (dict(ws_bytes=1000), EWS),
+    (dict(do=addr(6, 8)), EALIGN),
+    (dict(dh0=addr(13, 4)), EALIGN),
+    (dict(da=addr(11, 2)), EALIGN),
+    (dict(dq=addr(0, 512)), EALIAS),          # dq inside q
+    (dict(dv=addr(8, 256)), EALIAS),          # dv inside dq
+    (dict(dh0=addr(7)), EALIAS),              # dh0 is dht
+    (dict(ws=addr(10, 4096)), EALIAS),        # workspace inside dv
+])
+def test_backward_validation(lib, kw, code):
+    assert bwd_call(lib, **kw) == code
+
+
+def test_backward_workspace_and_empty_batch(gdn, lib):
+    # per chunk: the forward workspace, N (48 x 64 x 64) and two 48 x 128 x 128
+    # state stacks, bf16
+    w1 = gdn.prefill_bwd_workspace_bytes(1, 64, 16, 48)
+    w2 = gdn.prefill_bwd_workspace_bytes(1, 128, 16, 48)
+    fwd = gdn.prefill_workspace_bytes(1, 128, 16, 48) - gdn.prefill_workspace_bytes(1, 64, 16, 48)
+    assert w2 - w1 == fwd + 48 * 4096 * 2 + 2 * 48 * 128 * 128 * 2
+    assert gdn.prefill_bwd_workspace_bytes(1, 0, 16, 48) == 0
+    assert gdn.prefill_bwd_workspace_bytes(1, 64, 16, 48, D=64) == 0
+    assert bwd_call(lib, B=0) == OK
