@@ -44,6 +44,10 @@ gate_rmsnorm(o, gate, weight, eps)           -> y           NumPy float64
 np_prefill(q, k, v, alpha, beta, h0=None)    -> (o, ht)     NumPy twin (tiny sizes)
 subset_heads(...)                                           gather for sampled checks
 
+The gated attention layer of the same stack has its own float64 oracle in
+``oracle/attention.py`` (QK-Norm, partial RoPE, causal GQA softmax attention,
+sigmoid output gate), pinned in ``tests/test_attention_oracle.py``.
+
 Parity status: every function is pinned by tests in tests/test_oracle_pins.py
 (closed forms, invariants, brute force, textbook identities); see the module
 docstring there for which pin covers which possible mistake.
