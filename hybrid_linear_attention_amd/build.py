@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgdn.so")
 ARCH = "gfx950"
 
-SOURCES = ["gdn_api.hip", "gdn_backward.hip", "gdn_decode.hip", "gdn_prefill.hip"]
+SOURCES = ["gdn_api.hip", "gdn_attention.hip", "gdn_backward.hip", "gdn_decode.hip",
+           "gdn_prefill.hip"]
 
 COMMON = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",

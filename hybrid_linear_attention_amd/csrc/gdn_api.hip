@@ -507,4 +507,150 @@ gdn_status gdn_prefill_chunked_bwd(const void* q, const void* k, const void* v,
   return fail_hip(gdn::launch_backward(bl, st));
 }
 
+namespace {
+constexpr int kAttnD = 256;
+
+gdn_status check_attn_dims(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t rope_dim,
+                           float theta, float eps, gdn_dtype dt) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return GDN_ERR_SHAPE;
+  if (D != kAttnD || Hq / Hkv > 8 || Hq > 4096) return GDN_ERR_UNSUPPORTED;
+  if (dt != GDN_F32 && dt != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+  if (rope_dim < 0 || rope_dim > kAttnD || rope_dim % 8 != 0) return GDN_ERR_UNSUPPORTED;
+  if (!(theta > 0.f) || !(theta < 3.0e38f) || !(eps >= 0.f)) return GDN_ERR_SHAPE;
+  return GDN_OK;
+}
+
+// Attention workspace: rotated queries, then (prefill) rotated keys or
+// (decode) the split partials.
+size_t attn_prefill_ws(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, gdn_dtype dt) {
+  return round256((size_t)B * T * Hq * kAttnD * esize(dt)) +
+         round256((size_t)B * T * Hkv * kAttnD * esize(dt));
+}
+size_t attn_decode_ws(int64_t B, int64_t cache_len, int64_t Hq, gdn_dtype dt) {
+  const int64_t ns = gdn::attn_decode_splits((int)cache_len);
+  return round256((size_t)B * Hq * kAttnD * esize(dt)) + 2 * round256((size_t)B * Hq * ns * 4) +
+         round256((size_t)B * Hq * ns * kAttnD * 4);
+}
+}  // namespace
+
+size_t gdn_attn_prefill_workspace_bytes(int32_t B, int32_t T, int32_t H_q, int32_t H_kv,
+                                        int32_t D, gdn_dtype dt) {
+  if (check_attn_dims(B, H_q, H_kv, D, 0, 1.f, 0.f, dt) != GDN_OK || T < 0) return 0;
+  return attn_prefill_ws(B, T, H_q, H_kv, dt);
+}
+
+size_t gdn_attn_decode_workspace_bytes(int32_t B, int32_t cache_len, int32_t H_q, int32_t H_kv,
+                                       int32_t D, gdn_dtype dt) {
+  if (check_attn_dims(B, H_q, H_kv, D, 0, 1.f, 0.f, dt) != GDN_OK || cache_len <= 0) return 0;
+  return attn_decode_ws(B, cache_len, H_q, dt);
+}
+
+gdn_status gdn_attn_prefill(const void* q, const void* k, const void* v, const void* gate,
+                            const float* q_norm_w, const float* k_norm_w, float norm_eps, void* o,
+                            void* k_cache, void* v_cache, int32_t cache_len, int32_t B, int32_t T,
+                            int32_t H_q, int32_t H_kv, int32_t D, int32_t rope_dim,
+                            float rope_theta, gdn_dtype dt, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  gdn_status s = check_attn_dims(B, H_q, H_kv, D, rope_dim, rope_theta, norm_eps, dt);
+  if (s != GDN_OK) return s;
+  if (T < 0) return GDN_ERR_SHAPE;
+  if ((int64_t)B * T > (int64_t(1) << 31) / 64) return GDN_ERR_UNSUPPORTED;
+  if (B == 0 || T == 0) return GDN_OK;
+  if (!q || !k || !v || !gate || !o) return GDN_ERR_NULL;
+  if ((k_cache == nullptr) != (v_cache == nullptr)) return GDN_ERR_NULL;
+  const bool cached = k_cache != nullptr;
+  if (cached && cache_len < T) return GDN_ERR_SHAPE;
+  const int64_t clen = cached ? cache_len : T;
+  const size_t need = attn_prefill_ws(B, T, H_q, H_kv, dt);
+  if (!workspace) return GDN_ERR_WORKSPACE;
+  if (workspace_bytes < need) return GDN_ERR_WORKSPACE;
+  const void* p16[] = {q, k, v, gate, o, k_cache, v_cache, workspace};
+  for (const void* p : p16)
+    if (!aligned(p, 16)) return GDN_ERR_ALIGN;
+  if (!aligned(q_norm_w, 4) || !aligned(k_norm_w, 4)) return GDN_ERR_ALIGN;
+  const int64_t es = (int64_t)esize(dt), nt = (int64_t)B * T;
+  const Range ins[] = {span(q, nt * H_q * kAttnD * es), span(k, nt * H_kv * kAttnD * es),
+                       span(v, nt * H_kv * kAttnD * es), span(gate, nt * H_q * kAttnD * es),
+                       span(q_norm_w, q_norm_w ? kAttnD * 4 : 0),
+                       span(k_norm_w, k_norm_w ? kAttnD * 4 : 0)};
+  const Range outs[] = {span(o, nt * H_q * kAttnD * es),
+                        span(k_cache, (int64_t)B * clen * H_kv * kAttnD * es),
+                        span(v_cache, (int64_t)B * clen * H_kv * kAttnD * es),
+                        span(workspace, (int64_t)need)};
+  for (size_t a = 0; a < 4; ++a) {
+    for (const Range& in : ins)
+      if (overlap(outs[a], in)) return GDN_ERR_ALIAS;
+    for (size_t c = a + 1; c < 4; ++c)
+      if (overlap(outs[a], outs[c])) return GDN_ERR_ALIAS;
+  }
+  char* ws = static_cast<char*>(workspace);
+  gdn::AttnLaunch a{};
+  a.q = q; a.k = k; a.v = v; a.gate = gate; a.qw = q_norm_w; a.kw = k_norm_w;
+  a.eps = norm_eps; a.theta = rope_theta; a.rope_dim = rope_dim; a.pos = nullptr;
+  a.qrot = ws;
+  a.kc = cached ? k_cache : ws + round256((size_t)nt * H_q * kAttnD * es);
+  a.vc_write = cached ? v_cache : nullptr;
+  a.vc_read = cached ? v_cache : v;
+  a.o = o;
+  a.B = B; a.T = T; a.cache_len = (int)clen; a.Hq = H_q; a.Hkv = H_kv;
+  a.decode = false;
+  a.bf16_io = dt == GDN_BF16;
+  return fail_hip(gdn::launch_attention(a, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_attn_decode(const void* q, const void* k, const void* v, const void* gate,
+                           const float* q_norm_w, const float* k_norm_w, float norm_eps, void* o,
+                           void* k_cache, void* v_cache, const int32_t* pos, int32_t cache_len,
+                           int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t rope_dim,
+                           float rope_theta, gdn_dtype dt, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  gdn_status s = check_attn_dims(B, H_q, H_kv, D, rope_dim, rope_theta, norm_eps, dt);
+  if (s != GDN_OK) return s;
+  if (cache_len <= 0) return GDN_ERR_SHAPE;
+  if ((int64_t)B * cache_len > (int64_t(1) << 31) / 64) return GDN_ERR_UNSUPPORTED;
+  if (B == 0) return GDN_OK;
+  if (!q || !k || !v || !gate || !o || !k_cache || !v_cache || !pos) return GDN_ERR_NULL;
+  const size_t need = attn_decode_ws(B, cache_len, H_q, dt);
+  if (!workspace) return GDN_ERR_WORKSPACE;
+  if (workspace_bytes < need) return GDN_ERR_WORKSPACE;
+  const void* p16[] = {q, k, v, gate, o, k_cache, v_cache, workspace};
+  for (const void* p : p16)
+    if (!aligned(p, 16)) return GDN_ERR_ALIGN;
+  if (!aligned(q_norm_w, 4) || !aligned(k_norm_w, 4) || !aligned(pos, 4)) return GDN_ERR_ALIGN;
+  const int64_t es = (int64_t)esize(dt);
+  const Range ins[] = {span(q, (int64_t)B * H_q * kAttnD * es), span(k, (int64_t)B * H_kv * kAttnD * es),
+                       span(v, (int64_t)B * H_kv * kAttnD * es), span(gate, (int64_t)B * H_q * kAttnD * es),
+                       span(q_norm_w, q_norm_w ? kAttnD * 4 : 0),
+                       span(k_norm_w, k_norm_w ? kAttnD * 4 : 0), span(pos, (int64_t)B * 4)};
+  const Range outs[] = {span(o, (int64_t)B * H_q * kAttnD * es),
+                        span(k_cache, (int64_t)B * cache_len * H_kv * kAttnD * es),
+                        span(v_cache, (int64_t)B * cache_len * H_kv * kAttnD * es),
+                        span(workspace, (int64_t)need)};
+  for (size_t a = 0; a < 4; ++a) {
+    for (const Range& in : ins)
+      if (overlap(outs[a], in)) return GDN_ERR_ALIAS;
+    for (size_t c = a + 1; c < 4; ++c)
+      if (overlap(outs[a], outs[c])) return GDN_ERR_ALIAS;
+  }
+  char* ws = static_cast<char*>(workspace);
+  const int64_t ns = gdn::attn_decode_splits(cache_len);
+  const size_t oq = round256((size_t)B * H_q * kAttnD * es);
+  const size_t om = round256((size_t)B * H_q * ns * 4);
+  gdn::AttnLaunch a{};
+  a.q = q; a.k = k; a.v = v; a.gate = gate; a.qw = q_norm_w; a.kw = k_norm_w;
+  a.eps = norm_eps; a.theta = rope_theta; a.rope_dim = rope_dim; a.pos = pos;
+  a.qrot = ws;
+  a.pm = reinterpret_cast<float*>(ws + oq);
+  a.pl = reinterpret_cast<float*>(ws + oq + om);
+  a.po = reinterpret_cast<float*>(ws + oq + 2 * om);
+  a.kc = k_cache;
+  a.vc_write = v_cache;
+  a.vc_read = v_cache;
+  a.o = o;
+  a.B = B; a.T = 1; a.cache_len = cache_len; a.Hq = H_q; a.Hkv = H_kv;
+  a.decode = true;
+  a.bf16_io = dt == GDN_BF16;
+  return fail_hip(gdn::launch_attention(a, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -1,0 +1,510 @@
+// Gated attention layer of the hybrid stack on gfx950: QK-Norm, partial RoPE,
+// causal grouped-query softmax attention and the sigmoid output gate.
+//
+// Shapes follow the pages: 24 query heads and 4 key/value heads of head dim
+// 256 (page "Inside Qwen3.8-27B: Hybrid DeltaNet Architecture, 256k Context,
+// and 24GB Local Serving", section "The Role of Periodic Gated Attention"),
+// RoPE on a 64-channel subspace with theta = 1e7 (same section), QK-Norm and
+// the sigmoid output gate (card "Qwen3.8 (27B)", "Architecture concepts";
+// page "Qwen3.8 Explained ...", the note on attn_output_gate).  Per (token,
+// head): q, k <- RMSNorm(q, k) * w; the first rope_dim channels rotate in the
+// pairing (j, j + rope_dim/2) by pos * theta^(-2j/rope_dim); then
+// o = softmax_causal(q k^T / sqrt(256)) v, times sigmoid(gate) per channel.
+//
+// Kernels:
+//  * attn_prep: one wave per (token, head) row: RMSNorm, weight, rotation.
+//    The angle is formed and reduced modulo 2 pi in fp64 (at position 262,143
+//    an fp32 angle would be off by ~1e-2 rad), then sin/cos in fp32.  Query
+//    rows go to the workspace, key rows (and the value rows, unchanged) to the
+//    key/value cache at their positions.
+//  * attn_fwd (prefill): one workgroup per (32 query rows, key/value head,
+//    sequence) with two waves per query head of the group (16 rows each), so
+//    every K/V tile staged in LDS serves all six heads.  A wave keeps its
+//    query rows' Q fragments in registers and computes S^T = K Q^T: in that orientation each
+//    lane owns one query column, so the running max and sum of the online
+//    softmax stay in the lane (two shuffles across lane groups per block), and
+//    the probability tiles are directly the B operand of O^T = V^T P^T.  K/V
+//    tiles of 64 keys are double-buffered in LDS with direct global->LDS
+//    copies (bf16).  Only the diagonal block is masked.  Workgroups are issued
+//    longest (latest query block) first.
+//  * attn_decode + attn_combine: split-K over the cached keys.  One workgroup
+//    per (split of 512 keys, key/value head, sequence); 64-key blocks
+//    double-buffered in LDS; the six query heads are the MFMA N dimension and
+//    each of the four waves produces 64 of the 256 output channels; partial
+//    (max, sum, O) per split, merged and gated by the combine kernel.
+#include "gdn_device.hpp"
+#include "gdn_frag.hpp"
+#include "gdn_launch.hpp"
+
+namespace gdn {
+namespace attn {
+using namespace frag;
+
+constexpr int kDh = 256;        // head dim
+constexpr int kKvb = 64;        // keys per prefill block
+constexpr int kSplit = 512;     // keys per decode split
+
+// ------------------------------------------------------------ prep
+// rows: ntok * (Hq + Hkv); row = tok * (Hq + Hkv) + head, heads >= Hq are keys.
+// Token tok = b * T + t sits at position pos[b] (decode) or t (prefill, pos null).
+template <typename E>
+__global__ __launch_bounds__(256) void attn_prep_kernel(
+    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
+    const float* __restrict__ qw, const float* __restrict__ kw, float eps, int rope_dim,
+    float theta, const int32_t* __restrict__ pos, E* __restrict__ qo, E* __restrict__ kc,
+    E* __restrict__ vc, int64_t ntok, int T, int cache_len, int Hq, int Hkv) {
+  const int l = lane_id();
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave_id();
+  const int H = Hq + Hkv;
+  if (row >= ntok * H) return;
+  const int64_t tok = row / H;
+  const int hd = (int)(row - tok * H);
+  const bool is_q = hd < Hq;
+  const int b = (int)(tok / T), t = (int)(tok - (int64_t)b * T);
+  int p = pos ? pos[b] : t;
+  p = min(max(p, 0), cache_len - 1);                // stays inside the cache
+  const E* src = is_q ? q + (tok * Hq + hd) * kDh : k + (tok * Hkv + (hd - Hq)) * kDh;
+  float x[4];
+  if constexpr (sizeof(E) == 2) {
+    const bf16x4 r4 = *reinterpret_cast<const bf16x4*>(src + 4 * l);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = (float)r4[i];
+  } else {
+    const f32x4 r4 = *reinterpret_cast<const f32x4*>(src + 4 * l);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = r4[i];
+  }
+  float ss = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+  ss = wave_sum(ss);
+  const float rs = 1.f / sqrtf(ss * (1.f / kDh) + eps);
+  const float* w = is_q ? qw : kw;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] *= rs * (w ? w[4 * l + i] : 1.f);
+  // rotation: lanes [0, half/4) hold the first halves, their partners sit
+  // half/4 lanes up
+  const int half = rope_dim >> 1, hl = half >> 2;
+  float y[4];
+  const int partner = l < hl ? l + hl : (l < 2 * hl ? l - hl : l);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) y[i] = __shfl(x[i], partner, 64);
+  if (l < 2 * hl) {
+    const bool first = l < hl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = 4 * (first ? l : l - hl) + i;
+      const double inv = exp(-(2.0 * j / rope_dim) * log((double)theta));
+      double ang = (double)p * inv;
+      ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
+      float sn, cs;
+      sincosf((float)ang, &sn, &cs);
+      x[i] = first ? x[i] * cs - y[i] * sn : x[i] * cs + y[i] * sn;
+    }
+  }
+  E* dst = is_q ? qo + (tok * Hq + hd) * kDh
+                : kc + (((int64_t)b * cache_len + p) * Hkv + (hd - Hq)) * kDh;
+  store4(dst + 4 * l, f32x4{x[0], x[1], x[2], x[3]});
+  if (!is_q && vc) {
+    const E* vs = v + (tok * Hkv + (hd - Hq)) * kDh;
+    E* vd = vc + (((int64_t)b * cache_len + p) * Hkv + (hd - Hq)) * kDh;
+    *reinterpret_cast<uint2*>(vd + 4 * l) = *reinterpret_cast<const uint2*>(vs + 4 * l);
+    if constexpr (sizeof(E) == 4)
+      *reinterpret_cast<uint2*>(vd + 4 * l + 2) = *reinterpret_cast<const uint2*>(vs + 4 * l + 2);
+  }
+}
+
+// Rows [0, rows) of a row-major global matrix into an LDS matrix (rows >= `rows`
+// zero), by `nt` threads in 16-byte pieces.
+template <typename E, int W, int R>
+__device__ __forceinline__ void stage_rows(Lds<E, W> dst, const E* src, int64_t ld, int rows,
+                                           int nt) {
+  constexpr int EP = 16 / sizeof(E), PPR = W / EP;
+  for (int pc = threadIdx.x; pc < R * PPR; pc += nt) {
+    const int row = pc / PPR, c = (pc % PPR) * EP;
+    *reinterpret_cast<uint4*>(&dst(row, c)) =
+        row < rows ? *reinterpret_cast<const uint4*>(src + row * ld + c) : uint4{0u, 0u, 0u, 0u};
+  }
+}
+
+// ------------------------------------------------------------ prefill
+template <typename E>
+struct FwdSmem {
+  static constexpr int NB = sizeof(E) == 2 ? 2 : 1;     // K/V buffers
+  E K[NB][Lds<E, kDh>::size(kKvb)];
+  E V[NB][Lds<E, kDh>::size(kKvb)];
+};
+
+// QS waves per query head, each with QT tiles of 16 query rows: the workgroup
+// covers 16 QT QS rows of all G heads of its key/value head.  bf16: QT = 1,
+// QS = 2 (12 waves of at most 170 registers); fp32: QT = 1, QS = 1.
+template <typename E, int QT, int QS>
+__global__ __launch_bounds__(QS == 2 ? 768 : 512) void attn_fwd_kernel(
+    const E* __restrict__ qr, const E* __restrict__ kc, const E* __restrict__ vc,
+    const E* __restrict__ gate, E* __restrict__ o, int T, int cache_len, int Hq, int Hkv,
+    int nqb) {
+  constexpr bool BF = sizeof(E) == 2;
+  constexpr int KB = FragOf<E>::KB, NKB = kDh / KB, QR = 16 * QT, QRW = QR * QS;
+  __shared__ FwdSmem<E> sm;
+  const int G = Hq / Hkv, NWV = G * QS;
+  const int w = __builtin_amdgcn_readfirstlane(wave_id()), l = lane_id(), r = l & 15, g = l >> 4;
+  const int qb = nqb - 1 - (int)blockIdx.x;              // longest blocks first
+  const int kvh = blockIdx.y, b = blockIdx.z, h = kvh * G + w % G;
+  const int q0 = qb * QRW + (w / G) * QR;                // this wave's first query row
+  const int nblk = min((qb * QRW + QRW - 1) / kKvb + 1, (T + kKvb - 1) / kKvb);
+  const int64_t kv_ld = (int64_t)Hkv * kDh;
+  const E* kbase = kc + ((int64_t)b * cache_len * Hkv + kvh) * kDh;
+  const E* vbase = vc + ((int64_t)b * cache_len * Hkv + kvh) * kDh;
+
+  auto issue = [&](int j) {
+    const int nb = BF ? (j & 1) : 0;
+    if constexpr (BF) {
+      copy_rows<kDh, kKvb>(kbase + (int64_t)j * kKvb * kv_ld, kv_ld, T - j * kKvb, sm.K[nb], w, NWV);
+      copy_rows<kDh, kKvb>(vbase + (int64_t)j * kKvb * kv_ld, kv_ld, T - j * kKvb, sm.V[nb], w, NWV);
+    }
+  };
+
+  // Q fragments (B operand of S^T = K Q^T): rows q0 + 16qt + r, all 256 channels
+  Fr<E> Qf[QT][NKB];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int row = min(q0 + 16 * qt + r, T - 1);
+    const Glb<E> qm{qr + (((int64_t)b * T + row) * Hq + h) * kDh, 0, 1};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) Qf[qt][kb] = qm.rm(0, KB * kb);
+  }
+  f32x4 O[QT][16];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+    for (int dt = 0; dt < 16; ++dt) O[qt][dt] = zero4();
+  float m[QT], lsum[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) { m[qt] = -INFINITY; lsum[qt] = 0.f; }
+  const float c = 1.4426950408889634f / 16.f;             // log2(e) / sqrt(256)
+
+  if constexpr (BF) {
+    issue(0);
+    wait_copies();
+    barrier_lds();
+  }
+  for (int j = 0; j < nblk; ++j) {
+    const int nb = BF ? (j & 1) : 0;
+    if constexpr (BF) {
+      if (j + 1 < nblk) issue(j + 1);
+    } else {
+      __syncthreads();
+      stage_rows<E, kDh, kKvb>(Lds<E, kDh>{sm.K[0]}, kbase + (int64_t)j * kKvb * kv_ld, kv_ld,
+                               T - j * kKvb, 64 * NWV);
+      stage_rows<E, kDh, kKvb>(Lds<E, kDh>{sm.V[0]}, vbase + (int64_t)j * kKvb * kv_ld, kv_ld,
+                               T - j * kKvb, 64 * NWV);
+      __syncthreads();
+    }
+    const Lds<E, kDh> Ks{sm.K[nb]}, Vs{sm.V[nb]};
+    const Lane ln = lane_opaque();   // fragment addresses recomputed per block, not kept live
+    // S^T tiles: rows keys 64j + 16kt + 4g + i, column query q0 + 16qt + r
+    f32x4 S[QT][4];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) S[qt][kt] = zero4();
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const Fr<E> a = Ks.rm(16 * kt + ln.r, KB * kb, ln);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) S[qt][kt] = mma(S[qt][kt], a, Qf[qt][kb]);
+      }
+    const bool diag = kKvb * j + kKvb - 1 > q0;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const int qi = q0 + 16 * qt + r;
+      float mb = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float s = S[qt][kt][i] * c;
+          if (diag && kKvb * j + 16 * kt + 4 * g + i > qi) s = -INFINITY;
+          S[qt][kt][i] = s;
+          mb = fmaxf(mb, s);
+        }
+      mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
+      mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+      const float mn = fmaxf(m[qt], mb);
+      const float al = hw_exp2(m[qt] - mn);
+      m[qt] = mn;
+      float ps = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pv = hw_exp2(S[qt][kt][i] - mn);
+          S[qt][kt][i] = pv;
+          ps += pv;
+        }
+      lsum[qt] = lsum[qt] * al + ps;
+#pragma unroll
+      for (int dt = 0; dt < 16; ++dt) O[qt][dt] *= al;
+    }
+    // O^T += V^T P^T
+#pragma unroll
+    for (int kb = 0; kb < kKvb / KB; ++kb) {
+      Fr<E> pf[QT];
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) pf[qt] = acc_frag<E>(S[qt], kb);
+#pragma unroll
+      for (int dt = 0; dt < 16; ++dt) {
+        const Fr<E> a = Vs.cm(16 * dt + ln.r, KB * kb, ln);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) O[qt][dt] = mma(O[qt][dt], a, pf[qt]);
+      }
+    }
+    if constexpr (BF) {
+      wait_copies();
+      barrier_lds();
+    }
+  }
+  // normalise, gate, store: lane (r, g) holds channels 16dt + 4g .. +3 of query r
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    float lt = lsum[qt];
+    lt += __shfl_xor(lt, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    const float inv = 1.f / lt;
+    const int qi = q0 + 16 * qt + r;
+    if (qi < T) {
+      const int64_t base = (((int64_t)b * T + qi) * Hq + h) * kDh;
+#pragma unroll
+      for (int dt = 0; dt < 16; ++dt) {
+        const int ch = 16 * dt + 4 * g;
+        f32x4 gv;
+        if constexpr (BF) {
+          const bf16x4 g4 = *reinterpret_cast<const bf16x4*>(gate + base + ch);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) gv[i] = (float)g4[i];
+        } else {
+          gv = *reinterpret_cast<const f32x4*>(gate + base + ch);
+        }
+        f32x4 y;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[i] = O[qt][dt][i] * inv / (1.f + __expf(-gv[i]));
+        store4(o + base + ch, y);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ decode
+// Partials: m, l [B][Hq][ns], O [B][Hq][ns][256] fp32.  Wave w owns output
+// channels 64w .. 64w+63; every wave forms the same scores of the block (the
+// kernel is bound by the cache read, not by the matrix units), so the waves
+// never exchange anything.
+template <typename E>
+struct DecSmem {
+  static constexpr int NB = sizeof(E) == 2 ? 2 : 1;
+  E K[NB][Lds<E, kDh>::size(kKvb)];
+  E V[NB][Lds<E, kDh>::size(kKvb)];
+};
+
+template <typename E>
+__global__ __launch_bounds__(256) void attn_decode_kernel(
+    const E* __restrict__ qr, const E* __restrict__ kc, const E* __restrict__ vc,
+    const int32_t* __restrict__ pos, float* __restrict__ pm, float* __restrict__ pl,
+    float* __restrict__ po, int cache_len, int Hq, int Hkv, int ns) {
+  constexpr bool BF = sizeof(E) == 2;
+  constexpr int KB = FragOf<E>::KB, NKB = kDh / KB;
+  __shared__ DecSmem<E> sm;
+  const int G = Hq / Hkv;
+  const int w = __builtin_amdgcn_readfirstlane(wave_id()), l = lane_id(), r = l & 15, g = l >> 4;
+  const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int n = min(max(pos[b], 0), cache_len - 1) + 1;   // keys 0 .. pos inclusive
+  const int k0 = s * kSplit, k1 = min(n, k0 + kSplit);
+  const size_t pidx = ((size_t)b * Hq + kvh * G) * ns + s;  // head kvh*G, split s
+  if (k0 >= k1) {
+    // empty split: a neutral partial
+    if (threadIdx.x < G) {
+      pm[pidx + (size_t)threadIdx.x * ns] = -INFINITY;
+      pl[pidx + (size_t)threadIdx.x * ns] = 0.f;
+    }
+    return;
+  }
+  const int64_t kv_ld = (int64_t)Hkv * kDh;
+  const E* kbase = kc + ((int64_t)b * cache_len * Hkv + kvh) * kDh;
+  const E* vbase = vc + ((int64_t)b * cache_len * Hkv + kvh) * kDh;
+  const int nblk = (k1 - k0 + kKvb - 1) / kKvb;
+
+  auto issue = [&](int j) {
+    if constexpr (BF) {
+      const int kb0 = k0 + j * kKvb;
+      copy_rows<kDh, kKvb>(kbase + (int64_t)kb0 * kv_ld, kv_ld, k1 - kb0, sm.K[j & 1], w, 4);
+      copy_rows<kDh, kKvb>(vbase + (int64_t)kb0 * kv_ld, kv_ld, k1 - kb0, sm.V[j & 1], w, 4);
+    }
+  };
+
+  // query fragments: lane column r = head kvh*G + r (zero beyond the group)
+  Fr<E> Qf[NKB];
+  {
+    const bool ok = r < G;
+    const Glb<E> qm{qr + ((int64_t)b * Hq + kvh * G + (ok ? r : 0)) * kDh, 0, ok ? 1 : 0};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) Qf[kb] = qm.rm(0, KB * kb);
+  }
+  f32x4 O[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) O[dt] = zero4();
+  float m = -INFINITY, lsum = 0.f;
+  const float c = 1.4426950408889634f / 16.f;
+
+  if constexpr (BF) {
+    issue(0);
+    wait_copies();
+    barrier_lds();
+  }
+  for (int j = 0; j < nblk; ++j) {
+    const int kb0 = k0 + j * kKvb;
+    if constexpr (BF) {
+      if (j + 1 < nblk) issue(j + 1);
+    } else {
+      __syncthreads();
+      stage_rows<E, kDh, kKvb>(Lds<E, kDh>{sm.K[0]}, kbase + (int64_t)kb0 * kv_ld, kv_ld, k1 - kb0, 256);
+      stage_rows<E, kDh, kKvb>(Lds<E, kDh>{sm.V[0]}, vbase + (int64_t)kb0 * kv_ld, kv_ld, k1 - kb0, 256);
+      __syncthreads();
+    }
+    const Lds<E, kDh> Ks{sm.K[BF ? (j & 1) : 0]}, Vs{sm.V[BF ? (j & 1) : 0]};
+    // S^T: rows keys kb0 + 16kt + 4g + i, column head r
+    f32x4 S[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) S[kt] = zero4();
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) S[kt] = mma(S[kt], Ks.rm(16 * kt + r, KB * kb), Qf[kb]);
+    float mb = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float sv = S[kt][i] * c;
+        if (kb0 + 16 * kt + 4 * g + i >= k1) sv = -INFINITY;
+        S[kt][i] = sv;
+        mb = fmaxf(mb, sv);
+      }
+    mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
+    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+    const float mn = fmaxf(m, mb);           // finite: every block holds a valid key
+    const float al = hw_exp2(m - mn);
+    m = mn;
+    float ps = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pv = hw_exp2(S[kt][i] - mn);
+        S[kt][i] = pv;
+        ps += pv;
+      }
+    lsum = lsum * al + ps;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) O[dt] *= al;
+#pragma unroll
+    for (int kb = 0; kb < kKvb / KB; ++kb) {
+      const Fr<E> pf = acc_frag<E>(S, kb);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) O[dt] = mma(O[dt], Vs.cm(64 * w + 16 * dt + r, KB * kb), pf);
+    }
+    if constexpr (BF) {
+      wait_copies();
+      barrier_lds();
+    }
+  }
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  // lane (r, g) holds channels 64w + 16dt + 4g .. +3 of head column r
+  if (r < G) {
+    const size_t pi = pidx + (size_t)r * ns;
+    float* dst = po + pi * kDh + 64 * w;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) *reinterpret_cast<f32x4*>(dst + 16 * dt + 4 * g) = O[dt];
+    if (w == 0 && g == 0) {
+      pm[pi] = m;
+      pl[pi] = lsum;
+    }
+  }
+}
+
+// One wave per (sequence, query head): merge the splits, normalise, gate.
+template <typename E>
+__global__ __launch_bounds__(256) void attn_combine_kernel(
+    const float* __restrict__ pm, const float* __restrict__ pl, const float* __restrict__ po,
+    const E* __restrict__ gate, E* __restrict__ o, int rows, int ns) {
+  const int row = blockIdx.x * 4 + wave_id(), l = lane_id();
+  if (row >= rows) return;
+  float mx = -INFINITY;
+  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, pm[(size_t)row * ns + s]);
+  float lt = 0.f;
+  f32x4 acc = zero4();
+  for (int s = 0; s < ns; ++s) {
+    const float ms = pm[(size_t)row * ns + s];
+    if (ms == -INFINITY) continue;
+    const float sc = hw_exp2(ms - mx);
+    lt += sc * pl[(size_t)row * ns + s];
+    const f32x4 v4 = *reinterpret_cast<const f32x4*>(po + ((size_t)row * ns + s) * kDh + 4 * l);
+    acc += sc * v4;
+  }
+  const float inv = 1.f / lt;
+  f32x4 gv;
+  if constexpr (sizeof(E) == 2) {
+    const bf16x4 g4 = *reinterpret_cast<const bf16x4*>(gate + (size_t)row * kDh + 4 * l);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gv[i] = (float)g4[i];
+  } else {
+    gv = *reinterpret_cast<const f32x4*>(gate + (size_t)row * kDh + 4 * l);
+  }
+  f32x4 y;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) y[i] = acc[i] * inv / (1.f + __expf(-gv[i]));
+  store4(o + (size_t)row * kDh + 4 * l, y);
+}
+
+}  // namespace attn
+
+int attn_decode_splits(int cache_len) { return (cache_len + attn::kSplit - 1) / attn::kSplit; }
+
+template <typename E>
+static hipError_t attn_launch_t(const AttnLaunch& a, hipStream_t st) {
+  using namespace attn;
+  const int64_t ntok = a.decode ? a.B : (int64_t)a.B * a.T;
+  const int H = a.Hq + a.Hkv;
+  const int64_t rows = ntok * H;
+  hipLaunchKernelGGL((attn_prep_kernel<E>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st,
+                     (const E*)a.q, (const E*)a.k, (const E*)a.v, a.qw, a.kw, a.eps, a.rope_dim,
+                     a.theta, a.decode ? a.pos : nullptr, (E*)a.qrot, (E*)a.kc, (E*)a.vc_write, ntok,
+                     a.decode ? 1 : a.T, a.cache_len, a.Hq, a.Hkv);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int G = a.Hq / a.Hkv;
+  if (!a.decode) {
+    constexpr int QT = 1, QS = sizeof(E) == 2 ? 2 : 1;
+    const int nqb = (a.T + 16 * QT * QS - 1) / (16 * QT * QS);
+    hipLaunchKernelGGL((attn_fwd_kernel<E, QT, QS>), dim3(nqb, a.Hkv, a.B), dim3(64 * G * QS), 0, st,
+                       (const E*)a.qrot, (const E*)a.kc, (const E*)a.vc_read, (const E*)a.gate,
+                       (E*)a.o, a.T, a.cache_len, a.Hq, a.Hkv, nqb);
+    return hipGetLastError();
+  }
+  const int ns = attn_decode_splits(a.cache_len);
+  hipLaunchKernelGGL((attn_decode_kernel<E>), dim3(ns, a.Hkv, a.B), dim3(256), 0, st,
+                     (const E*)a.qrot, (const E*)a.kc,
+                     (const E*)a.vc_read, a.pos, a.pm, a.pl, a.po, a.cache_len, a.Hq, a.Hkv, ns);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int crow = a.B * a.Hq;
+  hipLaunchKernelGGL((attn_combine_kernel<E>), dim3((crow + 3) / 4), dim3(256), 0, st, a.pm, a.pl,
+                     a.po, (const E*)a.gate, (E*)a.o, crow, ns);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention(const AttnLaunch& a, hipStream_t st) {
+  return a.bf16_io ? attn_launch_t<bf16>(a, st) : attn_launch_t<float>(a, st);
+}
+
+}  // namespace gdn

@@ -51,6 +51,26 @@ struct BackwardLaunch {
 };
 hipError_t launch_backward(const BackwardLaunch& a, hipStream_t st);
 
+// Gated attention layer (prefill of B sequences of T tokens from position 0,
+// or one decode token per sequence at position pos[b]).
+struct AttnLaunch {
+  const void *q, *k, *v, *gate;
+  const float *qw, *kw;      // QK-Norm weights, or null (ones)
+  float eps, theta;
+  int rope_dim;
+  const int32_t* pos;        // decode: [B] positions (cached keys per sequence)
+  void* qrot;                // workspace: normalised, rotated queries
+  void* kc;                  // keys after norm and rotation [B][cache_len][Hkv][256]
+  void* vc_write;            // value cache to fill (or null: values read from v)
+  const void* vc_read;       // values the attention reads [B][cache_len][Hkv][256]
+  void* o;
+  float *pm, *pl, *po;       // decode split partials (workspace)
+  int B, T, cache_len, Hq, Hkv;
+  bool decode, bf16_io;
+};
+hipError_t launch_attention(const AttnLaunch& a, hipStream_t st);
+int attn_decode_splits(int cache_len);
+
 hipError_t launch_prepare(const PrefillLaunch& a, hipStream_t st);
 hipError_t launch_scan(const PrefillLaunch& a, hipStream_t st);
 hipError_t launch_varlen_table(const int32_t* cu, int N, int T_tot, int nc_max, int32_t* tab,

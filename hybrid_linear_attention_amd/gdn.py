@@ -67,6 +67,15 @@ def _load():
     lib.gdn_prefill_chunked_bwd.restype = ctypes.c_int
     lib.gdn_prefill_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int]
     lib.gdn_prefill_bwd_workspace_bytes.restype = sz
+    lib.gdn_attn_prefill.argtypes = ([vp] * 6 + [f32] + [vp] * 3 + [i32] * 7
+                                     + [f32, ctypes.c_int, vp, sz, vp])
+    lib.gdn_attn_prefill.restype = ctypes.c_int
+    lib.gdn_attn_decode.argtypes = ([vp] * 6 + [f32] + [vp] * 4 + [i32] * 6
+                                    + [f32, ctypes.c_int, vp, sz, vp])
+    lib.gdn_attn_decode.restype = ctypes.c_int
+    for name in ("gdn_attn_prefill_workspace_bytes", "gdn_attn_decode_workspace_bytes"):
+        getattr(lib, name).argtypes = [i32] * 5 + [ctypes.c_int]
+        getattr(lib, name).restype = sz
     lib.gdn_status_str.argtypes = [ctypes.c_int]
     lib.gdn_status_str.restype = ctypes.c_char_p
     lib.gdn_last_hip_error.argtypes = []
@@ -396,3 +405,80 @@ def prefill_varlen(q, k, v, alpha, beta, cu_seqlens, h0=None, *, gate=None,
                                 _dt(q), _ptr(ws), nbytes, _stream(dev))
     _check(rc, "gdn_prefill_varlen")
     return o, ht
+
+
+# ---------------------------------------------------------------- gated attention
+ATTN_DIM = 256
+
+
+def _attn_common(q, k, v, gate, q_norm_w, k_norm_w, lead):
+    _req(q, "q", ndim=len(lead) + 2)
+    dtype, dev = q.dtype, q.device
+    Hq, D = q.shape[-2], q.shape[-1]
+    Hkv = k.shape[-2]
+    for name, t, H in (("k", k, Hkv), ("v", v, Hkv), ("gate", gate, Hq)):
+        _req(t, name, dtype, len(lead) + 2, dev)
+        if tuple(t.shape) != tuple(lead) + (H, D):
+            raise ValueError("%s must be %s" % (name, tuple(lead) + (H, D)))
+    for name, t in (("q_norm_w", q_norm_w), ("k_norm_w", k_norm_w)):
+        _req(t, name, torch.float32, 1, dev)
+    return dtype, dev, Hq, Hkv, D
+
+
+def attn_prefill_workspace_bytes(B, T, H_q=24, H_kv=4, D=ATTN_DIM, dtype=torch.bfloat16) -> int:
+    dt = GDN_BF16 if dtype == torch.bfloat16 else GDN_F32
+    return int(lib.gdn_attn_prefill_workspace_bytes(B, T, H_q, H_kv, D, dt))
+
+
+def attn_decode_workspace_bytes(B, cache_len, H_q=24, H_kv=4, D=ATTN_DIM,
+                                dtype=torch.bfloat16) -> int:
+    dt = GDN_BF16 if dtype == torch.bfloat16 else GDN_F32
+    return int(lib.gdn_attn_decode_workspace_bytes(B, cache_len, H_q, H_kv, D, dt))
+
+
+def attn_prefill(q, k, v, gate, q_norm_w=None, k_norm_w=None, *, eps=1e-6, rope_dim=64,
+                 theta=1.0e7, k_cache=None, v_cache=None, o=None, workspace=None):
+    """Gated attention of a prefill (gdn_attn_prefill).  q, gate [B,T,Hq,256];
+    k, v [B,T,Hkv,256]; optional caches [B,cache_len,Hkv,256] receive the
+    normalised, rotated keys and the values of positions 0..T-1.  Returns o."""
+    B, T = q.shape[0], q.shape[1]
+    dtype, dev, Hq, Hkv, D = _attn_common(q, k, v, gate, q_norm_w, k_norm_w, (B, T))
+    cache_len = 0
+    if k_cache is not None or v_cache is not None:
+        _req(k_cache, "k_cache", dtype, 4, dev)
+        _req(v_cache, "v_cache", dtype, 4, dev)
+        cache_len = k_cache.shape[1]
+    if o is None:
+        o = torch.empty_like(q)
+    _req(o, "o", dtype, 4, dev)
+    nbytes = attn_prefill_workspace_bytes(B, T, Hq, Hkv, D, dtype)
+    ws = _workspace(nbytes, dev, workspace)
+    _check(lib.gdn_attn_prefill(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(q_norm_w), _ptr(k_norm_w), eps, _ptr(o),
+        _ptr(k_cache), _ptr(v_cache), cache_len, B, T, Hq, Hkv, D, rope_dim, theta, _dt(q),
+        _ptr(ws), nbytes, _stream(dev)), "gdn_attn_prefill")
+    return o
+
+
+def attn_decode(q, k, v, gate, k_cache, v_cache, pos, q_norm_w=None, k_norm_w=None, *,
+                eps=1e-6, rope_dim=64, theta=1.0e7, o=None, workspace=None):
+    """One decode token per sequence (gdn_attn_decode).  q, gate [B,Hq,256];
+    k, v [B,Hkv,256]; caches [B,cache_len,Hkv,256]; pos int32 [B] on the
+    device (tokens already cached).  Writes the token's key/value at pos and
+    returns o [B,Hq,256]."""
+    B = q.shape[0]
+    dtype, dev, Hq, Hkv, D = _attn_common(q, k, v, gate, q_norm_w, k_norm_w, (B,))
+    _req(k_cache, "k_cache", dtype, 4, dev)
+    _req(v_cache, "v_cache", dtype, 4, dev)
+    _req(pos, "pos", torch.int32, 1, dev)
+    cache_len = k_cache.shape[1]
+    if o is None:
+        o = torch.empty_like(q)
+    _req(o, "o", dtype, 3, dev)
+    nbytes = attn_decode_workspace_bytes(B, cache_len, Hq, Hkv, D, dtype)
+    ws = _workspace(nbytes, dev, workspace)
+    _check(lib.gdn_attn_decode(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(q_norm_w), _ptr(k_norm_w), eps, _ptr(o),
+        _ptr(k_cache), _ptr(v_cache), _ptr(pos), cache_len, B, Hq, Hkv, D, rope_dim, theta,
+        _dt(q), _ptr(ws), nbytes, _stream(dev)), "gdn_attn_decode")
+    return o

@@ -291,6 +291,78 @@ gdn_status gdn_prefill_chunked_bwd(const void *q, const void *k, const void *v,
 size_t gdn_prefill_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H_qk,
                                        int32_t H_v, int32_t D, gdn_dtype dt);
 
+/*
+ * Gated attention layer: the other layer type of the hybrid stack (one in four
+ * layers; page "Inside Qwen3.8-27B ...", section "The Role of Periodic Gated
+ * Attention": 24 query heads, 4 key/value heads, head dim 256, rotary
+ * embedding on a 64-channel subspace with theta = 10,000,000).  From the
+ * projected per-head activations, per (token, head):
+ *
+ *   q, k <- RMSNorm(q, k) * w      QK-Norm over the 256 channels (card
+ *                                  "Qwen3.8 (27B)", "Architecture concepts";
+ *                                  w = the norm weight, ones when NULL)
+ *   rotate channels (j, j + rope_dim/2), j < rope_dim/2, by the angle
+ *          pos * theta^(-2j / rope_dim); channels >= rope_dim pass through
+ *   o = softmax_causal(q k^T / sqrt(256)) v      query head h reads key/value
+ *                                  head h / (H_q / H_kv)
+ *   o <- o * sigmoid(gate)         channel by channel (the output gate that
+ *                                  the fused q projection carries: page
+ *                                  "Qwen3.8 Explained ...", the note on
+ *                                  attn_output_gate)
+ *
+ * D must be 256, H_q / H_kv <= 8, rope_dim a multiple of 8 in [0, 256],
+ * theta > 0, norm_eps >= 0.  All tensors of dtype dt except the fp32 norm
+ * weights; 16-byte aligned.
+ *
+ * gdn_attn_prefill - B sequences of T tokens at positions 0 .. T-1.
+ *   q, gate   [B, T, H_q, D]   dt
+ *   k, v      [B, T, H_kv, D]  dt
+ *   o         [B, T, H_q, D]   dt
+ *   k_cache, v_cache  [B, cache_len, H_kv, D] dt, both or neither.  When
+ *             given (cache_len >= T), rows 0 .. T-1 receive the normalised,
+ *             rotated keys and the values, ready for gdn_attn_decode; rows
+ *             >= T are untouched.
+ *   workspace at least gdn_attn_prefill_workspace_bytes(...) bytes.
+ */
+gdn_status gdn_attn_prefill(const void *q, const void *k, const void *v,
+                            const void *gate, const float *q_norm_w,
+                            const float *k_norm_w, float norm_eps, void *o,
+                            void *k_cache, void *v_cache, int32_t cache_len,
+                            int32_t B, int32_t T, int32_t H_q, int32_t H_kv,
+                            int32_t D, int32_t rope_dim, float rope_theta,
+                            gdn_dtype dt, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+size_t gdn_attn_prefill_workspace_bytes(int32_t B, int32_t T, int32_t H_q,
+                                        int32_t H_kv, int32_t D, gdn_dtype dt);
+
+/*
+ * gdn_attn_decode - one new token for each of B sequences.
+ *   q, gate   [B, H_q, D]  dt;   k, v [B, H_kv, D] dt;   o [B, H_q, D] dt
+ *   pos       [B] int32 DEVICE array: the token's position, i.e. the number
+ *             of tokens already in the cache (precondition 0 <= pos[b] <
+ *             cache_len; the kernels clamp it into range, never read it on
+ *             the host).
+ *   k_cache, v_cache [B, cache_len, H_kv, D] dt: row pos[b] receives the
+ *             token's normalised, rotated key and its value; the token then
+ *             attends to rows 0 .. pos[b].
+ *   workspace at least gdn_attn_decode_workspace_bytes(...) bytes (grows with
+ *             cache_len: split partials).
+ * The caller advances pos.
+ */
+gdn_status gdn_attn_decode(const void *q, const void *k, const void *v,
+                           const void *gate, const float *q_norm_w,
+                           const float *k_norm_w, float norm_eps, void *o,
+                           void *k_cache, void *v_cache, const int32_t *pos,
+                           int32_t cache_len, int32_t B, int32_t H_q,
+                           int32_t H_kv, int32_t D, int32_t rope_dim,
+                           float rope_theta, gdn_dtype dt, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+size_t gdn_attn_decode_workspace_bytes(int32_t B, int32_t cache_len,
+                                       int32_t H_q, int32_t H_kv, int32_t D,
+                                       gdn_dtype dt);
+
 /* Human-readable name of a status code (static string). */
 const char *gdn_status_str(gdn_status s);
 

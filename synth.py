@@ -101,6 +101,33 @@ def backward_inputs(B, T, dtype=torch.bfloat16, seed=0, h0_std=0.0, dht_std=0.0,
     return d
 
 
+def attention_inputs(B, T, dtype=torch.bfloat16, seed=0, Hq=24, Hkv=4, Dh=256):
+    """Gated attention layer inputs (projected activations): q, gate
+    ``[B,T,Hq,Dh]``, k, v ``[B,T,Hkv,Dh]`` ~ N(0, 1) in dtype, drawn in that
+    order; then the QK-Norm weights q_norm_w, k_norm_w = 1 + 0.1 N(0, 1) fp32
+    ``[Dh]``.  (Head counts and dim: page "Inside Qwen3.8-27B ...", "The Role
+    of Periodic Gated Attention".)"""
+    gen = torch.Generator().manual_seed(seed)
+    d = dict(q=_normal(gen, (B, T, Hq, Dh)).to(dtype).contiguous(),
+             k=_normal(gen, (B, T, Hkv, Dh)).to(dtype).contiguous(),
+             v=_normal(gen, (B, T, Hkv, Dh)).to(dtype).contiguous(),
+             gate=_normal(gen, (B, T, Hq, Dh)).to(dtype).contiguous())
+    d["q_norm_w"] = (1 + 0.1 * _normal(gen, (Dh,))).contiguous()
+    d["k_norm_w"] = (1 + 0.1 * _normal(gen, (Dh,))).contiguous()
+    return d
+
+
+def attention_decode_inputs(B, step, dtype=torch.bfloat16, seed=0, Hq=24, Hkv=4, Dh=256):
+    """One decode token per sequence: q, gate ``[B,Hq,Dh]``, k, v ``[B,Hkv,Dh]``
+    (seed + 7919 (step + 1), same order and distributions as
+    :func:`attention_inputs`)."""
+    gen = torch.Generator().manual_seed(seed + 7919 * (step + 1))
+    return dict(q=_normal(gen, (B, Hq, Dh)).to(dtype).contiguous(),
+                k=_normal(gen, (B, Hkv, Dh)).to(dtype).contiguous(),
+                v=_normal(gen, (B, Hkv, Dh)).to(dtype).contiguous(),
+                gate=_normal(gen, (B, Hq, Dh)).to(dtype).contiguous())
+
+
 def varlen_lengths(N, lo, hi, seed):
     gen = torch.Generator().manual_seed(seed)
     return torch.randint(lo, hi + 1, (N,), generator=gen).tolist()
