@@ -25,7 +25,8 @@
 //    softmax stay in the lane (two shuffles across lane groups per block), and
 //    the probability tiles are directly the B operand of O^T = V^T P^T.  K/V
 //    tiles of 64 keys are double-buffered in LDS with direct global->LDS
-//    copies (bf16).  Only the diagonal block is masked.  Workgroups are issued
+//    copies (bf16), in padded rows that make every fragment read free of bank
+//    conflicts.  Only the diagonal block is masked.  Workgroups are issued
 //    longest (latest query block) first.
 //  * attn_decode + attn_combine: split-K over the cached keys.  One workgroup
 //    per (split of 512 keys, key/value head, sequence); 64-key blocks
@@ -125,12 +126,65 @@ __device__ __forceinline__ void stage_rows(Lds<E, W> dst, const E* src, int64_t 
   }
 }
 
+// ------------------------------------------------------------ bf16 K/V tiles
+// 64 rows of 256 bf16 with padded rows, so that every fragment address is one
+// per-lane base plus a compile-time offset and no read meets a bank conflict
+// (64-bit LDS reads are served 32 lanes at a time over 64 four-byte banks):
+//  * KTile rows are 528 bytes (16 bytes of padding).  Row-pattern fragment
+//    reads (lane (r, g): 8 bytes of row r at channel 4g) land on banks
+//    4r + 2g (+1): all 64 banks once per 32 lanes.
+//  * VTile rows are 544 bytes (32 bytes of padding).  Transposed reads
+//    (ds_read_b64_tr_b16; lane (r, g) reads 8 bytes of row 4g + r/4 at
+//    channel 4(r%4)) land on banks 8 (4g + r/4) + 2 (r%4) (+1): all 64 once.
+template <int ROWB>
+struct PadTile {
+  static constexpr int kBytes = kKvb * ROWB;
+  char* p;
+  // A/B fragment with the lane index along rows (keys): slots are channels
+  // k0 + kslot(g, j).
+  __device__ bf16x8 rm(int row0, int k0, const Lane& ln) const {
+    const char* b = p + (row0 + ln.r) * ROWB + 8 * ln.g + 2 * k0;
+    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(b);
+    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(b + 32);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  // Fragment with the lane index along channels col0 + r: slots are rows
+  // k0 + kslot(g, j).
+  __device__ bf16x8 cm(int col0, int k0, const Lane& ln) const {
+    const char* b = p + (k0 + 4 * ln.g + (ln.r >> 2)) * ROWB + 2 * col0 + 8 * (ln.r & 3);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)b);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + 16 * ROWB));
+    return __builtin_shufflevector(as_bf16x4(lo), as_bf16x4(hi), 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+};
+typedef PadTile<528> KTile;
+typedef PadTile<544> VTile;
+
+// 64 rows (rows >= L repeat row L-1) of 256 bf16 with row stride ld into a
+// padded tile, copied straight into LDS; wave w of nw issues copies w, w + nw,
+// ...  Copy `it` fills LDS bytes [1024 it, 1024 it + 1024): a lane whose 16
+// bytes fall in padding is switched off.
+template <int ROWB>
+__device__ __forceinline__ void copy_tile(const bf16* src, int64_t ld, int L, char* dst, int w,
+                                          int nw) {
+  constexpr int NIT = (kKvb * ROWB + 1023) / 1024;
+  const int l = lane_id();
+  for (int it = w; it < NIT; it += nw) {
+    const int byte = 1024 * it + 16 * l, row = byte / ROWB, off = byte - row * ROWB;
+    if (row < kKvb && off < 2 * kDh)
+      dma16(src + (int64_t)min(row, L - 1) * ld + off / 2, dst + 1024 * it);
+  }
+}
+
 // ------------------------------------------------------------ prefill
 template <typename E>
 struct FwdSmem {
-  static constexpr int NB = sizeof(E) == 2 ? 2 : 1;     // K/V buffers
-  E K[NB][Lds<E, kDh>::size(kKvb)];
-  E V[NB][Lds<E, kDh>::size(kKvb)];
+  static constexpr bool BF = sizeof(E) == 2;
+  static constexpr int NB = BF ? 2 : 1;                 // K/V buffers
+  static constexpr int KB_ = BF ? KTile::kBytes : Lds<E, kDh>::size(kKvb) * (int)sizeof(E);
+  static constexpr int VB_ = BF ? VTile::kBytes : Lds<E, kDh>::size(kKvb) * (int)sizeof(E);
+  alignas(16) char K[NB][KB_];
+  alignas(16) char V[NB][VB_];
 };
 
 // QS waves per query head, each with QT tiles of 16 query rows: the workgroup
@@ -157,8 +211,8 @@ __global__ __launch_bounds__(QS == 2 ? 768 : 512) void attn_fwd_kernel(
   auto issue = [&](int j) {
     const int nb = BF ? (j & 1) : 0;
     if constexpr (BF) {
-      copy_rows<kDh, kKvb>(kbase + (int64_t)j * kKvb * kv_ld, kv_ld, T - j * kKvb, sm.K[nb], w, NWV);
-      copy_rows<kDh, kKvb>(vbase + (int64_t)j * kKvb * kv_ld, kv_ld, T - j * kKvb, sm.V[nb], w, NWV);
+      copy_tile<528>(kbase + (int64_t)j * kKvb * kv_ld, kv_ld, T - j * kKvb, sm.K[nb], w, NWV);
+      copy_tile<544>(vbase + (int64_t)j * kKvb * kv_ld, kv_ld, T - j * kKvb, sm.V[nb], w, NWV);
     }
   };
 
@@ -192,14 +246,21 @@ __global__ __launch_bounds__(QS == 2 ? 768 : 512) void attn_fwd_kernel(
       if (j + 1 < nblk) issue(j + 1);
     } else {
       __syncthreads();
-      stage_rows<E, kDh, kKvb>(Lds<E, kDh>{sm.K[0]}, kbase + (int64_t)j * kKvb * kv_ld, kv_ld,
-                               T - j * kKvb, 64 * NWV);
-      stage_rows<E, kDh, kKvb>(Lds<E, kDh>{sm.V[0]}, vbase + (int64_t)j * kKvb * kv_ld, kv_ld,
-                               T - j * kKvb, 64 * NWV);
+      stage_rows<E, kDh, kKvb>(Lds<E, kDh>{reinterpret_cast<E*>(sm.K[0])},
+                               kbase + (int64_t)j * kKvb * kv_ld, kv_ld, T - j * kKvb, 64 * NWV);
+      stage_rows<E, kDh, kKvb>(Lds<E, kDh>{reinterpret_cast<E*>(sm.V[0])},
+                               vbase + (int64_t)j * kKvb * kv_ld, kv_ld, T - j * kKvb, 64 * NWV);
       __syncthreads();
     }
-    const Lds<E, kDh> Ks{sm.K[nb]}, Vs{sm.V[nb]};
-    const Lane ln = lane_opaque();   // fragment addresses recomputed per block, not kept live
+    const Lane ln = lane_here();
+    const auto Ks = [&]() {
+      if constexpr (BF) return KTile{sm.K[nb]};
+      else return Lds<E, kDh>{reinterpret_cast<E*>(sm.K[nb])};
+    }();
+    const auto Vs = [&]() {
+      if constexpr (BF) return VTile{sm.V[nb]};
+      else return Lds<E, kDh>{reinterpret_cast<E*>(sm.V[nb])};
+    }();
     // S^T tiles: rows keys 64j + 16kt + 4g + i, column query q0 + 16qt + r
     f32x4 S[QT][4];
 #pragma unroll
@@ -210,7 +271,9 @@ __global__ __launch_bounds__(QS == 2 ? 768 : 512) void attn_fwd_kernel(
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        const Fr<E> a = Ks.rm(16 * kt + ln.r, KB * kb, ln);
+        Fr<E> a;
+        if constexpr (BF) a = Ks.rm(16 * kt, KB * kb, ln);
+        else a = Ks.rm(16 * kt + ln.r, KB * kb, ln);
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) S[qt][kt] = mma(S[qt][kt], a, Qf[qt][kb]);
       }
@@ -254,7 +317,9 @@ __global__ __launch_bounds__(QS == 2 ? 768 : 512) void attn_fwd_kernel(
       for (int qt = 0; qt < QT; ++qt) pf[qt] = acc_frag<E>(S[qt], kb);
 #pragma unroll
       for (int dt = 0; dt < 16; ++dt) {
-        const Fr<E> a = Vs.cm(16 * dt + ln.r, KB * kb, ln);
+        Fr<E> a;
+        if constexpr (BF) a = Vs.cm(16 * dt, KB * kb, ln);
+        else a = Vs.cm(16 * dt + ln.r, KB * kb, ln);
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) O[qt][dt] = mma(O[qt][dt], a, pf[qt]);
       }
@@ -300,11 +365,7 @@ __global__ __launch_bounds__(QS == 2 ? 768 : 512) void attn_fwd_kernel(
 // kernel is bound by the cache read, not by the matrix units), so the waves
 // never exchange anything.
 template <typename E>
-struct DecSmem {
-  static constexpr int NB = sizeof(E) == 2 ? 2 : 1;
-  E K[NB][Lds<E, kDh>::size(kKvb)];
-  E V[NB][Lds<E, kDh>::size(kKvb)];
-};
+using DecSmem = FwdSmem<E>;
 
 template <typename E>
 __global__ __launch_bounds__(256) void attn_decode_kernel(
@@ -336,8 +397,8 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
   auto issue = [&](int j) {
     if constexpr (BF) {
       const int kb0 = k0 + j * kKvb;
-      copy_rows<kDh, kKvb>(kbase + (int64_t)kb0 * kv_ld, kv_ld, k1 - kb0, sm.K[j & 1], w, 4);
-      copy_rows<kDh, kKvb>(vbase + (int64_t)kb0 * kv_ld, kv_ld, k1 - kb0, sm.V[j & 1], w, 4);
+      copy_tile<528>(kbase + (int64_t)kb0 * kv_ld, kv_ld, k1 - kb0, sm.K[j & 1], w, 4);
+      copy_tile<544>(vbase + (int64_t)kb0 * kv_ld, kv_ld, k1 - kb0, sm.V[j & 1], w, 4);
     }
   };
 
@@ -366,11 +427,22 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
       if (j + 1 < nblk) issue(j + 1);
     } else {
       __syncthreads();
-      stage_rows<E, kDh, kKvb>(Lds<E, kDh>{sm.K[0]}, kbase + (int64_t)kb0 * kv_ld, kv_ld, k1 - kb0, 256);
-      stage_rows<E, kDh, kKvb>(Lds<E, kDh>{sm.V[0]}, vbase + (int64_t)kb0 * kv_ld, kv_ld, k1 - kb0, 256);
+      stage_rows<E, kDh, kKvb>(Lds<E, kDh>{reinterpret_cast<E*>(sm.K[0])},
+                               kbase + (int64_t)kb0 * kv_ld, kv_ld, k1 - kb0, 256);
+      stage_rows<E, kDh, kKvb>(Lds<E, kDh>{reinterpret_cast<E*>(sm.V[0])},
+                               vbase + (int64_t)kb0 * kv_ld, kv_ld, k1 - kb0, 256);
       __syncthreads();
     }
-    const Lds<E, kDh> Ks{sm.K[BF ? (j & 1) : 0]}, Vs{sm.V[BF ? (j & 1) : 0]};
+    const int nb = BF ? (j & 1) : 0;
+    const Lane ln = lane_here();
+    const auto Ks = [&]() {
+      if constexpr (BF) return KTile{sm.K[nb]};
+      else return Lds<E, kDh>{reinterpret_cast<E*>(sm.K[nb])};
+    }();
+    const auto Vs = [&]() {
+      if constexpr (BF) return VTile{sm.V[nb]};
+      else return Lds<E, kDh>{reinterpret_cast<E*>(sm.V[nb])};
+    }();
     // S^T: rows keys kb0 + 16kt + 4g + i, column head r
     f32x4 S[4];
 #pragma unroll
@@ -378,7 +450,10 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) S[kt] = mma(S[kt], Ks.rm(16 * kt + r, KB * kb), Qf[kb]);
+      for (int kt = 0; kt < 4; ++kt) {
+        if constexpr (BF) S[kt] = mma(S[kt], Ks.rm(16 * kt, KB * kb, ln), Qf[kb]);
+        else S[kt] = mma(S[kt], Ks.rm(16 * kt + r, KB * kb, ln), Qf[kb]);
+      }
     float mb = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
@@ -410,7 +485,10 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     for (int kb = 0; kb < kKvb / KB; ++kb) {
       const Fr<E> pf = acc_frag<E>(S, kb);
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) O[dt] = mma(O[dt], Vs.cm(64 * w + 16 * dt + r, KB * kb), pf);
+      for (int dt = 0; dt < 4; ++dt) {
+        if constexpr (BF) O[dt] = mma(O[dt], Vs.cm(64 * w + 16 * dt, KB * kb, ln), pf);
+        else O[dt] = mma(O[dt], Vs.cm(64 * w + 16 * dt + r, KB * kb, ln), pf);
+      }
     }
     if constexpr (BF) {
       wait_copies();
