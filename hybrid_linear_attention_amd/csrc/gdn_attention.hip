@@ -13,8 +13,9 @@
 //
 // Kernels:
 //  * attn_prep: one wave per (token, head) row: RMSNorm, weight, rotation.
-//    The angle is formed and reduced modulo 2 pi in fp64 (at position 262,143
-//    an fp32 angle would be off by ~1e-2 rad), then sin/cos in fp32.  Query
+//    The angle is formed and reduced modulo 2 pi in fp64 from frequencies the
+//    host computes in double (at position 262,143 an fp32 angle would be off
+//    by ~1e-2 rad), then sin/cos in fp32.  Query
 //    rows go to the workspace, key rows (and the value rows, unchanged) to the
 //    key/value cache at their positions.
 //  * attn_fwd (prefill): one workgroup per (32 query rows, key/value head,
@@ -37,6 +38,8 @@
 #include "gdn_frag.hpp"
 #include "gdn_launch.hpp"
 
+#include <cmath>
+
 namespace gdn {
 namespace attn {
 using namespace frag;
@@ -46,13 +49,19 @@ constexpr int kKvb = 64;        // keys per prefill block
 constexpr int kSplit = 512;     // keys per decode split
 
 // ------------------------------------------------------------ prep
+// theta^(-2j / rope_dim) for j < rope_dim / 2, formed on the host in double
+// precision and passed by value with the launch.
+struct RopeFreq {
+  double inv[kDh / 2];
+};
+
 // rows: ntok * (Hq + Hkv); row = tok * (Hq + Hkv) + head, heads >= Hq are keys.
 // Token tok = b * T + t sits at position pos[b] (decode) or t (prefill, pos null).
 template <typename E>
 __global__ __launch_bounds__(256) void attn_prep_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ qw, const float* __restrict__ kw, float eps, int rope_dim,
-    float theta, const int32_t* __restrict__ pos, E* __restrict__ qo, E* __restrict__ kc,
+    RopeFreq fr, const int32_t* __restrict__ pos, E* __restrict__ qo, E* __restrict__ kc,
     E* __restrict__ vc, int64_t ntok, int T, int cache_len, int Hq, int Hkv) {
   const int l = lane_id();
   const int64_t row = (int64_t)blockIdx.x * 4 + wave_id();
@@ -93,8 +102,7 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int j = 4 * (first ? l : l - hl) + i;
-      const double inv = exp(-(2.0 * j / rope_dim) * log((double)theta));
-      double ang = (double)p * inv;
+      double ang = (double)p * fr.inv[j];
       ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
       float sn, cs;
       sincosf((float)ang, &sn, &cs);
@@ -103,7 +111,10 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(
   }
   E* dst = is_q ? qo + (tok * Hq + hd) * kDh
                 : kc + (((int64_t)b * cache_len + p) * Hkv + (hd - Hq)) * kDh;
-  store4(dst + 4 * l, f32x4{x[0], x[1], x[2], x[3]});
+  // queries carry the softmax scale log2(e) / sqrt(256) (the attention kernels
+  // work in base 2); the cache keeps the keys themselves
+  const float sc = is_q ? 1.4426950408889634f / 16.f : 1.f;
+  store4(dst + 4 * l, f32x4{x[0] * sc, x[1] * sc, x[2] * sc, x[3] * sc});
   if (!is_q && vc) {
     const E* vs = v + (tok * Hkv + (hd - Hq)) * kDh;
     E* vd = vc + (((int64_t)b * cache_len + p) * Hkv + (hd - Hq)) * kDh;
@@ -194,14 +205,29 @@ template <typename E, int QT, int QS>
 __global__ __launch_bounds__(QS == 2 ? 768 : 512) void attn_fwd_kernel(
     const E* __restrict__ qr, const E* __restrict__ kc, const E* __restrict__ vc,
     const E* __restrict__ gate, E* __restrict__ o, int T, int cache_len, int Hq, int Hkv,
-    int nqb) {
+    int nqb, int nseq) {
   constexpr bool BF = sizeof(E) == 2;
   constexpr int KB = FragOf<E>::KB, NKB = kDh / KB, QR = 16 * QT, QRW = QR * QS;
   __shared__ FwdSmem<E> sm;
   const int G = Hq / Hkv, NWV = G * QS;
   const int w = __builtin_amdgcn_readfirstlane(wave_id()), l = lane_id(), r = l & 15, g = l >> 4;
-  const int qb = nqb - 1 - (int)blockIdx.x;              // longest blocks first
-  const int kvh = blockIdx.y, b = blockIdx.z, h = kvh * G + w % G;
+  // Workgroups are dispatched to the eight XCDs round-robin by linear id.  When
+  // the (sequence, key/value head) streams divide eight, each XCD serves one
+  // stream, so its L2 holds that stream's keys and values only; within a
+  // stream, query blocks go longest (latest) first.
+  const int nst = Hkv * nseq;
+  int qidx, st;
+  if (nst <= 8 && 8 % nst == 0) {
+    const int xper = 8 / nst, lin = blockIdx.x, xcd = lin & 7;
+    st = xcd / xper;
+    qidx = (lin >> 3) * xper + xcd % xper;
+    if (qidx >= nqb) return;
+  } else {
+    st = blockIdx.x / nqb;
+    qidx = blockIdx.x - st * nqb;
+  }
+  const int qb = nqb - 1 - qidx;
+  const int kvh = st % Hkv, b = st / Hkv, h = kvh * G + w % G;
   const int q0 = qb * QRW + (w / G) * QR;                // this wave's first query row
   const int nblk = min((qb * QRW + QRW - 1) / kKvb + 1, (T + kKvb - 1) / kKvb);
   const int64_t kv_ld = (int64_t)Hkv * kDh;
@@ -233,7 +259,6 @@ __global__ __launch_bounds__(QS == 2 ? 768 : 512) void attn_fwd_kernel(
   float m[QT], lsum[QT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) { m[qt] = -INFINITY; lsum[qt] = 0.f; }
-  const float c = 1.4426950408889634f / 16.f;             // log2(e) / sqrt(256)
 
   if constexpr (BF) {
     issue(0);
@@ -286,7 +311,7 @@ __global__ __launch_bounds__(QS == 2 ? 768 : 512) void attn_fwd_kernel(
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float s = S[qt][kt][i] * c;
+          float s = S[qt][kt][i];
           if (diag && kKvb * j + 16 * kt + 4 * g + i > qi) s = -INFINITY;
           S[qt][kt][i] = s;
           mb = fmaxf(mb, s);
@@ -306,8 +331,12 @@ __global__ __launch_bounds__(QS == 2 ? 768 : 512) void attn_fwd_kernel(
           ps += pv;
         }
       lsum[qt] = lsum[qt] * al + ps;
+      // rescale O only when some lane's running max moved (rare after the
+      // first blocks)
+      if (__builtin_amdgcn_ballot_w64(al != 1.f)) {
 #pragma unroll
-      for (int dt = 0; dt < 16; ++dt) O[qt][dt] *= al;
+        for (int dt = 0; dt < 16; ++dt) O[qt][dt] *= al;
+      }
     }
     // O^T += V^T P^T
 #pragma unroll
@@ -414,7 +443,6 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) O[dt] = zero4();
   float m = -INFINITY, lsum = 0.f;
-  const float c = 1.4426950408889634f / 16.f;
 
   if constexpr (BF) {
     issue(0);
@@ -459,7 +487,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float sv = S[kt][i] * c;
+        float sv = S[kt][i];
         if (kb0 + 16 * kt + 4 * g + i >= k1) sv = -INFINITY;
         S[kt][i] = sv;
         mb = fmaxf(mb, sv);
@@ -479,8 +507,10 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
         ps += pv;
       }
     lsum = lsum * al + ps;
+    if (__builtin_amdgcn_ballot_w64(al != 1.f)) {
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) O[dt] *= al;
+      for (int dt = 0; dt < 4; ++dt) O[dt] *= al;
+    }
 #pragma unroll
     for (int kb = 0; kb < kKvb / KB; ++kb) {
       const Fr<E> pf = acc_frag<E>(S, kb);
@@ -554,9 +584,12 @@ static hipError_t attn_launch_t(const AttnLaunch& a, hipStream_t st) {
   const int64_t ntok = a.decode ? a.B : (int64_t)a.B * a.T;
   const int H = a.Hq + a.Hkv;
   const int64_t rows = ntok * H;
+  RopeFreq fr{};
+  for (int j = 0; j < a.rope_dim / 2; ++j)
+    fr.inv[j] = std::exp(-(2.0 * j / a.rope_dim) * std::log((double)a.theta));
   hipLaunchKernelGGL((attn_prep_kernel<E>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st,
                      (const E*)a.q, (const E*)a.k, (const E*)a.v, a.qw, a.kw, a.eps, a.rope_dim,
-                     a.theta, a.decode ? a.pos : nullptr, (E*)a.qrot, (E*)a.kc, (E*)a.vc_write, ntok,
+                     fr, a.decode ? a.pos : nullptr, (E*)a.qrot, (E*)a.kc, (E*)a.vc_write, ntok,
                      a.decode ? 1 : a.T, a.cache_len, a.Hq, a.Hkv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -564,9 +597,11 @@ static hipError_t attn_launch_t(const AttnLaunch& a, hipStream_t st) {
   if (!a.decode) {
     constexpr int QT = 1, QS = sizeof(E) == 2 ? 2 : 1;
     const int nqb = (a.T + 16 * QT * QS - 1) / (16 * QT * QS);
-    hipLaunchKernelGGL((attn_fwd_kernel<E, QT, QS>), dim3(nqb, a.Hkv, a.B), dim3(64 * G * QS), 0, st,
+    const int nst = a.Hkv * a.B;
+    const int nwg = (nst <= 8 && 8 % nst == 0) ? 8 * ((nqb + 8 / nst - 1) / (8 / nst)) : nqb * nst;
+    hipLaunchKernelGGL((attn_fwd_kernel<E, QT, QS>), dim3(nwg), dim3(64 * G * QS), 0, st,
                        (const E*)a.qrot, (const E*)a.kc, (const E*)a.vc_read, (const E*)a.gate,
-                       (E*)a.o, a.T, a.cache_len, a.Hq, a.Hkv, nqb);
+                       (E*)a.o, a.T, a.cache_len, a.Hq, a.Hkv, nqb, a.B);
     return hipGetLastError();
   }
   const int ns = attn_decode_splits(a.cache_len);
