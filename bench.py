@@ -223,6 +223,64 @@ def timed_backward(gdn, T, steps, warmup):
                 tflops=backward_flops(T) / (ms * 1e-3) / 1e12)
 
 
+ATT_HQ, ATT_HKV, ATT_D = 24, 4, 256
+
+
+def attention_prefill_flops(T, B=1):
+    """Algorithmic FLOPs of a causal gated-attention prefill: Q K^T and P V over
+    the T (T + 1) / 2 query-key pairs of every query head, 2 FLOPs per
+    multiply-add each."""
+    return B * ATT_HQ * 4 * ATT_D * T * (T + 1) / 2
+
+
+def attention_decode_bytes(B, n):
+    """Algorithmic bytes of one decode step over n cached keys per sequence:
+    the bf16 keys and values read once (the query, gate, output and the new
+    key/value row are under 0.1 % of it)."""
+    return B * n * ATT_HKV * ATT_D * 2 * 2
+
+
+def timed_attention(gdn, T, Bd, Ld, steps):
+    """Gated attention layer: a T-token prefill (batch 1) and a decode step of
+    Bd sequences with Ld - 1 cached keys each (bf16)."""
+    d = {k: v.to("cuda") for k, v in synth.attention_inputs(1, T, torch.bfloat16, seed=1201).items()}
+    ws = torch.empty(gdn.attn_prefill_workspace_bytes(1, T), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(d["q"])
+
+    def pre():
+        gdn.attn_prefill(d["q"], d["k"], d["v"], d["gate"], d["q_norm_w"], d["k_norm_w"], o=o,
+                         workspace=ws)
+
+    g = torch.Generator().manual_seed(1202)
+    kc = torch.randn((Bd, Ld, ATT_HKV, ATT_D), generator=g).to(torch.bfloat16).to("cuda")
+    vc = torch.randn((Bd, Ld, ATT_HKV, ATT_D), generator=g).to(torch.bfloat16).to("cuda")
+    s = {k: v.to("cuda") for k, v in synth.attention_decode_inputs(Bd, 0, torch.bfloat16,
+                                                                    seed=1203).items()}
+    pos = torch.full((Bd,), Ld - 1, dtype=torch.int32, device="cuda")
+    wsd = torch.empty(gdn.attn_decode_workspace_bytes(Bd, Ld), dtype=torch.uint8, device="cuda")
+    od = torch.empty_like(s["q"])
+
+    def dec():
+        gdn.attn_decode(s["q"], s["k"], s["v"], s["gate"], kc, vc, pos, d["q_norm_w"],
+                        d["k_norm_w"], o=od, workspace=wsd)
+
+    res = {}
+    stream = torch.cuda.current_stream()
+    for name, fn in (("prefill", pre), ("decode", dec)):
+        for _ in range(3):
+            fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / steps
+    return res
+
+
 def cpu_baseline(inp, T_sample, min_seconds=10.0, max_calls=64):
     """The float64 oracle, untuned, on the same workload: the first T_sample
     tokens of every value head, called repeatedly until about min_seconds of
@@ -307,6 +365,13 @@ def main():
     log("backward %.3f ms, %.2f M tokens/s, %.1f TFLOP/s" %
         (bwd["ms"], bwd["tokens_per_s"] / 1e6, bwd["tflops"]))
 
+    log("gated attention layer: prefill T=%d, decode 64 x 8192 keys" % T)
+    att = timed_attention(gdn, T, 64, 8192, 20)
+    att_tf = attention_prefill_flops(T) / (att["prefill"] * 1e-3) / 1e12
+    att_gbs = attention_decode_bytes(64, 8192) / (att["decode"] * 1e-3) / 1e9
+    log("attention prefill %.3f ms (%.1f TFLOP/s), decode %.4f ms (%.1f GB/s)"
+        % (att["prefill"], att_tf, att["decode"], att_gbs))
+
     out = {
         "metric": "GDN prefill tokens/s @T=8192 (% MFMA peak) + decode state GB/s (% HBM peak)",
         "value": tok_s,
@@ -360,6 +425,15 @@ def main():
         "tflops_algorithmic": bwd["tflops"], "frac_bf16_mfma_peak": bwd["tflops"] / PEAK_BF16_TFLOPS,
         "gflop_per_call": backward_flops(T) / 1e9,
         "grad_kernel_gflop_per_launch": grad_kernel_flops(T) / 1e9}
+    out["attention"] = {
+        "workload": "gated attention layer (24 query / 4 key-value heads, head dim 256, "
+                    "QK-Norm, RoPE on 64 channels with theta 1e7, causal, sigmoid output gate), "
+                    "bf16; prefill batch 1 T=8192; decode 64 sequences x 8192 cached keys",
+        "prefill": {"ms": att["prefill"], "tokens_per_s": T / (att["prefill"] * 1e-3),
+                    "tflops_algorithmic": att_tf, "frac_bf16_mfma_peak": att_tf / PEAK_BF16_TFLOPS,
+                    "gflop_per_call": attention_prefill_flops(T) / 1e9},
+        "decode": {"ms_per_step": att["decode"], "gbs": att_gbs, "frac": att_gbs / PEAK_HBM_GBS,
+                   "cache_bytes_per_step": attention_decode_bytes(64, 8192)}}
     if args.extended:
         log("extended: T=262144")
         inp3 = {k: (v.to("cuda") if isinstance(v, torch.Tensor) else v)

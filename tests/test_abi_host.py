@@ -307,3 +307,79 @@ def test_backward_workspace_and_empty_batch(gdn, lib):
     assert gdn.prefill_bwd_workspace_bytes(1, 0, 16, 48) == 0
     assert gdn.prefill_bwd_workspace_bytes(1, 64, 16, 48, D=64) == 0
     assert bwd_call(lib, B=0) == OK
+
+
+def attn_prefill_call(lib, **kw):
+    a = dict(q=addr(0), k=addr(1), v=addr(2), gate=addr(3), qw=addr(4), kw=addr(5), eps=1e-6,
+             o=addr(6), kc=addr(7), vc=addr(8), cache_len=256, B=1, T=128, Hq=24, Hkv=4, D=256,
+             rope=64, theta=1e7, dt=BF16, ws=addr(9), ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return lib.gdn_attn_prefill(a["q"], a["k"], a["v"], a["gate"], a["qw"], a["kw"], a["eps"],
+                                a["o"], a["kc"], a["vc"], a["cache_len"], a["B"], a["T"], a["Hq"],
+                                a["Hkv"], a["D"], a["rope"], a["theta"], a["dt"], a["ws"],
+                                a["ws_bytes"], a["stream"])
+
+
+def attn_decode_call(lib, **kw):
+    a = dict(q=addr(0), k=addr(1), v=addr(2), gate=addr(3), qw=addr(4), kw=addr(5), eps=1e-6,
+             o=addr(6), kc=addr(7), vc=addr(8), pos=addr(10), cache_len=256, B=4, Hq=24, Hkv=4,
+             D=256, rope=64, theta=1e7, dt=BF16, ws=addr(9), ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return lib.gdn_attn_decode(a["q"], a["k"], a["v"], a["gate"], a["qw"], a["kw"], a["eps"],
+                               a["o"], a["kc"], a["vc"], a["pos"], a["cache_len"], a["B"], a["Hq"],
+                               a["Hkv"], a["D"], a["rope"], a["theta"], a["dt"], a["ws"],
+                               a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=128), EUNSUP),
+    (dict(Hq=25), ESHAPE),
+    (dict(Hq=48), EUNSUP),                    # 12 query heads per key/value head
+    (dict(rope=60), EUNSUP),
+    (dict(rope=264), EUNSUP),
+    (dict(theta=0.0), ESHAPE),
+    (dict(eps=-1.0), ESHAPE),
+    (dict(T=-1), ESHAPE),
+    (dict(dt=5), EUNSUP),
+    (dict(q=None), ENULL),
+    (dict(gate=None), ENULL),
+    (dict(vc=None), ENULL),                   # caches come in pairs
+    (dict(cache_len=100), ESHAPE),            # cache shorter than the prompt
+    (dict(ws=None), EWS),
+    (dict(ws_bytes=4096), EWS),
+    (dict(q=addr(0, 8)), EALIGN),
+    (dict(qw=addr(4, 2)), EALIGN),
+    (dict(o=addr(0, 512)), EALIAS),           # o inside q
+    (dict(kc=addr(6)), EALIAS),               # key cache is o
+    (dict(ws=addr(8, 1024)), EALIAS),         # workspace inside the value cache
+])
+def test_attn_prefill_validation(lib, kw, code):
+    assert attn_prefill_call(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=128), EUNSUP),
+    (dict(cache_len=0), ESHAPE),
+    (dict(pos=None), ENULL),
+    (dict(kc=None), ENULL),
+    (dict(pos=addr(10, 2)), EALIGN),
+    (dict(o=addr(3, 64)), EALIAS),            # o inside the gate
+    (dict(ws=None), EWS),
+])
+def test_attn_decode_validation(lib, kw, code):
+    assert attn_decode_call(lib, **kw) == code
+
+
+def test_attn_empty_calls_and_workspace(gdn, lib):
+    assert attn_prefill_call(lib, T=0) == OK and attn_prefill_call(lib, B=0) == OK
+    assert attn_decode_call(lib, B=0) == OK
+    # prefill: rotated queries and keys in the element type
+    assert gdn.attn_prefill_workspace_bytes(1, 64) == 64 * 24 * 256 * 2 + 64 * 4 * 256 * 2
+    # decode: rotated queries, then per 512-key split a max, a sum and 256 fp32
+    def r256(x):
+        return (x + 255) // 256 * 256
+
+    for L, ns in ((512, 1), (1024, 2), (8192, 16)):
+        want = r256(2 * 24 * 256 * 2) + 2 * r256(2 * 24 * ns * 4) + r256(2 * 24 * ns * 256 * 4)
+        assert gdn.attn_decode_workspace_bytes(2, L) == want
+    assert gdn.attn_decode_workspace_bytes(2, 0) == 0
