@@ -526,8 +526,8 @@ size_t attn_prefill_ws(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, gdn_dtype 
   return round256((size_t)B * T * Hq * kAttnD * esize(dt)) +
          round256((size_t)B * T * Hkv * kAttnD * esize(dt));
 }
-size_t attn_decode_ws(int64_t B, int64_t cache_len, int64_t Hq, gdn_dtype dt) {
-  const int64_t ns = gdn::attn_decode_splits((int)cache_len);
+size_t attn_decode_ws(int64_t B, int64_t cache_len, int64_t Hq, int64_t Hkv, gdn_dtype dt) {
+  const int64_t ns = gdn::attn_decode_splits((int)B, (int)Hkv, (int)cache_len);
   return round256((size_t)B * Hq * kAttnD * esize(dt)) + 2 * round256((size_t)B * Hq * ns * 4) +
          round256((size_t)B * Hq * ns * kAttnD * 4);
 }
@@ -542,7 +542,7 @@ size_t gdn_attn_prefill_workspace_bytes(int32_t B, int32_t T, int32_t H_q, int32
 size_t gdn_attn_decode_workspace_bytes(int32_t B, int32_t cache_len, int32_t H_q, int32_t H_kv,
                                        int32_t D, gdn_dtype dt) {
   if (check_attn_dims(B, H_q, H_kv, D, 0, 1.f, 0.f, dt) != GDN_OK || cache_len <= 0) return 0;
-  return attn_decode_ws(B, cache_len, H_q, dt);
+  return attn_decode_ws(B, cache_len, H_q, H_kv, dt);
 }
 
 gdn_status gdn_attn_prefill(const void* q, const void* k, const void* v, const void* gate,
@@ -610,7 +610,7 @@ gdn_status gdn_attn_decode(const void* q, const void* k, const void* v, const vo
   if ((int64_t)B * cache_len > (int64_t(1) << 31) / 64) return GDN_ERR_UNSUPPORTED;
   if (B == 0) return GDN_OK;
   if (!q || !k || !v || !gate || !o || !k_cache || !v_cache || !pos) return GDN_ERR_NULL;
-  const size_t need = attn_decode_ws(B, cache_len, H_q, dt);
+  const size_t need = attn_decode_ws(B, cache_len, H_q, H_kv, dt);
   if (!workspace) return GDN_ERR_WORKSPACE;
   if (workspace_bytes < need) return GDN_ERR_WORKSPACE;
   const void* p16[] = {q, k, v, gate, o, k_cache, v_cache, workspace};
@@ -633,7 +633,7 @@ gdn_status gdn_attn_decode(const void* q, const void* k, const void* v, const vo
       if (overlap(outs[a], outs[c])) return GDN_ERR_ALIAS;
   }
   char* ws = static_cast<char*>(workspace);
-  const int64_t ns = gdn::attn_decode_splits(cache_len);
+  const int64_t ns = gdn::attn_decode_splits(B, H_kv, cache_len);
   const size_t oq = round256((size_t)B * H_q * kAttnD * es);
   const size_t om = round256((size_t)B * H_q * ns * 4);
   gdn::AttnLaunch a{};

@@ -30,14 +30,16 @@
 //    conflicts.  Only the diagonal block is masked.  Workgroups are issued
 //    longest (latest query block) first.
 //  * attn_decode + attn_combine: split-K over the cached keys.  One workgroup
-//    per (split of 512 keys, key/value head, sequence); 64-key blocks
-//    double-buffered in LDS; the six query heads are the MFMA N dimension and
+//    per (split of keys, key/value head, sequence), the split sized for about
+//    two workgroups per CU; 32-key blocks
+//    double-buffered in LDS (69 KB, two workgroups per CU); the six query heads are the MFMA N dimension and
 //    each of the four waves produces 64 of the 256 output channels; partial
 //    (max, sum, O) per split, merged and gated by the combine kernel.
 #include "gdn_device.hpp"
 #include "gdn_frag.hpp"
 #include "gdn_launch.hpp"
 
+#include <algorithm>
 #include <cmath>
 
 namespace gdn {
@@ -46,7 +48,7 @@ using namespace frag;
 
 constexpr int kDh = 256;        // head dim
 constexpr int kKvb = 64;        // keys per prefill block
-constexpr int kSplit = 512;     // keys per decode split
+// decode: keys per split are chosen per call (attn_decode_split)
 
 // ------------------------------------------------------------ prep
 // theta^(-2j / rope_dim) for j < rope_dim / 2, formed on the host in double
@@ -147,9 +149,9 @@ __device__ __forceinline__ void stage_rows(Lds<E, W> dst, const E* src, int64_t 
 //  * VTile rows are 544 bytes (32 bytes of padding).  Transposed reads
 //    (ds_read_b64_tr_b16; lane (r, g) reads 8 bytes of row 4g + r/4 at
 //    channel 4(r%4)) land on banks 8 (4g + r/4) + 2 (r%4) (+1): all 64 once.
-template <int ROWB>
+template <int ROWB, int ROWS = kKvb>
 struct PadTile {
-  static constexpr int kBytes = kKvb * ROWB;
+  static constexpr int kBytes = ROWS * ROWB;
   char* p;
   // A/B fragment with the lane index along rows (keys): slots are channels
   // k0 + kslot(g, j).
@@ -170,19 +172,22 @@ struct PadTile {
 };
 typedef PadTile<528> KTile;
 typedef PadTile<544> VTile;
+constexpr int kDkb = 32;                  // keys per decode block
+typedef PadTile<528, kDkb> KTileD;
+typedef PadTile<544, kDkb> VTileD;
 
 // 64 rows (rows >= L repeat row L-1) of 256 bf16 with row stride ld into a
 // padded tile, copied straight into LDS; wave w of nw issues copies w, w + nw,
 // ...  Copy `it` fills LDS bytes [1024 it, 1024 it + 1024): a lane whose 16
 // bytes fall in padding is switched off.
-template <int ROWB>
+template <int ROWB, int ROWS = kKvb>
 __device__ __forceinline__ void copy_tile(const bf16* src, int64_t ld, int L, char* dst, int w,
                                           int nw) {
-  constexpr int NIT = (kKvb * ROWB + 1023) / 1024;
+  constexpr int NIT = (ROWS * ROWB + 1023) / 1024;
   const int l = lane_id();
   for (int it = w; it < NIT; it += nw) {
     const int byte = 1024 * it + 16 * l, row = byte / ROWB, off = byte - row * ROWB;
-    if (row < kKvb && off < 2 * kDh)
+    if (row < ROWS && off < 2 * kDh)
       dma16(src + (int64_t)min(row, L - 1) * ld + off / 2, dst + 1024 * it);
   }
 }
@@ -394,13 +399,20 @@ __global__ __launch_bounds__(QS == 2 ? 768 : 512) void attn_fwd_kernel(
 // kernel is bound by the cache read, not by the matrix units), so the waves
 // never exchange anything.
 template <typename E>
-using DecSmem = FwdSmem<E>;
+struct DecSmem {
+  static constexpr bool BF = sizeof(E) == 2;
+  static constexpr int NB = BF ? 2 : 1;
+  static constexpr int KB_ = BF ? KTileD::kBytes : Lds<E, kDh>::size(kDkb) * (int)sizeof(E);
+  static constexpr int VB_ = BF ? VTileD::kBytes : Lds<E, kDh>::size(kDkb) * (int)sizeof(E);
+  alignas(16) char K[NB][KB_];
+  alignas(16) char V[NB][VB_];
+};
 
 template <typename E>
 __global__ __launch_bounds__(256) void attn_decode_kernel(
     const E* __restrict__ qr, const E* __restrict__ kc, const E* __restrict__ vc,
     const int32_t* __restrict__ pos, float* __restrict__ pm, float* __restrict__ pl,
-    float* __restrict__ po, int cache_len, int Hq, int Hkv, int ns) {
+    float* __restrict__ po, int cache_len, int Hq, int Hkv, int ns, int spl) {
   constexpr bool BF = sizeof(E) == 2;
   constexpr int KB = FragOf<E>::KB, NKB = kDh / KB;
   __shared__ DecSmem<E> sm;
@@ -408,7 +420,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
   const int w = __builtin_amdgcn_readfirstlane(wave_id()), l = lane_id(), r = l & 15, g = l >> 4;
   const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int n = min(max(pos[b], 0), cache_len - 1) + 1;   // keys 0 .. pos inclusive
-  const int k0 = s * kSplit, k1 = min(n, k0 + kSplit);
+  const int k0 = s * spl, k1 = min(n, k0 + spl);
   const size_t pidx = ((size_t)b * Hq + kvh * G) * ns + s;  // head kvh*G, split s
   if (k0 >= k1) {
     // empty split: a neutral partial
@@ -421,13 +433,13 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
   const int64_t kv_ld = (int64_t)Hkv * kDh;
   const E* kbase = kc + ((int64_t)b * cache_len * Hkv + kvh) * kDh;
   const E* vbase = vc + ((int64_t)b * cache_len * Hkv + kvh) * kDh;
-  const int nblk = (k1 - k0 + kKvb - 1) / kKvb;
+  const int nblk = (k1 - k0 + kDkb - 1) / kDkb;
 
   auto issue = [&](int j) {
     if constexpr (BF) {
-      const int kb0 = k0 + j * kKvb;
-      copy_tile<528>(kbase + (int64_t)kb0 * kv_ld, kv_ld, k1 - kb0, sm.K[j & 1], w, 4);
-      copy_tile<544>(vbase + (int64_t)kb0 * kv_ld, kv_ld, k1 - kb0, sm.V[j & 1], w, 4);
+      const int kb0 = k0 + j * kDkb;
+      copy_tile<528, kDkb>(kbase + (int64_t)kb0 * kv_ld, kv_ld, k1 - kb0, sm.K[j & 1], w, 4);
+      copy_tile<544, kDkb>(vbase + (int64_t)kb0 * kv_ld, kv_ld, k1 - kb0, sm.V[j & 1], w, 4);
     }
   };
 
@@ -450,41 +462,42 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     barrier_lds();
   }
   for (int j = 0; j < nblk; ++j) {
-    const int kb0 = k0 + j * kKvb;
+    const int kb0 = k0 + j * kDkb;
     if constexpr (BF) {
       if (j + 1 < nblk) issue(j + 1);
     } else {
       __syncthreads();
-      stage_rows<E, kDh, kKvb>(Lds<E, kDh>{reinterpret_cast<E*>(sm.K[0])},
+      stage_rows<E, kDh, kDkb>(Lds<E, kDh>{reinterpret_cast<E*>(sm.K[0])},
                                kbase + (int64_t)kb0 * kv_ld, kv_ld, k1 - kb0, 256);
-      stage_rows<E, kDh, kKvb>(Lds<E, kDh>{reinterpret_cast<E*>(sm.V[0])},
+      stage_rows<E, kDh, kDkb>(Lds<E, kDh>{reinterpret_cast<E*>(sm.V[0])},
                                vbase + (int64_t)kb0 * kv_ld, kv_ld, k1 - kb0, 256);
       __syncthreads();
     }
     const int nb = BF ? (j & 1) : 0;
     const Lane ln = lane_here();
     const auto Ks = [&]() {
-      if constexpr (BF) return KTile{sm.K[nb]};
+      if constexpr (BF) return KTileD{sm.K[nb]};
       else return Lds<E, kDh>{reinterpret_cast<E*>(sm.K[nb])};
     }();
     const auto Vs = [&]() {
-      if constexpr (BF) return VTile{sm.V[nb]};
+      if constexpr (BF) return VTileD{sm.V[nb]};
       else return Lds<E, kDh>{reinterpret_cast<E*>(sm.V[nb])};
     }();
     // S^T: rows keys kb0 + 16kt + 4g + i, column head r
-    f32x4 S[4];
+    constexpr int NKT = kDkb / 16;
+    f32x4 S[NKT];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) S[kt] = zero4();
+    for (int kt = 0; kt < NKT; ++kt) S[kt] = zero4();
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
+      for (int kt = 0; kt < NKT; ++kt) {
         if constexpr (BF) S[kt] = mma(S[kt], Ks.rm(16 * kt, KB * kb, ln), Qf[kb]);
         else S[kt] = mma(S[kt], Ks.rm(16 * kt + r, KB * kb, ln), Qf[kb]);
       }
     float mb = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float sv = S[kt][i];
@@ -499,7 +512,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     m = mn;
     float ps = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float pv = hw_exp2(S[kt][i] - mn);
@@ -512,7 +525,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
       for (int dt = 0; dt < 4; ++dt) O[dt] *= al;
     }
 #pragma unroll
-    for (int kb = 0; kb < kKvb / KB; ++kb) {
+    for (int kb = 0; kb < kDkb / KB; ++kb) {
       const Fr<E> pf = acc_frag<E>(S, kb);
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
@@ -576,7 +589,19 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
 
 }  // namespace attn
 
-int attn_decode_splits(int cache_len) { return (cache_len + attn::kSplit - 1) / attn::kSplit; }
+// Decode split: about two workgroups per CU over the (sequence, key/value head)
+// streams, splits a multiple of 32 keys.
+int attn_decode_split(int B, int Hkv, int cache_len) {
+  const int64_t streams = (int64_t)B * Hkv;
+  int64_t ns = (512 + streams - 1) / streams;
+  ns = std::max<int64_t>(1, std::min<int64_t>(ns, (cache_len + 31) / 32));
+  const int64_t spl = ((cache_len + ns - 1) / ns + 31) / 32 * 32;
+  return (int)spl;
+}
+int attn_decode_splits(int B, int Hkv, int cache_len) {
+  const int spl = attn_decode_split(B, Hkv, cache_len);
+  return (cache_len + spl - 1) / spl;
+}
 
 template <typename E>
 static hipError_t attn_launch_t(const AttnLaunch& a, hipStream_t st) {
@@ -604,10 +629,12 @@ static hipError_t attn_launch_t(const AttnLaunch& a, hipStream_t st) {
                        (E*)a.o, a.T, a.cache_len, a.Hq, a.Hkv, nqb, a.B);
     return hipGetLastError();
   }
-  const int ns = attn_decode_splits(a.cache_len);
+  const int spl = attn_decode_split(a.B, a.Hkv, a.cache_len);
+  const int ns = attn_decode_splits(a.B, a.Hkv, a.cache_len);
   hipLaunchKernelGGL((attn_decode_kernel<E>), dim3(ns, a.Hkv, a.B), dim3(256), 0, st,
                      (const E*)a.qrot, (const E*)a.kc,
-                     (const E*)a.vc_read, a.pos, a.pm, a.pl, a.po, a.cache_len, a.Hq, a.Hkv, ns);
+                     (const E*)a.vc_read, a.pos, a.pm, a.pl, a.po, a.cache_len, a.Hq, a.Hkv, ns,
+                     spl);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int crow = a.B * a.Hq;

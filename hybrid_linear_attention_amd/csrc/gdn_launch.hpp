@@ -69,7 +69,8 @@ struct AttnLaunch {
   bool decode, bf16_io;
 };
 hipError_t launch_attention(const AttnLaunch& a, hipStream_t st);
-int attn_decode_splits(int cache_len);
+int attn_decode_split(int B, int Hkv, int cache_len);
+int attn_decode_splits(int B, int Hkv, int cache_len);
 
 hipError_t launch_prepare(const PrefillLaunch& a, hipStream_t st);
 hipError_t launch_scan(const PrefillLaunch& a, hipStream_t st);

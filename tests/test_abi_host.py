@@ -379,7 +379,8 @@ def test_attn_empty_calls_and_workspace(gdn, lib):
     def r256(x):
         return (x + 255) // 256 * 256
 
-    for L, ns in ((512, 1), (1024, 2), (8192, 16)):
-        want = r256(2 * 24 * 256 * 2) + 2 * r256(2 * 24 * ns * 4) + r256(2 * 24 * ns * 256 * 4)
-        assert gdn.attn_decode_workspace_bytes(2, L) == want
+    # splits: about 512 workgroups over the B * 4 streams, multiples of 32 keys
+    for B, L, ns in ((2, 512, 16), (2, 8192, 64), (64, 8192, 2), (64, 100, 2), (1, 40, 2)):
+        want = r256(B * 24 * 256 * 2) + 2 * r256(B * 24 * ns * 4) + r256(B * 24 * ns * 256 * 4)
+        assert gdn.attn_decode_workspace_bytes(B, L) == want, (B, L)
     assert gdn.attn_decode_workspace_bytes(2, 0) == 0
