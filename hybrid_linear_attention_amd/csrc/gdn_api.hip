@@ -555,6 +555,7 @@ gdn_status gdn_attn_prefill(const void* q, const void* k, const void* v, const v
   if (s != GDN_OK) return s;
   if (T < 0) return GDN_ERR_SHAPE;
   if ((int64_t)B * T > (int64_t(1) << 31) / 64) return GDN_ERR_UNSUPPORTED;
+  if ((int64_t)B * T * (H_q + H_kv) >= (int64_t(1) << 31)) return GDN_ERR_UNSUPPORTED;
   if (B == 0 || T == 0) return GDN_OK;
   if (!q || !k || !v || !gate || !o) return GDN_ERR_NULL;
   if ((k_cache == nullptr) != (v_cache == nullptr)) return GDN_ERR_NULL;
@@ -608,6 +609,7 @@ gdn_status gdn_attn_decode(const void* q, const void* k, const void* v, const vo
   if (s != GDN_OK) return s;
   if (cache_len <= 0) return GDN_ERR_SHAPE;
   if ((int64_t)B * cache_len > (int64_t(1) << 31) / 64) return GDN_ERR_UNSUPPORTED;
+  if ((int64_t)B * (H_q + H_kv) >= (int64_t(1) << 31)) return GDN_ERR_UNSUPPORTED;
   if (B == 0) return GDN_OK;
   if (!q || !k || !v || !gate || !o || !k_cache || !v_cache || !pos) return GDN_ERR_NULL;
   const size_t need = attn_decode_ws(B, cache_len, H_q, H_kv, dt);

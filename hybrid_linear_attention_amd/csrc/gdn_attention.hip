@@ -13,9 +13,8 @@
 //
 // Kernels:
 //  * attn_prep: one wave per (token, head) row: RMSNorm, weight, rotation.
-//    The angle is formed and reduced modulo 2 pi in fp64 from frequencies the
-//    host computes in double (at position 262,143 an fp32 angle would be off
-//    by ~1e-2 rad), then sin/cos in fp32.  Query
+//    The angle is formed in turns and reduced in fp64 (at position 262,143 an
+//    fp32 angle would be off by ~1e-2 rad), then the hardware sin/cos in fp32.  Query
 //    rows go to the workspace, key rows (and the value rows, unchanged) to the
 //    key/value cache at their positions.
 //  * attn_fwd (prefill): one workgroup per (32 query rows, key/value head,
@@ -51,78 +50,91 @@ constexpr int kKvb = 64;        // keys per prefill block
 // decode: keys per split are chosen per call (attn_decode_split)
 
 // ------------------------------------------------------------ prep
-// theta^(-2j / rope_dim) for j < rope_dim / 2, formed on the host in double
-// precision and passed by value with the launch.
-struct RopeFreq {
-  double inv[kDh / 2];
-};
 
-// rows: ntok * (Hq + Hkv); row = tok * (Hq + Hkv) + head, heads >= Hq are keys.
+// Rows of token tok: heads 0 .. Hq-1 are queries, Hq .. Hq+Hkv-1 keys.
 // Token tok = b * T + t sits at position pos[b] (decode) or t (prefill, pos null).
 template <typename E>
 __global__ __launch_bounds__(256) void attn_prep_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ qw, const float* __restrict__ kw, float eps, int rope_dim,
-    RopeFreq fr, const int32_t* __restrict__ pos, E* __restrict__ qo, E* __restrict__ kc,
+    double log2_theta, const int32_t* __restrict__ pos, E* __restrict__ qo, E* __restrict__ kc,
     E* __restrict__ vc, int64_t ntok, int T, int cache_len, int Hq, int Hkv) {
-  const int l = lane_id();
-  const int64_t row = (int64_t)blockIdx.x * 4 + wave_id();
+  // one workgroup per token: its Hq + Hkv rows share one position, so each
+  // lane forms its rotation's sin and cos once and applies them to every row
+  const int l = lane_id(), w = wave_id();
+  const int64_t tok = blockIdx.x;
   const int H = Hq + Hkv;
-  if (row >= ntok * H) return;
-  const int64_t tok = row / H;
-  const int hd = (int)(row - tok * H);
-  const bool is_q = hd < Hq;
   const int b = (int)(tok / T), t = (int)(tok - (int64_t)b * T);
   int p = pos ? pos[b] : t;
-  p = min(max(p, 0), cache_len - 1);                // stays inside the cache
-  const E* src = is_q ? q + (tok * Hq + hd) * kDh : k + (tok * Hkv + (hd - Hq)) * kDh;
-  float x[4];
-  if constexpr (sizeof(E) == 2) {
-    const bf16x4 r4 = *reinterpret_cast<const bf16x4*>(src + 4 * l);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = (float)r4[i];
-  } else {
-    const f32x4 r4 = *reinterpret_cast<const f32x4*>(src + 4 * l);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = r4[i];
-  }
-  float ss = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
-  ss = wave_sum(ss);
-  const float rs = 1.f / sqrtf(ss * (1.f / kDh) + eps);
-  const float* w = is_q ? qw : kw;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) x[i] *= rs * (w ? w[4 * l + i] : 1.f);
-  // rotation: lanes [0, half/4) hold the first halves, their partners sit
-  // half/4 lanes up
+  p = min(max(p, 0), cache_len - 1);              // stays inside the cache
   const int half = rope_dim >> 1, hl = half >> 2;
-  float y[4];
   const int partner = l < hl ? l + hl : (l < 2 * hl ? l - hl : l);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) y[i] = __shfl(x[i], partner, 64);
-  if (l < 2 * hl) {
-    const bool first = l < hl;
+  const bool first = l < hl, rot = l < 2 * hl;
+  float cs[4] = {1.f, 1.f, 1.f, 1.f}, sn[4] = {0.f, 0.f, 0.f, 0.f};
+  if (rot) {
+    const int jl = first ? l : l - hl;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int j = 4 * (first ? l : l - hl) + i;
-      double ang = (double)p * fr.inv[j];
-      ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
-      float sn, cs;
-      sincosf((float)ang, &sn, &cs);
-      x[i] = first ? x[i] * cs - y[i] * sn : x[i] * cs + y[i] * sn;
+      // theta^(-2j / rope_dim) / (2 pi) turns per position, the angle reduced
+      // in fp64 (at position 262,143 an fp32 angle would be off by ~1e-2 rad),
+      // then the hardware sin and cos, which take turns
+      const double fq = exp2(-(2.0 * (4 * jl + i) / rope_dim) * log2_theta) * 0.15915494309189535;
+      double rev = (double)p * fq;
+      rev -= rint(rev);
+      sn[i] = __builtin_amdgcn_sinf((float)rev);
+      cs[i] = __builtin_amdgcn_cosf((float)rev);
     }
   }
-  E* dst = is_q ? qo + (tok * Hq + hd) * kDh
-                : kc + (((int64_t)b * cache_len + p) * Hkv + (hd - Hq)) * kDh;
-  // queries carry the softmax scale log2(e) / sqrt(256) (the attention kernels
-  // work in base 2); the cache keeps the keys themselves
-  const float sc = is_q ? 1.4426950408889634f / 16.f : 1.f;
-  store4(dst + 4 * l, f32x4{x[0] * sc, x[1] * sc, x[2] * sc, x[3] * sc});
-  if (!is_q && vc) {
-    const E* vs = v + (tok * Hkv + (hd - Hq)) * kDh;
-    E* vd = vc + (((int64_t)b * cache_len + p) * Hkv + (hd - Hq)) * kDh;
-    *reinterpret_cast<uint2*>(vd + 4 * l) = *reinterpret_cast<const uint2*>(vs + 4 * l);
-    if constexpr (sizeof(E) == 4)
-      *reinterpret_cast<uint2*>(vd + 4 * l + 2) = *reinterpret_cast<const uint2*>(vs + 4 * l + 2);
+  constexpr int RB = 8;                           // rows per wave per batch
+  for (int hb = w * RB; hb < H; hb += 4 * RB) {
+    f32x4 xs[RB];
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+      const int hd = hb + rr;
+      xs[rr] = zero4();
+      if (hd < H) {
+        const E* src = hd < Hq ? q + (tok * Hq + hd) * kDh : k + (tok * Hkv + (hd - Hq)) * kDh;
+        if constexpr (sizeof(E) == 2) {
+          const bf16x4 r4 = *reinterpret_cast<const bf16x4*>(src + 4 * l);
+          xs[rr] = f32x4{(float)r4[0], (float)r4[1], (float)r4[2], (float)r4[3]};
+        } else {
+          xs[rr] = *reinterpret_cast<const f32x4*>(src + 4 * l);
+        }
+      }
+    }
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+      const int hd = hb + rr;
+      if (hd >= H) break;                         // wave-uniform
+      const bool is_q = hd < Hq;
+      float x[4] = {xs[rr][0], xs[rr][1], xs[rr][2], xs[rr][3]};
+      const float ss = wave_sum(x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3]);
+      const float rs = 1.f / sqrtf(ss * (1.f / kDh) + eps);
+      const float* wt = is_q ? qw : kw;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] *= rs * (wt ? wt[4 * l + i] : 1.f);
+      float y[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[i] = __shfl(x[i], partner, 64);
+      if (rot) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          x[i] = first ? x[i] * cs[i] - y[i] * sn[i] : x[i] * cs[i] + y[i] * sn[i];
+      }
+      E* dst = is_q ? qo + (tok * Hq + hd) * kDh
+                    : kc + (((int64_t)b * cache_len + p) * Hkv + (hd - Hq)) * kDh;
+      // queries carry the softmax scale log2(e) / sqrt(256) (the attention
+      // kernels work in base 2); the cache keeps the keys themselves
+      const float sc = is_q ? 1.4426950408889634f / 16.f : 1.f;
+      store4(dst + 4 * l, f32x4{x[0] * sc, x[1] * sc, x[2] * sc, x[3] * sc});
+      if (!is_q && vc) {
+        const E* vs = v + (tok * Hkv + (hd - Hq)) * kDh;
+        E* vd = vc + (((int64_t)b * cache_len + p) * Hkv + (hd - Hq)) * kDh;
+        *reinterpret_cast<uint2*>(vd + 4 * l) = *reinterpret_cast<const uint2*>(vs + 4 * l);
+        if constexpr (sizeof(E) == 4)
+          *reinterpret_cast<uint2*>(vd + 4 * l + 2) = *reinterpret_cast<const uint2*>(vs + 4 * l + 2);
+      }
+    }
   }
 }
 
@@ -607,14 +619,9 @@ template <typename E>
 static hipError_t attn_launch_t(const AttnLaunch& a, hipStream_t st) {
   using namespace attn;
   const int64_t ntok = a.decode ? a.B : (int64_t)a.B * a.T;
-  const int H = a.Hq + a.Hkv;
-  const int64_t rows = ntok * H;
-  RopeFreq fr{};
-  for (int j = 0; j < a.rope_dim / 2; ++j)
-    fr.inv[j] = std::exp(-(2.0 * j / a.rope_dim) * std::log((double)a.theta));
-  hipLaunchKernelGGL((attn_prep_kernel<E>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st,
+  hipLaunchKernelGGL((attn_prep_kernel<E>), dim3((unsigned)ntok), dim3(256), 0, st,
                      (const E*)a.q, (const E*)a.k, (const E*)a.v, a.qw, a.kw, a.eps, a.rope_dim,
-                     fr, a.decode ? a.pos : nullptr, (E*)a.qrot, (E*)a.kc, (E*)a.vc_write, ntok,
+                     std::log2((double)a.theta), a.decode ? a.pos : nullptr, (E*)a.qrot, (E*)a.kc, (E*)a.vc_write, ntok,
                      a.decode ? 1 : a.T, a.cache_len, a.Hq, a.Hkv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
