@@ -78,6 +78,20 @@ __device__ __forceinline__ Lane lane_opaque() {
   return Lane{l & 15, l >> 4};
 }
 
+// XOR swizzle of the 8-byte units of row `row` of a bf16 matrix with W
+// columns.  64-bit LDS reads are served 32 lanes at a time over 64 banks; the
+// row-pattern fragment read (lane (r, g): row r, unit g) then touches rows
+// 0..15 with two units each, and the transposed read (16 lanes: 4 rows x 4
+// units) four rows of one 32-byte column block.  Rows sharing a 256-byte bank
+// line are spread by ((row / rpl) % nb) in unit bits 2+, and row bit 3 flips
+// unit bit 1, so both reads hit every bank once per pass.  Bit 0 is never
+// flipped: 16-byte pieces stay whole for the direct global->LDS copies.
+template <int W>
+__device__ __forceinline__ int swz_units(int row) {
+  constexpr int rpl = W <= 128 ? 128 / W : 1, nb = W >= 128 ? 8 : W / 16;
+  return (((row / rpl) % nb) << 2) | (((row >> 3) & 1) << 1);
+}
+
 // Row-major matrix of W columns in LDS.  bf16: unpadded rows with 8-byte
 // units XOR-swizzled so that both fragment reads below hit every bank once per
 // pass; fp32: rows padded by 4 floats.
@@ -89,8 +103,7 @@ struct Lds {
   E* p;
   __device__ static int at(int row, int col) {
     if constexpr (BF) {
-      constexpr int rpl = W <= 128 ? 128 / W : 1, nb = W >= 128 ? 8 : W / 16;
-      return row * W + ((((col >> 2) ^ (((row / rpl) % nb) << 2))) << 2) + (col & 3);
+      return row * W + ((((col >> 2) ^ swz_units<W>(row))) << 2) + (col & 3);
     } else {
       return row * LD + col;
     }
@@ -247,12 +260,11 @@ template <int W, int ROWS = kC>
 __device__ __forceinline__ void copy_rows(const bf16* src, int64_t ld, int L, bf16* dst, int w,
                                           int nw) {
   constexpr int RPK = 1024 / (2 * W), NIT = ROWS / RPK;
-  constexpr int rpl = W <= 128 ? 128 / W : 1, nb = W >= 128 ? 8 : W / 16;
   const int l = lane_id();
   const int rin = (16 * l) / (2 * W), pp = ((16 * l) % (2 * W)) / 16;
   for (int it = w; it < NIT; it += nw) {
     const int row = it * RPK + rin;
-    const int lp = pp ^ (((row / rpl) % nb) << 1);
+    const int lp = pp ^ (swz_units<W>(row) >> 1);
     dma16(src + (int64_t)min(row, L - 1) * ld + 8 * lp, reinterpret_cast<char*>(dst) + 1024 * it);
   }
 }
