@@ -316,19 +316,24 @@ __global__ __launch_bounds__(64 * NW) void bwd_chain_bf16_kernel(
     const Lds<E, 64> Ns{const_cast<E*>(B_.N)}, Ms{const_cast<E*>(B_.M)};
 
     // dO fragments (B operand, K = tokens), plain and gamma-scaled (masked)
+    // (loads unconditional, masks as selects: no branches in the chain)
     bf16x8 OB[2], OG[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       OB[kb] = Os.cm(16 * w + r, KB * kb);
+      const f32x4 g0 = *reinterpret_cast<const f32x4*>(&B_.gm[KB * kb + 4 * g]);
+      const f32x4 g1 = *reinterpret_cast<const f32x4*>(&B_.gm[KB * kb + 16 + 4 * g]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int tok = KB * kb + kslot<E>(g, e);
-        OG[kb][e] = (bf16)(tok < L ? B_.gm[tok] * (float)OB[kb][e] : 0.f);
+        const float gv = e < 4 ? g0[e] : g1[e - 4];
+        OG[kb][e] = (bf16)((tok < L ? gv : 0.f) * (float)OB[kb][e]);
       }
     }
     f32x4 dD[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
+      const f32x4 dc4 = *reinterpret_cast<const f32x4*>(&B_.dc[16 * mt + 4 * g]);
       f32x4 p = zero4(), m = zero4();
 #pragma unroll
       for (int kb = 0; kb < kD / KB; ++kb) p = mma(p, Ks.rm(16 * mt + r, KB * kb), acc_frag<E>(DT, kb));
@@ -336,7 +341,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chain_bf16_kernel(
       for (int kb = 0; kb < kC / KB; ++kb)
         if (!blk_below<E>(mt, kb)) m = mma(m, Ms.cm(16 * mt + r, KB * kb), OB[kb]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dD[mt][i] = m[i] + B_.dc[16 * mt + 4 * g + i] * p[i];
+      for (int i = 0; i < 4; ++i) dD[mt][i] = m[i] + dc4[i] * p[i];
     }
     f32x4 Z[4];
 #pragma unroll
@@ -345,10 +350,12 @@ __global__ __launch_bounds__(64 * NW) void bwd_chain_bf16_kernel(
 #pragma unroll
       for (int kb = 0; kb < kC / KB; ++kb)
         if (!blk_below<E>(mt, kb)) y = mma(y, Ns.cm(16 * mt + r, KB * kb), acc_frag<E>(dD, kb));
+      const f32x4 g4 = *reinterpret_cast<const f32x4*>(&B_.gm[16 * mt + 4 * g]);
+      const f32x4 b4 = *reinterpret_cast<const f32x4*>(&B_.bt[16 * mt + 4 * g]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tok = 16 * mt + 4 * g + i;
-        Z[mt][i] = tok < L ? -B_.gm[tok] * B_.bt[tok] * y[i] : 0.f;
+        Z[mt][i] = (tok < L ? -g4[i] * b4[i] : 0.f) * y[i];
       }
     }
     const float gl = B_.gm[kC - 1];
