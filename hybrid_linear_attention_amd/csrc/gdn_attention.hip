@@ -173,6 +173,11 @@ struct PadTile {
     const bf16x4 hi = *reinterpret_cast<const bf16x4*>(b + 32);
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
+  // Same, in the natural K order (slot j = channel k0 + 8g + j): one 16-byte
+  // read.  For products whose operands both come from memory (the scores).
+  __device__ bf16x8 rm8(int row0, int k0, const Lane& ln) const {
+    return *reinterpret_cast<const bf16x8*>(p + (row0 + ln.r) * ROWB + 16 * ln.g + 2 * k0);
+  }
   // Fragment with the lane index along channels col0 + r: slots are rows
   // k0 + kslot(g, j).
   __device__ bf16x8 cm(int col0, int k0, const Lane& ln) const {
@@ -264,9 +269,17 @@ __global__ __launch_bounds__(QS == 2 ? 768 : 512) void attn_fwd_kernel(
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const int row = min(q0 + 16 * qt + r, T - 1);
-    const Glb<E> qm{qr + (((int64_t)b * T + row) * Hq + h) * kDh, 0, 1};
+    const E* qrow = qr + (((int64_t)b * T + row) * Hq + h) * kDh;
+    if constexpr (BF) {
+      // natural K order (slot j = channel 32 kb + 8g + j), as the K tile reads
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) Qf[qt][kb] = qm.rm(0, KB * kb);
+      for (int kb = 0; kb < NKB; ++kb)
+        Qf[qt][kb] = *reinterpret_cast<const bf16x8*>(qrow + KB * kb + 8 * g);
+    } else {
+      const Glb<E> qm{qrow, 0, 1};
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) Qf[qt][kb] = qm.rm(0, KB * kb);
+    }
   }
   f32x4 O[QT][16];
 #pragma unroll
@@ -309,16 +322,30 @@ __global__ __launch_bounds__(QS == 2 ? 768 : 512) void attn_fwd_kernel(
     for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) S[qt][kt] = zero4();
+    // K fragments software-pipelined one channel block ahead: the reads of
+    // block kb + 1 are in flight while block kb's MFMAs issue
+    auto kfrag = [&](int kt, int kb) {
+      if constexpr (BF) return Ks.rm8(16 * kt, KB * kb, ln);
+      else return Ks.rm(16 * kt + ln.r, KB * kb, ln);
+    };
+    Fr<E> cur[4], nxt[4];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int kt = 0; kt < 4; ++kt) cur[kt] = kfrag(kt, 0);
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        Fr<E> a;
-        if constexpr (BF) a = Ks.rm(16 * kt, KB * kb, ln);
-        else a = Ks.rm(16 * kt + ln.r, KB * kb, ln);
+    for (int kb = 0; kb < NKB; ++kb) {
+      if (kb + 1 < NKB) {
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt) S[qt][kt] = mma(S[qt][kt], a, Qf[qt][kb]);
+        for (int kt = 0; kt < 4; ++kt) nxt[kt] = kfrag(kt, kb + 1);
       }
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) S[qt][kt] = mma(S[qt][kt], cur[kt], Qf[qt][kb]);
+      if (kb + 1 < NKB) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) cur[kt] = nxt[kt];
+      }
+    }
     const bool diag = kKvb * j + kKvb - 1 > q0;
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
@@ -459,9 +486,19 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
   Fr<E> Qf[NKB];
   {
     const bool ok = r < G;
-    const Glb<E> qm{qr + ((int64_t)b * Hq + kvh * G + (ok ? r : 0)) * kDh, 0, ok ? 1 : 0};
+    const E* qrow = qr + ((int64_t)b * Hq + kvh * G + (ok ? r : 0)) * kDh;
+    if constexpr (BF) {
+      // natural K order, as the K tile reads
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) Qf[kb] = qm.rm(0, KB * kb);
+      for (int kb = 0; kb < NKB; ++kb) {
+        Qf[kb] = *reinterpret_cast<const bf16x8*>(qrow + KB * kb + 8 * g);
+        if (!ok) Qf[kb] = bf16x8{};
+      }
+    } else {
+      const Glb<E> qm{qrow, 0, ok ? 1 : 0};
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) Qf[kb] = qm.rm(0, KB * kb);
+    }
   }
   f32x4 O[4];
 #pragma unroll
@@ -504,7 +541,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt) {
-        if constexpr (BF) S[kt] = mma(S[kt], Ks.rm(16 * kt, KB * kb, ln), Qf[kb]);
+        if constexpr (BF) S[kt] = mma(S[kt], Ks.rm8(16 * kt, KB * kb, ln), Qf[kb]);
         else S[kt] = mma(S[kt], Ks.rm(16 * kt + r, KB * kb, ln), Qf[kb]);
       }
     float mb = -INFINITY;
