@@ -394,6 +394,16 @@ __global__ __launch_bounds__(64 * NW) void bwd_chain_bf16_kernel(
 // global memory (L2) and keeps only the intermediates Dl, Y, E in LDS.
 constexpr int kGW = 8;  // waves
 
+// v[4 mt + i] is a sum already broadcast over the 16 lanes of lane group g
+// (token 16 mt + 4 g + i); lane r keeps the one of token 16 (r / 4) + 4 g +
+// r % 4, so that one unconditional store per lane writes all 64 tokens.
+__device__ __forceinline__ float pick16(const float (&v)[16], int r) {
+  float s = v[0];
+#pragma unroll
+  for (int k = 1; k < 16; ++k) s = r == k ? v[k] : s;
+  return s;
+}
+
 template <typename E>
 struct GradSmem {
   static constexpr bool BF = sizeof(E) == 2;
@@ -564,6 +574,8 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
         }
       }
       // dDl = M^T dO + diag(dec) K dS'^T, one token tile at a time; w_i partial
+      const int tk = 16 * (r >> 2) + 4 * g + (r & 3);   // the token this lane stores
+      float pwv[16];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         f32x4 kds = zero4(), m = zero4();
@@ -577,10 +589,10 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
         for (int i = 0; i < 4; ++i) {
           const int tok = 16 * mt + 4 * g + i;
           dD[mt][i] = m[i] + sm.dc[tok] * kds[i];
-          const float pw = sum16(Dl[mt][i] * kds[i]);
-          if (r == 0) sm.u3.part[w][2][tok] = sm.dc[tok] * pw;
+          pwv[4 * mt + i] = sum16(Dl[mt][i] * kds[i]);
         }
       }
+      sm.u3.part[w][2][tk] = sm.dc[tk] * pick16(pwv, r);
       // Y = N^T dDl
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
@@ -591,18 +603,19 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
         Y[mt] = y;
       }
       // beta and gate partials: Y.X and -gamma beta Y.(K S0^T) = -beta Y.(V - X)
+      {
+        float pbv[16], pgv[16];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tok = 16 * mt + 4 * g + i;
-          const float pb = sum16(Y[mt][i] * X[mt][i]);
-          const float pg = sum16(Y[mt][i] * (mV.get(tok, c) - X[mt][i]));
-          if (r == 0) {
-            sm.u3.part[w][0][tok] = pb;
-            sm.u3.part[w][1][tok] = -sm.bt[tok] * pg;
+          for (int i = 0; i < 4; ++i) {
+            const int tok = 16 * mt + 4 * g + i;
+            pbv[4 * mt + i] = sum16(Y[mt][i] * X[mt][i]);
+            pgv[4 * mt + i] = sum16(Y[mt][i] * (mV.get(tok, c) - X[mt][i]));
           }
-        }
+        sm.u3.part[w][0][tk] = pick16(pbv, r);
+        sm.u3.part[w][1][tk] = -sm.bt[tk] * pick16(pgv, r);
+      }
       ssl = wave_sum(ssl);
       if (l == 0) sm.ss[w] = ssl;
       __syncthreads();   // every wave is done with V, N, M (their LDS is reused)
@@ -614,7 +627,17 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
           const int tok = 16 * mt + 4 * g + i;
           Dls(tok, c) = from_f32<E>(Dl[mt][i]);
           Ys(tok, c) = from_f32<E>(Y[mt][i]);
-          if (tok < L) dvh[(size_t)tok * Hv * kD + c] = from_f32<E>(sm.bt[tok] * Y[mt][i]);
+        }
+      // dv: unguarded stores for a full chunk (the common case), guarded for
+      // the ragged tail
+      const bool full = L == kC;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tok = 16 * mt + 4 * g + i;
+          if (full || tok < L)
+            dvh[(size_t)tok * Hv * kD + c] = from_f32<E>(sm.bt[tok] * Y[mt][i]);
         }
     }
     __syncthreads();
@@ -654,7 +677,7 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
     for (int x = 0; x < 2; ++x) {
       if (tj[x] > ti[x]) continue;
       const int jj = 16 * tj[x] + r;
-      float colsum = 0.f;
+      float colsum = 0.f, rsv[4], rbv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int ii = 16 * ti[x] + 4 * g + i;
@@ -664,19 +687,32 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
         const float wa = sm.bt[ii] * dAG;
         const float P = dMG * QK[x][i] + wa * KK[x][i];
         // every location of E has exactly one writer: (ii, jj) on and below
-        // the diagonal, its mirror (jj, ii) above it
-        if (jj <= ii) Es(ii, jj) = from_f32<E>(dMG);
-        if (jj < ii) Es(jj, ii) = from_f32<E>(wa);
-        const float rs = sum16(P), rb = sum16(dAG * KK[x][i]);
-        if (r == 0) {
-          sm.rowp[tj[x]][ii] = rs;
-          sm.rowb[tj[x]][ii] = rb;
+        // the diagonal, its mirror (jj, ii) above it (off-diagonal tiles:
+        // every element is below)
+        if (tj[x] < ti[x]) {
+          Es(ii, jj) = from_f32<E>(dMG);
+          Es(jj, ii) = from_f32<E>(wa);
+        } else {
+          if (jj <= ii) Es(ii, jj) = from_f32<E>(dMG);
+          if (jj < ii) Es(jj, ii) = from_f32<E>(wa);
         }
+        rsv[i] = sum16(P);
+        rbv[i] = sum16(dAG * KK[x][i]);
         colsum += P;
+      }
+      // row sums: lane r stores row 16 ti + 4g + r%4 (four lanes write each
+      // row, the same value); column sums: every lane group writes the same
+      // column value
+      {
+        const int i4 = r & 3;
+        const float rs = i4 == 0 ? rsv[0] : (i4 == 1 ? rsv[1] : (i4 == 2 ? rsv[2] : rsv[3]));
+        const float rb = i4 == 0 ? rbv[0] : (i4 == 1 ? rbv[1] : (i4 == 2 ? rbv[2] : rbv[3]));
+        sm.rowp[tj[x]][16 * ti[x] + 4 * g + i4] = rs;
+        sm.rowb[tj[x]][16 * ti[x] + 4 * g + i4] = rb;
       }
       colsum += __shfl_xor(colsum, 16, 64);
       colsum += __shfl_xor(colsum, 32, 64);
-      if (g == 0) sm.colp[ti[x]][jj] = colsum;
+      sm.colp[ti[x]][jj] = colsum;
     }
     __syncthreads();
 
@@ -692,6 +728,8 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
     {
       // gamma dO S0 into dq (and the gate's q . dq partial)
       {
+        const int tk = 16 * (r >> 2) + 4 * g + (r & 3);
+        float pav[16];
         f32x4 T1[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) T1[mt] = zero4();
@@ -708,9 +746,9 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
             const int tok = 16 * mt + 4 * g + i;
             const float g1 = sm.gm[tok] * T1[mt][i];
             dQ[mt][i] += g1;
-            const float pa = sum16(mQ.get(tok, c) * g1);
-            if (r == 0) sm.pa[w][tok] = pa;
+            pav[4 * mt + i] = sum16(mQ.get(tok, c) * g1);
           }
+        sm.pa[w][tk] = pick16(pav, r);
       }
       // -gamma beta Y S0 into dk
       {
