@@ -549,11 +549,12 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
         for (int mt = 0; mt < 4; ++mt) X[mt] = zero4();
 #pragma unroll
         for (int kb = 0; kb < kD / KB; ++kb) {
-          const Fr<E> s0 = mS0.rm(c, KB * kb, ln), ds = mdS.rm(c, KB * kb, ln);
+          // natural K order (both operands from LDS): one 16-byte read each
+          const Fr<E> s0 = mS0.rmn(c, KB * kb, ln), ds = mdS.rmn(c, KB * kb, ln);
 #pragma unroll
           for (int e = 0; e < NS; ++e) ssl += (float)s0[e] * (float)ds[e];
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt) X[mt] = mma(X[mt], mK.rm(16 * mt + r, KB * kb, ln), s0);
+          for (int mt = 0; mt < 4; ++mt) X[mt] = mma(X[mt], mK.rmn(16 * mt + r, KB * kb, ln), s0);
         }
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
@@ -581,7 +582,7 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
         f32x4 kds = zero4(), m = zero4();
 #pragma unroll
         for (int kb = 0; kb < kD / KB; ++kb)
-          kds = mma(kds, mK.rm(16 * mt + r, KB * kb, ln), mdS.rm(c, KB * kb, ln));
+          kds = mma(kds, mK.rmn(16 * mt + r, KB * kb, ln), mdS.rmn(c, KB * kb, ln));
 #pragma unroll
         for (int kb = 0; kb < kC / KB; ++kb)
           if (!blk_below<E>(mt, kb)) m = mma(m, mM.cm(16 * mt + r, KB * kb, ln), mO.cm(c, KB * kb, ln));
@@ -663,12 +664,12 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
       if (tj[x] <= ti[x]) {
 #pragma unroll
         for (int kb = 0; kb < kD / KB; ++kb) {
-          const Fr<E> bd = Dls.rm(16 * tj[x] + r, KB * kb, ln);
-          OD[x] = mma(OD[x], mO.rm(16 * ti[x] + r, KB * kb, ln), bd);
-          YD[x] = mma(YD[x], Ys.rm(16 * ti[x] + r, KB * kb, ln), bd);
-          const Fr<E> bk = mK.rm(16 * tj[x] + r, KB * kb, ln);
-          KK[x] = mma(KK[x], mK.rm(16 * ti[x] + r, KB * kb, ln), bk);
-          QK[x] = mma(QK[x], mQ.rm(16 * ti[x] + r, KB * kb, ln), bk);
+          const Fr<E> bd = Dls.rmn(16 * tj[x] + r, KB * kb, ln);
+          OD[x] = mma(OD[x], mO.rmn(16 * ti[x] + r, KB * kb, ln), bd);
+          YD[x] = mma(YD[x], Ys.rmn(16 * ti[x] + r, KB * kb, ln), bd);
+          const Fr<E> bk = mK.rmn(16 * tj[x] + r, KB * kb, ln);
+          KK[x] = mma(KK[x], mK.rmn(16 * ti[x] + r, KB * kb, ln), bk);
+          QK[x] = mma(QK[x], mQ.rmn(16 * ti[x] + r, KB * kb, ln), bk);
         }
       }
     }

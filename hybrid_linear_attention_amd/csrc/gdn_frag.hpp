@@ -122,6 +122,13 @@ struct Lds {
       return *reinterpret_cast<const f32x4*>(p + row * LD + k0 + 4 * g);
     }
   }
+  // Natural K order (slot j = element (row, k0 + 8g + j) for bf16, k0 + 4g + j
+  // for fp32): one 16-byte read.  Usable when both operands of a product come
+  // from memory, so both can take this order.
+  __device__ Fr<E> rmn(int row, int k0, const Lane& ln) const {
+    if constexpr (BF) return *reinterpret_cast<const bf16x8*>(p + at(row, k0 + 8 * ln.g));
+    else return rm(row, k0, ln);
+  }
   // Lane index along columns (col = 16-aligned base + lane % 16): slot j =
   // element (k0 + kslot(g, j), col).  bf16 uses ds_read_b64_tr_b16: input lane
   // r of a 16-lane group reads four columns base + 4(r%4) .. +3 of row
@@ -163,6 +170,11 @@ struct Glb {
     for (int j = 0; j < kSlotsOf<E>; ++j)
       f[j] = row < rows ? p[row * ld + k0 + kslot<E>(g, j)] : (E)0.f;
     return f;
+  }
+  // natural K order (fp32 only: there it is the rm order)
+  __device__ Fr<E> rmn(int row, int k0, const Lane& ln) const {
+    static_assert(sizeof(E) == 4, "natural order from global memory: fp32 only");
+    return rm(row, k0, ln);
   }
   __device__ Fr<E> cm(int col, int k0) const { return cm(col, k0, lane_here()); }
   __device__ Fr<E> cm(int col, int k0, const Lane& ln) const {
