@@ -31,6 +31,12 @@ COMMON = [
 ]
 
 
+# Per-file code-generation options.  The backward kernels keep their MFMA
+# accumulators in VGPRs: their state tiles are touched by VALU every chunk,
+# and accumulators in AGPRs would cost two register moves per touch.
+EXTRA = {"gdn_backward.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _hipcc() -> str:
     for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -45,7 +51,7 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src):
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        cmd = [hipcc, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc, *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         res = subprocess.run(cmd, capture_output=True, text=True)
         out = "\n".join(x for x in (res.stdout + res.stderr).splitlines()
                         if "packed-fp32-ops" not in x)

@@ -41,6 +41,8 @@
 #include "gdn_frag.hpp"
 #include "gdn_launch.hpp"
 
+#include <type_traits>
+
 namespace gdn {
 namespace bwd {
 using namespace frag;
@@ -277,8 +279,12 @@ __global__ __launch_bounds__(64 * NW) void bwd_chain_bf16_kernel(
   const int h = blockIdx.y, b = blockIdx.z, gq = h / (Hv / Hqk);
   const int rbase = R * blockIdx.x, dv0 = rbase + 16 * w;
 
-  auto issue = [&](int j) {
-    ChainDmaBuf<NW>& B_ = buf[j & 1];
+  // The two buffers alternate with the iteration parity, which is a
+  // compile-time constant in the two-step unrolled loop below: both buffers
+  // then share one set of per-lane LDS offsets (the second one is an
+  // immediate offset away).
+  auto issue = [&](int j, auto bic) {
+    ChainDmaBuf<NW>& B_ = buf[decltype(bic)::value];
     const int cid = b * Nc + j, L = min(kC, T - kC * j);
     const size_t tok0 = (size_t)b * T + (size_t)kC * j;
     const size_t hc = (size_t)cid * Hv + h;
@@ -298,19 +304,22 @@ __global__ __launch_bounds__(64 * NW) void bwd_chain_bf16_kernel(
     DT[t] = dht ? *reinterpret_cast<const f32x4*>(
                       dht + (((size_t)b * Hv + h) * kD + dv0 + r) * kD + 16 * t + 4 * g)
                 : zero4();
-  if (Nc > 0) issue(Nc - 1);
+  const std::integral_constant<int, 0> ic0{};
+  const std::integral_constant<int, 1> ic1{};
+  if (Nc > 0) issue(Nc - 1, ic0);
   wait_copies();
   barrier_lds();
 
-  for (int j = Nc - 1; j >= 0; --j) {
+  auto step = [&](int j, auto bic) {
+    constexpr int bi = decltype(bic)::value;
     const int cid = b * Nc + j, L = min(kC, T - kC * j);
     const size_t hc = (size_t)cid * Hv + h;
     E* ddst = dSc + (hc * kD + dv0 + r) * kD;
 #pragma unroll
     for (int t = 0; t < 8; ++t) store4(ddst + 16 * t + 4 * g, DT[t]);
-    if (j > 0) issue(j - 1);
+    if (j > 0) issue(j - 1, std::integral_constant<int, 1 - bi>{});
 
-    const ChainDmaBuf<NW>& B_ = buf[j & 1];
+    const ChainDmaBuf<NW>& B_ = buf[bi];
     const Lds<E, 128> Ks{const_cast<E*>(B_.K)}, Qs{const_cast<E*>(B_.Q)};
     const Lds<E, R> Os{const_cast<E*>(B_.O)};
     const Lds<E, 64> Ns{const_cast<E*>(B_.N)}, Ms{const_cast<E*>(B_.M)};
@@ -371,7 +380,13 @@ __global__ __launch_bounds__(64 * NW) void bwd_chain_bf16_kernel(
     }
     wait_copies();
     barrier_lds();
+  };
+  int j = Nc - 1;
+  for (; j >= 1; j -= 2) {
+    step(j, ic0);
+    step(j - 1, ic1);
   }
+  if (j == 0) step(0, ic0);
   if (dh0) {
     float* dst = dh0 + (((size_t)b * Hv + h) * kD + dv0 + r) * kD;
 #pragma unroll
