@@ -223,8 +223,12 @@ struct FwdSmem {
 // QS waves per query head, each with QT tiles of 16 query rows: the workgroup
 // covers 16 QT QS rows of all G heads of its key/value head.  bf16: QT = 1,
 // QS = 2 (12 waves of at most 170 registers); fp32: QT = 1, QS = 1.
+// Largest workgroup an instantiation is compiled for (its register budget):
+// the launch must never exceed it.
+template <int QS> constexpr int fwd_max_threads() { return QS == 2 ? 768 : 512; }
+
 template <typename E, int QT, int QS>
-__global__ __launch_bounds__(QS == 2 ? 768 : 512) void attn_fwd_kernel(
+__global__ __launch_bounds__(fwd_max_threads<QS>()) void attn_fwd_kernel(
     const E* __restrict__ qr, const E* __restrict__ kc, const E* __restrict__ vc,
     const E* __restrict__ gate, E* __restrict__ o, int T, int cache_len, int Hq, int Hkv,
     int nqb, int nseq) {
@@ -664,14 +668,26 @@ static hipError_t attn_launch_t(const AttnLaunch& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   const int G = a.Hq / a.Hkv;
   if (!a.decode) {
-    constexpr int QT = 1, QS = sizeof(E) == 2 ? 2 : 1;
-    const int nqb = (a.T + 16 * QT * QS - 1) / (16 * QT * QS);
-    const int nst = a.Hkv * a.B;
-    const int nwg = (nst <= 8 && 8 % nst == 0) ? 8 * ((nqb + 8 / nst - 1) / (8 / nst)) : nqb * nst;
-    hipLaunchKernelGGL((attn_fwd_kernel<E, QT, QS>), dim3(nwg), dim3(64 * G * QS), 0, st,
-                       (const E*)a.qrot, (const E*)a.kc, (const E*)a.vc_read, (const E*)a.gate,
-                       (E*)a.o, a.T, a.cache_len, a.Hq, a.Hkv, nqb, a.B);
-    return hipGetLastError();
+    // bf16: two waves per query head (32 query rows per workgroup) while the
+    // workgroup fits the 768-thread instantiation (up to 6 heads per group);
+    // otherwise, and for fp32, one wave per head (16 rows, at most 8 heads).
+    auto launch = [&](auto kern, int qs, int max_threads) -> hipError_t {
+      const int threads = 64 * G * qs;
+      if (threads > max_threads) return hipErrorInvalidConfiguration;
+      const int nqb = (a.T + 16 * qs - 1) / (16 * qs);
+      const int nst = a.Hkv * a.B;
+      const int nwg = (nst <= 8 && 8 % nst == 0) ? 8 * ((nqb + 8 / nst - 1) / (8 / nst))
+                                                 : nqb * nst;
+      hipLaunchKernelGGL(kern, dim3(nwg), dim3(threads), 0, st, (const E*)a.qrot,
+                         (const E*)a.kc, (const E*)a.vc_read, (const E*)a.gate, (E*)a.o, a.T,
+                         a.cache_len, a.Hq, a.Hkv, nqb, a.B);
+      return hipGetLastError();
+    };
+    if constexpr (sizeof(E) == 2) {
+      if (64 * G * 2 <= fwd_max_threads<2>())
+        return launch(attn_fwd_kernel<E, 1, 2>, 2, fwd_max_threads<2>());
+    }
+    return launch(attn_fwd_kernel<E, 1, 1>, 1, fwd_max_threads<1>());
   }
   const int spl = attn_decode_split(a.B, a.Hkv, a.cache_len);
   const int ns = attn_decode_splits(a.B, a.Hkv, a.cache_len);

@@ -159,3 +159,30 @@ def test_attn_deterministic(gdn):
     o2 = gdn.attn_prefill(inp["q"], inp["k"], inp["v"], inp["gate"])
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 2), (12, 3), (4, 2)])
+def test_attn_other_head_layouts(gdn, dtype, Hq, Hkv):
+    # the kernels take the group size Hq / Hkv (1 .. 8) at run time
+    say("attn head layout", Hq, Hkv, dtype)
+    B, T = 2, 100
+    inp = synth.attention_inputs(B, T, dtype, seed=300 + Hq + Hkv, Hq=Hq, Hkv=Hkv)
+    d = dev(inp)
+    L = 128
+    kc = torch.zeros((B, L, Hkv, 256), dtype=dtype, device=DEV)
+    vc = torch.zeros((B, L, Hkv, 256), dtype=dtype, device=DEV)
+    o = gdn.attn_prefill(d["q"], d["k"], d["v"], d["gate"], d["q_norm_w"], d["k_norm_w"],
+                         k_cache=kc, v_cache=vc)
+    torch.cuda.synchronize()
+    ref = A.attention(inp["q"], inp["k"], inp["v"], inp["gate"], inp["q_norm_w"], inp["k_norm_w"])
+    assert rel(o, ref) <= TOL[dtype]
+    s = synth.attention_decode_inputs(B, 0, dtype, seed=400 + Hq, Hq=Hq, Hkv=Hkv)
+    pos_h = np.array([T, T - 37], dtype=np.int32)
+    kb, vb = kc.cpu(), vc.cpu()
+    od = gdn.attn_decode(*(s[x].to(DEV) for x in ("q", "k", "v", "gate")), kc, vc,
+                         torch.tensor(pos_h, device=DEV), d["q_norm_w"], d["k_norm_w"])
+    torch.cuda.synchronize()
+    refd, _ = A.decode(s["q"], s["k"], s["v"], s["gate"], kb, vb, pos_h, inp["q_norm_w"],
+                       inp["k_norm_w"])
+    assert rel(od, refd) <= TOL[dtype]
