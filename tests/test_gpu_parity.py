@@ -568,3 +568,18 @@ def test_backward_T8192_sampled_groups(gdn):
         say("  group %d rel " % gq + " ".join("%s %.3e" % (n, e) for n, e in zip(GRAD_NAMES, errs)))
         for n, e in zip(GRAD_NAMES, errs):
             assert e <= 2e-2, (gq, n, e)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+@pytest.mark.parametrize("Hqk,Hv", [(8, 8), (4, 16)])
+def test_backward_other_head_layouts(gdn, dtype, Hqk, Hv):
+    # the gradient kernel walks the Hv / Hqk value heads of a group at run time
+    say("backward head layout", Hqk, Hv, dtype)
+    inp = synth.backward_inputs(1, 150, dtype, seed=61 + Hv, h0_std=0.02, dht_std=0.02,
+                                Hqk=Hqk, Hv=Hv)
+    got = run_backward(gdn, inp)
+    ref = oracle.prefill_backward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"],
+                                  inp["do"], inp["h0"], inp["dht"])
+    for n, x, y in zip(GRAD_NAMES, got, ref):
+        e = rel(x, y)
+        assert e <= TOL[dtype], (n, e)
