@@ -433,7 +433,10 @@ def main():
                     "tflops_algorithmic": att_tf, "frac_bf16_mfma_peak": att_tf / PEAK_BF16_TFLOPS,
                     "gflop_per_call": attention_prefill_flops(T) / 1e9},
         "decode": {"ms_per_step": att["decode"], "gbs": att_gbs, "frac": att_gbs / PEAK_HBM_GBS,
-                   "cache_bytes_per_step": attention_decode_bytes(64, 8192)}}
+                   "cache_bytes_per_step": attention_decode_bytes(64, 8192),
+                   "roofline": {"bound": "hbm", "achieved": att_gbs, "peak": PEAK_HBM_GBS,
+                                "unit": "GB/s", "frac": att_gbs / PEAK_HBM_GBS,
+                                "traffic": counted_traffic("attn_decode_kernel")}}}
     if args.extended:
         log("extended: T=262144")
         inp3 = {k: (v.to("cuda") if isinstance(v, torch.Tensor) else v)
