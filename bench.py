@@ -95,6 +95,29 @@ def counted_traffic(kernel):
     return None
 
 
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_ops_prefill_T8192.md")
+
+
+def counted_mfma_gflop():
+    """Matrix-unit FLOPs one prefill call executes, from the committed
+    rocprofv3 SQ_INSTS_VALU_MFMA_* summary (per prepare + scan call), or None
+    when the summary is absent or the prefill source changed since."""
+    try:
+        lines = open(MFMA_FILE).read().splitlines()
+    except OSError:
+        return None
+    for ln in lines:
+        f = ln.split()
+        if len(f) == 5 and f[0] == "mfma_gflop" and f[1] == "prefill":
+            src = os.path.join(ROOT, "hybrid_linear_attention_amd", "csrc", f[2])
+            try:
+                h = hashlib.sha256(open(src, "rb").read()).hexdigest()
+            except OSError:
+                return None
+            return float(f[4]) if h == f[3] else None
+    return None
+
+
 def scan_bytes(T, B=1):
     """Algorithmic bytes of one scan launch (bf16): it reads q, v, the
     workspace (Tt and M: 64 x 64 bf16 per chunk and value head; K^T: 128 x 64
@@ -137,7 +160,13 @@ def timed_prefill(gdn, inp, steps, warmup):
     prep = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
     scan = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
     step = ev[0][0].elapsed_time(ev[-1][2]) / steps
-    return dict(step_ms=step, prepare_ms=prep, scan_ms=scan, wall_s=wall)
+    per_call = sorted(e[0].elapsed_time(e[2]) for e in ev)
+
+    def pct(p):
+        return per_call[min(len(per_call) - 1, int(round(p * (len(per_call) - 1))))]
+
+    return dict(step_ms=step, prepare_ms=prep, scan_ms=scan, wall_s=wall,
+                median_ms=pct(0.5), p10_ms=pct(0.1), p90_ms=pct(0.9))
 
 
 def timed_decode(gdn, B, steps, warmup, dtype=torch.bfloat16, state_dtype=torch.float32):
@@ -296,10 +325,44 @@ def cpu_baseline(inp, T_sample, min_seconds=10.0, max_calls=64):
         oracle.prefill(sl["q"], sl["k"], sl["v"], sl["alpha"], sl["beta"], None)
         dt += time.perf_counter() - t0
         calls += 1
+    model = ""
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return dict(value=calls * T_sample / dt, unit="tokens/s", cores=threads, kind="oracle",
                 sample="%d calls on the first %d of 8192 tokens, all 48 value heads, batch 1, "
                        "float64 sequential recurrence, OpenMP over heads (%.1f s)"
-                       % (calls, T_sample, dt))
+                       % (calls, T_sample, dt),
+                cpu_model=model, single_thread=cpu_single_thread())
+
+
+def cpu_single_thread(T_sample=256):
+    """The same oracle on one thread (a child process with OMP_NUM_THREADS=1),
+    on the first T_sample tokens, for about five seconds of work."""
+    import subprocess
+    code = ("import time, synth, oracle\n"
+            "oracle.build(force=False)\n"
+            "d = synth.config_inputs(1)\n"
+            "sl = {k: d[k][:, :%d] for k in ('q', 'k', 'v', 'alpha', 'beta')}\n"
+            "n, t = 0, 0.0\n"
+            "while t < 5.0 and n < 64:\n"
+            "    t0 = time.perf_counter()\n"
+            "    oracle.prefill(sl['q'], sl['k'], sl['v'], sl['alpha'], sl['beta'], None)\n"
+            "    t += time.perf_counter() - t0\n"
+            "    n += 1\n"
+            "print(n * %d / t)\n" % (T_sample, T_sample))
+    env = dict(os.environ, OMP_NUM_THREADS="1", CUDA_VISIBLE_DEVICES="", HIP_VISIBLE_DEVICES="")
+    try:
+        out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
+                             text=True, timeout=120)
+        return dict(value=float(out.stdout.strip().splitlines()[-1]), unit="tokens/s", cores=1,
+                    sample="first %d of 8192 tokens, all 48 value heads, float64" % T_sample)
+    except Exception as e:  # reported, never fatal: it is a side figure
+        return dict(value=None, error=str(e)[:200])
 
 
 def main():
@@ -391,7 +454,10 @@ def main():
                    "global_batch": 1, "seq_len": T, "parallelism": "single GPU"},
         "prefill": {"tflops_algorithmic": tflops, "frac_bf16_mfma_peak": tflops / PEAK_BF16_TFLOPS,
                     "prepare_ms": pre["prepare_ms"], "scan_ms": pre["scan_ms"],
-                    "gflop_per_call": prefill_flops(T) / 1e9},
+                    "per_call_ms": {"median": pre["median_ms"], "p10": pre["p10_ms"],
+                                    "p90": pre["p90_ms"]},
+                    "gflop_per_call": prefill_flops(T) / 1e9,
+                    "mfma_gflop_counted": counted_mfma_gflop()},
         "roofline": {"bound": "mfma", "kernel": dominant,
                      "achieved": scan_tflops if dominant == "scan" else None,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
