@@ -344,8 +344,9 @@ def cpu_single_thread(T_sample=256):
     """The same oracle on one thread (a child process with OMP_NUM_THREADS=1),
     on the first T_sample tokens, for about five seconds of work."""
     import subprocess
-    code = ("import time, synth, oracle\n"
+    code = ("import ctypes, time, synth, oracle\n"
             "oracle.build(force=False)\n"
+            "ctypes.CDLL('libgomp.so.1').omp_set_num_threads(1)\n"
             "d = synth.config_inputs(1)\n"
             "sl = {k: d[k][:, :%d] for k in ('q', 'k', 'v', 'alpha', 'beta')}\n"
             "n, t = 0, 0.0\n"
