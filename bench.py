@@ -141,7 +141,7 @@ def timed_prefill(gdn, inp, steps, warmup):
     ht = torch.empty((1, HV, D, D), dtype=torch.float32, device=dev)
     ws = torch.empty(gdn.prefill_workspace_bytes(1, T, HQK, HV, D, inp["q"].dtype),
                      dtype=torch.uint8, device=dev)
-    args = (inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], None, o, ht, ws)
+    args = (inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp.get("h0"), o, ht, ws)
     for _ in range(warmup):
         gdn.prefill_prepare(*args)
         gdn.prefill_scan(*args)
@@ -505,10 +505,18 @@ def main():
                                 "unit": "GB/s", "frac": att_gbs / PEAK_HBM_GBS,
                                 "traffic": counted_traffic("attn_decode_kernel")}}}
     if args.extended:
+        log("extended: config 0 (fp32, T=256)")
+        inp0 = {k: (v.to("cuda") if isinstance(v, torch.Tensor) else v)
+                for k, v in synth.config_inputs(0).items()}
+        r0 = timed_prefill(gdn, inp0, 100, 10)
+        out["config0_fp32_T256"] = {"median_ms": r0["median_ms"], "p10_ms": r0["p10_ms"],
+                                    "p90_ms": r0["p90_ms"],
+                                    "tokens_per_s": 256 / (r0["median_ms"] * 1e-3)}
+        del inp0
         log("extended: T=262144")
         inp3 = {k: (v.to("cuda") if isinstance(v, torch.Tensor) else v)
                 for k, v in synth.config_inputs(3).items()}
-        r3 = timed_prefill(gdn, inp3, 3, 1)
+        r3 = timed_prefill(gdn, inp3, 10, 3)
         out["long_context"] = {"T": 262144, "ms": r3["step_ms"],
                                "tokens_per_s": 262144 / (r3["step_ms"] * 1e-3),
                                "tflops_algorithmic": prefill_flops(262144) / (r3["step_ms"] * 1e-3) / 1e12}
@@ -522,17 +530,17 @@ def main():
             vargs = (inp4["q"], inp4["k"], inp4["v"], inp4["alpha"], inp4["beta"],
                     inp4["cu_seqlens"], inp4["h0"])
             kw = dict(gate=inp4["gate"]) if gated else {}
-            for _ in range(1):
+            for _ in range(3):
                 gdn.prefill_varlen(*vargs, **kw)
             torch.cuda.synchronize()
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record()
-            for _ in range(3):
+            for _ in range(10):
                 gdn.prefill_varlen(*vargs, **kw)
             e1.record()
             torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / 3
+            ms = e0.elapsed_time(e1) / 10
             res["gated" if gated else "plain"] = {"ms": ms, "tokens_per_s": T4 / (ms * 1e-3)}
             log("varlen %s: %.3f ms, %.1f M tokens/s" % ("gated" if gated else "plain", ms,
                                                          T4 / ms / 1e3))
