@@ -482,3 +482,36 @@ def attn_decode(q, k, v, gate, k_cache, v_cache, pos, q_norm_w=None, k_norm_w=No
         _ptr(k_cache), _ptr(v_cache), _ptr(pos), cache_len, B, Hq, Hkv, D, rope_dim, theta,
         _dt(q), _ptr(ws), nbytes, _stream(dev)), "gdn_attn_decode")
     return o
+
+
+# ---------------------------------------------------------------- autograd
+class GatedDeltaRule(torch.autograd.Function):
+    """The chunked prefill as a differentiable op: forward is
+    gdn_prefill_chunked, backward is gdn_prefill_chunked_bwd (which
+    recomputes the forward states; nothing but the inputs is saved).
+
+    ``o, ht = GatedDeltaRule.apply(q, k, v, alpha, beta, h0)``; h0 may be None.
+    Gradients flow to q, k, v, alpha, beta and h0."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, alpha, beta, h0):
+        o, ht = prefill_chunked(q, k, v, alpha, beta, h0)
+        ctx.save_for_backward(q, k, v, alpha, beta, h0)
+        ctx.has_h0 = h0 is not None
+        return o, ht
+
+    @staticmethod
+    def backward(ctx, do, dht):
+        q, k, v, alpha, beta, h0 = ctx.saved_tensors
+        if do is None:
+            do = torch.zeros((q.shape[0], q.shape[1], v.shape[2], v.shape[3]), dtype=q.dtype,
+                             device=q.device)
+        dq, dk, dv, da, db, dh0 = prefill_backward(
+            q, k, v, alpha, beta, do.contiguous(), h0 if ctx.has_h0 else None,
+            None if dht is None else dht.contiguous(), want_dh0=ctx.has_h0)
+        return dq, dk, dv, da, db, dh0
+
+
+def gated_delta_rule(q, k, v, alpha, beta, h0=None):
+    """Differentiable chunked prefill: returns (o, ht)."""
+    return GatedDeltaRule.apply(q, k, v, alpha, beta, h0)
