@@ -496,6 +496,28 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) { dQ[mt] = zero4(); dK[mt] = zero4(); }
 
+  // bf16 operands of value head hh copied straight into LDS.  Rows of dO and
+  // V beyond L repeat the last token; they only ever meet zero rows of K and
+  // Q, zero beta and the identity rows of N, so nothing they touch is stored.
+  // part 0: S0, dS', dO (read in phases 1 - 2 up to the state products);
+  // part 1: V, N, M (read in phase 1; their slots then hold Dl and Y).
+  auto stage_head = [&](int hh2, int part) {
+    if constexpr (BF) {
+      const int wu = __builtin_amdgcn_readfirstlane(w);
+      const int h2 = gq * G + hh2;
+      const size_t hc2 = (size_t)cid * Hv + h2;
+      if (part == 0) {
+        copy_rows<128, kD>(Sc + hc2 * kD * kD, kD, kD, sm.S0, wu, kGW);
+        copy_rows<128, kD>(dSc + hc2 * kD * kD, kD, kD, sm.dS, wu, kGW);
+        copy_rows<128>(dout + (tok0 * Hv + h2) * kD, (int64_t)Hv * kD, L, sm.dO, wu, kGW);
+      } else {
+        copy_rows<128>(v + (tok0 * Hv + h2) * kD, (int64_t)Hv * kD, L, sm.u1.V, wu, kGW);
+        copy_rows<64>(Nw + hc2 * kC * kC, kC, kC, sm.u2.nm.N, wu, kGW);
+        copy_rows<64>(Mw + hc2 * kC * kC, kC, kC, sm.u2.nm.M, wu, kGW);
+      }
+    }
+  };
+
   for (int hh = 0; hh < G; ++hh) {
     const int h = gq * G + hh;
     const Lane ln = lane_opaque();
@@ -528,17 +550,13 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
       else return Glb<E>{Mw + hc * kC * kC, kC, kC};
     }();
 
-    // ---- stage (bf16: copied straight into LDS.  Rows of dO and V beyond L
-    // repeat the last token; they only ever meet zero rows of K and Q, zero
-    // beta and the identity rows of N, so nothing they touch is stored.)
+    // ---- stage: head 0 here; later heads were issued during the previous
+    // head's phase 2 (stage_head below)
     if constexpr (BF) {
-      const int wu = __builtin_amdgcn_readfirstlane(w);
-      copy_rows<128, kD>(Sc + hc * kD * kD, kD, kD, sm.S0, wu, kGW);
-      copy_rows<128, kD>(dSc + hc * kD * kD, kD, kD, sm.dS, wu, kGW);
-      copy_rows<128>(oh, (int64_t)Hv * kD, L, sm.dO, wu, kGW);
-      copy_rows<128>(vh, (int64_t)Hv * kD, L, sm.u1.V, wu, kGW);
-      copy_rows<64>(Nw + hc * kC * kC, kC, kC, sm.u2.nm.N, wu, kGW);
-      copy_rows<64>(Mw + hc * kC * kC, kC, kC, sm.u2.nm.M, wu, kGW);
+      if (hh == 0) {
+        stage_head(0, 0);
+        stage_head(0, 1);
+      }
     }
     if (w == 0) {
       const float a = l < L ? alpha[(tok0 + l) * Hv + h] : 1.f;
@@ -801,6 +819,12 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
 #pragma unroll
           for (int i = 0; i < 4; ++i) dK[mt][i] += sm.dc[16 * mt + 4 * g + i] * T3[mt][i];
       }
+      // S0, dS' and dO are no longer read: the next head's copies start now
+      // and run under the E products and the gate reduction
+      if constexpr (BF) {
+        __syncthreads();
+        if (hh + 1 < G) stage_head(hh + 1, 0);
+      }
       // (dM * Gam) K into dq; (dM * Gam)^T Q and (Wa + Wa^T) K into dk
 #pragma unroll
       for (int kb = 0; kb < kC / KB; ++kb) {
@@ -835,8 +859,14 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
       }
     }
     __syncthreads();
+    // Dl, Y and E are dead: V, N and M of the next head go into their slots
+    if constexpr (BF) {
+      if (hh + 1 < G) stage_head(hh + 1, 1);
+    }
 
-    // ---- gates and beta for this head (wave 0, lane = token)
+    // ---- gates and beta for this head (wave 0, lane = token).  No barrier
+    // after it: the other waves touch nothing it reads before the barrier that
+    // follows the next head's gates, which wave 0 itself computes after this.
     if (w == 0) {
       const int t = l;
       float pa = 0.f, fw = sm.fin[2][t];
@@ -858,7 +888,6 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
         dbeta[gi] = sm.fin[1][t];
       }
     }
-    __syncthreads();
   }
 
   // ---- dq, dk of the group
