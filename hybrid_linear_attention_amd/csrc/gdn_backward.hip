@@ -914,13 +914,8 @@ hipError_t launch_backward(const BackwardLaunch& a, hipStream_t st) {
   const dim3 gchain(kD / (16 * NW), a.Hv, a.B);
   if (a.bf16_io) {
     typedef bf16 E;
-    if (a.Nc > 0 && !a.states_ready) {
-      hipLaunchKernelGGL((fwd_states_kernel<E, NW>), gchain, dim3(64 * NW), 0, st, (const E*)a.k,
-                         (const E*)a.v, a.beta, a.h0, (const E*)a.N, a.gam, a.dec, (E*)a.S,
-                         a.T, a.Nc, a.Hqk, a.Hv);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
+    // the chunk states were written by the forward scan (gdn_api.hip)
+    if (!a.states_ready) return hipErrorInvalidValue;
     constexpr int NWB = 2;
     hipLaunchKernelGGL((bwd_chain_bf16_kernel<NWB>), dim3(kD / (16 * NWB), a.Hv, a.B),
                        dim3(64 * NWB), 0, st, (const E*)a.q, (const E*)a.k, (const E*)a.dout,
