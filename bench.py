@@ -333,11 +333,16 @@ def cpu_baseline(inp, T_sample, min_seconds=10.0, max_calls=64):
                 break
     except OSError:
         pass
-    return dict(value=calls * T_sample / dt, unit="tokens/s", cores=threads, kind="oracle",
+    rate = calls * T_sample / dt
+    single = cpu_single_thread()
+    return dict(value=rate, unit="tokens/s", cores=threads, kind="oracle",
                 sample="%d calls on the first %d of 8192 tokens, all 48 value heads, batch 1, "
                        "float64 sequential recurrence, OpenMP over heads (%.1f s)"
                        % (calls, T_sample, dt),
-                cpu_model=model, single_thread=cpu_single_thread())
+                cpu_model=model, single_thread=single,
+                # per-token work does not depend on T, so the two rates compare
+                # directly: this is the speed-up the host actually gave the threads
+                parallel_speedup=(rate / single["value"]) if single.get("value") else None)
 
 
 def cpu_single_thread(T_sample=256):
