@@ -186,3 +186,31 @@ def test_attn_other_head_layouts(gdn, dtype, Hq, Hkv):
     refd, _ = A.decode(s["q"], s["k"], s["v"], s["gate"], kb, vb, pos_h, inp["q_norm_w"],
                        inp["k_norm_w"])
     assert rel(od, refd) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+def test_attn_full_rotation_and_first_token(gdn, dtype):
+    B, T = 2, 70
+    inp = synth.attention_inputs(B, T, dtype, seed=55)
+    d = dev(inp)
+    # every channel rotates (rope_dim = 256)
+    o = gdn.attn_prefill(d["q"], d["k"], d["v"], d["gate"], d["q_norm_w"], d["k_norm_w"],
+                         rope_dim=256, theta=1.0e6)
+    torch.cuda.synchronize()
+    ref = A.attention(inp["q"], inp["k"], inp["v"], inp["gate"], inp["q_norm_w"],
+                      inp["k_norm_w"], rope_dim=256, theta=1.0e6)
+    assert rel(o, ref) <= TOL[dtype]
+    # decode at position 0 with an empty cache: one key, softmax weight 1, so
+    # o = v * sigmoid(gate) for every query head of the group
+    L = 64
+    kc = torch.zeros((B, L, 4, 256), dtype=dtype, device=DEV)
+    vc = torch.zeros((B, L, 4, 256), dtype=dtype, device=DEV)
+    s = synth.attention_decode_inputs(B, 3, dtype, seed=56)
+    od = gdn.attn_decode(*(s[x].to(DEV) for x in ("q", "k", "v", "gate")), kc, vc,
+                         torch.zeros(B, dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    v64 = s["v"].double().numpy()
+    g64 = s["gate"].double().numpy()
+    want = np.stack([v64[:, h // 6] / (1 + np.exp(-g64[:, h])) for h in range(24)], axis=1)
+    assert rel(od, want) <= TOL[dtype]
+    assert torch.equal(vc[:, 0].cpu(), s["v"])
