@@ -311,8 +311,12 @@ size_t gdn_prefill_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H_qk,
  *                                  attn_output_gate)
  *
  * D must be 256, H_q / H_kv <= 8, rope_dim a multiple of 8 in [0, 256],
- * theta > 0, norm_eps >= 0.  All tensors of dtype dt except the fp32 norm
- * weights; 16-byte aligned.
+ * theta > 0, norm_eps >= 0 (else GDN_ERR_UNSUPPORTED or GDN_ERR_SHAPE).  All
+ * tensors of dtype dt except the fp32 norm weights; 16-byte aligned (norm
+ * weights and pos 4-byte).  Sizes: B * T (prefill) and B * cache_len
+ * (decode) at most 2^25, and B * T * (H_q + H_kv) below 2^31, else
+ * GDN_ERR_UNSUPPORTED.  Outputs (o, the caches, the workspace) may overlap
+ * neither an input nor each other.
  *
  * gdn_attn_prefill - B sequences of T tokens at positions 0 .. T-1.
  *   q, gate   [B, T, H_q, D]   dt
@@ -346,8 +350,11 @@ size_t gdn_attn_prefill_workspace_bytes(int32_t B, int32_t T, int32_t H_q,
  *   k_cache, v_cache [B, cache_len, H_kv, D] dt: row pos[b] receives the
  *             token's normalised, rotated key and its value; the token then
  *             attends to rows 0 .. pos[b].
- *   workspace at least gdn_attn_decode_workspace_bytes(...) bytes (grows with
- *             cache_len: split partials).
+ *   workspace at least gdn_attn_decode_workspace_bytes(...) bytes: the
+ *             rotated queries and one (max, sum, 256-wide sum) partial per
+ *             key split and query head; the keys are split so that the grid
+ *             holds about two workgroups per CU, so the size depends on B,
+ *             H_kv and cache_len.
  * The caller advances pos.
  */
 gdn_status gdn_attn_decode(const void *q, const void *k, const void *v,
