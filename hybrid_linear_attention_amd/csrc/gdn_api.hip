@@ -388,22 +388,131 @@ gdn_status gdn_prefill_varlen(const void* q, const void* k, const void* v, const
 }
 
 namespace {
-// Backward workspace: the forward layout, then N = (I + A)^-1 [nc][Hv][64][64],
-// the state entering every chunk and the gradient of the state leaving every
-// chunk ([nc][Hv][128][128] each), all in the element type.
+// Backward workspace: the forward layout (with the chunk table for a packed
+// batch), then N = (I + A)^-1 [nc][Hv][64][64], the state entering every chunk
+// and the gradient of the state leaving every chunk ([nc][Hv][128][128] each),
+// all in the element type.
 struct BwdLayout {
   WsLayout f;
   size_t n, s, ds, total;
 };
-BwdLayout bwd_layout(int64_t nc, int64_t Hqk, int64_t Hv, gdn_dtype dt) {
+BwdLayout bwd_layout(int64_t nc, int64_t Hqk, int64_t Hv, gdn_dtype dt, int64_t nseq_varlen) {
   BwdLayout b{};
-  b.f = ws_layout(nc, Hqk, Hv, dt, -1);
+  b.f = ws_layout(nc, Hqk, Hv, dt, nseq_varlen);
   const size_t st = round256((size_t)nc * Hv * gdn::kD * gdn::kD * esize(dt));
   b.n = b.f.total;
   b.s = b.n + round256((size_t)nc * Hv * gdn::kC * gdn::kC * esize(dt));
   b.ds = b.s + st;
   b.total = b.ds + st;
   return b;
+}
+
+struct BwdIO {
+  const void *q, *k, *v;
+  const float *alpha, *beta, *h0;
+  const void* dout;
+  const float* dht;
+  void *dq, *dk, *dv;
+  float *dalpha, *dbeta, *dh0;
+};
+
+// Shared by the fixed-length and packed backward calls: checks (all before
+// anything is enqueued), then prepare, the checkpointing scan, the reverse
+// chain and the gradient kernel.  `cu` is null for a fixed-length batch
+// (then cm describes it), else the device cu_seqlens of nseq sequences.
+gdn_status bwd_run(const BwdIO& io, int64_t nseq, int64_t ntok, gdn::ChunkMap cm, int64_t nc,
+                   const int32_t* cu, int32_t H_qk, int32_t H_v, gdn_dtype dt, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  if (nc > (int64_t(1) << 30) || nc * H_v * gdn::kD * gdn::kD > kMaxElems)
+    return GDN_ERR_UNSUPPORTED;
+  if (ntok > 0 && (!io.q || !io.k || !io.v || !io.alpha || !io.beta || !io.dout || !io.dq ||
+                   !io.dk || !io.dv || !io.dalpha || !io.dbeta))
+    return GDN_ERR_NULL;
+  if (ntok * H_v * gdn::kD > kMaxElems || nseq * H_v * gdn::kD * gdn::kD > kMaxElems)
+    return GDN_ERR_UNSUPPORTED;
+  const BwdLayout Lw = bwd_layout(nc, H_qk, H_v, dt, cu ? nseq : -1);
+  const size_t need = nc > 0 ? Lw.total : 0;
+  if (need > 0 && !workspace) return GDN_ERR_WORKSPACE;
+  if (workspace_bytes < need) return GDN_ERR_WORKSPACE;
+  const void* p16[] = {io.q, io.k, io.v, io.dout, io.dq, io.dk, io.dv, io.h0, io.dht, io.dh0,
+                       workspace};
+  for (const void* p : p16)
+    if (!aligned(p, 16)) return GDN_ERR_ALIGN;
+  const void* p4[] = {io.alpha, io.beta, io.dalpha, io.dbeta, cu};
+  for (const void* p : p4)
+    if (!aligned(p, 4)) return GDN_ERR_ALIGN;
+  const int64_t es = (int64_t)esize(dt), Dl = gdn::kD, SB = nseq * H_v * Dl * Dl * 4;
+  const Range ins[] = {span(io.q, ntok * H_qk * Dl * es), span(io.k, ntok * H_qk * Dl * es),
+                       span(io.v, ntok * H_v * Dl * es),  span(io.dout, ntok * H_v * Dl * es),
+                       span(io.alpha, ntok * H_v * 4),    span(io.beta, ntok * H_v * 4),
+                       span(io.h0, SB),                   span(io.dht, SB),
+                       span(cu, cu ? (nseq + 1) * 4 : 0)};
+  const Range outs[] = {span(io.dq, ntok * H_qk * Dl * es), span(io.dk, ntok * H_qk * Dl * es),
+                        span(io.dv, ntok * H_v * Dl * es),  span(io.dalpha, ntok * H_v * 4),
+                        span(io.dbeta, ntok * H_v * 4),     span(io.dh0, SB),
+                        span(workspace, (int64_t)need)};
+  // outputs overlap neither an input nor each other
+  for (size_t a = 0; a < sizeof(outs) / sizeof(outs[0]); ++a) {
+    for (const Range& in : ins)
+      if (overlap(outs[a], in)) return GDN_ERR_ALIAS;
+    for (size_t c = a + 1; c < sizeof(outs) / sizeof(outs[0]); ++c)
+      if (overlap(outs[a], outs[c])) return GDN_ERR_ALIAS;
+  }
+
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  gdn_status s = GDN_OK;
+  if (cu) {
+    int32_t* tab = reinterpret_cast<int32_t*>(ws + Lw.f.tab);
+    int32_t* seq_off = reinterpret_cast<int32_t*>(ws + Lw.f.seq);
+    s = fail_hip(gdn::launch_varlen_table(cu, (int)nseq, (int)ntok, (int)nc, tab, seq_off, st));
+    if (s != GDN_OK) return s;
+    cm = gdn::ChunkMap{tab, seq_off, 0, 0, (int)nc};
+  }
+  if (nc > 0) {
+    gdn::PrefillLaunch a{};
+    a.q = io.q; a.k = io.k; a.v = io.v; a.alpha = io.alpha; a.beta = io.beta;
+    a.Tt = ws + Lw.f.tt;
+    a.M = ws + Lw.f.m;
+    a.gam = reinterpret_cast<float*>(ws + Lw.f.gam);
+    a.dec = reinterpret_cast<float*>(ws + Lw.f.dec);
+    a.cm = cm;
+    a.nseq = (int)nseq;
+    a.ntok = ntok;
+    a.nc_launch = (int)nc;
+    a.Hqk = H_qk; a.Hv = H_v;
+    a.bf16_io = dt == GDN_BF16;
+    a.solve_only = true;
+    a.N = ws + Lw.n;
+    s = fail_hip(gdn::launch_prepare(a, st));
+    if (s != GDN_OK) return s;
+    if (a.bf16_io) {
+      // the forward scan, outputs off, writing the state entering every chunk
+      a.h0 = io.h0;
+      a.states = ws + Lw.s;
+      s = fail_hip(gdn::launch_scan(a, st));
+      if (s != GDN_OK) return s;
+    }
+  }
+  if (nseq == 0 || (nc == 0 && !io.dh0)) return GDN_OK;
+  gdn::BackwardLaunch bl{};
+  bl.q = io.q; bl.k = io.k; bl.v = io.v; bl.dout = io.dout; bl.alpha = io.alpha;
+  bl.beta = io.beta; bl.h0 = io.h0; bl.dht = io.dht;
+  bl.dq = io.dq; bl.dk = io.dk; bl.dv = io.dv; bl.dalpha = io.dalpha; bl.dbeta = io.dbeta;
+  bl.dh0 = io.dh0;
+  bl.N = ws ? ws + Lw.n : nullptr;
+  bl.states_ready = dt == GDN_BF16;
+  bl.M = ws ? ws + Lw.f.m : nullptr;
+  bl.S = ws ? ws + Lw.s : nullptr;
+  bl.dS = ws ? ws + Lw.ds : nullptr;
+  bl.gam = ws ? reinterpret_cast<float*>(ws + Lw.f.gam) : nullptr;
+  bl.dec = ws ? reinterpret_cast<float*>(ws + Lw.f.dec) : nullptr;
+  bl.cm = cm;
+  bl.nseq = (int)nseq;
+  bl.nc = (int)nc;
+  bl.Hqk = H_qk; bl.Hv = H_v;
+  bl.bf16_io = dt == GDN_BF16;
+  return fail_hip(gdn::launch_backward(bl, st));
 }
 }  // namespace
 
@@ -412,7 +521,14 @@ size_t gdn_prefill_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H_qk, int32
   if (check_dims(H_qk, H_v, D, dt) != GDN_OK || B < 0 || T < 0) return 0;
   const int64_t nc = (int64_t)B * (((int64_t)T + gdn::kC - 1) / gdn::kC);
   if (nc == 0) return 0;
-  return bwd_layout(nc, H_qk, H_v, dt).total;
+  return bwd_layout(nc, H_qk, H_v, dt, -1).total;
+}
+
+size_t gdn_varlen_bwd_workspace_bytes(int32_t N, int32_t T_tot, int32_t H_qk, int32_t H_v,
+                                      int32_t D, gdn_dtype dt) {
+  if (check_dims(H_qk, H_v, D, dt) != GDN_OK || N < 0 || T_tot < 0) return 0;
+  const int64_t nc = ((int64_t)T_tot + gdn::kC - 1) / gdn::kC + N;
+  return bwd_layout(nc, H_qk, H_v, dt, N).total;
 }
 
 gdn_status gdn_prefill_chunked_bwd(const void* q, const void* k, const void* v,
@@ -428,83 +544,29 @@ gdn_status gdn_prefill_chunked_bwd(const void* q, const void* k, const void* v,
   if (B > 65535) return GDN_ERR_UNSUPPORTED;
   const int64_t Nc = ((int64_t)T + gdn::kC - 1) / gdn::kC;
   const int64_t nc = (int64_t)B * Nc;
-  if (nc > (int64_t(1) << 30) || nc * H_v * gdn::kD * gdn::kD > kMaxElems)
-    return GDN_ERR_UNSUPPORTED;
-  const int64_t ntok = (int64_t)B * T;
-  if (ntok > 0 && (!q || !k || !v || !alpha || !beta || !dout || !dq || !dk || !dv ||
-                   !dalpha || !dbeta))
-    return GDN_ERR_NULL;
-  if (ntok * H_v * gdn::kD > kMaxElems || (int64_t)B * H_v * gdn::kD * gdn::kD > kMaxElems)
-    return GDN_ERR_UNSUPPORTED;
-  const BwdLayout Lw = bwd_layout(nc, H_qk, H_v, dt);
-  const size_t need = nc > 0 ? Lw.total : 0;
-  if (need > 0 && !workspace) return GDN_ERR_WORKSPACE;
-  if (workspace_bytes < need) return GDN_ERR_WORKSPACE;
-  const void* p16[] = {q, k, v, dout, dq, dk, dv, h0, dht, dh0, workspace};
-  for (const void* p : p16)
-    if (!aligned(p, 16)) return GDN_ERR_ALIGN;
-  const void* p4[] = {alpha, beta, dalpha, dbeta};
-  for (const void* p : p4)
-    if (!aligned(p, 4)) return GDN_ERR_ALIGN;
-  const int64_t es = (int64_t)esize(dt), Dl = gdn::kD, SB = (int64_t)B * H_v * Dl * Dl * 4;
-  const Range ins[] = {span(q, ntok * H_qk * Dl * es), span(k, ntok * H_qk * Dl * es),
-                       span(v, ntok * H_v * Dl * es),  span(dout, ntok * H_v * Dl * es),
-                       span(alpha, ntok * H_v * 4),    span(beta, ntok * H_v * 4),
-                       span(h0, SB),                   span(dht, SB)};
-  const Range outs[] = {span(dq, ntok * H_qk * Dl * es), span(dk, ntok * H_qk * Dl * es),
-                        span(dv, ntok * H_v * Dl * es),  span(dalpha, ntok * H_v * 4),
-                        span(dbeta, ntok * H_v * 4),     span(dh0, SB),
-                        span(workspace, (int64_t)need)};
-  // outputs overlap neither an input nor each other
-  for (size_t a = 0; a < sizeof(outs) / sizeof(outs[0]); ++a) {
-    for (const Range& in : ins)
-      if (overlap(outs[a], in)) return GDN_ERR_ALIAS;
-    for (size_t c = a + 1; c < sizeof(outs) / sizeof(outs[0]); ++c)
-      if (overlap(outs[a], outs[c])) return GDN_ERR_ALIAS;
-  }
+  if (nc > (int64_t(1) << 30)) return GDN_ERR_UNSUPPORTED;
+  const BwdIO io{q, k, v, alpha, beta, h0, dout, dht, dq, dk, dv, dalpha, dbeta, dh0};
+  return bwd_run(io, B, (int64_t)B * T, gdn::ChunkMap{nullptr, nullptr, T, (int)Nc, (int)nc},
+                 nc, nullptr, H_qk, H_v, dt, workspace, workspace_bytes, stream);
+}
 
-  char* ws = static_cast<char*>(workspace);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (nc > 0) {
-    gdn::PrefillLaunch a{};
-    a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta;
-    a.Tt = ws + Lw.f.tt;
-    a.M = ws + Lw.f.m;
-    a.gam = reinterpret_cast<float*>(ws + Lw.f.gam);
-    a.dec = reinterpret_cast<float*>(ws + Lw.f.dec);
-    a.cm = gdn::ChunkMap{nullptr, nullptr, T, (int)Nc, (int)nc};
-    a.nseq = B;
-    a.ntok = ntok;
-    a.nc_launch = (int)nc;
-    a.Hqk = H_qk; a.Hv = H_v;
-    a.bf16_io = dt == GDN_BF16;
-    a.solve_only = true;
-    a.N = ws + Lw.n;
-    s = fail_hip(gdn::launch_prepare(a, st));
-    if (s != GDN_OK) return s;
-    if (a.bf16_io) {
-      // the forward scan, outputs off, writing the state entering every chunk
-      a.h0 = h0;
-      a.states = ws + Lw.s;
-      s = fail_hip(gdn::launch_scan(a, st));
-      if (s != GDN_OK) return s;
-    }
-  }
-  if (B == 0 || (nc == 0 && !dh0)) return GDN_OK;
-  gdn::BackwardLaunch bl{};
-  bl.q = q; bl.k = k; bl.v = v; bl.dout = dout; bl.alpha = alpha; bl.beta = beta;
-  bl.h0 = h0; bl.dht = dht;
-  bl.dq = dq; bl.dk = dk; bl.dv = dv; bl.dalpha = dalpha; bl.dbeta = dbeta; bl.dh0 = dh0;
-  bl.N = ws ? ws + Lw.n : nullptr;
-  bl.states_ready = dt == GDN_BF16;
-  bl.M = ws ? ws + Lw.f.m : nullptr;
-  bl.S = ws ? ws + Lw.s : nullptr;
-  bl.dS = ws ? ws + Lw.ds : nullptr;
-  bl.gam = ws ? reinterpret_cast<float*>(ws + Lw.f.gam) : nullptr;
-  bl.dec = ws ? reinterpret_cast<float*>(ws + Lw.f.dec) : nullptr;
-  bl.B = B; bl.T = T; bl.Nc = (int)Nc; bl.Hqk = H_qk; bl.Hv = H_v;
-  bl.bf16_io = dt == GDN_BF16;
-  return fail_hip(gdn::launch_backward(bl, st));
+gdn_status gdn_prefill_varlen_bwd(const void* q, const void* k, const void* v,
+                                  const float* alpha, const float* beta,
+                                  const int32_t* cu_seqlens, int32_t N, int32_t T_tot,
+                                  const float* h0, const void* dout, const float* dht, void* dq,
+                                  void* dk, void* dv, float* dalpha, float* dbeta, float* dh0,
+                                  int32_t H_qk, int32_t H_v, int32_t D, gdn_dtype dt,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  gdn_status s = check_dims(H_qk, H_v, D, dt);
+  if (s != GDN_OK) return s;
+  if (N < 0 || T_tot < 0) return GDN_ERR_SHAPE;
+  if (N == 0) return T_tot == 0 ? GDN_OK : GDN_ERR_SHAPE;
+  if (N > 65535) return GDN_ERR_UNSUPPORTED;
+  if (!cu_seqlens) return GDN_ERR_NULL;
+  const int64_t nc = ((int64_t)T_tot + gdn::kC - 1) / gdn::kC + N;
+  const BwdIO io{q, k, v, alpha, beta, h0, dout, dht, dq, dk, dv, dalpha, dbeta, dh0};
+  return bwd_run(io, N, T_tot, gdn::ChunkMap{}, nc, cu_seqlens, H_qk, H_v, dt, workspace,
+                 workspace_bytes, stream);
 }
 
 namespace {

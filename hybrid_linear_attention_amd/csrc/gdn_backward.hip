@@ -38,6 +38,7 @@
 //     walks the value heads of its group and accumulates dq and dk for the
 //     group in registers, so no atomics and no reduction pass are needed.
 #include "gdn_device.hpp"
+#include "gdn_chunks.hpp"
 #include "gdn_frag.hpp"
 #include "gdn_launch.hpp"
 
@@ -68,14 +69,16 @@ template <typename E, int NW>
 __global__ __launch_bounds__(64 * NW) void fwd_states_kernel(
     const E* __restrict__ k, const E* __restrict__ v, const float* __restrict__ beta,
     const float* __restrict__ h0, const E* __restrict__ Nw, const float* __restrict__ gam,
-    const float* __restrict__ dec, E* __restrict__ Sc, int T, int Nc, int Hqk, int Hv) {
+    const float* __restrict__ dec, E* __restrict__ Sc, ChunkMap cm, int Hqk, int Hv) {
   constexpr int R = 16 * NW, KB = FragOf<E>::KB, NT = 64 * NW;
   __shared__ ChainSmem<E, NW> sm;
   const Lds<E, 128> Ks{sm.K};
   const Lds<E, R> Vs{sm.V};
   const Lds<E, 64> Ns{sm.N};
   const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
-  const int h = blockIdx.y, b = blockIdx.z, gq = h / (Hv / Hqk);
+  const int h = blockIdx.y, b = blockIdx.z, gq = h / (Hv / Hqk);   // b: sequence
+  int cid0, Nc;
+  seq_chunks(cm, b, cid0, Nc);
   const int rbase = R * blockIdx.x, dv0 = rbase + 16 * w;
 
   f32x4 ST[8];
@@ -86,8 +89,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_states_kernel(
                : zero4();
 
   for (int j = 0; j < Nc; ++j) {
-    const int cid = b * Nc + j, L = min(kC, T - kC * j);
-    const size_t tok0 = (size_t)b * T + (size_t)kC * j;
+    const int cid = cid0 + j;
+    int tok0i, L;
+    chunk_of(cm, cid, tok0i, L);
+    const size_t tok0 = (size_t)tok0i;
     const size_t hc = (size_t)cid * Hv + h;
     E* sdst = Sc + (hc * kD + dv0 + r) * kD;
 #pragma unroll
@@ -145,14 +150,16 @@ __global__ __launch_bounds__(64 * NW) void bwd_chain_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ dout,
     const float* __restrict__ beta, const float* __restrict__ dht, float* __restrict__ dh0,
     const E* __restrict__ Nw, const E* __restrict__ Mw, const float* __restrict__ gam,
-    const float* __restrict__ dec, E* __restrict__ dSc, int T, int Nc, int Hqk, int Hv) {
+    const float* __restrict__ dec, E* __restrict__ dSc, ChunkMap cm, int Hqk, int Hv) {
   constexpr int R = 16 * NW, KB = FragOf<E>::KB, NT = 64 * NW;
   __shared__ ChainSmem<E, NW> sm;
   const Lds<E, 128> Ks{sm.K}, Qs{sm.Q};
   const Lds<E, R> Os{sm.V};
   const Lds<E, 64> Ns{sm.N}, Ms{sm.M};
   const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
-  const int h = blockIdx.y, b = blockIdx.z, gq = h / (Hv / Hqk);
+  const int h = blockIdx.y, b = blockIdx.z, gq = h / (Hv / Hqk);   // b: sequence
+  int cid0, Nc;
+  seq_chunks(cm, b, cid0, Nc);
   const int rbase = R * blockIdx.x, dv0 = rbase + 16 * w;
   constexpr int EP = 16 / sizeof(E);
 
@@ -165,8 +172,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_chain_kernel(
                 : zero4();
 
   for (int j = Nc - 1; j >= 0; --j) {
-    const int cid = b * Nc + j, L = min(kC, T - kC * j);
-    const size_t tok0 = (size_t)b * T + (size_t)kC * j;
+    const int cid = cid0 + j;
+    int tok0i, L;
+    chunk_of(cm, cid, tok0i, L);
+    const size_t tok0 = (size_t)tok0i;
     const size_t hc = (size_t)cid * Hv + h;
     E* ddst = dSc + (hc * kD + dv0 + r) * kD;
 #pragma unroll
@@ -271,12 +280,14 @@ __global__ __launch_bounds__(64 * NW) void bwd_chain_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ dout,
     const float* __restrict__ beta, const float* __restrict__ dht, float* __restrict__ dh0,
     const bf16* __restrict__ Nw, const bf16* __restrict__ Mw, const float* __restrict__ gam,
-    const float* __restrict__ dec, bf16* __restrict__ dSc, int T, int Nc, int Hqk, int Hv) {
+    const float* __restrict__ dec, bf16* __restrict__ dSc, ChunkMap cm, int Hqk, int Hv) {
   typedef bf16 E;
   constexpr int R = 16 * NW, KB = 32;
   __shared__ ChainDmaBuf<NW> buf[2];
   const int w = __builtin_amdgcn_readfirstlane(wave_id()), l = lane_id(), r = l & 15, g = l >> 4;
-  const int h = blockIdx.y, b = blockIdx.z, gq = h / (Hv / Hqk);
+  const int h = blockIdx.y, b = blockIdx.z, gq = h / (Hv / Hqk);   // b: sequence
+  int cid0, Nc;
+  seq_chunks(cm, b, cid0, Nc);
   const int rbase = R * blockIdx.x, dv0 = rbase + 16 * w;
 
   // The two buffers alternate with the iteration parity, which is a
@@ -285,8 +296,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_chain_bf16_kernel(
   // immediate offset away).
   auto issue = [&](int j, auto bic) {
     ChainDmaBuf<NW>& B_ = buf[decltype(bic)::value];
-    const int cid = b * Nc + j, L = min(kC, T - kC * j);
-    const size_t tok0 = (size_t)b * T + (size_t)kC * j;
+    const int cid = cid0 + j;
+    int tok0i, L;
+    chunk_of(cm, cid, tok0i, L);
+    const size_t tok0 = (size_t)tok0i;
     const size_t hc = (size_t)cid * Hv + h;
     copy_rows<128>(k + (tok0 * Hqk + gq) * kD, (int64_t)Hqk * kD, L, B_.K, w, NW);
     copy_rows<128>(q + (tok0 * Hqk + gq) * kD, (int64_t)Hqk * kD, L, B_.Q, w, NW);
@@ -312,7 +325,9 @@ __global__ __launch_bounds__(64 * NW) void bwd_chain_bf16_kernel(
 
   auto step = [&](int j, auto bic) {
     constexpr int bi = decltype(bic)::value;
-    const int cid = b * Nc + j, L = min(kC, T - kC * j);
+    const int cid = cid0 + j;
+    int tok0i, L;
+    chunk_of(cm, cid, tok0i, L);
     const size_t hc = (size_t)cid * Hv + h;
     E* ddst = dSc + (hc * kD + dv0 + r) * kD;
 #pragma unroll
@@ -456,14 +471,16 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
     const E* __restrict__ dout, const float* __restrict__ alpha, const float* __restrict__ beta,
     const E* __restrict__ Nw, const E* __restrict__ Mw, const E* __restrict__ Sc,
     const E* __restrict__ dSc, E* __restrict__ dq, E* __restrict__ dk, E* __restrict__ dv,
-    float* __restrict__ dalpha, float* __restrict__ dbeta, int T, int Nc, int Hqk, int Hv) {
+    float* __restrict__ dalpha, float* __restrict__ dbeta, ChunkMap cm, int Hqk, int Hv) {
   constexpr bool BF = sizeof(E) == 2;
   constexpr int KB = FragOf<E>::KB, NT = 64 * kGW, NS = kSlotsOf<E>;
   __shared__ GradSmem<E> sm;
   const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
   const int cid = blockIdx.x, gq = blockIdx.y, G = Hv / Hqk;
-  const int b = cid / Nc, j = cid - b * Nc, L = min(kC, T - kC * j);
-  const size_t tok0 = (size_t)b * T + (size_t)kC * j;
+  int tok0i, L;
+  chunk_of(cm, cid, tok0i, L);
+  if (L <= 0) return;                     // unused slot of a packed batch's table
+  const size_t tok0 = (size_t)tok0i;
 
   const Lds<E, 128> Dls{sm.u1.Dl}, Ys{sm.u2.Y};
   const Lds<E, 64> Es{sm.u3.Em};
@@ -911,41 +928,41 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
 hipError_t launch_backward(const BackwardLaunch& a, hipStream_t st) {
   using namespace bwd;
   constexpr int NW = 2;
-  const dim3 gchain(kD / (16 * NW), a.Hv, a.B);
+  const dim3 gchain(kD / (16 * NW), a.Hv, a.nseq);
   if (a.bf16_io) {
     typedef bf16 E;
     // the chunk states were written by the forward scan (gdn_api.hip)
     if (!a.states_ready) return hipErrorInvalidValue;
     constexpr int NWB = 2;
-    hipLaunchKernelGGL((bwd_chain_bf16_kernel<NWB>), dim3(kD / (16 * NWB), a.Hv, a.B),
+    hipLaunchKernelGGL((bwd_chain_bf16_kernel<NWB>), dim3(kD / (16 * NWB), a.Hv, a.nseq),
                        dim3(64 * NWB), 0, st, (const E*)a.q, (const E*)a.k, (const E*)a.dout,
                        a.beta, a.dht, a.dh0, (const E*)a.N, (const E*)a.M, a.gam, a.dec,
-                       (E*)a.dS, a.T, a.Nc, a.Hqk, a.Hv);
+                       (E*)a.dS, a.cm, a.Hqk, a.Hv);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.Nc == 0) return e;
-    hipLaunchKernelGGL((bwd_grad_kernel<E>), dim3(a.B * a.Nc, a.Hqk), dim3(64 * kGW), 0, st,
+    if (e != hipSuccess || a.nc == 0) return e;
+    hipLaunchKernelGGL((bwd_grad_kernel<E>), dim3(a.nc, a.Hqk), dim3(64 * kGW), 0, st,
                        (const E*)a.q, (const E*)a.k, (const E*)a.v, (const E*)a.dout, a.alpha,
                        a.beta, (const E*)a.N, (const E*)a.M, (const E*)a.S, (const E*)a.dS,
-                       (E*)a.dq, (E*)a.dk, (E*)a.dv, a.dalpha, a.dbeta, a.T, a.Nc, a.Hqk, a.Hv);
+                       (E*)a.dq, (E*)a.dk, (E*)a.dv, a.dalpha, a.dbeta, a.cm, a.Hqk, a.Hv);
     return hipGetLastError();
   } else {
     typedef float E;
-    if (a.Nc > 0) {
+    if (a.nc > 0) {
       hipLaunchKernelGGL((fwd_states_kernel<E, NW>), gchain, dim3(64 * NW), 0, st, (const E*)a.k,
                          (const E*)a.v, a.beta, a.h0, (const E*)a.N, a.gam, a.dec, (E*)a.S,
-                         a.T, a.Nc, a.Hqk, a.Hv);
+                         a.cm, a.Hqk, a.Hv);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL((bwd_chain_kernel<E, NW>), gchain, dim3(64 * NW), 0, st, (const E*)a.q,
                        (const E*)a.k, (const E*)a.dout, a.beta, a.dht, a.dh0, (const E*)a.N,
-                       (const E*)a.M, a.gam, a.dec, (E*)a.dS, a.T, a.Nc, a.Hqk, a.Hv);
+                       (const E*)a.M, a.gam, a.dec, (E*)a.dS, a.cm, a.Hqk, a.Hv);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.Nc == 0) return e;
-    hipLaunchKernelGGL((bwd_grad_kernel<E>), dim3(a.B * a.Nc, a.Hqk), dim3(64 * kGW), 0, st,
+    if (e != hipSuccess || a.nc == 0) return e;
+    hipLaunchKernelGGL((bwd_grad_kernel<E>), dim3(a.nc, a.Hqk), dim3(64 * kGW), 0, st,
                        (const E*)a.q, (const E*)a.k, (const E*)a.v, (const E*)a.dout, a.alpha,
                        a.beta, (const E*)a.N, (const E*)a.M, (const E*)a.S, (const E*)a.dS,
-                       (E*)a.dq, (E*)a.dk, (E*)a.dv, a.dalpha, a.dbeta, a.T, a.Nc, a.Hqk, a.Hv);
+                       (E*)a.dq, (E*)a.dk, (E*)a.dv, a.dalpha, a.dbeta, a.cm, a.Hqk, a.Hv);
     return hipGetLastError();
   }
 }

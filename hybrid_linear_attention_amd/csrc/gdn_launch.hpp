@@ -35,7 +35,7 @@ struct PrefillLaunch {
   void* states;            // bf16 scan: state entering every chunk (backward pass), or null
 };
 
-// Backward pass of a fixed-length prefill (B sequences of T tokens).
+// Backward pass of a prefill: B sequences of T tokens, or N packed sequences.
 struct BackwardLaunch {
   const void *q, *k, *v, *dout;
   const float *alpha, *beta;
@@ -45,7 +45,9 @@ struct BackwardLaunch {
   float* dh0;              // or null (not written)
   void *N, *M, *S, *dS;    // workspace: prepare's solve and mask, chunk states, state grads
   float *gam, *dec;
-  int B, T, Nc, Hqk, Hv;
+  ChunkMap cm;             // where each chunk lives (fixed length, or the packed table)
+  int nseq, nc;            // sequences (h0/dht/dh0 rows) and chunk slots
+  int Hqk, Hv;
   bool bf16_io;
   bool states_ready;       // S already written (by the bf16 forward scan)
 };

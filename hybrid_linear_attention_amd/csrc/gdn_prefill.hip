@@ -40,6 +40,7 @@
 //    operands copied straight into LDS) and a generic one (scan_kernel: fp32
 //    inputs, and the gated RMSNorm epilogue), which stages operands through
 //    registers one chunk ahead.
+#include "gdn_chunks.hpp"
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
@@ -62,24 +63,6 @@ struct Work {
 // directly: G2_t = sum_{j<=t} log2(alpha_j), exp(G_i - G_j) = 2^(G2_i - G2_j).
 __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
-
-// The chunk table is read through the constant address space: every caller
-// passes a wave-uniform chunk id, so these become scalar loads.  A vector load
-// here would make any wait for it (vector loads complete in order) also wait
-// for the producer's in-flight global->LDS copies.
-typedef const __attribute__((address_space(4))) int32_t const_i32;
-
-__device__ __forceinline__ void chunk_of(const ChunkMap& cm, int cid, int& tok0, int& L) {
-  if (cm.tab) {
-    const_i32* t = (const_i32*)cm.tab;
-    tok0 = t[2 * cid];
-    L = t[2 * cid + 1];
-  } else {
-    const int b = cid / cm.Nc, j = cid - (cid / cm.Nc) * cm.Nc;
-    tok0 = b * cm.T + kC * j;
-    L = min(kC, cm.T - kC * j);
-  }
-}
 
 // 16 consecutive bytes of a row of q/k/v (8 bf16 or 4 fp32), zero if masked.
 template <typename E>

@@ -67,6 +67,11 @@ def _load():
     lib.gdn_prefill_chunked_bwd.restype = ctypes.c_int
     lib.gdn_prefill_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int]
     lib.gdn_prefill_bwd_workspace_bytes.restype = sz
+    lib.gdn_prefill_varlen_bwd.argtypes = ([vp] * 6 + [i32, i32] + [vp] * 9 + [i32] * 3
+                                           + [ctypes.c_int, vp, sz, vp])
+    lib.gdn_prefill_varlen_bwd.restype = ctypes.c_int
+    lib.gdn_varlen_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int]
+    lib.gdn_varlen_bwd_workspace_bytes.restype = sz
     lib.gdn_attn_prefill.argtypes = ([vp] * 6 + [f32] + [vp] * 3 + [i32] * 7
                                      + [f32, ctypes.c_int, vp, sz, vp])
     lib.gdn_attn_prefill.restype = ctypes.c_int
@@ -266,6 +271,49 @@ def prefill_backward(q, k, v, alpha, beta, do, h0=None, dht=None, *, grads=None,
         _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(h0), _ptr(do), _ptr(dht),
         _ptr(dq), _ptr(dk), _ptr(dv), _ptr(da), _ptr(db), _ptr(dh0),
         B, T, H_qk, H_v, D, _dt(q), _ptr(ws), nbytes, _stream(dev)), "gdn_prefill_chunked_bwd")
+    return dq, dk, dv, da, db, dh0
+
+
+def varlen_bwd_workspace_bytes(N, T_tot, H_qk, H_v, D=HEAD_DIM, dtype=torch.bfloat16) -> int:
+    dt = GDN_BF16 if dtype == torch.bfloat16 else GDN_F32
+    return int(lib.gdn_varlen_bwd_workspace_bytes(N, T_tot, H_qk, H_v, D, dt))
+
+
+def prefill_varlen_backward(q, k, v, alpha, beta, cu_seqlens, do, h0=None, dht=None, *,
+                            want_dh0=True, workspace=None):
+    """Gradients of a packed prefill (gdn_prefill_varlen_bwd): q, k [T_tot,
+    Hqk, 128]; v, do [T_tot, Hv, 128]; alpha, beta [T_tot, Hv]; cu_seqlens
+    int32 [N+1] on the device; h0, dht [N, Hv, 128, 128] fp32 or None.
+    Returns (dq, dk, dv, dalpha, dbeta, dh0)."""
+    _req(q, "q", ndim=3)
+    dtype, dev = q.dtype, q.device
+    T_tot, H_qk, D = q.shape
+    for name, t in (("k", k), ("v", v), ("do", do)):
+        _req(t, name, dtype, 3, dev)
+    H_v = v.shape[1]
+    if tuple(k.shape) != (T_tot, H_qk, D) or tuple(v.shape) != (T_tot, H_v, D) \
+            or tuple(do.shape) != (T_tot, H_v, D):
+        raise ValueError("q/k [T,Hqk,D], v/do [T,Hv,D] disagree")
+    for name, t in (("alpha", alpha), ("beta", beta)):
+        _req(t, name, torch.float32, 2, dev)
+        if tuple(t.shape) != (T_tot, H_v):
+            raise ValueError("%s must be [T_tot,Hv]" % name)
+    _req(cu_seqlens, "cu_seqlens", torch.int32, 1, dev)
+    N = cu_seqlens.numel() - 1
+    for name, t in (("h0", h0), ("dht", dht)):
+        _req(t, name, torch.float32, 4, dev)
+        if t is not None and tuple(t.shape) != (N, H_v, D, D):
+            raise ValueError("%s must be [N,Hv,D,D]" % name)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    da, db = torch.empty_like(alpha), torch.empty_like(beta)
+    dh0 = torch.empty((N, H_v, D, D), dtype=torch.float32, device=dev) if want_dh0 else None
+    nbytes = varlen_bwd_workspace_bytes(N, T_tot, H_qk, H_v, D, dtype)
+    ws = _workspace(nbytes, dev, workspace)
+    _check(lib.gdn_prefill_varlen_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(cu_seqlens), N, T_tot,
+        _ptr(h0), _ptr(do), _ptr(dht), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(da), _ptr(db),
+        _ptr(dh0), H_qk, H_v, D, _dt(q), _ptr(ws), nbytes, _stream(dev)),
+        "gdn_prefill_varlen_bwd")
     return dq, dk, dv, da, db, dh0
 
 

@@ -292,6 +292,31 @@ size_t gdn_prefill_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H_qk,
                                        int32_t H_v, int32_t D, gdn_dtype dt);
 
 /*
+ * gdn_prefill_varlen_bwd - gradients of a packed prefill (gdn_prefill_varlen
+ * without the gated output): N sequences packed along the token axis with
+ * cu_seqlens, as training batches pack them.  Layouts as for
+ * gdn_prefill_varlen and gdn_prefill_chunked_bwd with the token axis T_tot:
+ * dout, dv [T_tot, H_v, D]; dq, dk [T_tot, H_qk, D]; dalpha, dbeta
+ * [T_tot, H_v]; h0, dht, dh0 [N, H_v, D, D] float32 (h0, dht and dh0 may be
+ * NULL).  cu_seqlens is the same int32 DEVICE array (precondition: starts at
+ * 0, non-decreasing, ends at T_tot; never read on the host).  workspace at
+ * least gdn_varlen_bwd_workspace_bytes(...) bytes.
+ */
+gdn_status gdn_prefill_varlen_bwd(const void *q, const void *k, const void *v,
+                                  const float *alpha, const float *beta,
+                                  const int32_t *cu_seqlens, int32_t N,
+                                  int32_t T_tot, const float *h0,
+                                  const void *dout, const float *dht, void *dq,
+                                  void *dk, void *dv, float *dalpha,
+                                  float *dbeta, float *dh0, int32_t H_qk,
+                                  int32_t H_v, int32_t D, gdn_dtype dt,
+                                  void *workspace, size_t workspace_bytes,
+                                  void *stream);
+
+size_t gdn_varlen_bwd_workspace_bytes(int32_t N, int32_t T_tot, int32_t H_qk,
+                                      int32_t H_v, int32_t D, gdn_dtype dt);
+
+/*
  * Gated attention layer: the other layer type of the hybrid stack (one in four
  * layers; page "Inside Qwen3.8-27B ...", section "The Role of Periodic Gated
  * Attention": 24 query heads, 4 key/value heads, head dim 256, rotary

@@ -384,3 +384,39 @@ def test_attn_empty_calls_and_workspace(gdn, lib):
         want = r256(B * 24 * 256 * 2) + 2 * r256(B * 24 * ns * 4) + r256(B * 24 * ns * 256 * 4)
         assert gdn.attn_decode_workspace_bytes(B, L) == want, (B, L)
     assert gdn.attn_decode_workspace_bytes(2, 0) == 0
+
+
+def varlen_bwd_call(lib, **kw):
+    a = dict(q=addr(0), k=addr(1), v=addr(2), alpha=addr(3), beta=addr(4), cu=addr(15), N=3,
+             T=300, h0=addr(5), do=addr(6), dht=addr(7), dq=addr(8), dk=addr(9), dv=addr(10),
+             da=addr(11), db=addr(12), dh0=addr(13), Hqk=16, Hv=48, D=128, dt=BF16, ws=addr(14),
+             ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return lib.gdn_prefill_varlen_bwd(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["cu"],
+                                      a["N"], a["T"], a["h0"], a["do"], a["dht"], a["dq"],
+                                      a["dk"], a["dv"], a["da"], a["db"], a["dh0"], a["Hqk"],
+                                      a["Hv"], a["D"], a["dt"], a["ws"], a["ws_bytes"],
+                                      a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=64), EUNSUP),
+    (dict(N=-1), ESHAPE),
+    (dict(N=0), ESHAPE),                      # tokens without sequences
+    (dict(cu=None), ENULL),
+    (dict(do=None), ENULL),
+    (dict(ws=None), EWS),
+    (dict(cu=addr(15, 2)), EALIGN),
+    (dict(dk=addr(1, 256)), EALIAS),          # dk inside k
+    (dict(ws=addr(15)), EALIAS),              # workspace is cu_seqlens
+])
+def test_varlen_backward_validation(lib, kw, code):
+    assert varlen_bwd_call(lib, **kw) == code
+
+
+def test_varlen_backward_workspace(gdn, lib):
+    assert varlen_bwd_call(lib, N=0, T=0) == OK
+    # the fixed-length layout for ceil(T/64) + N chunks, plus the chunk table
+    w = gdn.varlen_bwd_workspace_bytes(3, 300, 16, 48)
+    assert w > gdn.prefill_bwd_workspace_bytes(1, 64 * 8, 16, 48)
+    assert gdn.varlen_bwd_workspace_bytes(3, 300, 16, 48, D=64) == 0
