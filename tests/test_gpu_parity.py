@@ -629,3 +629,48 @@ def test_varlen_backward_equals_separate_sequences(gdn, dtype):
                 continue
             err = rel(x, y)
             assert err <= TOL[dtype], (n, name, err)
+
+
+def test_graph_capture_replays_match_eager(gdn):
+    # every entry point only enqueues work on the current stream, so a HIP
+    # graph can hold them: four decode steps and a chunked prefill, replayed
+    # three times with eager work in between, each replay checked bitwise
+    # against the same calls run eagerly
+    B = 8
+    st0 = synth.decode_state(B, 91, 0.02).to(DEV)
+    steps = [to_dev(synth.decode_step_inputs(B, s, torch.bfloat16, seed=92)) for s in range(4)]
+    pre = to_dev(synth.prefill_inputs(1, 200, torch.bfloat16, seed=93, h0_std=0.02))
+    ws = torch.empty(gdn.prefill_workspace_bytes(1, 200, 16, 48), dtype=torch.uint8, device=DEV)
+    outs = [torch.empty((B, 48, 128), dtype=torch.bfloat16, device=DEV) for _ in range(4)]
+    o_pre = torch.empty((1, 200, 48, 128), dtype=torch.bfloat16, device=DEV)
+    ht_pre = torch.empty((1, 48, 128, 128), dtype=torch.float32, device=DEV)
+    state = st0.clone()
+
+    def work():
+        for s, d in enumerate(steps):
+            gdn.decode_step(d["q"], d["k"], d["v"], d["alpha"], d["beta"], state, o=outs[s])
+        gdn.prefill_chunked(pre["q"], pre["k"], pre["v"], pre["alpha"], pre["beta"], pre["h0"],
+                            o=o_pre, ht=ht_pre, workspace=ws)
+
+    work()                                   # eager reference
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in outs] + [state.clone(), o_pre.clone(), ht_pre.clone()]
+    state.copy_(st0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            work()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        state.copy_(st0)                     # eager work between replays
+        for x in outs:
+            x.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = outs + [state, o_pre, ht_pre]
+        for a, b in zip(got, ref):
+            assert torch.equal(a, b), rep
