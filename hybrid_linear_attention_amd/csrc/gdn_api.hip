@@ -127,6 +127,29 @@ gdn_status check_prefill(const void* q, const void* k, const void* v, const floa
   return GDN_OK;
 }
 
+// Debug mode (environment GDN_DEBUG=1): the packed calls copy cu_seqlens to
+// the host, synchronously on the caller's stream, and reject offsets that do
+// not run from 0 to T_tot without decreasing.  Off by default: the calls
+// then never read device memory on the host (the device-side chunk table
+// clamps malformed offsets, so they cannot send a kernel out of bounds).
+gdn_status debug_check_cu(const int32_t* cu, int32_t N, int32_t T_tot, void* stream) {
+  const char* e = getenv("GDN_DEBUG");
+  if (!e || e[0] != '1') return GDN_OK;
+  int32_t* h = static_cast<int32_t*>(malloc(sizeof(int32_t) * ((size_t)N + 1)));
+  if (!h) return GDN_ERR_UNSUPPORTED;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t he = hipMemcpyAsync(h, cu, sizeof(int32_t) * ((size_t)N + 1), hipMemcpyDeviceToHost, st);
+  if (he == hipSuccess) he = hipStreamSynchronize(st);
+  gdn_status s = fail_hip(he);
+  if (s == GDN_OK) {
+    bool ok = h[0] == 0 && h[N] == T_tot;
+    for (int32_t n = 0; n < N && ok; ++n) ok = h[n] <= h[n + 1];
+    if (!ok) s = GDN_ERR_SHAPE;
+  }
+  free(h);
+  return s;
+}
+
 enum Phase { kPrepare = 1, kScan = 2, kBoth = 3 };
 
 gdn_status prefill_fixed(const void* q, const void* k, const void* v, const float* alpha,
@@ -361,6 +384,8 @@ gdn_status gdn_prefill_varlen(const void* q, const void* k, const void* v, const
   s = check_prefill(q, k, v, alpha, beta, h0, o, ht, gate, norm_weight, cu_seqlens, N + 1,
                     T_tot, N, H_qk, H_v, dt, workspace, workspace_bytes, L.total, 4);
   if (s != GDN_OK) return s;
+  s = debug_check_cu(cu_seqlens, N, T_tot, stream);
+  if (s != GDN_OK) return s;
 
   char* ws = static_cast<char*>(workspace);
   int32_t* tab = reinterpret_cast<int32_t*>(ws + L.tab);
@@ -461,7 +486,8 @@ gdn_status bwd_run(const BwdIO& io, int64_t nseq, int64_t ntok, gdn::ChunkMap cm
 
   char* ws = static_cast<char*>(workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  gdn_status s = GDN_OK;
+  gdn_status s = cu ? debug_check_cu(cu, (int32_t)nseq, (int32_t)ntok, stream) : GDN_OK;
+  if (s != GDN_OK) return s;
   if (cu) {
     int32_t* tab = reinterpret_cast<int32_t*>(ws + Lw.f.tab);
     int32_t* seq_off = reinterpret_cast<int32_t*>(ws + Lw.f.seq);

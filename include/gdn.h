@@ -224,7 +224,11 @@ gdn_status gdn_decode_commit(const void *k, const void *v, const float *alpha,
  *   alpha, beta [T_tot, H_v]      float32
  *   cu_seqlens  [N + 1]           int32 DEVICE pointer: cu_seqlens[0] = 0,
  *                                 non-decreasing, cu_seqlens[N] = T_tot
- *                                 (precondition; never read on the host).
+ *                                 (precondition; never read on the host,
+ *                                 except with the environment variable
+ *                                 GDN_DEBUG=1: then the call copies it to
+ *                                 the host, synchronously on `stream`, and
+ *                                 returns GDN_ERR_SHAPE if it is malformed).
  *                                 Zero-length sequences are allowed.
  *   h0          [N, H_v, D, D]    float32 or NULL (zeros)
  *   o           [T_tot, H_v, D]   dt

@@ -674,3 +674,23 @@ def test_graph_capture_replays_match_eager(gdn):
         got = outs + [state, o_pre, ht_pre]
         for a, b in zip(got, ref):
             assert torch.equal(a, b), rep
+
+
+def test_debug_mode_rejects_malformed_cu_seqlens(gdn, monkeypatch):
+    # GDN_DEBUG=1: the packed calls read cu_seqlens on the host and refuse
+    # offsets that decrease or do not end at T_tot; without it they never read
+    vl = synth.varlen_inputs([40, 60], dtype=torch.bfloat16, seed=95, gate=False)
+    d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in vl.items()}
+    monkeypatch.setenv("GDN_DEBUG", "1")
+    y, _ = gdn.prefill_varlen(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["cu_seqlens"],
+                              d["h0"])
+    torch.cuda.synchronize()
+    for bad in ([0, 70, 60], [0, 40, 99], [5, 40, 100]):
+        cu = torch.tensor(bad, dtype=torch.int32, device=DEV)
+        with pytest.raises(gdn.GDNError) as ei:
+            gdn.prefill_varlen(d["q"], d["k"], d["v"], d["alpha"], d["beta"], cu, d["h0"])
+        assert ei.value.status == -2
+        do = torch.zeros((100, 48, 128), dtype=torch.bfloat16, device=DEV)
+        with pytest.raises(gdn.GDNError) as ei:
+            gdn.prefill_varlen_backward(d["q"], d["k"], d["v"], d["alpha"], d["beta"], cu, do)
+        assert ei.value.status == -2
