@@ -53,8 +53,10 @@ constexpr int kKvb = 64;        // keys per prefill block
 
 // Rows of token tok: heads 0 .. Hq-1 are queries, Hq .. Hq+Hkv-1 keys.
 // Token tok = b * T + t sits at position pos[b] (decode) or t (prefill, pos null).
+constexpr int kPrepWaves = 8;   // waves per token (a decode step has only B tokens)
+
 template <typename E>
-__global__ __launch_bounds__(256) void attn_prep_kernel(
+__global__ __launch_bounds__(64 * kPrepWaves) void attn_prep_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ qw, const float* __restrict__ kw, float eps, int rope_dim,
     double log2_theta, const int32_t* __restrict__ pos, E* __restrict__ qo, E* __restrict__ kc,
@@ -85,8 +87,8 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(
       cs[i] = __builtin_amdgcn_cosf((float)rev);
     }
   }
-  constexpr int RB = 8;                           // rows per wave per batch
-  for (int hb = w * RB; hb < H; hb += 4 * RB) {
+  constexpr int RB = 4;                           // rows per wave per batch
+  for (int hb = w * RB; hb < H; hb += kPrepWaves * RB) {
     f32x4 xs[RB];
 #pragma unroll
     for (int rr = 0; rr < RB; ++rr) {
@@ -660,7 +662,7 @@ template <typename E>
 static hipError_t attn_launch_t(const AttnLaunch& a, hipStream_t st) {
   using namespace attn;
   const int64_t ntok = a.decode ? a.B : (int64_t)a.B * a.T;
-  hipLaunchKernelGGL((attn_prep_kernel<E>), dim3((unsigned)ntok), dim3(256), 0, st,
+  hipLaunchKernelGGL((attn_prep_kernel<E>), dim3((unsigned)ntok), dim3(64 * kPrepWaves), 0, st,
                      (const E*)a.q, (const E*)a.k, (const E*)a.v, a.qw, a.kw, a.eps, a.rope_dim,
                      std::log2((double)a.theta), a.decode ? a.pos : nullptr, (E*)a.qrot, (E*)a.kc, (E*)a.vc_write, ntok,
                      a.decode ? 1 : a.T, a.cache_len, a.Hq, a.Hkv);
