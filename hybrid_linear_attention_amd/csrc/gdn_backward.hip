@@ -33,10 +33,13 @@
 //  3. bwd_chain: dL/dS carried from the last chunk to the first, storing the
 //     gradient of the state leaving every chunk; dh0 at the end.  Value rows
 //     never interact in either chain, so rows split across waves and
-//     workgroups as in the forward scan.
+//     workgroups as in the forward scan.  bf16: bwd_chain_bf16_kernel, its
+//     operands double-buffered in LDS by direct copies.
 //  4. bwd_grad: one workgroup per (chunk, query/key head), fully parallel.  It
 //     walks the value heads of its group and accumulates dq and dk for the
 //     group in registers, so no atomics and no reduction pass are needed.
+// Chunks are found through a ChunkMap, so the same kernels serve a
+// fixed-length batch and a packed (cu_seqlens) batch.
 #include "gdn_device.hpp"
 #include "gdn_chunks.hpp"
 #include "gdn_frag.hpp"
@@ -420,8 +423,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_chain_bf16_kernel(
 //            above it) and the gate and beta row/column sums.
 //  phase 2   wave w owns key columns 16w..16w+15 of dq and dk (rows: tokens),
 //            accumulated over the group's value heads in registers.
-// bf16 stages every operand in LDS (about 157 KB); fp32 reads the inputs from
-// global memory (L2) and keeps only the intermediates Dl, Y, E in LDS.
+// bf16 stages every operand in LDS (about 159 KB): the next value head's S0,
+// dS' and dO are copied while the current head's E products run, and its V, N
+// and M once Dl and Y are dead.  fp32 reads the inputs from global memory (L2)
+// and keeps only the intermediates Dl, Y, E in LDS.
 constexpr int kGW = 8;  // waves
 
 // v[4 mt + i] is a sum already broadcast over the 16 lanes of lane group g
