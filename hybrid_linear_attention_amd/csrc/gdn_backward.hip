@@ -412,6 +412,182 @@ __global__ __launch_bounds__(64 * NW) void bwd_chain_bf16_kernel(
   }
 }
 
+// bf16 reverse chain with a role split, as the forward scan has: per
+// workgroup two 16-row value slices; waves 0-1 are chain waves (slice s = w),
+// waves 2-3 helpers (slice s = w - 2).  The helpers issue every copy and take
+// the two state-independent products off the chain:
+//   helpers:  copies of chunk j-1; MdO = M^T dO[:, slice] -> LDS; barrier A;
+//             U = (gamma Q)^T dO[:, slice] -> LDS; barrier B; their copies
+//             complete; barrier C
+//   chain:    store dS (the gradient of the state leaving chunk j); P = K dS^T;
+//             barrier A; dDl = MdO + diag(dec) P; Y = N^T dDl; Z = -gamma beta Y;
+//             barrier B; dS^T <- gamma_L dS^T + U + K^T Z; barrier C
+// so a chain wave issues 38 MFMAs per chunk instead of 64.  A hand-off tile is
+// written after the barrier that ends the iteration in which it was last read.
+struct SplitHand {
+  f32x4 mdo[2][4][64];    // [slice][token tile][lane]: M^T dO, 64 tokens x 16 rows
+  f32x4 u[2][8][64];      // [slice][d_k tile][lane]: (gamma Q)^T dO, transposed like dS^T
+};
+
+__global__ __launch_bounds__(256) void bwd_chain_split_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ dout,
+    const float* __restrict__ beta, const float* __restrict__ dht, float* __restrict__ dh0,
+    const bf16* __restrict__ Nw, const bf16* __restrict__ Mw, const float* __restrict__ gam,
+    const float* __restrict__ dec, bf16* __restrict__ dSc, ChunkMap cm, int Hqk, int Hv) {
+  typedef bf16 E;
+  constexpr int NS = 2, R = 16 * NS, KB = 32;
+  __shared__ ChainDmaBuf<NS> buf[2];
+  __shared__ SplitHand hand;
+  const int w = __builtin_amdgcn_readfirstlane(wave_id()), l = lane_id(), r = l & 15, g = l >> 4;
+  const bool is_chain = w < NS;
+  const int sl = is_chain ? w : w - NS;                 // this wave's slice
+  const int h = blockIdx.y, b = blockIdx.z, gq = h / (Hv / Hqk);   // b: sequence
+  int cid0, Nc;
+  seq_chunks(cm, b, cid0, Nc);
+  const int rbase = R * blockIdx.x, dv0 = rbase + 16 * sl;
+
+  // copies of chunk j into buffer bi, by the two helper waves
+  auto issue = [&](int j, auto bic) {
+    ChainDmaBuf<NS>& B_ = buf[decltype(bic)::value];
+    const int cid = cid0 + j;
+    int tok0i, L;
+    chunk_of(cm, cid, tok0i, L);
+    const size_t tok0 = (size_t)tok0i;
+    const size_t hc = (size_t)cid * Hv + h;
+    const int hw = w - NS;
+    copy_rows<128>(k + (tok0 * Hqk + gq) * kD, (int64_t)Hqk * kD, L, B_.K, hw, NS);
+    copy_rows<128>(q + (tok0 * Hqk + gq) * kD, (int64_t)Hqk * kD, L, B_.Q, hw, NS);
+    copy_rows<R>(dout + (tok0 * Hv + h) * kD + rbase, (int64_t)Hv * kD, L, B_.O, hw, NS);
+    copy_rows<64>(Nw + hc * kC * kC, kC, kC, B_.N, hw, NS);
+    copy_rows<64>(Mw + hc * kC * kC, kC, kC, B_.M, hw, NS);
+    if (hw == 0) {
+      dma4(gam + hc * kC + l, B_.gm);
+      dma4(beta + (tok0 + min(l, L - 1)) * Hv + h, B_.bt);
+    } else {
+      dma4(dec + hc * kC + l, B_.dc);
+    }
+  };
+
+  f32x4 DT[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+    DT[t] = (is_chain && dht) ? *reinterpret_cast<const f32x4*>(
+                                    dht + (((size_t)b * Hv + h) * kD + dv0 + r) * kD + 16 * t + 4 * g)
+                              : zero4();
+  const std::integral_constant<int, 0> ic0{};
+  const std::integral_constant<int, 1> ic1{};
+  if (!is_chain && Nc > 0) issue(Nc - 1, ic0);
+  wait_copies();
+  barrier_lds();
+
+  auto step = [&](int j, auto bic) {
+    constexpr int bi = decltype(bic)::value;
+    const int cid = cid0 + j;
+    int tok0i, L;
+    chunk_of(cm, cid, tok0i, L);
+    const ChainDmaBuf<NS>& B_ = buf[bi];
+    const Lds<E, 128> Ks{const_cast<E*>(B_.K)}, Qs{const_cast<E*>(B_.Q)};
+    const Lds<E, R> Os{const_cast<E*>(B_.O)};
+    const Lds<E, 64> Ns{const_cast<E*>(B_.N)}, Ms{const_cast<E*>(B_.M)};
+    if (is_chain) {
+      const size_t hc = (size_t)cid * Hv + h;
+      E* ddst = dSc + (hc * kD + dv0 + r) * kD;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) store4(ddst + 16 * t + 4 * g, DT[t]);
+      // P = K dS^T (rows: tokens, column: this lane's value row)
+      f32x4 P[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        f32x4 p = zero4();
+#pragma unroll
+        for (int kb = 0; kb < kD / KB; ++kb) p = mma(p, Ks.rm(16 * mt + r, KB * kb), acc_frag<E>(DT, kb));
+        P[mt] = p;
+      }
+      barrier_lds();                                   // A: M^T dO ready
+      f32x4 dD[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const f32x4 dc4 = *reinterpret_cast<const f32x4*>(&B_.dc[16 * mt + 4 * g]);
+        const f32x4 m = hand.mdo[sl][mt][l];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dD[mt][i] = m[i] + dc4[i] * P[mt][i];
+      }
+      f32x4 Z[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        f32x4 y = zero4();
+#pragma unroll
+        for (int kb = 0; kb < kC / KB; ++kb)
+          if (!blk_below<E>(mt, kb)) y = mma(y, Ns.cm(16 * mt + r, KB * kb), acc_frag<E>(dD, kb));
+        const f32x4 g4 = *reinterpret_cast<const f32x4*>(&B_.gm[16 * mt + 4 * g]);
+        const f32x4 b4 = *reinterpret_cast<const f32x4*>(&B_.bt[16 * mt + 4 * g]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tok = 16 * mt + 4 * g + i;
+          Z[mt][i] = (tok < L ? -g4[i] * b4[i] : 0.f) * y[i];
+        }
+      }
+      barrier_lds();                                   // B: (gamma Q)^T dO ready
+      const float gl = B_.gm[kC - 1];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        f32x4 a = DT[t] * gl + hand.u[sl][t][l];
+#pragma unroll
+        for (int kb = 0; kb < kC / KB; ++kb) a = mma(a, Ks.cm(16 * t + r, KB * kb), acc_frag<E>(Z, kb));
+        DT[t] = a;
+      }
+      barrier_lds();                                   // C
+    } else {
+      if (j > 0) issue(j - 1, std::integral_constant<int, 1 - bi>{});
+      // dO fragments of this slice (B operand, K = tokens), plain and
+      // gamma-scaled (masked)
+      bf16x8 OB[2], OG[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        OB[kb] = Os.cm(16 * sl + r, KB * kb);
+        const f32x4 g0 = *reinterpret_cast<const f32x4*>(&B_.gm[KB * kb + 4 * g]);
+        const f32x4 g1 = *reinterpret_cast<const f32x4*>(&B_.gm[KB * kb + 16 + 4 * g]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int tok = KB * kb + kslot<E>(g, e);
+          const float gv = e < 4 ? g0[e] : g1[e - 4];
+          OG[kb][e] = (bf16)((tok < L ? gv : 0.f) * (float)OB[kb][e]);
+        }
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        f32x4 m = zero4();
+#pragma unroll
+        for (int kb = 0; kb < kC / KB; ++kb)
+          if (!blk_below<E>(mt, kb)) m = mma(m, Ms.cm(16 * mt + r, KB * kb), OB[kb]);
+        hand.mdo[sl][mt][l] = m;
+      }
+      barrier_lds();                                   // A
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        f32x4 u = zero4();
+#pragma unroll
+        for (int kb = 0; kb < kC / KB; ++kb) u = mma(u, Qs.cm(16 * t + r, KB * kb), OG[kb]);
+        hand.u[sl][t][l] = u;
+      }
+      barrier_lds();                                   // B
+      wait_copies();
+      barrier_lds();                                   // C
+    }
+  };
+  int j = Nc - 1;
+  for (; j >= 1; j -= 2) {
+    step(j, ic0);
+    step(j - 1, ic1);
+  }
+  if (j == 0) step(0, ic0);
+  if (is_chain && dh0) {
+    float* dst = dh0 + (((size_t)b * Hv + h) * kD + dv0 + r) * kD;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) *reinterpret_cast<f32x4*>(dst + 16 * t + 4 * g) = DT[t];
+  }
+}
+
 // ------------------------------------------------------------ per-chunk gradients
 // One workgroup of 8 waves per (chunk, query/key head).  Per value head of the
 // group:
@@ -938,9 +1114,8 @@ hipError_t launch_backward(const BackwardLaunch& a, hipStream_t st) {
     typedef bf16 E;
     // the chunk states were written by the forward scan (gdn_api.hip)
     if (!a.states_ready) return hipErrorInvalidValue;
-    constexpr int NWB = 2;
-    hipLaunchKernelGGL((bwd_chain_bf16_kernel<NWB>), dim3(kD / (16 * NWB), a.Hv, a.nseq),
-                       dim3(64 * NWB), 0, st, (const E*)a.q, (const E*)a.k, (const E*)a.dout,
+    hipLaunchKernelGGL(bwd_chain_split_kernel, dim3(kD / 32, a.Hv, a.nseq), dim3(256), 0, st,
+                       (const E*)a.q, (const E*)a.k, (const E*)a.dout,
                        a.beta, a.dht, a.dh0, (const E*)a.N, (const E*)a.M, a.gam, a.dec,
                        (E*)a.dS, a.cm, a.Hqk, a.Hv);
     hipError_t e = hipGetLastError();
