@@ -255,6 +255,12 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
 __device__ __forceinline__ void dma4(const void* src, void* lds_dst) {
   __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_dst, 4, 0, 0);
 }
+// ds_read_b64_tr_b16: 4 x 16-bit elements, transposed across each group of 16
+// lanes (input lane p reads 8 bytes at its address; output lane m receives
+// element m % 4 of input lanes m / 4, m / 4 + 4, m / 4 + 8, m / 4 + 12).
+__device__ __forceinline__ s16x4 lds_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+}
 __device__ __forceinline__ void barrier_lds() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }

@@ -42,6 +42,7 @@
 //    registers one chunk ahead.
 #include "gdn_chunks.hpp"
 #include "gdn_device.hpp"
+#include "gdn_frag.hpp"
 #include "gdn_launch.hpp"
 
 #include <type_traits>
@@ -61,8 +62,8 @@ struct Work {
 
 // Gates are kept in base 2 so that the hardware v_exp_f32 / v_log_f32 apply
 // directly: G2_t = sum_{j<=t} log2(alpha_j), exp(G_i - G_j) = 2^(G2_i - G2_j).
-__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
+using frag::hw_exp2;
+using frag::hw_log2;
 
 // 16 consecutive bytes of a row of q/k/v (8 bf16 or 4 fp32), zero if masked.
 template <typename E>
@@ -665,8 +666,11 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
 //    Tt X, the state update; it hands S^T (as the B fragments it built for P)
 //    and Dl to the output wave through LDS.  40 MFMAs per chunk.
 //  * one output wave for both slices, one chunk behind: O = diag(gam) Q S^T +
-//    M Dl.  Each Q and M fragment read from LDS serves both slices: 44 MFMAs
-//    per chunk.
+//    M Dl, formed transposed (O^T = S Q^T diag(gam) + Dl^T M^T: the chain's
+//    fragments are the A operands, Q and M rows the B operands), so that each
+//    lane holds four consecutive value rows of one token and stores them to
+//    global memory as one 8-byte write.  Each Q and M fragment read from LDS
+//    serves both slices: 44 MFMAs per chunk.
 //  * two producer waves: copy K, Tt, V, gam, dec of chunk c+2 and Q, M of
 //    chunk c from global memory straight into LDS rings
 //    (global_load_lds_dwordx4: no registers, no VALU) while chunk c is
@@ -746,23 +750,11 @@ __device__ __forceinline__ int ksw(int row) { return ((row & 3) << 2) | ((row >>
 // 8 apart per lane group, so the piece order is rotated by (token / 8) % 4.
 __device__ __forceinline__ int vswz(int tok) { return (tok >> 3) & 3; }
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-__device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_dst, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const void* src, void* lds_dst) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_dst, 4, 0, 0);
-}
-__device__ __forceinline__ s16x4 lds_tr16(const void* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-}
-
-__device__ __forceinline__ void barrier_lds() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
+using frag::barrier_lds;
+using frag::dma16;
+using frag::dma4;
+using frag::lds_tr16;
+using frag::s16x4;
 
 // Copies of a [rows][bytes_per_row] tile of 16-byte pieces with XOR swizzle:
 // instruction `it` fills LDS bytes [1024 it, 1024 it + 1024).
@@ -1058,51 +1050,37 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) DB[s][kk] = sm.hand[c & 1][s].db[kk][l];
       }
-      f32x4 O[kSlices][4];
+      bf16* ob = o + (size_t)tok0 * hv_stride + (size_t)h * kD + dvb + 4 * g;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const int row = 16 * mt + r;
+      for (int nt = 0; nt < 4; ++nt) {
+        const int row = 16 * nt + r;
+        f32x4 OT[kSlices];
 #pragma unroll
-        for (int s = 0; s < kSlices; ++s) O[s][mt] = zero4();
+        for (int s = 0; s < kSlices; ++s) OT[s] = zero4();
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(Qs.Q + row * 256 + 16 * ((4 * kk + g) ^ swz(row)));
+          const bf16x8 bq = *reinterpret_cast<const bf16x8*>(Qs.Q + row * 256 + 16 * ((4 * kk + g) ^ swz(row)));
 #pragma unroll
-          for (int s = 0; s < kSlices; ++s) O[s][mt] = mfma_bf16(a, SB[s][kk], O[s][mt]);
+          for (int s = 0; s < kSlices; ++s) OT[s] = mfma_bf16(SB[s][kk], bq, OT[s]);
         }
-        const f32x4 gm = *reinterpret_cast<const f32x4*>(Gd.gam + 16 * mt + 4 * g);
+        const float gm = Gd.gam[row];
 #pragma unroll
-        for (int s = 0; s < kSlices; ++s)
-#pragma unroll
-          for (int i2 = 0; i2 < 4; ++i2) O[s][mt][i2] *= gm[i2];
+        for (int s = 0; s < kSlices; ++s) OT[s] *= gm;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          if (kk == 1 && mt < 2) continue;
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(Qs.M + row * 128 + 16 * ((4 * kk + g) ^ swz(row)));
+          if (kk == 1 && nt < 2) continue;
+          const bf16x8 bm = *reinterpret_cast<const bf16x8*>(Qs.M + row * 128 + 16 * ((4 * kk + g) ^ swz(row)));
 #pragma unroll
-          for (int s = 0; s < kSlices; ++s) O[s][mt] = mfma_bf16(a, DB[s][kk], O[s][mt]);
+          for (int s = 0; s < kSlices; ++s) OT[s] = mfma_bf16(DB[s][kk], bm, OT[s]);
         }
-      }
-      wave_lds_fence();
+        if (row < L) {
 #pragma unroll
-      for (int s = 0; s < kSlices; ++s) {
-        bf16* st = reinterpret_cast<bf16*>(&sm.hand[c & 1][s]);
+          for (int s = 0; s < kSlices; ++s) {
+            bf16x4 ov;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int i2 = 0; i2 < 4; ++i2) st[(16 * mt + 4 * g + i2) * 16 + r] = (bf16)O[s][mt][i2];
-      }
-      wave_lds_fence();
-#pragma unroll
-      for (int s = 0; s < kSlices; ++s) {
-        const bf16* st = reinterpret_cast<const bf16*>(&sm.hand[c & 1][s]);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int pc = l + 64 * j, t = pc >> 1, half = pc & 1;
-          const uint4 val = *reinterpret_cast<const uint4*>(st + t * 16 + 8 * half);
-          if (t < L)
-            *reinterpret_cast<uint4*>(o + (size_t)(tok0 + t) * hv_stride + (size_t)h * kD + dvb +
-                                      16 * s + 8 * half) = val;
+            for (int e = 0; e < 4; ++e) ov[e] = (bf16)OT[s][e];
+            *reinterpret_cast<bf16x4*>(ob + (size_t)row * hv_stride + 16 * s) = ov;
+          }
         }
       }
     }
