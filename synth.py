@@ -24,6 +24,14 @@ in float32, in this order):
 6. h0 ~ N(0, std^2) fp32 when a non-zero initial state is asked for;
 7. gate logits ~ N(0, 1) in the working dtype (varlen with gate).
 
+Strong decay (``strong_decay=True``; prefill, varlen, backward and decode draws), after
+every draw above from the same generator: alpha is redrawn as
+exp(-softplus(x)) = sigmoid(-x), x ~ N(0, 1), so that alpha spans about
+[0.02, 0.98] with median 1/2 (the "input-dependent state decay" of the
+recurrence, pushed to its strong end); then u ~ U[0, 1) per (token, head) sets
+beta = 0 where u < 1/8 and beta = 1 where u >= 7/8 (the two ends of the
+write strength).
+
 Decode: the carried state is drawn from ``seed``; the per-step tensors of
 step s come from seed + 7919 * (s + 1).
 
@@ -82,23 +90,35 @@ def _draw(gen, lead, Hqk, Hv, Dh, dtype, h0_shape, h0_std, with_gate):
     return dict(q=q, k=k, v=v, alpha=alpha, beta=beta, h0=h0, gate=gate)
 
 
+def _strong(gen, d):
+    shape = d["alpha"].shape
+    d["alpha"] = torch.sigmoid(-_normal(gen, shape).double()).float().contiguous()
+    u = torch.rand(shape, generator=gen, dtype=torch.float32)
+    beta = d["beta"].clone()
+    beta[u < 0.125] = 0.0
+    beta[u >= 0.875] = 1.0
+    d["beta"] = beta.contiguous()
+    return d
+
+
 def prefill_inputs(B, T, dtype=torch.bfloat16, seed=0, h0_std=0.0,
-                   Hqk=H_QK, Hv=H_V, Dh=D):
+                   Hqk=H_QK, Hv=H_V, Dh=D, strong_decay=False):
     """q, k ``[B,T,Hqk,Dh]``, v ``[B,T,Hv,Dh]`` (dtype); alpha, beta
     ``[B,T,Hv]`` fp32; h0 ``[B,Hv,Dh,Dh]`` fp32 or None."""
     gen = torch.Generator().manual_seed(seed)
-    return _draw(gen, (B, T), Hqk, Hv, Dh, dtype, (B, Hv, Dh, Dh), h0_std, False)
+    d = _draw(gen, (B, T), Hqk, Hv, Dh, dtype, (B, Hv, Dh, Dh), h0_std, False)
+    return _strong(gen, d) if strong_decay else d
 
 
 def backward_inputs(B, T, dtype=torch.bfloat16, seed=0, h0_std=0.0, dht_std=0.0,
-                    Hqk=H_QK, Hv=H_V, Dh=D):
+                    Hqk=H_QK, Hv=H_V, Dh=D, strong_decay=False):
     """:func:`prefill_inputs` plus ``do [B,T,Hv,Dh]`` (dtype) and ``dht
     [B,Hv,Dh,Dh]`` fp32 or None."""
     gen = torch.Generator().manual_seed(seed)
     d = _draw(gen, (B, T), Hqk, Hv, Dh, dtype, (B, Hv, Dh, Dh), h0_std, False)
     d["do"] = _normal(gen, (B, T, Hv, Dh)).to(dtype).contiguous()
     d["dht"] = (_normal(gen, (B, Hv, Dh, Dh)) * dht_std).contiguous() if dht_std else None
-    return d
+    return _strong(gen, d) if strong_decay else d
 
 
 def attention_inputs(B, T, dtype=torch.bfloat16, seed=0, Hq=24, Hkv=4, Dh=256):
@@ -134,7 +154,8 @@ def varlen_lengths(N, lo, hi, seed):
 
 
 def varlen_inputs(lengths=None, N=8, lo=1024, hi=32768, dtype=torch.bfloat16,
-                  seed=0, h0_std=0.02, gate=True, Hqk=H_QK, Hv=H_V, Dh=D):
+                  seed=0, h0_std=0.02, gate=True, Hqk=H_QK, Hv=H_V, Dh=D,
+                  strong_decay=False):
     """Packed sequences.  Lengths are drawn first from the same generator
     unless given.  Returns q, k ``[T_tot,Hqk,Dh]``, v, gate ``[T_tot,Hv,Dh]``,
     alpha, beta ``[T_tot,Hv]``, h0 ``[N,Hv,Dh,Dh]``, cu_seqlens int32
@@ -146,6 +167,8 @@ def varlen_inputs(lengths=None, N=8, lo=1024, hi=32768, dtype=torch.bfloat16,
     N = len(lengths)
     T_tot = sum(lengths)
     out = _draw(gen, (T_tot,), Hqk, Hv, Dh, dtype, (N, Hv, Dh, Dh), h0_std, gate)
+    if strong_decay:
+        out = _strong(gen, out)
     cu = torch.zeros(N + 1, dtype=torch.int32)
     if N:
         cu[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0).to(torch.int32)
@@ -159,14 +182,14 @@ def decode_state(B, seed, std=0.02, Hv=H_V, Dh=D):
 
 
 def decode_step_inputs(B, step, dtype=torch.bfloat16, seed=0, Hqk=H_QK,
-                       Hv=H_V, Dh=D):
+                       Hv=H_V, Dh=D, strong_decay=False):
     """Per-step tensors of decode step ``step``: q, k ``[B,Hqk,Dh]``,
     v ``[B,Hv,Dh]``, alpha, beta ``[B,Hv]``."""
     gen = torch.Generator().manual_seed(seed + 7919 * (step + 1))
     d = _draw(gen, (B,), Hqk, Hv, Dh, dtype, None, 0.0, False)
     d.pop("h0")
     d.pop("gate")
-    return d
+    return _strong(gen, d) if strong_decay else d
 
 
 def config_inputs(cfg_id):

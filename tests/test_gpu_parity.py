@@ -45,6 +45,19 @@ def rel(x, ref):
     return float(np.linalg.norm(x - ref) / (den if den > 0 else 1.0))
 
 
+def worst_head(x, ref, axis):
+    """Largest relative L2 error over the value heads (entries of ``axis``):
+    one head far off cannot hide in the norm of all of them."""
+    x = x.detach().cpu().double().numpy() if isinstance(x, torch.Tensor) else np.asarray(x)
+    x, ref = np.moveaxis(x, axis, 0), np.moveaxis(np.asarray(ref, np.float64), axis, 0)
+    return max(rel(a, b) for a, b in zip(x, ref))
+
+
+# one value head of every query/key group (16 groups of 3), at every position
+# inside a group
+SAMPLED_HEADS = [3 * g + g % 3 for g in range(16)]
+
+
 def to_dev(d):
     return {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
 
@@ -71,13 +84,16 @@ def test_prefill_small(gdn, dtype, B, T, h0std):
     inp = synth.prefill_inputs(B, T, dtype, seed=7 + T + B, h0_std=h0std)
     o, ht = run_prefill(gdn, inp)
     o_ref, ht_ref = oracle_prefill(inp)
-    eo, eh = rel(o, o_ref), rel(ht, ht_ref)
-    say("  rel o %.3e ht %.3e" % (eo, eh))
+    eo, eh = worst_head(o, o_ref, 2), worst_head(ht, ht_ref, 1)
+    say("  worst head rel o %.3e ht %.3e" % (eo, eh))
     assert eo <= TOL[dtype] and eh <= TOL[dtype]
-    # element-wise: no single output far off (guards against a masked-row bug
-    # hiding in the norm)
-    err = np.abs(o.cpu().double().numpy() - o_ref).max() / np.abs(o_ref).max()
-    assert err <= 20 * TOL[dtype]
+    # element-wise, per head: no single output far off (guards against a
+    # masked-row bug hiding in the norm)
+    on = o.cpu().double().numpy()
+    err = max(np.abs(on[:, :, h] - o_ref[:, :, h]).max() / np.abs(o_ref[:, :, h]).max()
+              for h in range(on.shape[2]))
+    say("  worst head max element error / max |o| %.3e" % err)
+    assert err <= 5 * TOL[dtype]
 
 
 def test_prefill_T0_passes_state(gdn):
@@ -416,8 +432,9 @@ def test_config0_T256_fp32(gdn):
     inp = synth.config_inputs(0)
     o, ht = run_prefill(gdn, inp, h0=False)
     o_ref, ht_ref = oracle_prefill(inp, h0=False)
-    eo, eh = rel(o, o_ref), rel(ht, ht_ref)
-    say("config0 rel o %.3e ht %.3e" % (eo, eh))
+    eo, eh = worst_head(o, o_ref, 2), worst_head(ht, ht_ref, 1)
+    say("config0 worst head rel o %.3e ht %.3e (all heads %.3e %.3e)"
+        % (eo, eh, rel(o, o_ref), rel(ht, ht_ref)))
     assert eo <= 1e-5 and eh <= 1e-5 and c["dtype"] == torch.float32
 
 
@@ -426,8 +443,9 @@ def test_config1_T8192_bf16(gdn):
     t0 = time.time()
     o, ht = run_prefill(gdn, inp, h0=False)
     o_ref, ht_ref = oracle_prefill(inp, h0=False)
-    eo, eh = rel(o, o_ref), rel(ht, ht_ref)
-    say("config1 rel o %.3e ht %.3e (%.1fs)" % (eo, eh, time.time() - t0))
+    eo, eh = worst_head(o, o_ref, 2), worst_head(ht, ht_ref, 1)
+    say("config1 worst head rel o %.3e ht %.3e (all heads %.3e %.3e, %.1fs)"
+        % (eo, eh, rel(o, o_ref), rel(ht, ht_ref), time.time() - t0))
     assert eo <= 2e-2 and eh <= 2e-2
 
 
@@ -458,7 +476,7 @@ def test_config3_T262144_sampled_heads(gdn):
     inp = synth.config_inputs(3)
     say("config3 inputs ready")
     o, ht = run_prefill(gdn, inp)
-    heads = [0, 25, 47]
+    heads = SAMPLED_HEADS
     sub = oracle.subset_heads(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"],
                               inp["h0"], heads, 16, 48)
     t0 = time.time()
@@ -479,7 +497,7 @@ def test_config4_varlen_sampled_heads(gdn):
     y, ht = gdn.prefill_varlen(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["cu_seqlens"],
                                d["h0"], gate=d["gate"], norm_eps=1e-6)
     torch.cuda.synchronize()
-    heads = [4, 31]
+    heads = SAMPLED_HEADS
     q_s, k_s, v_s, a_s, b_s, h_s = oracle.subset_heads(inp["q"], inp["k"], inp["v"],
                                                        inp["alpha"], inp["beta"], inp["h0"],
                                                        heads, 16, 48)

@@ -526,6 +526,21 @@ def test_synth_inputs_deterministic_and_normalised():
     assert scipy.stats.kstest(z.ravel(), "norm").pvalue > 1e-4
 
 
+def test_synth_strong_decay_reaches_the_ends():
+    import torch
+    import synth
+    inp = synth.prefill_inputs(2, 200, torch.float32, seed=501, strong_decay=True)
+    base = synth.prefill_inputs(2, 200, torch.float32, seed=501)
+    a, b = inp["alpha"], inp["beta"]
+    assert a.min() < 0.05 and a.max() > 0.9 and (a > 0).all() and (a < 1).all()
+    assert (b == 0).any() and (b == 1).any()
+    frac0, frac1 = (b == 0).double().mean().item(), (b == 1).double().mean().item()
+    assert 0.08 < frac0 < 0.17 and 0.08 < frac1 < 0.17
+    # q, k, v are the plain recipe's draws; only alpha and beta change
+    for key in ("q", "k", "v"):
+        assert torch.equal(inp[key], base[key])
+
+
 # ------------------------------------------------------------- backward pins
 # The oracle's backward (oracle.prefill_backward) is the chain rule applied by
 # hand to the sequential recurrence.  It is pinned by (1) central finite
@@ -630,3 +645,63 @@ def test_chunked_backward_equals_sequential(oracle_mod, C):
     chk = chunked_form.chunked_backward(q, k, v, a, b, do, s0, dht, C=C)
     for x, y in zip(seq, chk):
         assert np.linalg.norm(x - y) <= 1e-12 * np.linalg.norm(x)
+
+
+# ------------------------------------------------------------- head sampling
+# oracle.subset_heads gathers single value heads (with the query/key head each
+# one reads) so that very long sequences can be checked a few heads at a time.
+# Pinned against the full multi-head oracle: the sampled heads' outputs and
+# final states must be the very same numbers, bit for bit (each head's chain
+# is computed independently, in the same order, either way).
+
+def _subset_case(seed, Hqk, Hv, T=9, D=8):
+    r = rng(seed)
+    return rand_inputs(r, 2, T, Hqk, Hv, D)
+
+
+@pytest.mark.parametrize("with_h0", [True, False])
+def test_subset_heads_equals_full_prefill(oracle_mod, with_h0):
+    Hqk, Hv = 4, 12
+    q, k, v, alpha, beta, s0 = _subset_case(41, Hqk, Hv)
+    if not with_h0:
+        s0 = None
+    o, ht = oracle.prefill(q, k, v, alpha, beta, s0)
+    heads = [11, 0, 5, 6, 7, 3]                 # unordered, several per group
+    o_s, ht_s = oracle.prefill(*oracle.subset_heads(q, k, v, alpha, beta, s0, heads, Hqk, Hv))
+    assert o_s.shape == (2, 9, len(heads), 8) and ht_s.shape == (2, len(heads), 8, 8)
+    assert np.array_equal(o_s, o[:, :, heads])
+    assert np.array_equal(ht_s, ht[:, heads])
+
+
+def test_subset_heads_torch_inputs(oracle_mod):
+    """The torch path (gather before widening) gives the numpy path's arrays."""
+    import torch
+    Hqk, Hv = 2, 6
+    q, k, v, alpha, beta, s0 = _subset_case(42, Hqk, Hv)
+    bf = lambda x: torch.from_numpy(x).to(torch.bfloat16)
+    f32 = lambda x: torch.from_numpy(x).float()
+    tq, tk, tv = bf(q), bf(k), bf(v)
+    ta, tb, th = f32(alpha), f32(beta), f32(s0)
+    heads = [5, 1, 2]
+    got = oracle.subset_heads(tq, tk, tv, ta, tb, th, heads, Hqk, Hv)
+    want = oracle.subset_heads(tq.double().numpy(), tk.double().numpy(), tv.double().numpy(),
+                               ta.double().numpy(), tb.double().numpy(), th.double().numpy(),
+                               heads, Hqk, Hv)
+    for a, b in zip(got, want):
+        assert a.dtype == np.float64 and np.array_equal(a, b)
+    # query/key head of value head h is h // (Hv / Hqk): 5 -> 1, 1 -> 0, 2 -> 0
+    assert np.array_equal(got[0][:, :, 0], tq[:, :, 1].double().numpy())
+    assert np.array_equal(got[0][:, :, 1], tq[:, :, 0].double().numpy())
+
+
+def test_subset_heads_wrong_group_map_is_caught(oracle_mod):
+    """A gather that takes the query/key head as h % Hqk (a plausible slip)
+    fails the equality above."""
+    Hqk, Hv = 4, 12
+    q, k, v, alpha, beta, s0 = _subset_case(43, Hqk, Hv)
+    o, _ = oracle.prefill(q, k, v, alpha, beta, s0)
+    heads = np.array([1, 8])                    # groups 0 and 2; h % Hqk gives 1 and 0
+    bad = (q[:, :, heads % Hqk], k[:, :, heads % Hqk], v[:, :, heads],
+           alpha[:, :, heads], beta[:, :, heads], s0[:, heads])
+    o_b, _ = oracle.prefill(*bad)
+    assert not np.array_equal(o_b, o[:, :, heads])
