@@ -33,8 +33,9 @@
 //  3. bwd_chain: dL/dS carried from the last chunk to the first, storing the
 //     gradient of the state leaving every chunk; dh0 at the end.  Value rows
 //     never interact in either chain, so rows split across waves and
-//     workgroups as in the forward scan.  bf16: bwd_chain_bf16_kernel, its
-//     operands double-buffered in LDS by direct copies.
+//     workgroups as in the forward scan.  bf16: bwd_chain_split_kernel, chain
+//     and helper waves per pair of value slices, its operands double-buffered
+//     in LDS by direct copies.
 //  4. bwd_grad: one workgroup per (chunk, query/key head), fully parallel.  It
 //     walks the value heads of its group and accumulates dq and dk for the
 //     group in registers, so no atomics and no reduction pass are needed.
@@ -258,9 +259,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_chain_kernel(
   }
 }
 
-// bf16 reverse chain with operands copied straight into LDS
-// (global_load_lds_dwordx4: no registers, no VALU), double-buffered: the copies
-// of chunk j-1 are in flight while chunk j is computed.  Copy instruction `it`
+// Operand buffer of the bf16 reverse chain (bwd_chain_split_kernel below),
+// filled by copies straight into LDS (global_load_lds_dwordx4: no registers,
+// no VALU) and double-buffered: the copies of chunk j-1 are in flight while
+// chunk j is computed.  Copy instruction `it`
 // of a tile fills LDS bytes [1024 it, 1024 it + 1024); lane l's 16 bytes are
 // the piece of the swizzled layout at that position, so each lane reads the
 // global piece the swizzle puts there.  Rows beyond the chunk's length repeat
@@ -277,140 +279,6 @@ struct ChainDmaBuf {
   bf16 M[kC * kC];
   float gm[kC], dc[kC], bt[kC];
 };
-
-template <int NW>
-__global__ __launch_bounds__(64 * NW) void bwd_chain_bf16_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ dout,
-    const float* __restrict__ beta, const float* __restrict__ dht, float* __restrict__ dh0,
-    const bf16* __restrict__ Nw, const bf16* __restrict__ Mw, const float* __restrict__ gam,
-    const float* __restrict__ dec, bf16* __restrict__ dSc, ChunkMap cm, int Hqk, int Hv) {
-  typedef bf16 E;
-  constexpr int R = 16 * NW, KB = 32;
-  __shared__ ChainDmaBuf<NW> buf[2];
-  const int w = __builtin_amdgcn_readfirstlane(wave_id()), l = lane_id(), r = l & 15, g = l >> 4;
-  const int h = blockIdx.y, b = blockIdx.z, gq = h / (Hv / Hqk);   // b: sequence
-  int cid0, Nc;
-  seq_chunks(cm, b, cid0, Nc);
-  const int rbase = R * blockIdx.x, dv0 = rbase + 16 * w;
-
-  // The two buffers alternate with the iteration parity, which is a
-  // compile-time constant in the two-step unrolled loop below: both buffers
-  // then share one set of per-lane LDS offsets (the second one is an
-  // immediate offset away).
-  auto issue = [&](int j, auto bic) {
-    ChainDmaBuf<NW>& B_ = buf[decltype(bic)::value];
-    const int cid = cid0 + j;
-    int tok0i, L;
-    chunk_of(cm, cid, tok0i, L);
-    const size_t tok0 = (size_t)tok0i;
-    const size_t hc = (size_t)cid * Hv + h;
-    copy_rows<128>(k + (tok0 * Hqk + gq) * kD, (int64_t)Hqk * kD, L, B_.K, w, NW);
-    copy_rows<128>(q + (tok0 * Hqk + gq) * kD, (int64_t)Hqk * kD, L, B_.Q, w, NW);
-    copy_rows<R>(dout + (tok0 * Hv + h) * kD + rbase, (int64_t)Hv * kD, L, B_.O, w, NW);
-    copy_rows<64>(Nw + hc * kC * kC, kC, kC, B_.N, w, NW);
-    copy_rows<64>(Mw + hc * kC * kC, kC, kC, B_.M, w, NW);
-    if (w == 0) dma4(gam + hc * kC + l, B_.gm);
-    if (w == NW - 1) dma4(dec + hc * kC + l, B_.dc);
-    if (w == (NW > 2 ? 1 : 0)) dma4(beta + (tok0 + min(l, L - 1)) * Hv + h, B_.bt);
-  };
-
-  f32x4 DT[8];
-#pragma unroll
-  for (int t = 0; t < 8; ++t)
-    DT[t] = dht ? *reinterpret_cast<const f32x4*>(
-                      dht + (((size_t)b * Hv + h) * kD + dv0 + r) * kD + 16 * t + 4 * g)
-                : zero4();
-  const std::integral_constant<int, 0> ic0{};
-  const std::integral_constant<int, 1> ic1{};
-  if (Nc > 0) issue(Nc - 1, ic0);
-  wait_copies();
-  barrier_lds();
-
-  auto step = [&](int j, auto bic) {
-    constexpr int bi = decltype(bic)::value;
-    const int cid = cid0 + j;
-    int tok0i, L;
-    chunk_of(cm, cid, tok0i, L);
-    const size_t hc = (size_t)cid * Hv + h;
-    E* ddst = dSc + (hc * kD + dv0 + r) * kD;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) store4(ddst + 16 * t + 4 * g, DT[t]);
-    if (j > 0) issue(j - 1, std::integral_constant<int, 1 - bi>{});
-
-    const ChainDmaBuf<NW>& B_ = buf[bi];
-    const Lds<E, 128> Ks{const_cast<E*>(B_.K)}, Qs{const_cast<E*>(B_.Q)};
-    const Lds<E, R> Os{const_cast<E*>(B_.O)};
-    const Lds<E, 64> Ns{const_cast<E*>(B_.N)}, Ms{const_cast<E*>(B_.M)};
-
-    // dO fragments (B operand, K = tokens), plain and gamma-scaled (masked)
-    // (loads unconditional, masks as selects: no branches in the chain)
-    bf16x8 OB[2], OG[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      OB[kb] = Os.cm(16 * w + r, KB * kb);
-      const f32x4 g0 = *reinterpret_cast<const f32x4*>(&B_.gm[KB * kb + 4 * g]);
-      const f32x4 g1 = *reinterpret_cast<const f32x4*>(&B_.gm[KB * kb + 16 + 4 * g]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int tok = KB * kb + kslot<E>(g, e);
-        const float gv = e < 4 ? g0[e] : g1[e - 4];
-        OG[kb][e] = (bf16)((tok < L ? gv : 0.f) * (float)OB[kb][e]);
-      }
-    }
-    f32x4 dD[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const f32x4 dc4 = *reinterpret_cast<const f32x4*>(&B_.dc[16 * mt + 4 * g]);
-      f32x4 p = zero4(), m = zero4();
-#pragma unroll
-      for (int kb = 0; kb < kD / KB; ++kb) p = mma(p, Ks.rm(16 * mt + r, KB * kb), acc_frag<E>(DT, kb));
-#pragma unroll
-      for (int kb = 0; kb < kC / KB; ++kb)
-        if (!blk_below<E>(mt, kb)) m = mma(m, Ms.cm(16 * mt + r, KB * kb), OB[kb]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dD[mt][i] = m[i] + dc4[i] * p[i];
-    }
-    f32x4 Z[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      f32x4 y = zero4();
-#pragma unroll
-      for (int kb = 0; kb < kC / KB; ++kb)
-        if (!blk_below<E>(mt, kb)) y = mma(y, Ns.cm(16 * mt + r, KB * kb), acc_frag<E>(dD, kb));
-      const f32x4 g4 = *reinterpret_cast<const f32x4*>(&B_.gm[16 * mt + 4 * g]);
-      const f32x4 b4 = *reinterpret_cast<const f32x4*>(&B_.bt[16 * mt + 4 * g]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = 16 * mt + 4 * g + i;
-        Z[mt][i] = (tok < L ? -g4[i] * b4[i] : 0.f) * y[i];
-      }
-    }
-    const float gl = B_.gm[kC - 1];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      f32x4 a = DT[t] * gl;
-#pragma unroll
-      for (int kb = 0; kb < kC / KB; ++kb) {
-        a = mma(a, Qs.cm(16 * t + r, KB * kb), OG[kb]);
-        a = mma(a, Ks.cm(16 * t + r, KB * kb), acc_frag<E>(Z, kb));
-      }
-      DT[t] = a;
-    }
-    wait_copies();
-    barrier_lds();
-  };
-  int j = Nc - 1;
-  for (; j >= 1; j -= 2) {
-    step(j, ic0);
-    step(j - 1, ic1);
-  }
-  if (j == 0) step(0, ic0);
-  if (dh0) {
-    float* dst = dh0 + (((size_t)b * Hv + h) * kD + dv0 + r) * kD;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) *reinterpret_cast<f32x4*>(dst + 16 * t + 4 * g) = DT[t];
-  }
-}
 
 // bf16 reverse chain with a role split, as the forward scan has: per
 // workgroup two 16-row value slices; waves 0-1 are chain waves (slice s = w),
@@ -643,7 +511,7 @@ struct GradSmem {
   float rowp[4][kC], colp[4][kC], rowb[4][kC];
   float pa[kGW][kC];
   float fin[3][kC];                         // gate, beta, w
-  float G2[kC], gm[kC], dc[kC], bt[kC], al[kC];
+  float G2[kC], G2lo[kC], gm[kC], dc[kC], bt[kC], al[kC];   // G2 + G2lo: compensated prefix
 };
 
 template <typename E>
@@ -758,11 +626,13 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
     }
     if (w == 0) {
       const float a = l < L ? alpha[(tok0 + l) * Hv + h] : 1.f;
-      const float G2 = wave_inclusive_sum(hw_log2(a));
-      const float Glast = __shfl(G2, kC - 1, 64);
+      float G2lo;
+      const float G2 = wave_inclusive_sum2(hw_log2(a), G2lo);
+      const float Glast = __shfl(G2, kC - 1, 64), Glastlo = __shfl(G2lo, kC - 1, 64);
       sm.G2[l] = G2;
+      sm.G2lo[l] = G2lo;
       sm.gm[l] = hw_exp2(G2);
-      sm.dc[l] = hw_exp2(Glast - G2);
+      sm.dc[l] = hw_exp2((Glast - G2) + (Glastlo - G2lo));
       sm.bt[l] = l < L ? beta[(tok0 + l) * Hv + h] : 0.f;
       sm.al[l] = a;
     }
@@ -913,7 +783,8 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int ii = 16 * ti[x] + 4 * g + i;
-        const float gam_ = jj <= ii ? hw_exp2(sm.G2[ii] - sm.G2[jj]) : 0.f;
+        const float gam_ =
+            jj <= ii ? hw_exp2((sm.G2[ii] - sm.G2[jj]) + (sm.G2lo[ii] - sm.G2lo[jj])) : 0.f;
         const float dMG = jj <= ii ? OD[x][i] * gam_ : 0.f;
         const float dAG = jj < ii ? -YD[x][i] * gam_ : 0.f;
         const float wa = sm.bt[ii] * dAG;

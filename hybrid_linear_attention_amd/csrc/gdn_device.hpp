@@ -80,16 +80,6 @@ __device__ __forceinline__ bf16x8 pack_b(const f32x4& lo, const f32x4& hi) {
   return r;
 }
 
-// A fragment (bf16) from a row-major LDS matrix, K order as above:
-// row `row`, K block starting at column k0 (multiple of 32).
-__device__ __forceinline__ bf16x8 lds_a_bf16(const bf16* A, int lda, int row, int k0) {
-  const int g = lane_id() >> 4;
-  const bf16* p = A + row * lda + k0 + 4 * g;
-  bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
-  bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 16);
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
 // Plain A/B fragment (bf16, hardware-natural K order k = 8g + j) of a
 // row-major LDS matrix whose rows are indexed by the fragment's M (for A) or
 // N (for B): used when both operands come from LDS (Gram matrices).
@@ -99,17 +89,8 @@ __device__ __forceinline__ bf16x8 lds_row8_bf16(const bf16* A, int lda, int row,
 }
 
 // acc(16 x 16) += A[row0 .. row0+15][k-range] * B, where B's K rows come as
-// accumulator tiles bt[0 .. nkb-1] (16 K rows each) and A is row-major in LDS
-// with the K range starting at column kcol0.  fp32 and bf16 versions.
-template <int NKB>
-__device__ __forceinline__ void mma_acc_bf16(f32x4& acc, const bf16* A, int lda,
-                                             int row0, int kcol0, const bf16x8* b) {
-  const int r = lane_id() & 15;
-#pragma unroll
-  for (int kk = 0; kk < NKB / 2; ++kk)
-    acc = mfma_bf16(lds_a_bf16(A, lda, row0 + r, kcol0 + 32 * kk), b[kk], acc);
-}
-
+// accumulator tiles bt[0 .. nkb-1] (16 K rows each) and A is row-major fp32
+// in LDS with the K range starting at column kcol0.
 template <int NKB>
 __device__ __forceinline__ void mma_acc_f32(f32x4& acc, const float* A, int lda,
                                             int row0, int kcol0, const f32x4* bt) {
@@ -145,6 +126,33 @@ __device__ __forceinline__ float wave_inclusive_sum(float x) {
     if (l >= off) x += y;
   }
   return x;
+}
+
+// Wave-wide inclusive prefix sum carried as an unevaluated pair hi + lo
+// (hi = the float nearest the sum, lo = its rounding error, kept by the
+// error-free transformation TwoSum at every step).  A difference of two
+// prefixes, (hi_i - hi_j) + (lo_i - lo_j), then keeps relative accuracy even
+// when both prefixes are large and nearly equal: the strong-decay case of the
+// gate prefix, whose differences are exponents.
+__device__ __forceinline__ float two_sum_err(float a, float b, float s) {
+  const float bb = s - a;
+  return (a - (s - bb)) + (b - bb);
+}
+__device__ __forceinline__ float wave_inclusive_sum2(float x, float& lo) {
+  const int l = lane_id();
+  float hi = x;
+  lo = 0.f;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float yh = __shfl_up(hi, off, 64), yl = __shfl_up(lo, off, 64);
+    if (l >= off) {
+      const float s = hi + yh;
+      const float e = two_sum_err(hi, yh, s) + (lo + yl);
+      hi = s + e;
+      lo = e - (hi - s);
+    }
+  }
+  return hi;
 }
 
 }  // namespace gdn

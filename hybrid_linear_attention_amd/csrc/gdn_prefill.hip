@@ -87,8 +87,14 @@ struct PrepSmem {
     float buf[NB][kC * kLdT];       // per value head: A, then (I + A)^-1 in place
   } u;
   float gate[NB][kC];               // G2 (base-2 log-decay prefix) per head
+  bf16 gatelo[NB][kC];              // its rounding error (G2 = gate + gatelo; |gatelo|
+                                    // <= ulp(gate) / 2, so bf16 keeps it to ~1e-8)
   float bet[NB][kC];
 };
+// Three bf16 prepare workgroups (two fp32 ones) share a CU's 160 KB of LDS,
+// allocated in 512-byte granules.
+static_assert(sizeof(PrepSmem<bf16>) <= 106 * 512, "bf16 prepare LDS above 3 workgroups per CU");
+static_assert(sizeof(PrepSmem<float>) <= 160 * 512, "fp32 prepare LDS above 2 workgroups per CU");
 
 // acc = A[arow0.., acol0..] (16x16) * B[brow0.., bcol0..] (16x16), both fp32 in LDS.
 __device__ __forceinline__ f32x4 mm16_lds(const float* A, int arow0, int acol0,
@@ -193,7 +199,9 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 3 : 2) void prepare_kernel(
   }
   for (int hb = 0; hb < G; hb += NB) {
     const int nb = min(NB, G - hb);
-    // Gates: G2_t = sum_{j<=t} log2(alpha_j) over the chunk, one wave per head.
+    // Gates: G2_t = sum_{j<=t} log2(alpha_j) over the chunk, one wave per head,
+    // as a compensated pair, so that exponent differences G2_i - G2_j stay
+    // accurate at strong decay (|G2| of hundreds within one chunk).
     if (w < nb) {
       const int h = gq * G + hb + w;
       float al = al0, bl = bl0;
@@ -202,11 +210,13 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 3 : 2) void prepare_kernel(
         al = (l < L) ? alpha[gi] : 1.f;
         bl = (l < L) ? beta[gi] : 0.f;
       }
-      const float Gl = wave_inclusive_sum(hw_log2(al));
-      const float Glast = __shfl(Gl, kC - 1, 64);
+      float Glo;
+      const float Gl = wave_inclusive_sum2(hw_log2(al), Glo);
+      const float Glast = __shfl(Gl, kC - 1, 64), Glastlo = __shfl(Glo, kC - 1, 64);
       ws.gam[((size_t)cid * Hv + h) * kC + l] = hw_exp2(Gl);
-      ws.dec[((size_t)cid * Hv + h) * kC + l] = hw_exp2(Glast - Gl);
+      ws.dec[((size_t)cid * Hv + h) * kC + l] = hw_exp2((Glast - Gl) + (Glastlo - Glo));
       sm.gate[w][l] = Gl;
+      sm.gatelo[w][l] = (bf16)Glo;
       sm.bet[w][l] = bl;
     }
     __syncthreads();   // gates visible; K/Q tiles (first batch) or the previous
@@ -220,6 +230,7 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 3 : 2) void prepare_kernel(
       float* A = sm.u.buf[hh];
       E* mo = ws.M + ((size_t)cid * Hv + h) * kC * kC;
       const f32x4 gj = *reinterpret_cast<const f32x4*>(&sm.gate[hh][16 * w + 4 * g]);
+      const bf16x4 gjlo = *reinterpret_cast<const bf16x4*>(&sm.gatelo[hh][16 * w + 4 * g]);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         const int i = 16 * nt + r;
@@ -228,11 +239,11 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 3 : 2) void prepare_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) { a4[e] = 0.f; m4[e] = 0.f; }
         } else {
-          const float gi_ = sm.gate[hh][i], bi = sm.bet[hh][i];
+          const float gi_ = sm.gate[hh][i], gilo = (float)sm.gatelo[hh][i], bi = sm.bet[hh][i];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int j = 16 * w + 4 * g + e;
-            const float dg = (j <= i) ? hw_exp2(gi_ - gj[e]) : 0.f;
+            const float dg = (j <= i) ? hw_exp2((gi_ - gj[e]) + (gilo - (float)gjlo[e])) : 0.f;
             a4[e] = (j < i) ? bi * dg * kk[nt][e] : 0.f;
             m4[e] = dg * kq[nt][e];
           }
@@ -344,15 +355,14 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 3 : 2) void prepare_kernel(
 }
 
 // ---------------------------------------------------------------- scan
+// fp32 inputs only (the bf16 scan is scan_split_kernel below).
 template <typename E, int NW, bool GATED>
 struct ScanSmem {
-  static constexpr bool BF = sizeof(E) == 2;
+  static_assert(sizeof(E) == 4, "fp32 scan");
   static constexpr int LDK = 132;                   // K, Q row stride
   static constexpr int LDO = GATED ? 16 * NW + 4 : 16 * NW + 8;
   E Ks[kC * LDK];
   E Qs[kC * LDK];
-  E KT[BF ? kD * kLdT : 1];                         // K^T (bf16 only)
-  E Vt[BF ? 16 * NW * kLdT : 1];                    // V^T slice (bf16 only)
   E Tt[kC * kLdT];
   E Ms[kC * kLdT];
   typename std::conditional<GATED, float, E>::type Os[kC * LDO];
@@ -367,7 +377,6 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
     const E* __restrict__ gate, const float* __restrict__ norm_w, float norm_eps,
     Work<E> ws, ChunkMap cm, int Hqk, int Hv, int G) {
   using Sm = ScanSmem<E, NW, GATED>;
-  constexpr bool BF = Sm::BF;
   constexpr int LDK = Sm::LDK, LDO = Sm::LDO;
   constexpr int NT = 64 * NW;
   constexpr int EPV = 16 / sizeof(E);
@@ -416,10 +425,9 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
   // after the staging barrier, consumed at the next staging), so their global
   // latency hides behind the current chunk's MFMA work.
   constexpr int KP = kC * (kD / EPV) / NT;          // 16-byte pieces of K (and Q) per thread
-  constexpr int VP = BF ? kC * (16 * NW / 8) / NT : 1;
   constexpr int TP = kC * kC / EPV / NT;            // pieces of Tt (and M) per thread
   static_assert(KP * NT == kC * (kD / EPV) && TP * NT == kC * kC / EPV, "piece split");
-  uint4 rk[KP], rq[KP], rv[VP], rt[TP], rm[TP];
+  uint4 rk[KP], rq[KP], rt[TP], rm[TP];
   float rg = 0.f, rgl = 0.f;
 
   auto fetch = [&](int cid, int tok0, int L) {
@@ -429,13 +437,6 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
       const size_t off = ((size_t)(tok0 + t) * Hqk + gq) * kD + cb * EPV;
       rk[it] = ld16(k + off, t < L);
       rq[it] = ld16(q + off, t < L);
-    }
-    if constexpr (BF) {
-#pragma unroll
-      for (int it = 0; it < VP; ++it) {
-        const int p = tid + NT * it, t = p & 63, cb = p >> 6;
-        rv[it] = ld16(v + ((size_t)(tok0 + t) * Hv + h) * kD + dvb + cb * 8, t < L);
-      }
     }
     const E* tsrc = ws.Tt + ((size_t)cid * Hv + h) * kC * kC;
     const E* msrc = ws.M + ((size_t)cid * Hv + h) * kC * kC;
@@ -459,20 +460,6 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
       uint2* dq = reinterpret_cast<uint2*>(sm.Qs + t * LDK + cb * EPV);
       dk[0] = uint2{rk[it].x, rk[it].y}; dk[1] = uint2{rk[it].z, rk[it].w};
       dq[0] = uint2{rq[it].x, rq[it].y}; dq[1] = uint2{rq[it].z, rq[it].w};
-      if constexpr (BF) {
-        const bf16* e8 = reinterpret_cast<const bf16*>(&rk[it]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sm.KT[(cb * 8 + e) * kLdT + t] = e8[e];
-      }
-    }
-    if constexpr (BF) {
-#pragma unroll
-      for (int it = 0; it < VP; ++it) {
-        const int p = tid + NT * it, t = p & 63, cb = p >> 6;
-        const bf16* e8 = reinterpret_cast<const bf16*>(&rv[it]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sm.Vt[(cb * 8 + e) * kLdT + t] = e8[e];
-      }
     }
 #pragma unroll
     for (int it = 0; it < TP; ++it) {
@@ -547,21 +534,10 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
     for (int mt = 0; mt < 4; ++mt) { P[mt] = zero4(); QS[mt] = zero4(); Dl[mt] = zero4(); }
 
     // P = K S0^T and QS = Q S0^T (contraction over d_k).
-    if constexpr (BF) {
-      bf16x8 SB[4];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) SB[kk] = pack_b(ST[2 * kk], ST[2 * kk + 1]);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        mma_acc_bf16<8>(P[mt], reinterpret_cast<const bf16*>(sm.Ks), LDK, 16 * mt, 0, SB);
-        mma_acc_bf16<8>(QS[mt], reinterpret_cast<const bf16*>(sm.Qs), LDK, 16 * mt, 0, SB);
-      }
-    } else {
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        mma_acc_f32<8>(P[mt], reinterpret_cast<const float*>(sm.Ks), LDK, 16 * mt, 0, ST);
-        mma_acc_f32<8>(QS[mt], reinterpret_cast<const float*>(sm.Qs), LDK, 16 * mt, 0, ST);
-      }
+    for (int mt = 0; mt < 4; ++mt) {
+      mma_acc_f32<8>(P[mt], sm.Ks, LDK, 16 * mt, 0, ST);
+      mma_acc_f32<8>(QS[mt], sm.Qs, LDK, 16 * mt, 0, ST);
     }
 
     // X = V - diag(exp G) P.
@@ -569,34 +545,16 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
     for (int mt = 0; mt < 4; ++mt) {
       const int t0 = 16 * mt + 4 * g;
       float vv[4];
-      if constexpr (BF) {
-        const bf16x4 v4 =
-            *reinterpret_cast<const bf16x4*>(reinterpret_cast<const bf16*>(sm.Vt) +
-                                             (16 * w + r) * kLdT + t0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) vv[i] = (float)v4[i];
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          vv[i] = (t0 + i < L)
-                      ? to_f32(v[((size_t)(tok0 + t0 + i) * Hv + h) * kD + dv0 + r])
-                      : 0.f;
-      }
+      for (int i = 0; i < 4; ++i)
+        vv[i] = (t0 + i < L) ? v[((size_t)(tok0 + t0 + i) * Hv + h) * kD + dv0 + r] : 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) X[mt][i] = vv[i] - sm.gam[t0 + i] * P[mt][i];
     }
 
     // Dl = Tt X (contraction over tokens of the chunk).
-    if constexpr (BF) {
-      bf16x8 XB[2] = {pack_b(X[0], X[1]), pack_b(X[2], X[3])};
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        mma_acc_bf16<4>(Dl[mt], reinterpret_cast<const bf16*>(sm.Tt), kLdT, 16 * mt, 0, XB);
-    } else {
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        mma_acc_f32<4>(Dl[mt], reinterpret_cast<const float*>(sm.Tt), kLdT, 16 * mt, 0, X);
-    }
+    for (int mt = 0; mt < 4; ++mt) mma_acc_f32<4>(Dl[mt], sm.Tt, kLdT, 16 * mt, 0, X);
 
     // O = diag(exp G) QS + M Dl  ->  LDS staging.
     {
@@ -604,16 +562,8 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) QS[mt][i] *= sm.gam[16 * mt + 4 * g + i];
-      if constexpr (BF) {
-        bf16x8 DB[2] = {pack_b(Dl[0], Dl[1]), pack_b(Dl[2], Dl[3])};
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-          mma_acc_bf16<4>(QS[mt], reinterpret_cast<const bf16*>(sm.Ms), kLdT, 16 * mt, 0, DB);
-      } else {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-          mma_acc_f32<4>(QS[mt], reinterpret_cast<const float*>(sm.Ms), kLdT, 16 * mt, 0, Dl);
-      }
+      for (int mt = 0; mt < 4; ++mt) mma_acc_f32<4>(QS[mt], sm.Ms, kLdT, 16 * mt, 0, Dl);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -633,16 +583,8 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel(
       for (int i = 0; i < 4; ++i) Dl[mt][i] *= sm.dec[16 * mt + 4 * g + i];
 #pragma unroll
     for (int t = 0; t < 8; ++t) ST[t] *= gL;
-    if constexpr (BF) {
-      bf16x8 DTB[2] = {pack_b(Dl[0], Dl[1]), pack_b(Dl[2], Dl[3])};
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
-        mma_acc_bf16<4>(ST[t], reinterpret_cast<const bf16*>(sm.KT), kLdT, 16 * t, 0, DTB);
-    } else {
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-        mma_acc_f32_tA<4>(ST[t], reinterpret_cast<const float*>(sm.Ks), LDK, 16 * t, 0, Dl);
-    }
+    for (int t = 0; t < 8; ++t) mma_acc_f32_tA<4>(ST[t], sm.Ks, LDK, 16 * t, 0, Dl);
     ptok0 = tok0;
     pL = L;
     tok0 = ntok0;
