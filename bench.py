@@ -1,14 +1,18 @@
 """Benchmark of the Gated DeltaNet recurrence on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--decode-steps S] [--extended] [--copy-calibration]
+                    [--decode-steps S] [--no-other-workloads] [--copy-calibration]
 
 One step = one chunked prefill call of the T = 8192 workload (batch 1, 16
 query/key heads, 48 value heads, head dim 128, bf16 q/k/v, fp32 gates, zero
 initial state, final state emitted): the prepare kernel followed by the scan
 kernel, on inputs already resident in HBM.  The decode workload (64 sequences
 x 1 token, fp32 state 64 x 48 x 128 x 128 updated in place) is timed in the
-same run and reported under "decode".  Prints one JSON line.
+same run and reported under "decode"; so are the other prefill workloads
+(fp32 T = 256; T = 262,144 with a carried state; the packed batch of 8
+sequences of 1,024 .. 32,768 tokens, plain and with the gated RMSNorm
+epilogue), the backward of the T = 8192 call and the gated attention layer.
+Prints one JSON line.
 
 Rates:
 * prefill: tokens/s = T / step time; TFLOP/s from the method's algorithmic
@@ -74,10 +78,22 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_bytes_prefill_T8192_decode_B64.md")
 
 
+def sources_hash(names):
+    """sha256 over the concatenated bytes of the listed csrc files (a kernel's
+    source and every header it includes), or None if one is missing."""
+    h = hashlib.sha256()
+    try:
+        for n in names.split(","):
+            h.update(open(os.path.join(ROOT, "hybrid_linear_attention_amd", "csrc", n), "rb").read())
+    except OSError:
+        return None
+    return h.hexdigest()
+
+
 def counted_traffic(kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3
     FETCH_SIZE / WRITE_SIZE summary (calibrated against a plain copy), or None
-    when there is no such line or the kernel's source has changed since the
+    when there is no such line or the kernel's sources have changed since the
     counters were taken."""
     try:
         lines = open(TRAFFIC_FILE).read().splitlines()
@@ -86,12 +102,7 @@ def counted_traffic(kernel):
     for ln in lines:
         f = ln.split()
         if len(f) == 5 and f[0] == "traffic" and f[1] == kernel:
-            src = os.path.join(ROOT, "hybrid_linear_attention_amd", "csrc", f[2])
-            try:
-                h = hashlib.sha256(open(src, "rb").read()).hexdigest()
-            except OSError:
-                return None
-            return int(f[4]) if h == f[3] else None
+            return int(f[4]) if sources_hash(f[2]) == f[3] else None
     return None
 
 
@@ -109,12 +120,7 @@ def counted_mfma_gflop():
     for ln in lines:
         f = ln.split()
         if len(f) == 5 and f[0] == "mfma_gflop" and f[1] == "prefill":
-            src = os.path.join(ROOT, "hybrid_linear_attention_amd", "csrc", f[2])
-            try:
-                h = hashlib.sha256(open(src, "rb").read()).hexdigest()
-            except OSError:
-                return None
-            return float(f[4]) if h == f[3] else None
+            return float(f[4]) if sources_hash(f[2]) == f[3] else None
     return None
 
 
@@ -318,7 +324,7 @@ def cpu_baseline(inp, T_sample, min_seconds=10.0, max_calls=64):
     import oracle
     oracle.build(force=False)
     sl = {k: inp[k][:, :T_sample].cpu() for k in ("q", "k", "v", "alpha", "beta")}
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    threads = oracle.num_threads()               # team size of the oracle's parallel region
     calls, dt = 0, 0.0
     while calls < max_calls and dt < min_seconds:
         t0 = time.perf_counter()
@@ -346,12 +352,18 @@ def cpu_baseline(inp, T_sample, min_seconds=10.0, max_calls=64):
 
 
 def cpu_single_thread(T_sample=256):
-    """The same oracle on one thread (a child process with OMP_NUM_THREADS=1),
-    on the first T_sample tokens, for about five seconds of work."""
+    """The same oracle on one thread: a child process pinned to one CPU
+    (sched_setaffinity before anything loads OpenMP) whose oracle runs a team
+    of one thread (OMP_NUM_THREADS=1 and the oracle's own omp_set_num_threads),
+    on the first T_sample tokens, for about five seconds of work.  It reports
+    the team size the oracle's parallel region actually ran with."""
     import subprocess
-    code = ("import ctypes, time, synth, oracle\n"
+    code = ("import os\n"
+            "cpu = sorted(os.sched_getaffinity(0))[0]\n"
+            "os.sched_setaffinity(0, {cpu})\n"
+            "import time, synth, oracle\n"
             "oracle.build(force=False)\n"
-            "ctypes.CDLL('libgomp.so.1').omp_set_num_threads(1)\n"
+            "oracle.set_num_threads(1)\n"
             "d = synth.config_inputs(1)\n"
             "sl = {k: d[k][:, :%d] for k in ('q', 'k', 'v', 'alpha', 'beta')}\n"
             "n, t = 0, 0.0\n"
@@ -360,13 +372,16 @@ def cpu_single_thread(T_sample=256):
             "    oracle.prefill(sl['q'], sl['k'], sl['v'], sl['alpha'], sl['beta'], None)\n"
             "    t += time.perf_counter() - t0\n"
             "    n += 1\n"
-            "print(n * %d / t)\n" % (T_sample, T_sample))
+            "print(n * %d / t, oracle.num_threads(), len(os.sched_getaffinity(0)))\n"
+            % (T_sample, T_sample))
     env = dict(os.environ, OMP_NUM_THREADS="1", CUDA_VISIBLE_DEVICES="", HIP_VISIBLE_DEVICES="")
     try:
         out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
                              text=True, timeout=120)
-        return dict(value=float(out.stdout.strip().splitlines()[-1]), unit="tokens/s", cores=1,
-                    sample="first %d of 8192 tokens, all 48 value heads, float64" % T_sample)
+        rate, nthr, ncpu = out.stdout.strip().splitlines()[-1].split()
+        return dict(value=float(rate), unit="tokens/s", cores=int(ncpu), threads=int(nthr),
+                    sample="first %d of 8192 tokens, all 48 value heads, float64, pinned to "
+                           "one CPU" % T_sample)
     except Exception as e:  # reported, never fatal: it is a side figure
         return dict(value=None, error=str(e)[:200])
 
@@ -379,8 +394,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=8192)
-    ap.add_argument("--extended", action="store_true",
-                    help="also time the T=262,144 prefill and the packed varlen batch")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the fp32 T=256, T=262,144 and packed varlen prefill figures")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one plain 1 GiB device copy (for scaling HBM byte counters)")
     args = ap.parse_args()
@@ -509,8 +524,8 @@ def main():
                    "roofline": {"bound": "hbm", "achieved": att_gbs, "peak": PEAK_HBM_GBS,
                                 "unit": "GB/s", "frac": att_gbs / PEAK_HBM_GBS,
                                 "traffic": counted_traffic("attn_decode_kernel")}}}
-    if args.extended:
-        log("extended: config 0 (fp32, T=256)")
+    if not args.no_other_workloads:
+        log("fp32 prefill, T=256")
         inp0 = {k: (v.to("cuda") if isinstance(v, torch.Tensor) else v)
                 for k, v in synth.config_inputs(0).items()}
         r0 = timed_prefill(gdn, inp0, 100, 10)
@@ -518,7 +533,7 @@ def main():
                                     "p90_ms": r0["p90_ms"],
                                     "tokens_per_s": 256 / (r0["median_ms"] * 1e-3)}
         del inp0
-        log("extended: T=262144")
+        log("bf16 prefill, T=262144, carried state")
         inp3 = {k: (v.to("cuda") if isinstance(v, torch.Tensor) else v)
                 for k, v in synth.config_inputs(3).items()}
         r3 = timed_prefill(gdn, inp3, 10, 3)
@@ -526,7 +541,7 @@ def main():
                                "tokens_per_s": 262144 / (r3["step_ms"] * 1e-3),
                                "tflops_algorithmic": prefill_flops(262144) / (r3["step_ms"] * 1e-3) / 1e12}
         del inp3
-        log("extended: packed varlen batch with the gated RMSNorm epilogue")
+        log("packed varlen batch, plain and with the gated RMSNorm epilogue")
         inp4 = {k: (v.to("cuda") if isinstance(v, torch.Tensor) else v)
                 for k, v in synth.config_inputs(4).items()}
         T4 = int(inp4["cu_seqlens"][-1].item())

@@ -96,8 +96,22 @@ def _load():
             lib.oracle_gdn_decode_step.restype = ctypes.c_int
             lib.oracle_gdn_backward.argtypes = [dp] * 14 + [i64] * 5
             lib.oracle_gdn_backward.restype = ctypes.c_int
+            lib.oracle_num_threads.argtypes = []
+            lib.oracle_num_threads.restype = ctypes.c_int
+            lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+            lib.oracle_set_num_threads.restype = None
             _lib = lib
     return _lib
+
+
+def num_threads() -> int:
+    """Threads an OpenMP parallel region of the C oracle runs on here."""
+    return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Team size of the C oracle's later parallel regions."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def _f64(x) -> np.ndarray:

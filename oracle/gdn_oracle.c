@@ -36,6 +36,7 @@
  *                          emitted) and may be the same pointer as h0.
  * Returns 0, or -1 for inconsistent sizes.
  */
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -255,3 +256,19 @@ int oracle_gdn_backward(const double *q, const double *k, const double *v,
     }
     return bad ? -2 : 0;
 }
+
+/* Team size of an OpenMP parallel region here: the number of threads the
+ * chains above really run on (for reporting the CPU baseline). */
+int oracle_num_threads(void) {
+  int n = 1;
+#pragma omp parallel
+  {
+#pragma omp single
+    n = omp_get_num_threads();
+  }
+  return n;
+}
+
+/* Sets the team size of the oracle's later parallel regions (the OpenMP
+ * runtime this library is linked with, whatever else the process loaded). */
+void oracle_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
