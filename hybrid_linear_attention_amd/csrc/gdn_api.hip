@@ -1,9 +1,12 @@
 // Host side of the C ABI declared in include/gdn.h: argument checks (all of
 // them before anything is enqueued), workspace layout, and launches on the
 // caller's stream.  No allocation, no synchronisation, no global mutable state
-// beyond the thread-local last-error code.
+// beyond the thread-local last-error code and the per-device address of the
+// static scratch array of gdn_prefill_chunked_noalloc (set once per device).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <mutex>
 #include <stdint.h>
 #include <stdlib.h>
 
@@ -150,7 +153,7 @@ gdn_status debug_check_cu(const int32_t* cu, int32_t N, int32_t T_tot, void* str
   return s;
 }
 
-enum Phase { kPrepare = 1, kScan = 2, kBoth = 3 };
+enum Phase { kCheckOnly = 0, kPrepare = 1, kScan = 2, kBoth = 3 };
 
 gdn_status prefill_fixed(const void* q, const void* k, const void* v, const float* alpha,
                          const float* beta, const void* h0, void* o, void* ht, int32_t B,
@@ -165,11 +168,12 @@ gdn_status prefill_fixed(const void* q, const void* k, const void* v, const floa
   const int64_t nc = (int64_t)B * Nc;
   if (nc > (int64_t(1) << 30)) return GDN_ERR_UNSUPPORTED;
   const WsLayout L = ws_layout(nc, H_qk, H_v, dt, -1);
-  const size_t need = nc > 0 ? L.total : 0;
+  // kCheckOnly: every check but the workspace's
+  const size_t need = (nc > 0 && phase != kCheckOnly) ? L.total : 0;
   s = check_prefill(q, k, v, alpha, beta, h0, o, ht, nullptr, nullptr, nullptr, 0,
                     (int64_t)B * T, B, H_qk, H_v, dt, workspace, workspace_bytes, need,
                     state_bf16 ? 2 : 4);
-  if (s != GDN_OK) return s;
+  if (s != GDN_OK || phase == kCheckOnly) return s;
 
   gdn::PrefillLaunch a{};
   a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.h0 = h0; a.o = o; a.ht = ht;
@@ -200,6 +204,50 @@ gdn_status prefill_fixed(const void* q, const void* k, const void* v, const floa
 
 }  // namespace
 
+// Workspace of gdn_prefill_chunked_noalloc: one copy per device, held from the
+// code object's load until the process ends.  In host code `scratch` is only
+// a stand-in for the symbol; its device address comes from
+// hipGetSymbolAddress, once per device (scratch_on below).
+static __device__ __align__(256) unsigned char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the device that runs `stream` (the current
+// device for the default stream).  The first call on a device looks the
+// symbol up with that device current and restores the caller's device.
+gdn_status scratch_on(hipStream_t stream, void** out) {
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e);
+  if (dev < 0 || dev >= kMaxDevices) return GDN_ERR_UNSUPPORTED;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+      int cur = 0;
+      if ((e = hipGetDevice(&cur)) != hipSuccess) return fail_hip(e);
+      if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return fail_hip(e);
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (cur != dev) {
+        const hipError_t e2 = hipSetDevice(cur);
+        if (e == hipSuccess) e = e2;
+      }
+      if (e != hipSuccess) return fail_hip(e);
+      if (!p) return fail_hip(hipErrorInvalidSymbol);
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return GDN_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int gdn_abi_version(void) { return 100; }
@@ -216,6 +264,9 @@ const char* gdn_status_str(gdn_status s) {
     case GDN_ERR_ALIAS: return "GDN_ERR_ALIAS: an output overlaps another buffer";
     case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE: workspace missing or too small";
     case GDN_ERR_HIP: return "GDN_ERR_HIP: a HIP launch failed";
+    case GDN_ERR_TOO_LARGE:
+      return "GDN_ERR_TOO_LARGE: the call needs more workspace than the static scratch array "
+             "of gdn_prefill_chunked_noalloc holds (GDN_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown gdn_status";
   }
 }
@@ -242,6 +293,27 @@ gdn_status gdn_prefill_chunked(const void* q, const void* k, const void* v, cons
                                void* stream) {
   return prefill_fixed(q, k, v, alpha, beta, h0, o, ht, B, T, H_qk, H_v, D, dt, workspace,
                        workspace_bytes, stream, kBoth, false);
+}
+
+gdn_status gdn_prefill_chunked_noalloc(const void* q, const void* k, const void* v,
+                                       const float* alpha, const float* beta, const float* h0,
+                                       void* o, float* ht, int32_t B, int32_t T, int32_t H_qk,
+                                       int32_t H_v, int32_t D, gdn_dtype dt, void* stream) {
+  // Every host check first (nothing touches the device on an error): the
+  // arguments with no workspace, then the workspace size against the array.
+  gdn_status s = prefill_fixed(q, k, v, alpha, beta, h0, o, ht, B, T, H_qk, H_v, D, dt,
+                               nullptr, 0, stream, kCheckOnly, false);
+  if (s != GDN_OK) return s;
+  const size_t need = gdn_prefill_workspace_bytes(B, T, H_qk, H_v, D, dt);
+  if (need > GDN_NOALLOC_SCRATCH_BYTES) return GDN_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  if (need > 0) {
+    s = scratch_on(static_cast<hipStream_t>(stream), &ws);
+    if (s != GDN_OK) return s;
+  }
+  // The workspace needs no clearing: prepare writes every part the scan reads.
+  return prefill_fixed(q, k, v, alpha, beta, h0, o, ht, B, T, H_qk, H_v, D, dt, ws,
+                       GDN_NOALLOC_SCRATCH_BYTES, stream, kBoth, false);
 }
 
 gdn_status gdn_prefill_prepare(const void* q, const void* k, const void* v, const float* alpha,

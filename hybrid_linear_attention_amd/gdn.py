@@ -45,6 +45,8 @@ def _load():
         fn = getattr(lib, name)
         fn.argtypes = pre
         fn.restype = ctypes.c_int
+    lib.gdn_prefill_chunked_noalloc.argtypes = pre[:14] + [vp]
+    lib.gdn_prefill_chunked_noalloc.restype = ctypes.c_int
     lib.gdn_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int]
     lib.gdn_prefill_workspace_bytes.restype = sz
     lib.gdn_varlen_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int]
@@ -216,6 +218,40 @@ def prefill_chunked(q, k, v, alpha, beta, h0=None, *, o=None, ht=None,
         _check(lib.gdn_prefill_chunked_bf16_state(*args), "gdn_prefill_chunked_bf16_state")
     else:
         _check(lib.gdn_prefill_chunked(*args), "gdn_prefill_chunked")
+    return o, ht
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20
+
+
+def prefill_chunked_noalloc(q, k, v, alpha, beta, h0=None, *, o, ht=None):
+    """gdn_prefill_chunked_noalloc: the chunked prefill with the library's
+    static scratch array as its workspace (the caller passes o, and ht when the
+    final state is wanted: this call allocates nothing).  fp32 states.  Calls
+    that overlap on one GPU race on the array."""
+    _req(q, "q", ndim=4)
+    dtype, dev = q.dtype, q.device
+    B, T, H_qk, D = q.shape
+    _req(k, "k", dtype, 4, dev)
+    _req(v, "v", dtype, 4, dev)
+    H_v = v.shape[2]
+    if tuple(k.shape) != (B, T, H_qk, D) or tuple(v.shape) != (B, T, H_v, D):
+        raise ValueError("q/k [B,T,Hqk,D] and v [B,T,Hv,D] disagree")
+    for name, t in (("alpha", alpha), ("beta", beta)):
+        _req(t, name, torch.float32, 3, dev)
+        if tuple(t.shape) != (B, T, H_v):
+            raise ValueError("%s must be [B,T,Hv]" % name)
+    _req(h0, "h0", torch.float32, 4, dev)
+    _req(o, "o", dtype, 4, dev)
+    _req(ht, "ht", torch.float32, 4, dev)
+    if tuple(o.shape) != (B, T, H_v, D):
+        raise ValueError("o must be [B,T,Hv,D]")
+    for name, t in (("h0", h0), ("ht", ht)):
+        if t is not None and tuple(t.shape) != (B, H_v, D, D):
+            raise ValueError("%s must be [B,Hv,D,D]" % name)
+    _check(lib.gdn_prefill_chunked_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(h0), _ptr(o), _ptr(ht),
+        B, T, H_qk, H_v, D, _dt(q), _stream(dev)), "gdn_prefill_chunked_noalloc")
     return o, ht
 
 

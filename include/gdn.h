@@ -42,6 +42,8 @@
  *    synchronises.  Device faults surface at the caller's next synchronisation.
  *  - The caller owns every buffer, including the workspace; the library keeps
  *    no global mutable state, so calls from several host threads are safe.
+ *    The one exception is gdn_prefill_chunked_noalloc, whose workspace is a
+ *    static array of the library (see there).
  *  - Every argument check runs on the host before anything is enqueued: a
  *    call that returns an error has enqueued nothing.
  *  - Pointers must be 16-byte aligned (alpha, beta: 4-byte).  Outputs must not
@@ -68,6 +70,7 @@ typedef int gdn_status;
 #define GDN_ERR_ALIAS (-5)       /* an output overlaps another buffer       */
 #define GDN_ERR_WORKSPACE (-6)   /* workspace missing or too small          */
 #define GDN_ERR_HIP (-7)         /* a HIP launch failed; see gdn_last_hip_error */
+#define GDN_ERR_TOO_LARGE (-8)   /* needs more than GDN_NOALLOC_SCRATCH_BYTES  */
 
 /* Tokens per chunk of the block-parallel prefill. */
 #define GDN_CHUNK 64
@@ -95,6 +98,35 @@ gdn_status gdn_prefill_chunked(const void *q, const void *k, const void *v,
                                int32_t B, int32_t T, int32_t H_qk, int32_t H_v,
                                int32_t D, gdn_dtype dt, void *workspace,
                                size_t workspace_bytes, void *stream);
+
+/*
+ * gdn_prefill_chunked_noalloc - gdn_prefill_chunked without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ *
+ * Same arguments, layouts, results and errors as gdn_prefill_chunked, minus
+ * workspace/workspace_bytes.  The workspace is a static device array of the
+ * library, GDN_NOALLOC_SCRATCH_BYTES (128 MiB) per GPU, held from the
+ * library's first use on that GPU until the process ends.  A call whose
+ * gdn_prefill_workspace_bytes(...) exceeds it returns GDN_ERR_TOO_LARGE and
+ * enqueues nothing (bf16 or fp32 at H_v = 48: B * ceil(T / 64) <= 165 or 84
+ * chunks, e.g. one T = 8192 bf16 sequence).  Nothing in the array needs to
+ * start at zero; it keeps the last call's contents.
+ *
+ * Every call on one GPU uses that GPU's single array: calls whose execution
+ * overlaps on one GPU (different streams, or host threads racing on
+ * different streams) race on it and give wrong results.  Serialise them, e.g.
+ * by using one stream per GPU.  The first call on a GPU looks up the array's
+ * device address (hipGetSymbolAddress), which neither allocates nor
+ * synchronises.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+gdn_status gdn_prefill_chunked_noalloc(const void *q, const void *k,
+                                       const void *v, const float *alpha,
+                                       const float *beta, const float *h0,
+                                       void *o, float *ht, int32_t B,
+                                       int32_t T, int32_t H_qk, int32_t H_v,
+                                       int32_t D, gdn_dtype dt, void *stream);
 
 /* Workspace bytes for gdn_prefill_chunked (0 on unsupported arguments).
  * Grows with the number of chunks (per-chunk solve results), never with the

@@ -15,6 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gdn.h")
 
 OK, ENULL, ESHAPE, EUNSUP, EALIGN, EALIAS, EWS, EHIP = 0, -1, -2, -3, -4, -5, -6, -7
+ETOOLARGE = -8
 F32, BF16 = 0, 1
 
 
@@ -49,7 +50,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(gdn):
-    for code in (OK, ENULL, ESHAPE, EUNSUP, EALIGN, EALIAS, EWS, EHIP):
+    for code in (OK, ENULL, ESHAPE, EUNSUP, EALIGN, EALIAS, EWS, EHIP, ETOOLARGE):
         s = gdn.status_str(code)
         assert s.startswith("GDN_")
     assert "unknown" in gdn.status_str(12345)
@@ -120,6 +121,46 @@ def prefill_call(lib, name="gdn_prefill_chunked", **kw):
 ])
 def test_prefill_validation(lib, name, kw, code):
     assert prefill_call(lib, name, **kw) == code
+
+
+def noalloc_call(lib, **kw):
+    args = dict(q=addr(0), k=addr(1), v=addr(2), alpha=addr(3), beta=addr(4), h0=addr(5),
+                o=addr(6), ht=addr(7), B=1, T=128, Hqk=16, Hv=48, D=128, dt=BF16, stream=None)
+    args.update(kw)
+    return lib.gdn_prefill_chunked_noalloc(
+        args["q"], args["k"], args["v"], args["alpha"], args["beta"], args["h0"], args["o"],
+        args["ht"], args["B"], args["T"], args["Hqk"], args["Hv"], args["D"], args["dt"],
+        args["stream"])
+
+
+# Every host check of the allocation-free prefill runs before it touches the
+# device, so these return on a machine without a GPU.
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=64), EUNSUP),
+    (dict(dt=7), EUNSUP),
+    (dict(Hv=47), ESHAPE),
+    (dict(T=-1), ESHAPE),
+    (dict(q=None), ENULL),
+    (dict(o=None), ENULL),
+    (dict(q=addr(0, 8)), EALIGN),
+    (dict(o=addr(0, 256)), EALIAS),
+    (dict(ht=addr(5, 1024)), EALIAS),
+    # the static scratch array holds 165 bf16 / 84 fp32 chunks of 48 value heads
+    (dict(T=64 * 166), ETOOLARGE),
+    (dict(B=2, T=64 * 83), ETOOLARGE),
+    (dict(T=64 * 85, dt=F32), ETOOLARGE),
+])
+def test_noalloc_validation(lib, kw, code):
+    assert noalloc_call(lib, **kw) == code
+
+
+def test_noalloc_scratch_limit_matches_workspace_sizes(gdn):
+    lim = 128 << 20
+    assert gdn.NOALLOC_SCRATCH_BYTES == lim
+    assert gdn.prefill_workspace_bytes(1, 64 * 165, 16, 48) <= lim
+    assert gdn.prefill_workspace_bytes(1, 64 * 166, 16, 48) > lim
+    assert gdn.prefill_workspace_bytes(1, 8192, 16, 48) <= lim      # the T = 8192 workload
+    assert "GDN_ERR_TOO_LARGE" in gdn.status_str(ETOOLARGE)
 
 
 def decode_call(lib, **kw):
