@@ -15,7 +15,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libgdn.so")
+# GDN_LIB_PATH selects another build of the same library (e.g. one whose host
+# code carries sanitizers); by default the in-tree libgdn.so.
+LIB_PATH = os.environ.get("GDN_LIB_PATH") or os.path.join(_HERE, "libgdn.so")
 
 GDN_F32 = 0
 GDN_BF16 = 1

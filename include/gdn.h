@@ -59,7 +59,12 @@
 extern "C" {
 #endif
 
-typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+/* Element type of q, k, v, o and gate: GDN_F32 or GDN_BF16.  A plain integer
+ * rather than an enum, so that any value a caller passes is well defined on
+ * the library side (an unknown one returns GDN_ERR_UNSUPPORTED). */
+typedef int32_t gdn_dtype;
+#define GDN_F32 0
+#define GDN_BF16 1
 
 typedef int gdn_status;
 #define GDN_OK 0

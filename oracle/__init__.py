@@ -63,7 +63,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gdn_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# GDN_ORACLE_LIB selects another build of gdn_oracle.c (e.g. with sanitizers).
+_LIB_PATH = os.environ.get("GDN_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 _lock = threading.Lock()
 
