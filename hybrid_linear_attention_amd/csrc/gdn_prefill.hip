@@ -75,8 +75,14 @@ __device__ __forceinline__ uint4 ld16(const E* p, bool ok) {
 // ---------------------------------------------------------------- prepare
 constexpr int kLdT = 68;   // LDS row stride of 64-wide fp32/bf16 tiles
 
+// fp32 only: the rounding error of the gate prefix (G2 = gate + gatelo;
+// |gatelo| <= ulp(gate) / 2, so bf16 keeps it to ~1e-8).  Absent (an empty
+// base) for bf16, whose layout must keep three workgroups per CU.
+template <typename E> struct PrepLo { bf16 gatelo[3][kC]; };
+template <> struct PrepLo<bf16> {};
+
 template <typename E>
-struct PrepSmem {
+struct PrepSmem : PrepLo<E> {
   static constexpr int LDK = 136;   // K/Q row stride: rows 16-byte aligned for b128 reads
   static constexpr int NB = 3;      // value heads whose A matrices are resident at once
   union {
@@ -87,14 +93,12 @@ struct PrepSmem {
     float buf[NB][kC * kLdT];       // per value head: A, then (I + A)^-1 in place
   } u;
   float gate[NB][kC];               // G2 (base-2 log-decay prefix) per head
-  bf16 gatelo[NB][kC];              // its rounding error (G2 = gate + gatelo; |gatelo|
-                                    // <= ulp(gate) / 2, so bf16 keeps it to ~1e-8)
   float bet[NB][kC];
 };
-// Three bf16 prepare workgroups (two fp32 ones) share a CU's 160 KB of LDS,
-// allocated in 512-byte granules.
-static_assert(sizeof(PrepSmem<bf16>) <= 106 * 512, "bf16 prepare LDS above 3 workgroups per CU");
-static_assert(sizeof(PrepSmem<float>) <= 160 * 512, "fp32 prepare LDS above 2 workgroups per CU");
+// Three bf16 prepare workgroups (two fp32 ones) share a CU's 160 KB of LDS;
+// the bf16 layout is measured to allow three, and 384 bytes more do not.
+static_assert(sizeof(PrepSmem<bf16>) <= 53760, "bf16 prepare LDS above 3 workgroups per CU");
+static_assert(sizeof(PrepSmem<float>) <= 80 * 1024, "fp32 prepare LDS above 2 workgroups per CU");
 
 // acc = A[arow0.., acol0..] (16x16) * B[brow0.., bcol0..] (16x16), both fp32 in LDS.
 __device__ __forceinline__ f32x4 mm16_lds(const float* A, int arow0, int acol0,
@@ -199,9 +203,11 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 3 : 2) void prepare_kernel(
   }
   for (int hb = 0; hb < G; hb += NB) {
     const int nb = min(NB, G - hb);
-    // Gates: G2_t = sum_{j<=t} log2(alpha_j) over the chunk, one wave per head,
-    // as a compensated pair, so that exponent differences G2_i - G2_j stay
-    // accurate at strong decay (|G2| of hundreds within one chunk).
+    // Gates: G2_t = sum_{j<=t} log2(alpha_j) over the chunk, one wave per head.
+    // fp32 inputs carry it as a compensated pair, so that exponent
+    // differences G2_i - G2_j stay accurate to ~1e-7 at strong decay (|G2| of
+    // hundreds within one chunk); bf16 inputs round A and M to bf16 anyway
+    // (2^-9), far above the ~1e-5 of the plain prefix.
     if (w < nb) {
       const int h = gq * G + hb + w;
       float al = al0, bl = bl0;
@@ -210,13 +216,14 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 3 : 2) void prepare_kernel(
         al = (l < L) ? alpha[gi] : 1.f;
         bl = (l < L) ? beta[gi] : 0.f;
       }
-      float Glo;
-      const float Gl = wave_inclusive_sum2(hw_log2(al), Glo);
-      const float Glast = __shfl(Gl, kC - 1, 64), Glastlo = __shfl(Glo, kC - 1, 64);
+      float Glo = 0.f;
+      const float Gl = BF ? wave_inclusive_sum(hw_log2(al)) : wave_inclusive_sum2(hw_log2(al), Glo);
+      const float Glast = __shfl(Gl, kC - 1, 64);
+      const float Glastlo = BF ? 0.f : __shfl(Glo, kC - 1, 64);
       ws.gam[((size_t)cid * Hv + h) * kC + l] = hw_exp2(Gl);
-      ws.dec[((size_t)cid * Hv + h) * kC + l] = hw_exp2((Glast - Gl) + (Glastlo - Glo));
+      ws.dec[((size_t)cid * Hv + h) * kC + l] = hw_exp2(BF ? Glast - Gl : (Glast - Gl) + (Glastlo - Glo));
       sm.gate[w][l] = Gl;
-      sm.gatelo[w][l] = (bf16)Glo;
+      if constexpr (!BF) sm.gatelo[w][l] = (bf16)Glo;
       sm.bet[w][l] = bl;
     }
     __syncthreads();   // gates visible; K/Q tiles (first batch) or the previous
@@ -230,7 +237,8 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 3 : 2) void prepare_kernel(
       float* A = sm.u.buf[hh];
       E* mo = ws.M + ((size_t)cid * Hv + h) * kC * kC;
       const f32x4 gj = *reinterpret_cast<const f32x4*>(&sm.gate[hh][16 * w + 4 * g]);
-      const bf16x4 gjlo = *reinterpret_cast<const bf16x4*>(&sm.gatelo[hh][16 * w + 4 * g]);
+      bf16x4 gjlo{};
+      if constexpr (!BF) gjlo = *reinterpret_cast<const bf16x4*>(&sm.gatelo[hh][16 * w + 4 * g]);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         const int i = 16 * nt + r;
@@ -239,11 +247,14 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 3 : 2) void prepare_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) { a4[e] = 0.f; m4[e] = 0.f; }
         } else {
-          const float gi_ = sm.gate[hh][i], gilo = (float)sm.gatelo[hh][i], bi = sm.bet[hh][i];
+          const float gi_ = sm.gate[hh][i], bi = sm.bet[hh][i];
+          float gilo = 0.f;
+          if constexpr (!BF) gilo = (float)sm.gatelo[hh][i];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int j = 16 * w + 4 * g + e;
-            const float dg = (j <= i) ? hw_exp2((gi_ - gj[e]) + (gilo - (float)gjlo[e])) : 0.f;
+            const float dx = BF ? gi_ - gj[e] : (gi_ - gj[e]) + (gilo - (float)gjlo[e]);
+            const float dg = (j <= i) ? hw_exp2(dx) : 0.f;
             a4[e] = (j < i) ? bi * dg * kk[nt][e] : 0.f;
             m4[e] = dg * kq[nt][e];
           }
@@ -1030,6 +1041,399 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
   }
 }
 
+// ---------------------------------------------------------------- head-wide scan (bf16)
+// The bf16 scan with one workgroup per (value head, sequence), for calls with
+// many (sequence, head) pairs and for the gated RMSNorm epilogue, which needs
+// every value row of a token in one workgroup:
+//
+//  * four chain waves, one per SIMD, each owning 32 value rows as two
+//    independent 16-row slices whose MFMA chains interleave (one slice's
+//    products fill the other's dependency gaps, and every A fragment read
+//    from LDS serves both).  Besides the chain (P = K S^T, X, Dl = Tt X, the
+//    state update) each forms its rows of the output,
+//    O^T = S Q^T diag(gam) + Dl^T M^T, as the split scan's output wave does,
+//    with the same products in the same order (so the plain output equals the
+//    split scan's bit for bit).  Chunk c's output is stored at the start of
+//    iteration c+1 and its stores are waited for at the end of that
+//    iteration, a whole chunk of work after they were issued;
+//  * four copy waves: K, Q, V (all 128 value rows) with gam/dec, and Tt with
+//    M of chunk c+1 go straight into the other slot of a two-slot LDS ring
+//    (global_load_lds_dwordx4) while chunk c is computed.
+//
+// Fragment layouts, swizzles and the token / d_k permutation are those of
+// the split scan.  V rows (256 bytes, 16 pieces) are swizzled by vsw so that
+// a chain wave's transposed read of 16 tokens x 16 value rows spreads over
+// eight 32-byte segments, two tokens each.
+//
+// Gated: y = o / sqrt(mean_dv o^2 + eps) * w * sigmoid(gate).  The chain
+// waves add only the per-token sums of o^2 over their rows (into LDS, three
+// chunks deep).  The copy waves, which have issue slots to spare, apply the
+// epilogue two chunks behind: once chunk c's o is in memory (stored in
+// iteration c+1, complete before the barrier ending it), they read it back
+// with the gate, scale it and write y over it in iteration c+2.
+namespace hw {
+using frag::barrier_lds;
+using frag::dma16;
+using frag::dma4;
+using frag::lds_tr16;
+using frag::s16x4;
+constexpr int kCW = 4;                      // chain waves (32 value rows each)
+constexpr int kPW = 4;                      // copy waves
+constexpr int kWaves = kCW + kPW;
+struct Slot {
+  alignas(16) uint8_t K[kC * kD * 2];       // [64 tokens][128 d_k], 256-byte rows, ksw
+  alignas(16) uint8_t Q[kC * kD * 2];       // [64 tokens][128 d_k], 256-byte rows, swz
+  alignas(16) uint8_t T[kC * kC * 2];       // [64][64], 128-byte rows, swz
+  alignas(16) uint8_t M[kC * kC * 2];       // [64][64], 128-byte rows, swz
+  alignas(16) uint8_t V[kC * kD * 2];       // [64 tokens][128 value rows], 256-byte rows, vsw
+  alignas(16) float gam[kC];
+  alignas(16) float dec[kC];
+};
+struct Smem {
+  Slot slot[2];
+  float part[3][kCW][kC];                   // gated: per-wave sums of o^2 per token
+};
+static_assert(sizeof(Smem) <= 160 * 1024, "LDS");
+__device__ __forceinline__ int vsw(int tok) { return 2 * ((tok & 3) | (((tok >> 3) & 1) << 2)); }
+// Wait until at most N of this wave's vector memory operations are pending
+// (they complete in issue order).
+template <int N> __device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+}  // namespace hw
+
+template <bool GATED>
+__global__ __launch_bounds__(64 * hw::kWaves) void scan_head_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const void* __restrict__ h0, bf16* __restrict__ o, void* __restrict__ ht, bool sbf,
+    const bf16* __restrict__ gate, const float* __restrict__ norm_w, float norm_eps,
+    Work<bf16> ws, ChunkMap cm, int Hqk, int Hv, int G) {
+  using namespace hw;
+  using split::ksw;
+  using split::prow;
+  using split::swz;
+  __shared__ Smem sm;
+
+  // Heads of one query/key group on consecutive ids of one XCD (ids are dealt
+  // to the 8 XCDs round-robin), so that their K and Q meet in one L2.
+  int lin = blockIdx.x;
+  if ((Hqk & 7) == 0) {
+    const int xcd = lin & 7, j = lin >> 3;
+    lin = (xcd + 8 * (j / G)) * G + (j - (j / G) * G);
+  }
+  if (lin >= Hv) return;                           // whole workgroup leaves together
+  const int h = lin, gq = h / G, seq = blockIdx.y;
+  const int w = __builtin_amdgcn_readfirstlane(wave_id()), l = lane_id(), r = l & 15, g = l >> 4;
+  int cid0, nch;
+  seq_chunks(cm, seq, cid0, nch);
+  const size_t hv_stride = (size_t)Hv * kD;
+  const size_t qk_stride = (size_t)Hqk * kD;
+
+  // Iterations 0 .. nch+1: chunk i computed in iteration i, its output
+  // stored in iteration i+1, its gated epilogue applied in iteration i+2.
+  if (w >= kCW) {
+    // ------------------------------------------------------------ copy waves
+    // Rows beyond L repeat the last token (K: they meet zero Tt columns and
+    // zero decay-scaled Dl rows; Q: their outputs are never stored; V: zero
+    // Tt columns).
+    const int pw = w - kCW;
+    auto issue = [&](int c) {
+      const int cid = cid0 + c;
+      int tok0, L;
+      chunk_of(cm, cid, tok0, L);
+      Slot& S = sm.slot[c & 1];
+      if (pw < 3) {
+        const bf16* base = pw == 0   ? k + (size_t)tok0 * qk_stride + (size_t)gq * kD
+                           : pw == 1 ? q + (size_t)tok0 * qk_stride + (size_t)gq * kD
+                                     : v + (size_t)tok0 * hv_stride + (size_t)h * kD;
+        const size_t stride = pw == 2 ? hv_stride : qk_stride;
+        uint8_t* dst = pw == 0 ? S.K : pw == 1 ? S.Q : S.V;
+#pragma unroll
+        for (int it = 0; it < 16; ++it) {
+          const int row = 4 * it + (l >> 4);
+          const int sw = pw == 0 ? ksw(row) : pw == 1 ? swz(row) : vsw(row);
+          dma16(base + (size_t)min(row, L - 1) * stride + 8 * ((l & 15) ^ sw), dst + 1024 * it);
+        }
+        if (pw == 2) {
+          dma4(ws.gam + ((size_t)cid * Hv + h) * kC + l, S.gam);
+          dma4(ws.dec + ((size_t)cid * Hv + h) * kC + l, S.dec);
+        }
+      } else {
+        const size_t tm = ((size_t)cid * Hv + h) * kC * kC;
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+          const int row = 8 * it + (l >> 3), p = (l & 7) ^ swz(row);
+          dma16(ws.Tt + tm + row * kC + 8 * p, S.T + 1024 * it);
+          dma16(ws.M + tm + row * kC + 8 * p, S.M + 1024 * it);
+        }
+      }
+    };
+    // gated epilogue of chunk c: this wave's 16 tokens 16 pw + l/4, lane
+    // quarter l%4 holds value rows 32(l%4) .. +31
+    const int erow = 16 * pw + (l >> 2), edv = 32 * (l & 3);
+    float nw[32];
+    if constexpr (GATED) {
+#pragma unroll
+      for (int e = 0; e < 32; ++e) nw[e] = norm_w ? norm_w[edv + e] : 1.f;
+    }
+    uint4 ov[4], gv[4];
+    size_t eoff = 0;
+    int eL = 0;
+    auto epilogue_load = [&](int c) {
+      int tok0;
+      chunk_of(cm, cid0 + c, tok0, eL);
+      eoff = ((size_t)tok0 + min(erow, eL - 1)) * hv_stride + (size_t)h * kD + edv;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ov[j] = *reinterpret_cast<const uint4*>(o + eoff + 8 * j);
+        gv[j] = *reinterpret_cast<const uint4*>(gate + eoff + 8 * j);
+      }
+    };
+    auto epilogue = [&](int c) {
+      const size_t off = eoff;
+      const int L = eL;
+      float tot = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kCW; ++ww) tot += sm.part[c % 3][ww][erow];
+      const float rn = rsqrtf(tot * (1.f / kD) + norm_eps);
+      if (erow < L) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16* o8 = reinterpret_cast<const bf16*>(&ov[j]);
+          const bf16* g8 = reinterpret_cast<const bf16*>(&gv[j]);
+          bf16x8 y;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            // hardware reciprocal (1 ulp): far below the bf16 rounding of y
+            const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-(float)g8[e]));
+            y[e] = (bf16)((float)o8[e] * rn * nw[8 * j + e] * sg);
+          }
+          *reinterpret_cast<bf16x8*>(o + off + 8 * j) = y;
+        }
+      }
+    };
+    if (nch > 0) issue(0);
+    wait_vm<0>();
+    barrier_lds();
+    for (int i = 0; i <= nch + 1; ++i) {
+      if (i + 1 < nch) issue(i + 1);
+      if constexpr (GATED) {
+        if (i >= 2) {
+          // chunk i-2's o and gate are read, and its y written, after the
+          // copies (the counted wait below relies on that order: vector
+          // memory operations complete in issue order)
+          asm volatile("" ::: "memory");
+          epilogue_load(i - 2);
+          epilogue(i - 2);
+          // the copies of chunk i+1 are complete; the y stores (the last
+          // four operations, issued unless no token of this wave is in the
+          // chunk) may still be in flight
+          if (16 * pw < eL) wait_vm<4>();
+          else wait_vm<0>();
+        } else {
+          wait_vm<0>();
+        }
+      } else {
+        wait_vm<0>();
+      }
+      barrier_lds();
+    }
+    return;
+  }
+
+  // -------------------------------------------------------------- chain waves
+  const int dvw = 32 * w;                          // first value row of this wave
+  f32x4 ST[2][8];                                  // ST[s][t][i] = S[dvw + 16s + r][prow(t, 4g + i)]
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const size_t hrow = (((size_t)seq * Hv + h) * kD + dvw + 16 * s + r) * kD;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) ST[s][t] = h0 ? load_state4(h0, hrow + prow(t, 4 * g), sbf) : zero4();
+  }
+  bf16x4 OB[2][4];                                 // the previous chunk's o
+  int ptok0 = 0, pL = 0;
+  barrier_lds();
+  for (int i = 0; i <= nch + 1; ++i) {
+    if (i >= 1 && i <= nch) {
+      bf16* ob = o + (size_t)ptok0 * hv_stride + (size_t)h * kD + dvw + 4 * g;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int row = 16 * nt + r;
+        if (row < pL) {
+#pragma unroll
+          for (int s = 0; s < 2; ++s) *reinterpret_cast<bf16x4*>(ob + (size_t)row * hv_stride + 16 * s) = OB[s][nt];
+        }
+      }
+    }
+    if (i < nch) {
+      int tok0, L;
+      chunk_of(cm, cid0 + i, tok0, L);
+      const Slot& S = sm.slot[i & 1];
+      // P = K S^T for both slices (rows: physical tokens prow(mt, r))
+      bf16x8 SB[2][4];
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) SB[s][kk] = pack_b(ST[s][2 * kk], ST[s][2 * kk + 1]);
+      f32x4 P[2][4];
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) P[s][mt] = zero4();
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int row = prow(mt, r);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(S.K + row * 256 + 16 * ((4 * kk + g) ^ ksw(row)));
+#pragma unroll
+          for (int s = 0; s < 2; ++s) P[s][mt] = mfma_bf16(a, SB[s][kk], P[s][mt]);
+        }
+      }
+      // O^T (first part) = S Q^T: lane (r, g) holds value rows 16s + 4g + e of
+      // token 16nt + r
+      f32x4 OT[2][4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int row = 16 * nt + r;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) OT[s][nt] = zero4();
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const bf16x8 bq = *reinterpret_cast<const bf16x8*>(S.Q + row * 256 + 16 * ((4 * kk + g) ^ swz(row)));
+#pragma unroll
+          for (int s = 0; s < 2; ++s) OT[s][nt] = mfma_bf16(SB[s][kk], bq, OT[s][nt]);
+        }
+      }
+      // X = V - diag(gam) P, V of this lane's value row by transposed reads
+      // (as input lane r of group g: 4 value rows 16s + 4(r%4) .. +3 of token
+      // 32(mt/2) + 8g + 4(mt%2) + r/4)
+      f32x4 X[2][4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int tb = 32 * (mt >> 1) + 8 * g + 4 * (mt & 1);
+        const f32x4 gm = *reinterpret_cast<const f32x4*>(S.gam + tb);
+        const int tok = tb + (r >> 2);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const int col = dvw + 16 * s + 4 * (r & 3);
+          const s16x4 vt = lds_tr16(S.V + tok * 256 + 16 * ((col >> 3) ^ vsw(tok)) + 2 * (col & 7));
+          const bf16* v4 = reinterpret_cast<const bf16*>(&vt);
+#pragma unroll
+          for (int i2 = 0; i2 < 4; ++i2) X[s][mt][i2] = (float)v4[i2] - gm[i2] * P[s][mt][i2];
+        }
+      }
+      // Dl = Tt X (Tt lower triangular: tiles mt < 2 have nothing in columns 32..63)
+      f32x4 Dl[2][4];
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) Dl[s][mt] = zero4();
+      {
+        bf16x8 XB[2][2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          XB[s][0] = pack_b(X[s][0], X[s][1]);
+          XB[s][1] = pack_b(X[s][2], X[s][3]);
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const int row = prow(mt, r);
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            if (kk == 1 && mt < 2) continue;
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(S.T + row * 128 + 16 * ((4 * kk + g) ^ swz(row)));
+#pragma unroll
+            for (int s = 0; s < 2; ++s) Dl[s][mt] = mfma_bf16(a, XB[s][kk], Dl[s][mt]);
+          }
+        }
+      }
+      // state update: S^T <- gam_last S^T + K^T diag(dec) Dl; the A fragments
+      // of K^T by transposed reads of the K tile (as in the split scan)
+      bf16x8 DB[2][2], DTB[2][2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        DB[s][0] = pack_b(Dl[s][0], Dl[s][1]);
+        DB[s][1] = pack_b(Dl[s][2], Dl[s][3]);
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const f32x4 dc = *reinterpret_cast<const f32x4*>(S.dec + 32 * (mt >> 1) + 8 * g + 4 * (mt & 1));
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int i2 = 0; i2 < 4; ++i2) Dl[s][mt][i2] *= dc[i2];
+      }
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        DTB[s][0] = pack_b(Dl[s][0], Dl[s][1]);
+        DTB[s][1] = pack_b(Dl[s][2], Dl[s][3]);
+      }
+      const float gL = S.gam[kC - 1];
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) ST[s][t] *= gL;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int dk = 32 * (t >> 1) + 8 * (r & 3) + 4 * (t & 1);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const int t0 = 32 * kk + 8 * g + (r >> 2), t1 = t0 + 4;
+          const s16x4 lo = lds_tr16(S.K + t0 * 256 + 16 * ((dk >> 3) ^ ksw(t0)) + 2 * (dk & 7));
+          const s16x4 hi = lds_tr16(S.K + t1 * 256 + 16 * ((dk >> 3) ^ ksw(t1)) + 2 * (dk & 7));
+          const s16x4 lh[2] = {lo, hi};
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(lh);
+#pragma unroll
+          for (int s = 0; s < 2; ++s) ST[s][t] = mfma_bf16(a, DTB[s][kk], ST[s][t]);
+        }
+      }
+      // O^T (second part): diag(gam) then + Dl^T M^T (M lower triangular)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int row = 16 * nt + r;
+        const float gm = S.gam[row];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) OT[s][nt] *= gm;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          if (kk == 1 && nt < 2) continue;
+          const bf16x8 bm = *reinterpret_cast<const bf16x8*>(S.M + row * 128 + 16 * ((4 * kk + g) ^ swz(row)));
+#pragma unroll
+          for (int s = 0; s < 2; ++s) OT[s][nt] = mfma_bf16(DB[s][kk], bm, OT[s][nt]);
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) OB[s][nt][e] = (bf16)OT[s][nt][e];
+        if constexpr (GATED) {
+          // per-token sum of o^2 over this wave's 32 rows
+          float ss = 0.f;
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ss += OT[s][nt][e] * OT[s][nt][e];
+          ss += __shfl_xor(ss, 16, 64);
+          ss += __shfl_xor(ss, 32, 64);
+          if (g == 0) sm.part[i % 3][w][row] = ss;
+        }
+      }
+      ptok0 = tok0;
+      pL = L;
+    }
+    wait_vm<0>();                                  // the stores issued at the start of this iteration
+    barrier_lds();
+  }
+  if (ht) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const size_t hrow = (((size_t)seq * Hv + h) * kD + dvw + 16 * s + r) * kD;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) store_state4(ht, hrow + prow(t, 4 * g), ST[s][t], sbf);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- varlen table
 // Builds, from cu_seqlens, the chunk table {first token, length} and the first
 // chunk of every sequence.  Values are clamped to [0, T_tot] and the table to
@@ -1080,9 +1484,10 @@ __global__ __launch_bounds__(256) void varlen_table_kernel(const int32_t* __rest
 // ---------------------------------------------------------------- gated output
 // In place on a bf16 output o [rows = tokens x value heads][128]:
 //   y = o / sqrt(mean_d(o^2) + eps) * w * sigmoid(gate)
-// (RMS normalisation over the head dim, then the sigmoid output gate).  The
-// bf16 scan leaves each head's 128 channels spread over four workgroups, so
-// this runs as its own bandwidth-bound pass: 16 lanes per row, 8 channels
+// (RMS normalisation over the head dim, then the sigmoid output gate), after
+// the split scan, which leaves each head's 128 channels spread over four
+// workgroups (calls with few (sequence, head) pairs; the head-wide scan
+// applies the epilogue itself).  A bandwidth-bound pass: 16 lanes per row, 8 channels
 // (16 bytes) each, 16 rows per workgroup, sums of squares by xor shuffles
 // inside the 16-lane group.
 __global__ __launch_bounds__(256) void gate_norm_kernel(bf16* __restrict__ o,
@@ -1163,9 +1568,33 @@ static hipError_t launch_scan_split(const PrefillLaunch& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// (sequence, value head) pairs from which the plain bf16 scan runs head-wide
+constexpr int64_t kHeadScanMinPairs = 256;
+
+template <bool GATED>
+static hipError_t launch_scan_head(const PrefillLaunch& a, hipStream_t st) {
+  if (a.nseq <= 0) return hipSuccess;
+  Work<bf16> ws{(bf16*)a.Tt, (bf16*)a.M, a.gam, a.dec, nullptr};
+  int nlin = a.Hv;
+  if ((a.Hqk & 7) == 0) nlin = ((nlin + 7) / 8) * 8;
+  dim3 grid((unsigned)nlin, (unsigned)a.nseq), block(64 * hw::kWaves);
+  hipLaunchKernelGGL(scan_head_kernel<GATED>, grid, block, 0, st, (const bf16*)a.q,
+                     (const bf16*)a.k, (const bf16*)a.v, a.h0, (bf16*)a.o, a.ht, a.state_bf16,
+                     (const bf16*)a.gate, a.norm_w, a.norm_eps, ws, a.cm, a.Hqk, a.Hv,
+                     a.Hv / a.Hqk);
+  return hipGetLastError();
+}
+
 hipError_t launch_scan(const PrefillLaunch& a, hipStream_t st) {
   if (!a.bf16_io)
     return a.gate ? launch_scan_t<float, 8, true>(a, st) : launch_scan_t<float, 4, false>(a, st);
+  // bf16: calls with enough (sequence, head) pairs to fill the chip run the
+  // head-wide scan (four chain waves per CU against the split scan's two,
+  // and the gated epilogue inside it); smaller ones the split scan, whose
+  // gated output then takes a separate pass.  The backward's state
+  // checkpoints come from the split scan.
+  const bool wide = !a.states && (int64_t)a.nseq * a.Hv >= kHeadScanMinPairs;
+  if (wide) return a.gate ? launch_scan_head<true>(a, st) : launch_scan_head<false>(a, st);
   hipError_t e = launch_scan_split(a, st);
   if (e != hipSuccess || !a.gate || a.ntok == 0) return e;
   const int64_t nrows = a.ntok * a.Hv;

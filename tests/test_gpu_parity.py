@@ -426,6 +426,64 @@ def test_varlen_equals_separate_calls(gdn):
         assert torch.equal(ht_n[0], ht[n])
 
 
+# ------------------------------------------------------------------ head-wide scan
+# bf16 calls with at least 256 (sequence, value head) pairs run the head-wide
+# scan (one workgroup per head and sequence, gated epilogue inside); smaller
+# calls run the split scan (and a separate gated pass).  Both perform the same
+# products in the same order, so their plain outputs agree bit for bit.
+
+def test_head_scan_equals_split_scan_bitwise(gdn):
+    lengths = [200, 64, 1, 333, 129, 70]                   # 6 x 48 = 288 pairs
+    inp = synth.varlen_inputs(lengths, dtype=torch.bfloat16, seed=91, h0_std=0.05, gate=False)
+    d = to_dev(inp)
+    o, ht = gdn.prefill_varlen(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["cu_seqlens"],
+                               d["h0"])
+    cu = inp["cu_seqlens"].tolist()
+    for n in range(len(lengths)):                          # 48 pairs each: split scan
+        s, e = cu[n], cu[n + 1]
+        o_n, ht_n = gdn.prefill_chunked(*(x[None, s:e].contiguous() for x in
+                                          (d["q"], d["k"], d["v"], d["alpha"], d["beta"])),
+                                        d["h0"][n:n + 1].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(o_n[0], o[s:e]), n
+        assert torch.equal(ht_n[0], ht[n]), n
+
+
+@pytest.mark.parametrize("B,T,Hqk,Hv", [(6, 150, 16, 48), (4, 100, 4, 64), (3, 70, 32, 96)])
+def test_head_scan_against_oracle(gdn, B, T, Hqk, Hv):
+    say("head scan", B, T, Hqk, Hv)
+    inp = synth.prefill_inputs(B, T, torch.bfloat16, seed=92 + T, h0_std=0.05, Hqk=Hqk, Hv=Hv)
+    o, ht = run_prefill(gdn, inp)
+    o_ref, ht_ref = oracle_prefill(inp)
+    eo, eh = worst_head(o, o_ref, 2), worst_head(ht, ht_ref, 1)
+    say("  worst head rel o %.3e ht %.3e" % (eo, eh))
+    assert eo <= 2e-2 and eh <= 2e-2
+
+
+# one sequence (48 pairs): split scan + the separate gated pass; six
+# sequences (288 pairs): the head-wide scan with the epilogue inside
+@pytest.mark.parametrize("lengths", [[300], [64, 1, 130, 0, 77, 200]])
+def test_head_scan_gated_strong_decay(gdn, lengths):
+    inp = synth.varlen_inputs(lengths, dtype=torch.bfloat16, seed=93, h0_std=0.05, gate=True,
+                              strong_decay=True)
+    d = to_dev(inp)
+    w = torch.linspace(1.5, 0.5, 128)
+    y, ht = gdn.prefill_varlen(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["cu_seqlens"],
+                               d["h0"], gate=d["gate"], norm_weight=w.to(DEV), norm_eps=1e-6)
+    torch.cuda.synchronize()
+    y_ref, ht_ref = oracle.varlen(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"],
+                                  inp["cu_seqlens"].numpy(), inp["h0"], gate=inp["gate"],
+                                  norm_weight=w.numpy(), eps=1e-6)
+    cu = inp["cu_seqlens"].tolist()
+    for n in range(len(lengths)):
+        s, e = cu[n], cu[n + 1]
+        if e > s:
+            ey = worst_head(y[s:e], y_ref[s:e], 1)
+            say("  gated seq %d worst head rel %.3e" % (n, ey))
+            assert ey <= 2e-2, n
+        assert worst_head(ht[n], ht_ref[n], 0) <= 2e-2, n
+
+
 # ------------------------------------------------------------------ full-size workloads
 def test_config0_T256_fp32(gdn):
     c = synth.CONFIGS[0]
