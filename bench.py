@@ -75,7 +75,7 @@ def decode_state_bytes(B):
 
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_bytes_prefill_T8192_decode_B64.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_bytes_bench_workloads.md")
 
 
 def sources_hash(names):
@@ -106,7 +106,7 @@ def counted_traffic(kernel):
     return None
 
 
-MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_ops_prefill_T8192.md")
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_ops_bench_workloads.md")
 
 
 def counted_mfma_gflop():
@@ -483,7 +483,7 @@ def main():
                      "achieved": scan_tflops if dominant == "scan" else None,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": (scan_tflops / PEAK_BF16_TFLOPS) if dominant == "scan" else None,
-                     "traffic": counted_traffic("scan_split_kernel") if dominant == "scan" else None,
+                     "traffic": counted_traffic("scan_split_kernel<false>") if dominant == "scan" else None,
                      "algorithmic_bytes": scan_bytes(T),
                      "hbm_gbs": scan_bytes(T) / (pre["scan_ms"] * 1e-3) / 1e9},
         "decode": {"metric": "decode state GB/s", "value": dec["gbs"], "unit": "GB/s",
@@ -492,7 +492,7 @@ def main():
                                "bf16 q/k/v",
                    "roofline": {"bound": "hbm", "achieved": dec["gbs"], "peak": PEAK_HBM_GBS,
                                 "unit": "GB/s", "frac": dec["gbs"] / PEAK_HBM_GBS,
-                                "traffic": counted_traffic("decode_step_kernel")},
+                                "traffic": counted_traffic("decode_step_kernel@B64")},
                    "dram_diagnostic_B256": {"ms_per_step": dec256["step_ms"], "gbs": dec256["gbs"],
                                             "frac": dec256["gbs"] / PEAK_HBM_GBS},
                    "bf16_state": {"ms_per_step": decb["step_ms"], "gbs": decb["gbs"],
@@ -564,7 +564,10 @@ def main():
             res["gated" if gated else "plain"] = {"ms": ms, "tokens_per_s": T4 / (ms * 1e-3)}
             log("varlen %s: %.3f ms, %.1f M tokens/s" % ("gated" if gated else "plain", ms,
                                                          T4 / ms / 1e3))
+        res["plain"]["traffic"] = counted_traffic("scan_head_kernel<false>")
+        res["gated"]["traffic"] = counted_traffic("scan_head_kernel<true>")
         out["varlen_8_sequences"] = dict(tokens=T4, lengths=[int(x) for x in inp4["lengths"]],
+                                         scan="head-wide (one workgroup per head and sequence)",
                                          **res)
         del inp4
     if not args.no_cpu_baseline:
