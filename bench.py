@@ -352,11 +352,14 @@ def cpu_baseline(inp, T_sample, min_seconds=10.0, max_calls=64):
 
 
 def cpu_single_thread(T_sample=256):
-    """The same oracle on one thread: a child process pinned to one CPU
-    (sched_setaffinity before anything loads OpenMP) whose oracle runs a team
-    of one thread (OMP_NUM_THREADS=1 and the oracle's own omp_set_num_threads),
-    on the first T_sample tokens, for about five seconds of work.  It reports
-    the team size the oracle's parallel region actually ran with."""
+    """The same oracle on one core: a child process pinned to one CPU
+    (sched_setaffinity before anything loads OpenMP) that calls the oracle one
+    value head at a time (oracle.subset_heads), so that each call holds a
+    single chain and one thread does all the work whatever team size the
+    OpenMP runtime uses; the first T_sample tokens of all 48 heads, repeated
+    for about five seconds.  It reports the team size the oracle's parallel
+    region ran with (a team larger than one shares the one CPU and has one
+    chain to run)."""
     import subprocess
     code = ("import os\n"
             "cpu = sorted(os.sched_getaffinity(0))[0]\n"
@@ -366,22 +369,26 @@ def cpu_single_thread(T_sample=256):
             "oracle.set_num_threads(1)\n"
             "d = synth.config_inputs(1)\n"
             "sl = {k: d[k][:, :%d] for k in ('q', 'k', 'v', 'alpha', 'beta')}\n"
+            "subs = [oracle.subset_heads(sl['q'], sl['k'], sl['v'], sl['alpha'], sl['beta'], None,\n"
+            "                            [h], 16, 48) for h in range(48)]\n"
             "n, t = 0, 0.0\n"
             "while t < 5.0 and n < 64:\n"
             "    t0 = time.perf_counter()\n"
-            "    oracle.prefill(sl['q'], sl['k'], sl['v'], sl['alpha'], sl['beta'], None)\n"
+            "    for sub in subs:\n"
+            "        oracle.prefill(*sub)\n"
             "    t += time.perf_counter() - t0\n"
             "    n += 1\n"
             "print(n * %d / t, oracle.num_threads(), len(os.sched_getaffinity(0)))\n"
             % (T_sample, T_sample))
-    env = dict(os.environ, OMP_NUM_THREADS="1", CUDA_VISIBLE_DEVICES="", HIP_VISIBLE_DEVICES="")
+    env = dict(os.environ, OMP_NUM_THREADS="1", OMP_WAIT_POLICY="PASSIVE", GOMP_SPINCOUNT="0",
+               CUDA_VISIBLE_DEVICES="", HIP_VISIBLE_DEVICES="")
     try:
         out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
                              text=True, timeout=120)
         rate, nthr, ncpu = out.stdout.strip().splitlines()[-1].split()
-        return dict(value=float(rate), unit="tokens/s", cores=int(ncpu), threads=int(nthr),
-                    sample="first %d of 8192 tokens, all 48 value heads, float64, pinned to "
-                           "one CPU" % T_sample)
+        return dict(value=float(rate), unit="tokens/s", cores=int(ncpu), team_size=int(nthr),
+                    sample="first %d of 8192 tokens, all 48 value heads one head per call, "
+                           "float64, pinned to one CPU" % T_sample)
     except Exception as e:  # reported, never fatal: it is a side figure
         return dict(value=None, error=str(e)[:200])
 
