@@ -59,7 +59,7 @@ template <typename E>
 __global__ __launch_bounds__(64 * kPrepWaves) void attn_prep_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ qw, const float* __restrict__ kw, float eps, int rope_dim,
-    double log2_theta, const int32_t* __restrict__ pos, E* __restrict__ qo, E* __restrict__ kc,
+    double fstep, const int32_t* __restrict__ pos, E* __restrict__ qo, E* __restrict__ kc,
     E* __restrict__ vc, int64_t ntok, int T, int cache_len, int Hq, int Hkv) {
   // one workgroup per token: its Hq + Hkv rows share one position, so each
   // lane forms its rotation's sin and cos once and applies them to every row
@@ -75,12 +75,19 @@ __global__ __launch_bounds__(64 * kPrepWaves) void attn_prep_kernel(
   float cs[4] = {1.f, 1.f, 1.f, 1.f}, sn[4] = {0.f, 0.f, 0.f, 0.f};
   if (rot) {
     const int jl = first ? l : l - hl;
+    // frequency j is theta^(-2j / rope_dim) = fstep^j (fstep = theta^(-2 /
+    // rope_dim), formed on the host): fstep^(4 jl) by repeated squaring, then
+    // one more factor per i; the rounding of these fp64 products (~1e-15
+    // relative) is far below the fp32 rounding of the reduced angle
+    double fb = 1.0, sq = fstep;
+    for (int e = 4 * jl; e; e >>= 1, sq *= sq)
+      if (e & 1) fb *= sq;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i, fb *= fstep) {
       // theta^(-2j / rope_dim) / (2 pi) turns per position, the angle reduced
       // in fp64 (at position 262,143 an fp32 angle would be off by ~1e-2 rad),
       // then the hardware sin and cos, which take turns
-      const double fq = exp2(-(2.0 * (4 * jl + i) / rope_dim) * log2_theta) * 0.15915494309189535;
+      const double fq = fb * 0.15915494309189535;
       double rev = (double)p * fq;
       rev -= rint(rev);
       sn[i] = __builtin_amdgcn_sinf((float)rev);
@@ -664,7 +671,8 @@ static hipError_t attn_launch_t(const AttnLaunch& a, hipStream_t st) {
   const int64_t ntok = a.decode ? a.B : (int64_t)a.B * a.T;
   hipLaunchKernelGGL((attn_prep_kernel<E>), dim3((unsigned)ntok), dim3(64 * kPrepWaves), 0, st,
                      (const E*)a.q, (const E*)a.k, (const E*)a.v, a.qw, a.kw, a.eps, a.rope_dim,
-                     std::log2((double)a.theta), a.decode ? a.pos : nullptr, (E*)a.qrot, (E*)a.kc, (E*)a.vc_write, ntok,
+                     a.rope_dim > 0 ? std::pow((double)a.theta, -2.0 / a.rope_dim) : 1.0,
+                     a.decode ? a.pos : nullptr, (E*)a.qrot, (E*)a.kc, (E*)a.vc_write, ntok,
                      a.decode ? 1 : a.T, a.cache_len, a.Hq, a.Hkv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
