@@ -865,12 +865,6 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
     barrier_lds();
     for (int i = 0; i <= nch; ++i) {
       if (i < nch) {
-        if constexpr (CKPT) {
-          // the state entering chunk i, for the backward pass
-          const size_t srow = (((size_t)(cid0 + i) * Hv + h) * kD + dv0 + r) * kD;
-#pragma unroll
-          for (int t = 0; t < 8; ++t) store_state4(states, srow + prow(t, 4 * g), ST[t], true);
-        }
         const Slot& S = sm.slot[i % kSlots];
         const GateSlot& Gd = sm.gd[i % kGdSlots];
         Hand& H = sm.hand[i & 1][s];
@@ -985,10 +979,25 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
   }
 
   // -------------------------------------------------------------- output wave
-  // Chunk c's O at iteration c+1 for both value slices (no outputs in the
-  // state-checkpoint pass of the backward).
+  // Chunk c's O at iteration c+1 for both value slices.  In the
+  // state-checkpoint pass of the backward there are no outputs: instead this
+  // wave stores the state entering chunk c (bf16), from the fragments the
+  // chain waves hand over, so that the chain waves issue no global stores.
   barrier_lds();
   for (int i = 0; i <= nch; ++i) {
+    if (i >= 1 && CKPT) {
+      const int c = i - 1;
+#pragma unroll
+      for (int s = 0; s < kSlices; ++s) {
+        // lane (r, g): value row dvb + 16s + r; its fragment kk holds d_k
+        // prow(2kk, 4g) .. +3 then prow(2kk + 1, 4g) .. +3, i.e. the eight
+        // consecutive d_k 32kk + 8g .. +7
+        bf16* srow = states + ((((size_t)(cid0 + c) * Hv + h) * kD + dvb + 16 * s + r) * kD);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          *reinterpret_cast<bf16x8*>(srow + 32 * kk + 8 * g) = sm.hand[c & 1][s].sb[kk][l];
+      }
+    }
     if (i >= 1 && !CKPT) {
       const int c = i - 1;
       int tok0, L;
