@@ -1577,8 +1577,11 @@ static hipError_t launch_scan_split(const PrefillLaunch& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// (sequence, value head) pairs from which the plain bf16 scan runs head-wide
-constexpr int64_t kHeadScanMinPairs = 256;
+// (sequence, value head) pairs from which the bf16 scan runs head-wide: from
+// 128 pairs the split scan needs two full rounds of one-per-CU workgroups
+// (measured at T = 8192: 96 pairs split 0.404 ms / head-wide 0.440; 144 pairs
+// 0.585 / 0.451).
+constexpr int64_t kHeadScanMinPairs = 128;
 
 template <bool GATED>
 static hipError_t launch_scan_head(const PrefillLaunch& a, hipStream_t st) {

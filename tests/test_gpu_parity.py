@@ -427,13 +427,13 @@ def test_varlen_equals_separate_calls(gdn):
 
 
 # ------------------------------------------------------------------ head-wide scan
-# bf16 calls with at least 256 (sequence, value head) pairs run the head-wide
+# bf16 calls with at least 128 (sequence, value head) pairs run the head-wide
 # scan (one workgroup per head and sequence, gated epilogue inside); smaller
 # calls run the split scan (and a separate gated pass).  Both perform the same
 # products in the same order, so their plain outputs agree bit for bit.
 
 def test_head_scan_equals_split_scan_bitwise(gdn):
-    lengths = [200, 64, 1, 333, 129, 70]                   # 6 x 48 = 288 pairs
+    lengths = [200, 64, 1, 333, 129, 70]                   # 6 x 48 = 288 pairs: head-wide
     inp = synth.varlen_inputs(lengths, dtype=torch.bfloat16, seed=91, h0_std=0.05, gate=False)
     d = to_dev(inp)
     o, ht = gdn.prefill_varlen(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["cu_seqlens"],
@@ -449,7 +449,8 @@ def test_head_scan_equals_split_scan_bitwise(gdn):
         assert torch.equal(ht_n[0], ht[n]), n
 
 
-@pytest.mark.parametrize("B,T,Hqk,Hv", [(6, 150, 16, 48), (4, 100, 4, 64), (3, 70, 32, 96)])
+@pytest.mark.parametrize("B,T,Hqk,Hv", [(6, 150, 16, 48), (4, 100, 4, 64), (3, 70, 32, 96),
+                                         (2, 90, 16, 64)])     # 128 pairs: the threshold
 def test_head_scan_against_oracle(gdn, B, T, Hqk, Hv):
     say("head scan", B, T, Hqk, Hv)
     inp = synth.prefill_inputs(B, T, torch.bfloat16, seed=92 + T, h0_std=0.05, Hqk=Hqk, Hv=Hv)
