@@ -259,39 +259,44 @@ __global__ __launch_bounds__(64 * NW) void bwd_chain_kernel(
   }
 }
 
-// Operand buffer of the bf16 reverse chain (bwd_chain_split_kernel below),
+// Operand buffers of the bf16 reverse chain (bwd_chain_split_kernel below),
 // filled by copies straight into LDS (global_load_lds_dwordx4: no registers,
-// no VALU) and double-buffered: the copies of chunk j-1 are in flight while
-// chunk j is computed.  Copy instruction `it`
-// of a tile fills LDS bytes [1024 it, 1024 it + 1024); lane l's 16 bytes are
-// the piece of the swizzled layout at that position, so each lane reads the
-// global piece the swizzle puts there.  Rows beyond the chunk's length repeat
-// its last token: such tokens get a zero gamma wherever they could reach the
-// state gradient (the gamma-scaled dO and the beta-scaled Y), and the mask
-// matrix M, written by prepare from zero rows, is zero there.
-template <int NW>
-struct ChainDmaBuf {
-  static constexpr int R = 16 * NW;
+// no VALU).  Copy instruction `it` of a tile fills LDS bytes [1024 it, 1024 it
+// + 1024); lane l's 16 bytes are the piece of the swizzled layout at that
+// position, so each lane reads the global piece the swizzle puts there.  Rows
+// beyond the chunk's length repeat its last token: such tokens get a zero
+// gamma wherever they could reach the state gradient (the gamma-scaled dO and
+// the beta-scaled Y), and the mask matrix M, written by prepare from zero
+// rows, is zero there.
+struct ChainOps {                 // what the chain waves read for chunk j
   bf16 K[kC * kD];
+  bf16 N[kC * kC];
+  float gm[kC], dc[kC], bt[kC];
+};
+template <int NW>
+struct HelperOps {                // what the helper waves read for chunk j
+  static constexpr int R = 16 * NW;
   bf16 Q[kC * kD];
   bf16 O[kC * R];
-  bf16 N[kC * kC];
   bf16 M[kC * kC];
-  float gm[kC], dc[kC], bt[kC];
+  float gm[kC];
 };
 
 // bf16 reverse chain with a role split, as the forward scan has: per
 // workgroup two 16-row value slices; waves 0-1 are chain waves (slice s = w),
-// waves 2-3 helpers (slice s = w - 2).  The helpers issue every copy and take
-// the two state-independent products off the chain:
-//   helpers:  copies of chunk j-1; MdO = M^T dO[:, slice] -> LDS; barrier A;
-//             U = (gamma Q)^T dO[:, slice] -> LDS; barrier B; their copies
-//             complete; barrier C
+// waves 2-3 helpers (slice s = w - 2).  The helpers issue every copy and form
+// the two state-independent products of each chunk a chunk ahead of the
+// chain, so that the chain never waits for them.  In the iteration of chunk j
+// (chunks run from the last to the first), with one barrier at its end:
 //   chain:    store dS (the gradient of the state leaving chunk j); P = K dS^T;
-//             barrier A; dDl = MdO + diag(dec) P; Y = N^T dDl; Z = -gamma beta Y;
-//             barrier B; dS^T <- gamma_L dS^T + U + K^T Z; barrier C
-// so a chain wave issues 38 MFMAs per chunk instead of 64.  A hand-off tile is
-// written after the barrier that ends the iteration in which it was last read.
+//             dDl = MdO_j + diag(dec) P; Y = N^T dDl; Z = -gamma beta Y;
+//             dS^T <- gamma_L dS^T + U_j + K^T Z
+//   helpers:  MdO_{j-1} = M^T dO[:, slice] and U_{j-1} = (gamma Q)^T dO[:, slice]
+//             into the other hand-off buffer; copies of the chain's operands of
+//             chunk j-1 and of their own operands of chunk j-2
+// Chain operands, helper operands and hand-off tiles each have two buffers,
+// chunk j's in buffer (Nc - 1 - j) % 2.  A chain wave issues 38 MFMAs per
+// chunk instead of 64.
 struct SplitHand {
   f32x4 mdo[2][4][64];    // [slice][token tile][lane]: M^T dO, 64 tokens x 16 rows
   f32x4 u[2][8][64];      // [slice][d_k tile][lane]: (gamma Q)^T dO, transposed like dS^T
@@ -304,8 +309,9 @@ __global__ __launch_bounds__(256) void bwd_chain_split_kernel(
     const float* __restrict__ dec, bf16* __restrict__ dSc, ChunkMap cm, int Hqk, int Hv) {
   typedef bf16 E;
   constexpr int NS = 2, R = 16 * NS, KB = 32;
-  __shared__ ChainDmaBuf<NS> buf[2];
-  __shared__ SplitHand hand;
+  __shared__ ChainOps cbuf[2];
+  __shared__ HelperOps<NS> hbuf[2];
+  __shared__ SplitHand hand[2];
   const int w = __builtin_amdgcn_readfirstlane(wave_id()), l = lane_id(), r = l & 15, g = l >> 4;
   const bool is_chain = w < NS;
   const int sl = is_chain ? w : w - NS;                 // this wave's slice
@@ -313,26 +319,75 @@ __global__ __launch_bounds__(256) void bwd_chain_split_kernel(
   int cid0, Nc;
   seq_chunks(cm, b, cid0, Nc);
   const int rbase = R * blockIdx.x, dv0 = rbase + 16 * sl;
+  const int hw = w - NS;                                // helper index
 
-  // copies of chunk j into buffer bi, by the two helper waves
-  auto issue = [&](int j, auto bic) {
-    ChainDmaBuf<NS>& B_ = buf[decltype(bic)::value];
+  // copies of chunk j, by the two helper waves
+  auto issue_chain = [&](int j, auto bic) {
+    ChainOps& B_ = cbuf[decltype(bic)::value];
     const int cid = cid0 + j;
     int tok0i, L;
     chunk_of(cm, cid, tok0i, L);
     const size_t tok0 = (size_t)tok0i;
     const size_t hc = (size_t)cid * Hv + h;
-    const int hw = w - NS;
     copy_rows<128>(k + (tok0 * Hqk + gq) * kD, (int64_t)Hqk * kD, L, B_.K, hw, NS);
-    copy_rows<128>(q + (tok0 * Hqk + gq) * kD, (int64_t)Hqk * kD, L, B_.Q, hw, NS);
-    copy_rows<R>(dout + (tok0 * Hv + h) * kD + rbase, (int64_t)Hv * kD, L, B_.O, hw, NS);
     copy_rows<64>(Nw + hc * kC * kC, kC, kC, B_.N, hw, NS);
-    copy_rows<64>(Mw + hc * kC * kC, kC, kC, B_.M, hw, NS);
     if (hw == 0) {
       dma4(gam + hc * kC + l, B_.gm);
       dma4(beta + (tok0 + min(l, L - 1)) * Hv + h, B_.bt);
     } else {
       dma4(dec + hc * kC + l, B_.dc);
+    }
+  };
+  auto issue_help = [&](int j, auto bic) {
+    HelperOps<NS>& B_ = hbuf[decltype(bic)::value];
+    const int cid = cid0 + j;
+    int tok0i, L;
+    chunk_of(cm, cid, tok0i, L);
+    const size_t tok0 = (size_t)tok0i;
+    const size_t hc = (size_t)cid * Hv + h;
+    copy_rows<128>(q + (tok0 * Hqk + gq) * kD, (int64_t)Hqk * kD, L, B_.Q, hw, NS);
+    copy_rows<R>(dout + (tok0 * Hv + h) * kD + rbase, (int64_t)Hv * kD, L, B_.O, hw, NS);
+    copy_rows<64>(Mw + hc * kC * kC, kC, kC, B_.M, hw, NS);
+    if (hw == 0) dma4(gam + hc * kC + l, B_.gm);
+  };
+  // helpers: M^T dO and (gamma Q)^T dO of chunk j from hbuf[bi] into hand[bi]
+  auto helper_products = [&](int j, auto bic) {
+    constexpr int bi = decltype(bic)::value;
+    int tok0i, L;
+    chunk_of(cm, cid0 + j, tok0i, L);
+    const HelperOps<NS>& B_ = hbuf[bi];
+    const Lds<E, 128> Qs{const_cast<E*>(B_.Q)};
+    const Lds<E, R> Os{const_cast<E*>(B_.O)};
+    const Lds<E, 64> Ms{const_cast<E*>(B_.M)};
+    // dO fragments of this slice (B operand, K = tokens), plain and
+    // gamma-scaled (masked)
+    bf16x8 OB[2], OG[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      OB[kb] = Os.cm(16 * sl + r, KB * kb);
+      const f32x4 g0 = *reinterpret_cast<const f32x4*>(&B_.gm[KB * kb + 4 * g]);
+      const f32x4 g1 = *reinterpret_cast<const f32x4*>(&B_.gm[KB * kb + 16 + 4 * g]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int tok = KB * kb + kslot<E>(g, e);
+        const float gv = e < 4 ? g0[e] : g1[e - 4];
+        OG[kb][e] = (bf16)((tok < L ? gv : 0.f) * (float)OB[kb][e]);
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x4 m = zero4();
+#pragma unroll
+      for (int kb = 0; kb < kC / KB; ++kb)
+        if (!blk_below<E>(mt, kb)) m = mma(m, Ms.cm(16 * mt + r, KB * kb), OB[kb]);
+      hand[bi].mdo[sl][mt][l] = m;
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      f32x4 u = zero4();
+#pragma unroll
+      for (int kb = 0; kb < kC / KB; ++kb) u = mma(u, Qs.cm(16 * t + r, KB * kb), OG[kb]);
+      hand[bi].u[sl][t][l] = u;
     }
   };
 
@@ -344,20 +399,28 @@ __global__ __launch_bounds__(256) void bwd_chain_split_kernel(
                               : zero4();
   const std::integral_constant<int, 0> ic0{};
   const std::integral_constant<int, 1> ic1{};
-  if (!is_chain && Nc > 0) issue(Nc - 1, ic0);
+  // chunk Nc-1: chain and helper operands in buffer 0; chunk Nc-2's helper
+  // operands in buffer 1; the products of chunk Nc-1
+  if (!is_chain && Nc > 0) {
+    issue_chain(Nc - 1, ic0);
+    issue_help(Nc - 1, ic0);
+    if (Nc > 1) issue_help(Nc - 2, ic1);
+  }
   wait_copies();
+  barrier_lds();
+  if (!is_chain && Nc > 0) helper_products(Nc - 1, ic0);
   barrier_lds();
 
   auto step = [&](int j, auto bic) {
     constexpr int bi = decltype(bic)::value;
-    const int cid = cid0 + j;
-    int tok0i, L;
-    chunk_of(cm, cid, tok0i, L);
-    const ChainDmaBuf<NS>& B_ = buf[bi];
-    const Lds<E, 128> Ks{const_cast<E*>(B_.K)}, Qs{const_cast<E*>(B_.Q)};
-    const Lds<E, R> Os{const_cast<E*>(B_.O)};
-    const Lds<E, 64> Ns{const_cast<E*>(B_.N)}, Ms{const_cast<E*>(B_.M)};
+    const std::integral_constant<int, 1 - bi> nbic{};
     if (is_chain) {
+      const int cid = cid0 + j;
+      int tok0i, L;
+      chunk_of(cm, cid, tok0i, L);
+      const ChainOps& B_ = cbuf[bi];
+      const Lds<E, 128> Ks{const_cast<E*>(B_.K)};
+      const Lds<E, 64> Ns{const_cast<E*>(B_.N)};
       const size_t hc = (size_t)cid * Hv + h;
       E* ddst = dSc + (hc * kD + dv0 + r) * kD;
 #pragma unroll
@@ -371,12 +434,11 @@ __global__ __launch_bounds__(256) void bwd_chain_split_kernel(
         for (int kb = 0; kb < kD / KB; ++kb) p = mma(p, Ks.rm(16 * mt + r, KB * kb), acc_frag<E>(DT, kb));
         P[mt] = p;
       }
-      barrier_lds();                                   // A: M^T dO ready
       f32x4 dD[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const f32x4 dc4 = *reinterpret_cast<const f32x4*>(&B_.dc[16 * mt + 4 * g]);
-        const f32x4 m = hand.mdo[sl][mt][l];
+        const f32x4 m = hand[bi].mdo[sl][mt][l];
 #pragma unroll
         for (int i = 0; i < 4; ++i) dD[mt][i] = m[i] + dc4[i] * P[mt][i];
       }
@@ -395,53 +457,21 @@ __global__ __launch_bounds__(256) void bwd_chain_split_kernel(
           Z[mt][i] = (tok < L ? -g4[i] * b4[i] : 0.f) * y[i];
         }
       }
-      barrier_lds();                                   // B: (gamma Q)^T dO ready
       const float gl = B_.gm[kC - 1];
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        f32x4 a = DT[t] * gl + hand.u[sl][t][l];
+        f32x4 a = DT[t] * gl + hand[bi].u[sl][t][l];
 #pragma unroll
         for (int kb = 0; kb < kC / KB; ++kb) a = mma(a, Ks.cm(16 * t + r, KB * kb), acc_frag<E>(Z, kb));
         DT[t] = a;
       }
-      barrier_lds();                                   // C
     } else {
-      if (j > 0) issue(j - 1, std::integral_constant<int, 1 - bi>{});
-      // dO fragments of this slice (B operand, K = tokens), plain and
-      // gamma-scaled (masked)
-      bf16x8 OB[2], OG[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        OB[kb] = Os.cm(16 * sl + r, KB * kb);
-        const f32x4 g0 = *reinterpret_cast<const f32x4*>(&B_.gm[KB * kb + 4 * g]);
-        const f32x4 g1 = *reinterpret_cast<const f32x4*>(&B_.gm[KB * kb + 16 + 4 * g]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int tok = KB * kb + kslot<E>(g, e);
-          const float gv = e < 4 ? g0[e] : g1[e - 4];
-          OG[kb][e] = (bf16)((tok < L ? gv : 0.f) * (float)OB[kb][e]);
-        }
-      }
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        f32x4 m = zero4();
-#pragma unroll
-        for (int kb = 0; kb < kC / KB; ++kb)
-          if (!blk_below<E>(mt, kb)) m = mma(m, Ms.cm(16 * mt + r, KB * kb), OB[kb]);
-        hand.mdo[sl][mt][l] = m;
-      }
-      barrier_lds();                                   // A
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        f32x4 u = zero4();
-#pragma unroll
-        for (int kb = 0; kb < kC / KB; ++kb) u = mma(u, Qs.cm(16 * t + r, KB * kb), OG[kb]);
-        hand.u[sl][t][l] = u;
-      }
-      barrier_lds();                                   // B
+      if (j >= 1) issue_chain(j - 1, nbic);
+      if (j >= 2) issue_help(j - 2, bic);
+      if (j >= 1) helper_products(j - 1, nbic);
       wait_copies();
-      barrier_lds();                                   // C
     }
+    barrier_lds();
   };
   int j = Nc - 1;
   for (; j >= 1; j -= 2) {
