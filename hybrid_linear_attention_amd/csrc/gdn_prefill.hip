@@ -987,15 +987,20 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
   for (int i = 0; i <= nch; ++i) {
     if (i >= 1 && CKPT) {
       const int c = i - 1;
+      // Fragment kk of chain lane (r', g') holds d_k prow(2kk, 4g') .. +3 then
+      // prow(2kk + 1, 4g') .. +3, i.e. the eight consecutive d_k 32kk + 8g' ..
+      // +7, of value row 16s + r'.  Each store writes four whole 256-byte rows:
+      // lane l takes row 4j + l/16 and d_k 8p .. +7 (p = l % 16), which chain
+      // lane (4j + l/16, p % 4) holds in fragment p / 4.
+      const int pc = l & 15, rr = l >> 4;
 #pragma unroll
       for (int s = 0; s < kSlices; ++s) {
-        // lane (r, g): value row dvb + 16s + r; its fragment kk holds d_k
-        // prow(2kk, 4g) .. +3 then prow(2kk + 1, 4g) .. +3, i.e. the eight
-        // consecutive d_k 32kk + 8g .. +7
-        bf16* srow = states + ((((size_t)(cid0 + c) * Hv + h) * kD + dvb + 16 * s + r) * kD);
+        bf16* sbase = states + ((((size_t)(cid0 + c) * Hv + h) * kD + dvb + 16 * s) * kD) + 8 * pc;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          *reinterpret_cast<bf16x8*>(srow + 32 * kk + 8 * g) = sm.hand[c & 1][s].sb[kk][l];
+        for (int j = 0; j < 4; ++j) {
+          const int row = 4 * j + rr;
+          *reinterpret_cast<bf16x8*>(sbase + (size_t)row * kD) = sm.hand[c & 1][s].sb[pc >> 2][row + 16 * (pc & 3)];
+        }
       }
     }
     if (i >= 1 && !CKPT) {
