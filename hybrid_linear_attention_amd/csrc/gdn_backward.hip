@@ -284,7 +284,8 @@ struct HelperOps {                // what the helper waves read for chunk j
 
 // bf16 reverse chain with a role split, as the forward scan has: per
 // workgroup two 16-row value slices; waves 0-1 are chain waves (slice s = w),
-// waves 2-3 helpers (slice s = w - 2).  The helpers issue every copy and form
+// waves 2-3 helpers (slice s = w - 2), waves 4-5 copy waves (the chain's
+// operands, the helpers' operands).  The helpers form
 // the two state-independent products of each chunk a chunk ahead of the
 // chain, so that the chain never waits for them.  In the iteration of chunk j
 // (chunks run from the last to the first), with one barrier at its end:
@@ -292,17 +293,21 @@ struct HelperOps {                // what the helper waves read for chunk j
 //             dDl = MdO_j + diag(dec) P; Y = N^T dDl; Z = -gamma beta Y;
 //             dS^T <- gamma_L dS^T + U_j + K^T Z
 //   helpers:  MdO_{j-1} = M^T dO[:, slice] and U_{j-1} = (gamma Q)^T dO[:, slice]
-//             into the other hand-off buffer; copies of the chain's operands of
-//             chunk j-1 and of their own operands of chunk j-2
-// Chain operands, helper operands and hand-off tiles each have two buffers,
-// chunk j's in buffer (Nc - 1 - j) % 2.  A chain wave issues 38 MFMAs per
-// chunk instead of 64.
+//             into the other hand-off buffer
+//   copies:   the chain's operands of chunk j-1 and the helpers' of chunk j-2
+// The copies have waves of their own because a wave's later LDS accesses are
+// ordered after its outstanding copies into LDS: a helper issuing them would
+// wait for them before its first hand-off write.  The copy waves also touch
+// chunk j-3's operands (one 4-byte copy per 128-byte line), so that their
+// copies two iterations later find them in L2.  Chain operands, helper
+// operands and hand-off tiles each have two buffers, chunk j's in buffer
+// (Nc - 1 - j) % 2.  A chain wave issues 38 MFMAs per chunk instead of 64.
 struct SplitHand {
   f32x4 mdo[2][4][64];    // [slice][token tile][lane]: M^T dO, 64 tokens x 16 rows
   f32x4 u[2][8][64];      // [slice][d_k tile][lane]: (gamma Q)^T dO, transposed like dS^T
 };
 
-__global__ __launch_bounds__(256) void bwd_chain_split_kernel(
+__global__ __launch_bounds__(384) void bwd_chain_split_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ dout,
     const float* __restrict__ beta, const float* __restrict__ dht, float* __restrict__ dh0,
     const bf16* __restrict__ Nw, const bf16* __restrict__ Mw, const float* __restrict__ gam,
@@ -312,16 +317,30 @@ __global__ __launch_bounds__(256) void bwd_chain_split_kernel(
   __shared__ ChainOps cbuf[2];
   __shared__ HelperOps<NS> hbuf[2];
   __shared__ SplitHand hand[2];
+  __shared__ uint32_t warm[2][64];
   const int w = __builtin_amdgcn_readfirstlane(wave_id()), l = lane_id(), r = l & 15, g = l >> 4;
   const bool is_chain = w < NS;
-  const int sl = is_chain ? w : w - NS;                 // this wave's slice
-  const int h = blockIdx.y, b = blockIdx.z, gq = h / (Hv / Hqk);   // b: sequence
+  const int sl = is_chain ? w : w - NS;                 // this wave's slice (waves 0-3)
+  const bool is_copy = w >= 2 * NS;
+  const int cw = w - 2 * NS;                            // copy wave: 0 chain, 1 helper operands
+  // Workgroup -> (value head, row block): the workgroups of one query/key
+  // group (its value heads' row blocks) get consecutive ids of one XCD (ids
+  // are dealt to the 8 XCDs round-robin), so that they share that XCD's L2
+  // for the group's K and Q and each head's N and M.
+  constexpr int NSL = kD / R;
+  const int G = Hv / Hqk, per_group = G * NSL;
+  int lin = blockIdx.x;
+  if ((Hqk & 7) == 0) {
+    const int xcd = lin & 7, jj = lin >> 3;
+    lin = (xcd + 8 * (jj / per_group)) * per_group + (jj - (jj / per_group) * per_group);
+  }
+  if (lin >= Hv * NSL) return;                           // whole workgroup leaves together
+  const int h = lin / NSL, b = blockIdx.y, gq = h / G;   // b: sequence
   int cid0, Nc;
   seq_chunks(cm, b, cid0, Nc);
-  const int rbase = R * blockIdx.x, dv0 = rbase + 16 * sl;
-  const int hw = w - NS;                                // helper index
+  const int rbase = R * (lin - h * NSL), dv0 = rbase + 16 * sl;
 
-  // copies of chunk j, by the two helper waves
+  // copies of chunk j, by the copy wave
   auto issue_chain = [&](int j, auto bic) {
     ChainOps& B_ = cbuf[decltype(bic)::value];
     const int cid = cid0 + j;
@@ -329,14 +348,11 @@ __global__ __launch_bounds__(256) void bwd_chain_split_kernel(
     chunk_of(cm, cid, tok0i, L);
     const size_t tok0 = (size_t)tok0i;
     const size_t hc = (size_t)cid * Hv + h;
-    copy_rows<128>(k + (tok0 * Hqk + gq) * kD, (int64_t)Hqk * kD, L, B_.K, hw, NS);
-    copy_rows<64>(Nw + hc * kC * kC, kC, kC, B_.N, hw, NS);
-    if (hw == 0) {
-      dma4(gam + hc * kC + l, B_.gm);
-      dma4(beta + (tok0 + min(l, L - 1)) * Hv + h, B_.bt);
-    } else {
-      dma4(dec + hc * kC + l, B_.dc);
-    }
+    copy_rows<128>(k + (tok0 * Hqk + gq) * kD, (int64_t)Hqk * kD, L, B_.K, 0, 1);
+    copy_rows<64>(Nw + hc * kC * kC, kC, kC, B_.N, 0, 1);
+    dma4(gam + hc * kC + l, B_.gm);
+    dma4(beta + (tok0 + min(l, L - 1)) * Hv + h, B_.bt);
+    dma4(dec + hc * kC + l, B_.dc);
   };
   auto issue_help = [&](int j, auto bic) {
     HelperOps<NS>& B_ = hbuf[decltype(bic)::value];
@@ -345,10 +361,34 @@ __global__ __launch_bounds__(256) void bwd_chain_split_kernel(
     chunk_of(cm, cid, tok0i, L);
     const size_t tok0 = (size_t)tok0i;
     const size_t hc = (size_t)cid * Hv + h;
-    copy_rows<128>(q + (tok0 * Hqk + gq) * kD, (int64_t)Hqk * kD, L, B_.Q, hw, NS);
-    copy_rows<R>(dout + (tok0 * Hv + h) * kD + rbase, (int64_t)Hv * kD, L, B_.O, hw, NS);
-    copy_rows<64>(Mw + hc * kC * kC, kC, kC, B_.M, hw, NS);
-    if (hw == 0) dma4(gam + hc * kC + l, B_.gm);
+    copy_rows<128>(q + (tok0 * Hqk + gq) * kD, (int64_t)Hqk * kD, L, B_.Q, 0, 1);
+    copy_rows<R>(dout + (tok0 * Hv + h) * kD + rbase, (int64_t)Hv * kD, L, B_.O, 0, 1);
+    copy_rows<64>(Mw + hc * kC * kC, kC, kC, B_.M, 0, 1);
+    dma4(gam + hc * kC + l, B_.gm);
+  };
+  // one 4-byte copy per 128-byte line of chunk j's chain operands (copy
+  // wave 0: 6 copies) or helper operands (copy wave 1: 4) into a scratch word
+  auto touch = [&](int j) {
+    const int cid = cid0 + j;
+    int tok0i, L;
+    chunk_of(cm, cid, tok0i, L);
+    const size_t row = (size_t)tok0i + min(l, L - 1);
+    const size_t hc = (size_t)cid * Hv + h;
+    if (cw == 0) {
+      const bf16* kr = k + (row * Hqk + gq) * kD;
+      dma4(kr, &warm[0][0]);
+      dma4(kr + 64, &warm[0][0]);
+      dma4(Nw + hc * kC * kC + 64 * l, &warm[0][0]);
+      dma4(gam + hc * kC + l, &warm[0][0]);
+      dma4(dec + hc * kC + l, &warm[0][0]);
+      dma4(beta + row * Hv + h, &warm[0][0]);
+    } else {
+      const bf16* qr = q + (row * Hqk + gq) * kD;
+      dma4(qr, &warm[1][0]);
+      dma4(qr + 64, &warm[1][0]);
+      dma4(dout + (row * Hv + h) * kD + rbase, &warm[1][0]);
+      dma4(Mw + hc * kC * kC + 64 * l, &warm[1][0]);
+    }
   };
   // helpers: M^T dO and (gamma Q)^T dO of chunk j from hbuf[bi] into hand[bi]
   auto helper_products = [&](int j, auto bic) {
@@ -401,14 +441,17 @@ __global__ __launch_bounds__(256) void bwd_chain_split_kernel(
   const std::integral_constant<int, 1> ic1{};
   // chunk Nc-1: chain and helper operands in buffer 0; chunk Nc-2's helper
   // operands in buffer 1; the products of chunk Nc-1
-  if (!is_chain && Nc > 0) {
-    issue_chain(Nc - 1, ic0);
-    issue_help(Nc - 1, ic0);
-    if (Nc > 1) issue_help(Nc - 2, ic1);
+  if (is_copy && Nc > 0) {
+    if (cw == 0) {
+      issue_chain(Nc - 1, ic0);
+    } else {
+      issue_help(Nc - 1, ic0);
+      if (Nc > 1) issue_help(Nc - 2, ic1);
+    }
   }
   wait_copies();
   barrier_lds();
-  if (!is_chain && Nc > 0) helper_products(Nc - 1, ic0);
+  if (!is_chain && !is_copy && Nc > 0) helper_products(Nc - 1, ic0);
   barrier_lds();
 
   auto step = [&](int j, auto bic) {
@@ -465,11 +508,24 @@ __global__ __launch_bounds__(256) void bwd_chain_split_kernel(
         for (int kb = 0; kb < kC / KB; ++kb) a = mma(a, Ks.cm(16 * t + r, KB * kb), acc_frag<E>(Z, kb));
         DT[t] = a;
       }
+    } else if (is_copy) {
+      if (cw == 0) {
+        if (j >= 1) issue_chain(j - 1, nbic);
+      } else {
+        if (j >= 2) issue_help(j - 2, bic);
+      }
+      // chunk j-3 (chain operands copied in iteration j-2, helper operands in
+      // j-1): touched after the copies, so that the counted wait leaves only
+      // the touches in flight
+      if (j >= 3) {
+        touch(j - 3);
+        if (cw == 0) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      } else {
+        wait_copies();
+      }
     } else {
-      if (j >= 1) issue_chain(j - 1, nbic);
-      if (j >= 2) issue_help(j - 2, bic);
       if (j >= 1) helper_products(j - 1, nbic);
-      wait_copies();
     }
     barrier_lds();
   };
@@ -1015,7 +1071,7 @@ hipError_t launch_backward(const BackwardLaunch& a, hipStream_t st) {
     typedef bf16 E;
     // the chunk states were written by the forward scan (gdn_api.hip)
     if (!a.states_ready) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(bwd_chain_split_kernel, dim3(kD / 32, a.Hv, a.nseq), dim3(256), 0, st,
+    hipLaunchKernelGGL(bwd_chain_split_kernel, dim3(a.Hv * (kD / 32), a.nseq), dim3(384), 0, st,
                        (const E*)a.q, (const E*)a.k, (const E*)a.dout,
                        a.beta, a.dht, a.dh0, (const E*)a.N, (const E*)a.M, a.gam, a.dec,
                        (E*)a.dS, a.cm, a.Hqk, a.Hv);
