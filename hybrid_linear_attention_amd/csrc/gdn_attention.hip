@@ -191,8 +191,8 @@ struct PadTile {
   // k0 + kslot(g, j).
   __device__ bf16x8 cm(int col0, int k0, const Lane& ln) const {
     const char* b = p + (k0 + 4 * ln.g + (ln.r >> 2)) * ROWB + 2 * col0 + 8 * (ln.r & 3);
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)b);
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + 16 * ROWB));
+    const s16x4 lo = lds_tr16(b);
+    const s16x4 hi = lds_tr16(b + 16 * ROWB);
     return __builtin_shufflevector(as_bf16x4(lo), as_bf16x4(hi), 0, 1, 2, 3, 4, 5, 6, 7);
   }
 };
@@ -303,6 +303,14 @@ __global__ __launch_bounds__(fwd_max_threads<QS>()) void attn_fwd_kernel(
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) { m[qt] = -INFINITY; lsum[qt] = 0.f; }
 
+  // The Q fragments are first used inside the block loop, whose waits for the
+  // copies are inline asm the compiler cannot see: left pending, their loads
+  // would make it wait for every outstanding copy (vmcnt(0)) at the first
+  // score product of every block.  An empty use here retires them once.
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) asm volatile("" ::"v"(Qf[qt][kb]));
   if constexpr (BF) {
     issue(0);
     wait_copies();

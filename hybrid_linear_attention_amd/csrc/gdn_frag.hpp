@@ -10,6 +10,18 @@ namespace frag {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
+// ds_read_b64_tr_b16: 4 x 16-bit elements, transposed across each group of 16
+// lanes (input lane p reads 8 bytes at its address; output lane m receives
+// element m % 4 of input lanes m / 4, m / 4 + 4, m / 4 + 8, m / 4 + 12).
+// The compiler orders an LDS read that carries no alias information after
+// every direct global->LDS copy still in flight (a full vmcnt(0) wait), so a
+// transposed read placed after the next tile's copies were issued would stall
+// until they land.  Every read of copied data here is ordered by an explicit
+// copy wait and barrier instead; the restrict-qualified argument gives the
+// inlined read a scope of its own, which drops the implied wait.
+__device__ __forceinline__ s16x4 lds_tr16(const void* __restrict__ p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+}
 __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
 
@@ -138,10 +150,8 @@ struct Lds {
     const int r = ln.r, g = ln.g;
     if constexpr (BF) {
       const int c0 = col - r + 4 * (r & 3);
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4*)(p + at(k0 + 4 * g + (r >> 2), c0)));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4*)(p + at(k0 + 16 + 4 * g + (r >> 2), c0)));
+      const s16x4 lo = lds_tr16(p + at(k0 + 4 * g + (r >> 2), c0));
+      const s16x4 hi = lds_tr16(p + at(k0 + 16 + 4 * g + (r >> 2), c0));
       return __builtin_shufflevector(as_bf16x4(lo), as_bf16x4(hi), 0, 1, 2, 3, 4, 5, 6, 7);
     } else {
       f32x4 f;
@@ -254,12 +264,6 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
 }
 __device__ __forceinline__ void dma4(const void* src, void* lds_dst) {
   __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_dst, 4, 0, 0);
-}
-// ds_read_b64_tr_b16: 4 x 16-bit elements, transposed across each group of 16
-// lanes (input lane p reads 8 bytes at its address; output lane m receives
-// element m % 4 of input lanes m / 4, m / 4 + 4, m / 4 + 8, m / 4 + 12).
-__device__ __forceinline__ s16x4 lds_tr16(const void* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
 }
 __device__ __forceinline__ void barrier_lds() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
