@@ -559,21 +559,51 @@ __global__ __launch_bounds__(384) void bwd_chain_split_kernel(
 // and keeps only the intermediates Dl, Y, E in LDS.
 constexpr int kGW = 8;  // waves
 
-// v[4 mt + i] is a sum already broadcast over the 16 lanes of lane group g
-// (token 16 mt + 4 g + i); lane r keeps the one of token 16 (r / 4) + 4 g +
-// r % 4, so that one unconditional store per lane writes all 64 tokens.
-__device__ __forceinline__ float pick16(const float (&v)[16], int r) {
-  float s = v[0];
+// Row sums of 16 terms, scattered: v[4 mt + i] is this lane's term of token
+// 16 mt + 4 g + i (lane group g); lane r of the group returns the sum over the
+// group's 16 lanes of token 16 (r / 4) + 4 g + r % 4, so that one
+// unconditional store per lane writes all 64 tokens.  Recursive halving with
+// row rotations: at step b a lane keeps the half of its partial sums whose
+// index bit b equals its lane bit b, and adds the other half from the lane
+// 2^b away in the row, which has the same lower bits and the opposite bit b.
+// (A select chain over v[r] is turned by the compiler into a stack array
+// indexed per lane, i.e. scratch memory traffic.)
+template <int S, int N>
+__device__ __forceinline__ void halve(const float (&a)[2 * N], float (&o)[N], bool hi) {
 #pragma unroll
-  for (int k = 1; k < 16; ++k) s = r == k ? v[k] : s;
-  return s;
+  for (int j = 0; j < N; ++j) {
+    const float keep = hi ? a[2 * j + 1] : a[2 * j];
+    const float send = hi ? a[2 * j] : a[2 * j + 1];
+    o[j] = keep + row_ror<S>(send);
+  }
+}
+__device__ __forceinline__ float rsum16(const float (&v)[16], int r) {
+  float a[8], b[4], c[2], d[1];
+  halve<1, 8>(v, a, r & 1);
+  halve<2, 4>(a, b, r & 2);
+  halve<4, 2>(b, c, r & 4);
+  halve<8, 1>(c, d, r & 8);
+  return d[0];
 }
 
 template <typename E>
 struct GradSmem {
   static constexpr bool BF = sizeof(E) == 2;
+  // The per-token arrays come first: below 64 KiB, every access to them is one
+  // per-lane base plus an immediate offset.  Placed after the tiles, each
+  // array needs a base register of its own, which the compiler keeps live
+  // across the head loop (and spills).
+  float ss[kGW];                            // per-wave <dS', S0>
+  float rowp[4][kC], colp[4][kC], rowb[4][kC];
+  float pa[kGW][kC];
+  float fin[3][kC];                         // gate, beta, w
+  float G2[kC], G2lo[kC], gm[kC], dc[kC], bt[kC], al[kC];   // G2 + G2lo: compensated prefix
+  union {
+    float part[kGW][3][kC];                 // phase 1 per-wave row sums
+    E Em[Lds<E, 64>::size(kC)];             // phase 1.5 output
+  } u3;
   // bf16 only (fp32 reads these from global memory)
-  E K[BF ? Lds<E, 128>::size(kC) : 1];
+  alignas(256) E K[BF ? Lds<E, 128>::size(kC) : 1];
   E Q[BF ? Lds<E, 128>::size(kC) : 1];
   E S0[BF ? Lds<E, 128>::size(kD) : 1];
   E dS[BF ? Lds<E, 128>::size(kD) : 1];
@@ -589,15 +619,6 @@ struct GradSmem {
     } nm;                                    // phase 1 inputs (bf16)
     E Y[Lds<E, 128>::size(kC)];             // phase 1 output
   } u2;
-  union {
-    float part[kGW][3][kC];                 // phase 1 per-wave row sums
-    E Em[Lds<E, 64>::size(kC)];             // phase 1.5 output
-  } u3;
-  float ss[kGW];                            // per-wave <dS', S0>
-  float rowp[4][kC], colp[4][kC], rowb[4][kC];
-  float pa[kGW][kC];
-  float fin[3][kC];                         // gate, beta, w
-  float G2[kC], G2lo[kC], gm[kC], dc[kC], bt[kC], al[kC];   // G2 + G2lo: compensated prefix
 };
 
 template <typename E>
@@ -658,14 +679,18 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
       const int wu = __builtin_amdgcn_readfirstlane(w);
       const int h2 = gq * G + hh2;
       const size_t hc2 = (size_t)cid * Hv + h2;
+      // per-lane copy addresses recomputed at each call rather than hoisted
+      // out of the head loop (where they would be spilled)
+      int lo = lane_id();
+      asm volatile("" : "+v"(lo));
       if (part == 0) {
-        copy_rows<128, kD>(Sc + hc2 * kD * kD, kD, kD, sm.S0, wu, kGW);
-        copy_rows<128, kD>(dSc + hc2 * kD * kD, kD, kD, sm.dS, wu, kGW);
-        copy_rows<128>(dout + (tok0 * Hv + h2) * kD, (int64_t)Hv * kD, L, sm.dO, wu, kGW);
+        copy_rows<128, kD>(Sc + hc2 * kD * kD, kD, kD, sm.S0, wu, kGW, lo);
+        copy_rows<128, kD>(dSc + hc2 * kD * kD, kD, kD, sm.dS, wu, kGW, lo);
+        copy_rows<128>(dout + (tok0 * Hv + h2) * kD, (int64_t)Hv * kD, L, sm.dO, wu, kGW, lo);
       } else {
-        copy_rows<128>(v + (tok0 * Hv + h2) * kD, (int64_t)Hv * kD, L, sm.u1.V, wu, kGW);
-        copy_rows<64>(Nw + hc2 * kC * kC, kC, kC, sm.u2.nm.N, wu, kGW);
-        copy_rows<64>(Mw + hc2 * kC * kC, kC, kC, sm.u2.nm.M, wu, kGW);
+        copy_rows<128>(v + (tok0 * Hv + h2) * kD, (int64_t)Hv * kD, L, sm.u1.V, wu, kGW, lo);
+        copy_rows<64>(Nw + hc2 * kC * kC, kC, kC, sm.u2.nm.N, wu, kGW, lo);
+        copy_rows<64>(Mw + hc2 * kC * kC, kC, kC, sm.u2.nm.M, wu, kGW, lo);
       }
     }
   };
@@ -777,10 +802,10 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
         for (int i = 0; i < 4; ++i) {
           const int tok = 16 * mt + 4 * g + i;
           dD[mt][i] = m[i] + sm.dc[tok] * kds[i];
-          pwv[4 * mt + i] = sum16(Dl[mt][i] * kds[i]);
+          pwv[4 * mt + i] = Dl[mt][i] * kds[i];
         }
       }
-      sm.u3.part[w][2][tk] = sm.dc[tk] * pick16(pwv, r);
+      sm.u3.part[w][2][tk] = sm.dc[tk] * rsum16(pwv, r);
       // Y = N^T dDl
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
@@ -798,11 +823,11 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int tok = 16 * mt + 4 * g + i;
-            pbv[4 * mt + i] = sum16(Y[mt][i] * X[mt][i]);
-            pgv[4 * mt + i] = sum16(Y[mt][i] * (mV.get(tok, c) - X[mt][i]));
+            pbv[4 * mt + i] = Y[mt][i] * X[mt][i];
+            pgv[4 * mt + i] = Y[mt][i] * (mV.get(tok, c) - X[mt][i]);
           }
-        sm.u3.part[w][0][tk] = pick16(pbv, r);
-        sm.u3.part[w][1][tk] = -sm.bt[tk] * pick16(pgv, r);
+        sm.u3.part[w][0][tk] = rsum16(pbv, r);
+        sm.u3.part[w][1][tk] = -sm.bt[tk] * rsum16(pgv, r);
       }
       ssl = wave_sum(ssl);
       if (l == 0) sm.ss[w] = ssl;
@@ -935,9 +960,9 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
             const int tok = 16 * mt + 4 * g + i;
             const float g1 = sm.gm[tok] * T1[mt][i];
             dQ[mt][i] += g1;
-            pav[4 * mt + i] = sum16(mQ.get(tok, c) * g1);
+            pav[4 * mt + i] = mQ.get(tok, c) * g1;
           }
-        sm.pa[w][tk] = pick16(pav, r);
+        sm.pa[w][tk] = rsum16(pav, r);
       }
       // -gamma beta Y S0 into dk
       {

@@ -280,9 +280,8 @@ __device__ __forceinline__ void wait_copies() {
 // the swizzle puts there.
 template <int W, int ROWS = kC>
 __device__ __forceinline__ void copy_rows(const bf16* src, int64_t ld, int L, bf16* dst, int w,
-                                          int nw) {
+                                          int nw, int l = lane_id()) {
   constexpr int RPK = 1024 / (2 * W), NIT = ROWS / RPK;
-  const int l = lane_id();
   const int rin = (16 * l) / (2 * W), pp = ((16 * l) % (2 * W)) / 16;
   for (int it = w; it < NIT; it += nw) {
     const int row = it * RPK + rin;
