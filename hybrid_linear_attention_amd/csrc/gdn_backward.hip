@@ -631,7 +631,7 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
   constexpr bool BF = sizeof(E) == 2;
   constexpr int KB = FragOf<E>::KB, NT = 64 * kGW, NS = kSlotsOf<E>;
   __shared__ GradSmem<E> sm;
-  const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(wave_id()), l = lane_id(), r = l & 15, g = l >> 4;
   const int cid = blockIdx.x, gq = blockIdx.y, G = Hv / Hqk;
   int tok0i, L;
   chunk_of(cm, cid, tok0i, L);
@@ -999,11 +999,16 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
 #pragma unroll
           for (int i = 0; i < 4; ++i) dK[mt][i] += sm.dc[16 * mt + 4 * g + i] * T3[mt][i];
       }
-      // S0, dS' and dO are no longer read: the next head's copies start now
-      // and run under the E products and the gate reduction
+      // S0, dS', dO, V, N, M and their slots' later tenants Dl and Y are no
+      // longer read (the E products below read only E, K and Q): all the next
+      // head's copies start now and run under the E products and the gate
+      // reduction
       if constexpr (BF) {
         __syncthreads();
-        if (hh + 1 < G) stage_head(hh + 1, 0);
+        if (hh + 1 < G) {
+          stage_head(hh + 1, 0);
+          stage_head(hh + 1, 1);
+        }
       }
       // (dM * Gam) K into dq; (dM * Gam)^T Q and (Wa + Wa^T) K into dk
 #pragma unroll
@@ -1039,10 +1044,6 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
       }
     }
     __syncthreads();
-    // Dl, Y and E are dead: V, N and M of the next head go into their slots
-    if constexpr (BF) {
-      if (hh + 1 < G) stage_head(hh + 1, 1);
-    }
 
     // ---- gates and beta for this head (wave 0, lane = token).  No barrier
     // after it: the other waves touch nothing it reads before the barrier that

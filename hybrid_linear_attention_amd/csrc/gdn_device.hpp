@@ -54,7 +54,7 @@ __device__ __forceinline__ void store_state4(void* base, size_t idx, const f32x4
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // Orders this wave's LDS traffic: every earlier LDS access has completed and
 // no later one is hoisted above this point.
