@@ -832,7 +832,11 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
       ssl = wave_sum(ssl);
       if (l == 0) sm.ss[w] = ssl;
       __syncthreads();   // every wave is done with V, N, M (their LDS is reused)
-      E* dvh = dv + (tok0 * Hv + h) * kD;
+      // dv through a uniform base and 32-bit byte offsets (a chunk's rows
+      // span far less than 2 GiB): one add per store, no 64-bit multiply
+      char* dvh = reinterpret_cast<char*>(dv + (tok0 * Hv + h) * kD);
+      const uint32_t rstr = (uint32_t)(Hv * kD * sizeof(E));
+      const uint32_t lo = (uint32_t)(4 * g) * rstr + (uint32_t)(c * sizeof(E));
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -850,7 +854,8 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
         for (int i = 0; i < 4; ++i) {
           const int tok = 16 * mt + 4 * g + i;
           if (full || tok < L)
-            dvh[(size_t)tok * Hv * kD + c] = from_f32<E>(sm.bt[tok] * Y[mt][i]);
+            *reinterpret_cast<E*>(dvh + (lo + (uint32_t)(16 * mt + i) * rstr)) =
+                from_f32<E>(sm.bt[tok] * Y[mt][i]);
         }
     }
     __syncthreads();
@@ -1072,17 +1077,20 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
   }
 
   // ---- dq, dk of the group
-  E* dqg = dq + (tok0 * Hqk + gq) * kD;
-  E* dkg = dk + (tok0 * Hqk + gq) * kD;
+  char* dqg = reinterpret_cast<char*>(dq + (tok0 * Hqk + gq) * kD);
+  char* dkg = reinterpret_cast<char*>(dk + (tok0 * Hqk + gq) * kD);
   const int c = 16 * w + r;
+  const uint32_t rstr = (uint32_t)(Hqk * kD * sizeof(E));
+  const uint32_t lo = (uint32_t)(4 * g) * rstr + (uint32_t)(c * sizeof(E));
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tok = 16 * mt + 4 * g + i;
       if (tok < L) {
-        dqg[(size_t)tok * Hqk * kD + c] = from_f32<E>(dQ[mt][i]);
-        dkg[(size_t)tok * Hqk * kD + c] = from_f32<E>(dK[mt][i]);
+        const uint32_t off = lo + (uint32_t)(16 * mt + i) * rstr;
+        *reinterpret_cast<E*>(dqg + off) = from_f32<E>(dQ[mt][i]);
+        *reinterpret_cast<E*>(dkg + off) = from_f32<E>(dK[mt][i]);
       }
     }
 }

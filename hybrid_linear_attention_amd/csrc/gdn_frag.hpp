@@ -100,8 +100,11 @@ __device__ __forceinline__ Lane lane_opaque() {
 // flipped: 16-byte pieces stay whole for the direct global->LDS copies.
 template <int W>
 __device__ __forceinline__ int swz_units(int row) {
-  constexpr int rpl = W <= 128 ? 128 / W : 1, nb = W >= 128 ? 8 : W / 16;
-  return (((row / rpl) % nb) << 2) | (((row >> 3) & 1) << 1);
+  // unsigned: rows are never negative, and signed / and % by powers of two
+  // cost a sign fix-up each
+  constexpr unsigned rpl = W <= 128 ? 128 / W : 1, nb = W >= 128 ? 8 : W / 16;
+  const unsigned ur = (unsigned)row;
+  return (int)((((ur / rpl) % nb) << 2) | (((ur >> 3) & 1u) << 1));
 }
 
 // Row-major matrix of W columns in LDS.  bf16: unpadded rows with 8-byte
@@ -282,7 +285,7 @@ template <int W, int ROWS = kC>
 __device__ __forceinline__ void copy_rows(const bf16* src, int64_t ld, int L, bf16* dst, int w,
                                           int nw, int l = lane_id()) {
   constexpr int RPK = 1024 / (2 * W), NIT = ROWS / RPK;
-  const int rin = (16 * l) / (2 * W), pp = ((16 * l) % (2 * W)) / 16;
+  const int rin = (int)((16u * l) / (2 * W)), pp = (int)(((16u * l) % (2 * W)) / 16);
   for (int it = w; it < NIT; it += nw) {
     const int row = it * RPK + rin;
     const int lp = pp ^ (swz_units<W>(row) >> 1);
