@@ -214,7 +214,8 @@ __device__ __forceinline__ void copy_tile(const bf16* src, int64_t ld, int L, ch
   for (int it = w; it < NIT; it += nw) {
     const int byte = 1024 * it + 16 * l, row = byte / ROWB, off = byte - row * ROWB;
     if (row < ROWS && off < 2 * kDh)
-      dma16(src + (int64_t)min(row, L - 1) * ld + off / 2, dst + 1024 * it);
+      dma16(reinterpret_cast<const char*>(src) + ((uint32_t)min(row, L - 1) * (uint32_t)(2 * ld) + off),
+            dst + 1024 * it);
   }
 }
 

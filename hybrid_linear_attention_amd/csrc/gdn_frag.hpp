@@ -286,10 +286,15 @@ __device__ __forceinline__ void copy_rows(const bf16* src, int64_t ld, int L, bf
                                           int nw, int l = lane_id()) {
   constexpr int RPK = 1024 / (2 * W), NIT = ROWS / RPK;
   const int rin = (int)((16u * l) / (2 * W)), pp = (int)(((16u * l) % (2 * W)) / 16);
+  // a uniform base and 32-bit byte offsets (the rows of one copy span far
+  // less than 2 GiB): no 64-bit multiply per copy
+  const char* sb = reinterpret_cast<const char*>(src);
+  const uint32_t rowb = (uint32_t)(2 * ld);
   for (int it = w; it < NIT; it += nw) {
     const int row = it * RPK + rin;
     const int lp = pp ^ (swz_units<W>(row) >> 1);
-    dma16(src + (int64_t)min(row, L - 1) * ld + 8 * lp, reinterpret_cast<char*>(dst) + 1024 * it);
+    dma16(sb + ((uint32_t)min(row, L - 1) * rowb + 16u * lp),
+          reinterpret_cast<char*>(dst) + 1024 * it);
   }
 }
 

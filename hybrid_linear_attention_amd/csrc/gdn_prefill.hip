@@ -751,6 +751,8 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
   if (w >= kSlices + 1) {
     // ------------------------------------------------------------ producers
     const int pw = w - kSlices - 1;
+    // Copy sources are a uniform base plus a 32-bit byte offset (one chunk's
+    // rows span far less than 2 GiB), which avoids a 64-bit multiply per copy.
     // Tt, V, gam, dec of chunk c into ring slots (c % 3, c % 4).
     auto issue_a = [&](int c) {
       const int cid = cid0 + c;
@@ -761,13 +763,15 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
 #pragma unroll
       for (int it = 0; it < kTB / 1024; ++it) {
         const int row = 8 * it + (l >> 3), p = (l & 7) ^ swz(row);
-        dma16(tb + row * kC + 8 * p, S.T + 1024 * it);
+        dma16(reinterpret_cast<const char*>(tb) + (uint32_t)(2 * (row * kC + 8 * p)), S.T + 1024 * it);
       }
       const bf16* vbase = v + (size_t)tok0 * hv_stride + (size_t)h * kD + dvb;
 #pragma unroll
       for (int it = 0; it < kVB / 1024; ++it) {
         const int row = 16 * it + (l >> 2), p = (l & 3) ^ vswz(row);
-        dma16(vbase + (size_t)min(row, L - 1) * hv_stride + 8 * p, S.V + 1024 * it);
+        dma16(reinterpret_cast<const char*>(vbase) +
+                  ((uint32_t)min(row, L - 1) * (uint32_t)(2 * hv_stride) + 16u * p),
+              S.V + 1024 * it);
       }
       GateSlot& Gd = sm.gd[c % kGdSlots];
       dma4(ws.gam + ((size_t)cid * Hv + h) * kC + l, Gd.gam);
@@ -783,13 +787,15 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
 #pragma unroll
       for (int it = 0; it < kQB / 1024; ++it) {
         const int row = 4 * it + (l >> 4), p = (l & 15) ^ swz(row);
-        dma16(qbase + (size_t)min(row, L - 1) * qk_stride + 8 * p, Qs.Q + 1024 * it);
+        dma16(reinterpret_cast<const char*>(qbase) +
+                  ((uint32_t)min(row, L - 1) * (uint32_t)(2 * qk_stride) + 16u * p),
+              Qs.Q + 1024 * it);
       }
       const bf16* mb = ws.M + ((size_t)cid * Hv + h) * kC * kC;
 #pragma unroll
       for (int it = 0; it < kMB / 1024; ++it) {
         const int row = 8 * it + (l >> 3), p = (l & 7) ^ swz(row);
-        dma16(mb + row * kC + 8 * p, Qs.M + 1024 * it);
+        dma16(reinterpret_cast<const char*>(mb) + (uint32_t)(2 * (row * kC + 8 * p)), Qs.M + 1024 * it);
       }
     };
     // K of chunk c into slot c % 3, from the input: 4 tokens per copy, rows
@@ -804,7 +810,9 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
 #pragma unroll
       for (int it = 0; it < kKTB / 1024; ++it) {
         const int row = 4 * it + (l >> 4), p = (l & 15) ^ ksw(row);
-        dma16(kbase + (size_t)min(row, L - 1) * qk_stride + 8 * p, S.K + 1024 * it);
+        dma16(reinterpret_cast<const char*>(kbase) +
+                  ((uint32_t)min(row, L - 1) * (uint32_t)(2 * qk_stride) + 16u * p),
+              S.K + 1024 * it);
       }
     };
     // Chunk c's chain operands must be in LDS by the barrier that ends
@@ -1166,7 +1174,9 @@ __global__ __launch_bounds__(64 * hw::kWaves) void scan_head_kernel(
         for (int it = 0; it < 16; ++it) {
           const int row = 4 * it + (l >> 4);
           const int sw = pw == 0 ? ksw(row) : pw == 1 ? swz(row) : vsw(row);
-          dma16(base + (size_t)min(row, L - 1) * stride + 8 * ((l & 15) ^ sw), dst + 1024 * it);
+          dma16(reinterpret_cast<const char*>(base) +
+                    ((uint32_t)min(row, L - 1) * (uint32_t)(2 * stride) + 16u * ((l & 15) ^ sw)),
+                dst + 1024 * it);
         }
         if (pw == 2) {
           dma4(ws.gam + ((size_t)cid * Hv + h) * kC + l, S.gam);
@@ -1177,8 +1187,9 @@ __global__ __launch_bounds__(64 * hw::kWaves) void scan_head_kernel(
 #pragma unroll
         for (int it = 0; it < 8; ++it) {
           const int row = 8 * it + (l >> 3), p = (l & 7) ^ swz(row);
-          dma16(ws.Tt + tm + row * kC + 8 * p, S.T + 1024 * it);
-          dma16(ws.M + tm + row * kC + 8 * p, S.M + 1024 * it);
+          const uint32_t off = (uint32_t)(2 * (row * kC + 8 * p));
+          dma16(reinterpret_cast<const char*>(ws.Tt + tm) + off, S.T + 1024 * it);
+          dma16(reinterpret_cast<const char*>(ws.M + tm) + off, S.M + 1024 * it);
         }
       }
     };
