@@ -651,10 +651,19 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
     if constexpr (BF) return Lds<E, 128>{sm.Q};
     else return Glb<E>{qg, (int64_t)Hqk * kD, L};
   }();
+  // K and Q: copied straight into LDS for a full chunk (waited for with the
+  // first head's operands); a ragged chunk stages them through registers,
+  // since its rows beyond L must read as zero.  The barrier that follows the
+  // first head's copies orders both.
   if constexpr (BF) {
-    stage<E, 128, kC, NT>(Lds<E, 128>{sm.K}, kg, (int64_t)Hqk * kD, L);
-    stage<E, 128, kC, NT>(Lds<E, 128>{sm.Q}, qg, (int64_t)Hqk * kD, L);
-    __syncthreads();
+    if (L == kC) {
+      const int wu = __builtin_amdgcn_readfirstlane(w);
+      copy_rows<128>(kg, (int64_t)Hqk * kD, L, sm.K, wu, kGW);
+      copy_rows<128>(qg, (int64_t)Hqk * kD, L, sm.Q, wu, kGW);
+    } else {
+      stage<E, 128, kC, NT>(Lds<E, 128>{sm.K}, kg, (int64_t)Hqk * kD, L);
+      stage<E, 128, kC, NT>(Lds<E, 128>{sm.Q}, qg, (int64_t)Hqk * kD, L);
+    }
   }
 
   // This wave's two 64x64 tiles (ti, tj) of the phase-1.5 products.
@@ -695,6 +704,14 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
     }
   };
 
+  // wave 0: alpha and beta of the next head, loaded a head ahead (lane =
+  // token); wave 1: what the gate reduction of a head reads that the next
+  // head's set-up overwrites
+  float a_nx = 1.f, b_nx = 0.f, al_g = 1.f, gmL_g = 0.f;
+  if (w == 0 && l < L) {
+    a_nx = alpha[(tok0 + l) * Hv + gq * G];
+    b_nx = beta[(tok0 + l) * Hv + gq * G];
+  }
   for (int hh = 0; hh < G; ++hh) {
     const int h = gq * G + hh;
     const Lane ln = lane_opaque();
@@ -736,7 +753,7 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
       }
     }
     if (w == 0) {
-      const float a = l < L ? alpha[(tok0 + l) * Hv + h] : 1.f;
+      const float a = a_nx;
       float G2lo;
       const float G2 = wave_inclusive_sum2(hw_log2(a), G2lo);
       const float Glast = __shfl(G2, kC - 1, 64), Glastlo = __shfl(G2lo, kC - 1, 64);
@@ -744,7 +761,7 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
       sm.G2lo[l] = G2lo;
       sm.gm[l] = hw_exp2(G2);
       sm.dc[l] = hw_exp2((Glast - G2) + (Glastlo - G2lo));
-      sm.bt[l] = l < L ? beta[(tok0 + l) * Hv + h] : 0.f;
+      sm.bt[l] = b_nx;
       sm.al[l] = a;
     }
     if constexpr (BF) wait_copies();
@@ -1008,8 +1025,16 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
       // longer read (the E products below read only E, K and Q): all the next
       // head's copies start now and run under the E products and the gate
       // reduction
+      if constexpr (BF) __syncthreads();
+      if (w == 0 && hh + 1 < G && l < L) {
+        a_nx = alpha[(tok0 + l) * Hv + h + 1];
+        b_nx = beta[(tok0 + l) * Hv + h + 1];
+      }
+      if (w == 1) {
+        al_g = sm.al[l];
+        gmL_g = sm.gm[L - 1];
+      }
       if constexpr (BF) {
-        __syncthreads();
         if (hh + 1 < G) {
           stage_head(hh + 1, 0);
           stage_head(hh + 1, 1);
@@ -1050,10 +1075,12 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
     }
     __syncthreads();
 
-    // ---- gates and beta for this head (wave 0, lane = token).  No barrier
-    // after it: the other waves touch nothing it reads before the barrier that
-    // follows the next head's gates, which wave 0 itself computes after this.
-    if (w == 0) {
+    // ---- gates and beta for this head (wave 1, lane = token), beside wave
+    // 0's set-up of the next head.  No barrier after it: the other waves
+    // write nothing it reads (alpha and gamma of this head it took into
+    // registers before the last barrier) before the barrier that ends the
+    // next head's set-up, which it reaches only after this.
+    if (w == 1) {
       const int t = l;
       float pa = 0.f, fw = sm.fin[2][t];
 #pragma unroll
@@ -1063,14 +1090,14 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
       for (int x = 0; x < kGW; ++x) ss += sm.ss[x];
       const float wsum = wave_sum(t < L ? fw : 0.f);
       float dG = t < L ? pa + sm.fin[0][t] - fw : 0.f;
-      if (t == L - 1) dG += wsum + sm.gm[t] * ss;
+      if (t == L - 1) dG += wsum + gmL_g * ss;
       // reverse inclusive prefix: sum over i >= t
       const float tot = wave_sum(dG);
       const float incl = wave_inclusive_sum(dG);
       const float dlog = tot - incl + dG;
       if (t < L) {
         const size_t gi = (tok0 + t) * Hv + h;
-        dalpha[gi] = dlog / sm.al[t];
+        dalpha[gi] = dlog / al_g;
         dbeta[gi] = sm.fin[1][t];
       }
     }
