@@ -667,11 +667,16 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
   }
 
   // This wave's two 64x64 tiles (ti, tj) of the phase-1.5 products.
+  // The ten tiles on and below the diagonal: waves 0 and 1 take two, the
+  // others one, so that (waves w and w + 4 sharing a SIMD) no SIMD holds more
+  // than three.  Entries past the tenth are above the diagonal: skipped.
+  constexpr int kTi[16] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3, 0, 0, 0, 0, 0, 0};
+  constexpr int kTj[16] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3, 1, 1, 1, 1, 1, 1};
   int ti[2], tj[2];
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
-    ti[x] = (2 * w + x) >> 2;
-    tj[x] = (2 * w + x) & 3;
+    ti[x] = kTi[8 * x + w];
+    tj[x] = kTj[8 * x + w];
   }
 
   f32x4 dQ[4], dK[4];
@@ -769,6 +774,26 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
 
     // ---- phase 1: this wave's value columns c = 16w + r
     const int c = 16 * w + r;
+    // Elements (16 mt + 4 g + i, c) of a matrix, in this lane's accumulator
+    // order: they are the slots of transposed fragment reads of column c, two
+    // reads (bf16) or four (fp32) instead of sixteen element reads.
+    auto col16 = [&](const auto& mx, float (&out)[16]) {
+      if constexpr (BF) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const Fr<E> f = mx.cm(c, KB * kb, ln);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) out[4 * (2 * kb + (j >> 2)) + (j & 3)] = (float)f[j];
+        }
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const Fr<E> f = mx.cm(c, KB * mt, ln);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) out[4 * mt + i] = f[i];
+        }
+      }
+    };
     {
       float ssl = 0.f;
       f32x4 X[4], Dl[4], dD[4], Y[4];
@@ -785,12 +810,14 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt) X[mt] = mma(X[mt], mK.rmn(16 * mt + r, KB * kb, ln), s0);
         }
+        float vv[16];
+        col16(mV, vv);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int tok = 16 * mt + 4 * g + i;
-            X[mt][i] = mV.get(tok, c) - sm.gm[tok] * X[mt][i];   // V - gamma K S0^T
+            X[mt][i] = vv[4 * mt + i] - sm.gm[tok] * X[mt][i];   // V - gamma K S0^T
             XB[mt][i] = sm.bt[tok] * X[mt][i];
           }
         // Dl = N (beta X)
@@ -834,14 +861,14 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
       }
       // beta and gate partials: Y.X and -gamma beta Y.(K S0^T) = -beta Y.(V - X)
       {
-        float pbv[16], pgv[16];
+        float pbv[16], pgv[16], vv[16];
+        col16(mV, vv);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int tok = 16 * mt + 4 * g + i;
             pbv[4 * mt + i] = Y[mt][i] * X[mt][i];
-            pgv[4 * mt + i] = Y[mt][i] * (mV.get(tok, c) - X[mt][i]);
+            pgv[4 * mt + i] = Y[mt][i] * (vv[4 * mt + i] - X[mt][i]);
           }
         sm.u3.part[w][0][tk] = rsum16(pbv, r);
         sm.u3.part[w][1][tk] = -sm.bt[tk] * rsum16(pgv, r);
@@ -849,6 +876,15 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
       ssl = wave_sum(ssl);
       if (l == 0) sm.ss[w] = ssl;
       __syncthreads();   // every wave is done with V, N, M (their LDS is reused)
+      // ---- reduce the phase 1 partials (fixed order); done before the
+      // barrier that precedes the E products, which overwrite them
+      if (threadIdx.x < 3 * kC) {
+        const int qn = threadIdx.x / kC, t = threadIdx.x % kC;
+        float s = 0.f;
+#pragma unroll
+        for (int x = 0; x < kGW; ++x) s += sm.u3.part[x][qn][t];
+        sm.fin[qn == 0 ? 1 : (qn == 1 ? 0 : 2)][t] = s;
+      }
       // dv through a uniform base and 32-bit byte offsets (a chunk's rows
       // span far less than 2 GiB): one add per store, no 64-bit multiply
       char* dvh = reinterpret_cast<char*>(dv + (tok0 * Hv + h) * kD);
@@ -877,14 +913,6 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
     }
     __syncthreads();
 
-    // ---- reduce the phase 1 partials (fixed order)
-    if (threadIdx.x < 3 * kC) {
-      const int qn = threadIdx.x / kC, t = threadIdx.x % kC;
-      float s = 0.f;
-#pragma unroll
-      for (int x = 0; x < kGW; ++x) s += sm.u3.part[x][qn][t];
-      sm.fin[qn == 0 ? 1 : (qn == 1 ? 0 : 2)][t] = s;
-    }
     // ---- phase 1.5: dO Dl^T and Y Dl^T on this wave's tiles, with K K^T
     // and Q K^T on the same tiles (recomputed per head: cheaper than keeping
     // them live)
@@ -907,7 +935,8 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
         }
       }
     }
-    __syncthreads();   // partials consumed; E may overwrite them
+    // (no barrier: the phase 1 partials that E overwrites were reduced before
+    // the last one)
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
       if (tj[x] > ti[x]) continue;
@@ -975,6 +1004,8 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt) T1[mt] = mma(T1[mt], mO.rm(16 * mt + r, KB * kb, ln), s0);
         }
+        float qq[16];
+        col16(mQ, qq);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -982,7 +1013,7 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
             const int tok = 16 * mt + 4 * g + i;
             const float g1 = sm.gm[tok] * T1[mt][i];
             dQ[mt][i] += g1;
-            pav[4 * mt + i] = mQ.get(tok, c) * g1;
+            pav[4 * mt + i] = qq[4 * mt + i] * g1;
           }
         sm.pa[w][tk] = rsum16(pav, r);
       }
