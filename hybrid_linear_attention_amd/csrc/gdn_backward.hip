@@ -709,6 +709,48 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
     }
   };
 
+  // The same copies of value head hh2, two at a time (piece j = 0..6 of this
+  // wave's fourteen with eight waves), so that they can be spread over the E
+  // products: issued all at once they kept the waves stalled ~3-5 k cycles
+  // before the products could start.
+  auto stage_piece = [&](int hh2, int j) {
+    if constexpr (BF) {
+      static_assert(kGW == 8, "copy pieces are laid out for eight waves");
+      const int wu = __builtin_amdgcn_readfirstlane(w);
+      const int h2 = gq * G + hh2;
+      const size_t hc2 = (size_t)cid * Hv + h2;
+      int lo = lane_id();
+      asm volatile("" : "+v"(lo));
+      const bf16* st = Sc + hc2 * kD * kD;
+      const bf16* ds = dSc + hc2 * kD * kD;
+      const bf16* og = dout + (tok0 * Hv + h2) * kD;
+      const bf16* vg = v + (tok0 * Hv + h2) * kD;
+      const int64_t hs = (int64_t)Hv * kD;
+      switch (j) {
+        case 0: case 1:      // S0: copies w + 16 j, w + 16 j + 8 of 32
+          copy_row_one<128, kD>(st, kD, kD, sm.S0, wu + 16 * j, lo);
+          copy_row_one<128, kD>(st, kD, kD, sm.S0, wu + 16 * j + 8, lo);
+          break;
+        case 2: case 3:      // dS'
+          copy_row_one<128, kD>(ds, kD, kD, sm.dS, wu + 16 * (j - 2), lo);
+          copy_row_one<128, kD>(ds, kD, kD, sm.dS, wu + 16 * (j - 2) + 8, lo);
+          break;
+        case 4:              // dO: copies w, w + 8 of 16
+          copy_row_one<128>(og, hs, L, sm.dO, wu, lo);
+          copy_row_one<128>(og, hs, L, sm.dO, wu + 8, lo);
+          break;
+        case 5:              // V
+          copy_row_one<128>(vg, hs, L, sm.u1.V, wu, lo);
+          copy_row_one<128>(vg, hs, L, sm.u1.V, wu + 8, lo);
+          break;
+        default:             // N, M: copy w of 8 each
+          copy_row_one<64>(Nw + hc2 * kC * kC, kC, kC, sm.u2.nm.N, wu, lo);
+          copy_row_one<64>(Mw + hc2 * kC * kC, kC, kC, sm.u2.nm.M, wu, lo);
+          break;
+      }
+    }
+  };
+
   // wave 0: alpha and beta of the next head, loaded a head ahead (lane =
   // token); wave 1: what the gate reduction of a head reads that the next
   // head's set-up overwrites
@@ -1065,18 +1107,15 @@ __global__ __launch_bounds__(64 * kGW) void bwd_grad_kernel(
         al_g = sm.al[l];
         gmL_g = sm.gm[L - 1];
       }
-      if constexpr (BF) {
-        if (hh + 1 < G) {
-          stage_head(hh + 1, 0);
-          stage_head(hh + 1, 1);
-        }
-      }
+      // the next head's copies are issued two at a time between the E
+      // product steps below
       // (dM * Gam) K into dq; (dM * Gam)^T Q and (Wa + Wa^T) K into dk
 #pragma unroll
       for (int kb = 0; kb < kC / KB; ++kb) {
         const Fr<E> bk = mK.cm(c, KB * kb, ln), bq = mQ.cm(c, KB * kb, ln);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
+          if (hh + 1 < G && 4 * kb + mt < 7) stage_piece(hh + 1, 4 * kb + mt);
           const int row = 16 * mt + r;
           if (blk_below<E>(mt, kb)) {          // every K index below the row
             const Fr<E> e_rm = Es.rm(row, KB * kb, ln), e_cm = Es.cm(row, KB * kb, ln);

@@ -275,6 +275,20 @@ __device__ __forceinline__ void wait_copies() {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// Copy number `it` (it < ROWS * 2W / 1024) of copy_rows below: for callers
+// that spread a tile's copies over other work.
+template <int W, int ROWS = kC>
+__device__ __forceinline__ void copy_row_one(const bf16* src, int64_t ld, int L, bf16* dst, int it,
+                                             int l = lane_id()) {
+  constexpr int RPK = 1024 / (2 * W);
+  const int rin = (int)((16u * l) / (2 * W)), pp = (int)(((16u * l) % (2 * W)) / 16);
+  const int row = it * RPK + rin;
+  const int lp = pp ^ (swz_units<W>(row) >> 1);
+  // a uniform base and 32-bit byte offsets (the rows of one copy span far
+  // less than 2 GiB): no 64-bit multiply per copy
+  dma16(reinterpret_cast<const char*>(src) + ((uint32_t)min(row, L - 1) * (uint32_t)(2 * ld) + 16u * lp),
+        reinterpret_cast<char*>(dst) + 1024 * it);
+}
 // ROWS rows (rows >= L repeat row L-1) of a bf16 matrix with W columns into the
 // Lds<bf16, W> layout at dst; wave w of nw issues copies w, w + nw, ...  (w
 // must be wave-uniform: the LDS destination goes through M0).  Copy `it`
@@ -284,18 +298,8 @@ __device__ __forceinline__ void wait_copies() {
 template <int W, int ROWS = kC>
 __device__ __forceinline__ void copy_rows(const bf16* src, int64_t ld, int L, bf16* dst, int w,
                                           int nw, int l = lane_id()) {
-  constexpr int RPK = 1024 / (2 * W), NIT = ROWS / RPK;
-  const int rin = (int)((16u * l) / (2 * W)), pp = (int)(((16u * l) % (2 * W)) / 16);
-  // a uniform base and 32-bit byte offsets (the rows of one copy span far
-  // less than 2 GiB): no 64-bit multiply per copy
-  const char* sb = reinterpret_cast<const char*>(src);
-  const uint32_t rowb = (uint32_t)(2 * ld);
-  for (int it = w; it < NIT; it += nw) {
-    const int row = it * RPK + rin;
-    const int lp = pp ^ (swz_units<W>(row) >> 1);
-    dma16(sb + ((uint32_t)min(row, L - 1) * rowb + 16u * lp),
-          reinterpret_cast<char*>(dst) + 1024 * it);
-  }
+  constexpr int NIT = ROWS * 2 * W / 1024;
+  for (int it = w; it < NIT; it += nw) copy_row_one<W, ROWS>(src, ld, L, dst, it, l);
 }
 
 
