@@ -818,6 +818,7 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
     // Chunk c's chain operands must be in LDS by the barrier that ends
     // iteration c-1, its Q and M by the one that ends iteration c.  Each
     // producer waits until only its newest chain-operand copies are pending.
+    // The state-checkpoint pass has no outputs, so it copies no Q and M.
     if (pw == 0) {
       if (nch > 0) issue_a(0);
       if (nch > 1) {
@@ -828,7 +829,7 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
       }
       barrier_lds();
       for (int i = 0; i <= nch; ++i) {
-        if (i < nch) issue_qm(i);
+        if (!CKPT && i < nch) issue_qm(i);
         if (i + 2 < nch) {
           issue_a(i + 2);
           asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kOpsA) : "memory");

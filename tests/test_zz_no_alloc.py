@@ -4,6 +4,7 @@ gdn_prefill_chunked on the same inputs, on two calls in a row, the second
 smaller than the first, and must stay within the parity tolerance of the
 float64 oracle.
 """
+import gc
 import sys
 
 import numpy as np
@@ -43,9 +44,17 @@ def both(gdn, inp, with_h0):
     o = torch.full_like(o_ref, float("nan"))
     ht = torch.full_like(ht_ref, float("nan"))
     torch.cuda.synchronize()
-    before = torch.cuda.memory_allocated()
-    gdn.prefill_chunked_noalloc(d["q"], d["k"], d["v"], d["alpha"], d["beta"], h0, o=o, ht=ht)
-    after = torch.cuda.memory_allocated()
+    # Python's collector, run during the call, can free device tensors that
+    # earlier tests left in reference cycles and lower the count: collect
+    # first and keep it off while the count is compared.
+    gc.collect()
+    gc.disable()
+    try:
+        before = torch.cuda.memory_allocated()
+        gdn.prefill_chunked_noalloc(d["q"], d["k"], d["v"], d["alpha"], d["beta"], h0, o=o, ht=ht)
+        after = torch.cuda.memory_allocated()
+    finally:
+        gc.enable()
     torch.cuda.synchronize()
     assert after == before
     return o, ht, o_ref, ht_ref
