@@ -662,10 +662,9 @@ constexpr int kVB = kC * kRows * 2;          // V tile of the workgroup's value 
 constexpr int kQB = kC * kD * 2;             // Q tile
 constexpr int kMB = kC * kC * 2;             // M tile
 // Copy ops of each producer per chunk; each keeps at most 63 in flight.
-constexpr int kOpsA = kTB / 1024 + kVB / 1024 + 2;      // Tt, V, gam, dec   (chunk c+2)
-constexpr int kOpsQM = kQB / 1024 + kMB / 1024;         // Q, M             (chunk c)
-constexpr int kOpsKT = kKTB / 1024;                     // K                (chunk c+2)
-static_assert(2 * kOpsA + kOpsQM <= 63 && 2 * kOpsKT <= 63, "vmcnt range");
+constexpr int kOpsT = kTB / 1024 + 2;                   // producer 0: Tt, gam, dec (chunk c+2)
+constexpr int kOpsKV = kKTB / 1024 + kVB / 1024;        // producer 1: K, V         (chunk c+2)
+static_assert(2 * kOpsT + kQB / 1024 <= 63 && 2 * kOpsKV + kMB / 1024 <= 63, "vmcnt range");
 
 struct Slot {
   alignas(16) uint8_t K[kKTB];               // [64 tokens][128 d_k], 256-byte rows
@@ -753,11 +752,12 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
     const int pw = w - kSlices - 1;
     // Copy sources are a uniform base plus a 32-bit byte offset (one chunk's
     // rows span far less than 2 GiB), which avoids a 64-bit multiply per copy.
-    // Tt, V, gam, dec of chunk c into ring slots (c % 3, c % 4).
-    auto issue_a = [&](int c) {
+    // Rows beyond L repeat the last token: K rows meet zero Tt columns and
+    // zero decay-scaled Dl rows, V rows zero Tt columns, Q rows outputs that
+    // are not stored.
+    // Tt, gam, dec of chunk c into ring slots (c % 3, c % 4).
+    auto issue_t = [&](int c) {
       const int cid = cid0 + c;
-      int tok0, L;
-      chunk_of(cm, cid, tok0, L);
       Slot& S = sm.slot[c % kSlots];
       const bf16* tb = ws.Tt + ((size_t)cid * Hv + h) * kC * kC;
 #pragma unroll
@@ -765,43 +765,13 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
         const int row = 8 * it + (l >> 3), p = (l & 7) ^ swz(row);
         dma16(reinterpret_cast<const char*>(tb) + (uint32_t)(2 * (row * kC + 8 * p)), S.T + 1024 * it);
       }
-      const bf16* vbase = v + (size_t)tok0 * hv_stride + (size_t)h * kD + dvb;
-#pragma unroll
-      for (int it = 0; it < kVB / 1024; ++it) {
-        const int row = 16 * it + (l >> 2), p = (l & 3) ^ vswz(row);
-        dma16(reinterpret_cast<const char*>(vbase) +
-                  ((uint32_t)min(row, L - 1) * (uint32_t)(2 * hv_stride) + 16u * p),
-              S.V + 1024 * it);
-      }
       GateSlot& Gd = sm.gd[c % kGdSlots];
       dma4(ws.gam + ((size_t)cid * Hv + h) * kC + l, Gd.gam);
       dma4(ws.dec + ((size_t)cid * Hv + h) * kC + l, Gd.dec);
     };
-    // Q, M of chunk c into qm slot c % 2.
-    auto issue_qm = [&](int c) {
-      const int cid = cid0 + c;
-      int tok0, L;
-      chunk_of(cm, cid, tok0, L);
-      QmSlot& Qs = sm.qm[c % kQmSlots];
-      const bf16* qbase = q + (size_t)tok0 * qk_stride + (size_t)gq * kD;
-#pragma unroll
-      for (int it = 0; it < kQB / 1024; ++it) {
-        const int row = 4 * it + (l >> 4), p = (l & 15) ^ swz(row);
-        dma16(reinterpret_cast<const char*>(qbase) +
-                  ((uint32_t)min(row, L - 1) * (uint32_t)(2 * qk_stride) + 16u * p),
-              Qs.Q + 1024 * it);
-      }
-      const bf16* mb = ws.M + ((size_t)cid * Hv + h) * kC * kC;
-#pragma unroll
-      for (int it = 0; it < kMB / 1024; ++it) {
-        const int row = 8 * it + (l >> 3), p = (l & 7) ^ swz(row);
-        dma16(reinterpret_cast<const char*>(mb) + (uint32_t)(2 * (row * kC + 8 * p)), Qs.M + 1024 * it);
-      }
-    };
-    // K of chunk c into slot c % 3, from the input: 4 tokens per copy, rows
-    // beyond L repeat the last token (they meet zero Tt columns and zero
-    // decay-scaled Dl rows).
-    auto issue_kt = [&](int c) {
+    // K (4 tokens per copy, from the input) and the workgroup's V rows of
+    // chunk c into slot c % 3.
+    auto issue_kv = [&](int c) {
       const int cid = cid0 + c;
       int tok0, L;
       chunk_of(cm, cid, tok0, L);
@@ -814,49 +784,72 @@ __global__ __launch_bounds__(64 * split::kWaves) void scan_split_kernel(
                   ((uint32_t)min(row, L - 1) * (uint32_t)(2 * qk_stride) + 16u * p),
               S.K + 1024 * it);
       }
+      const bf16* vbase = v + (size_t)tok0 * hv_stride + (size_t)h * kD + dvb;
+#pragma unroll
+      for (int it = 0; it < kVB / 1024; ++it) {
+        const int row = 16 * it + (l >> 2), p = (l & 3) ^ vswz(row);
+        dma16(reinterpret_cast<const char*>(vbase) +
+                  ((uint32_t)min(row, L - 1) * (uint32_t)(2 * hv_stride) + 16u * p),
+              S.V + 1024 * it);
+      }
+    };
+    // Q, and M, of chunk c into qm slot c % 2.
+    auto issue_q = [&](int c) {
+      const int cid = cid0 + c;
+      int tok0, L;
+      chunk_of(cm, cid, tok0, L);
+      QmSlot& Qs = sm.qm[c % kQmSlots];
+      const bf16* qbase = q + (size_t)tok0 * qk_stride + (size_t)gq * kD;
+#pragma unroll
+      for (int it = 0; it < kQB / 1024; ++it) {
+        const int row = 4 * it + (l >> 4), p = (l & 15) ^ swz(row);
+        dma16(reinterpret_cast<const char*>(qbase) +
+                  ((uint32_t)min(row, L - 1) * (uint32_t)(2 * qk_stride) + 16u * p),
+              Qs.Q + 1024 * it);
+      }
+    };
+    auto issue_m = [&](int c) {
+      const int cid = cid0 + c;
+      QmSlot& Qs = sm.qm[c % kQmSlots];
+      const bf16* mb = ws.M + ((size_t)cid * Hv + h) * kC * kC;
+#pragma unroll
+      for (int it = 0; it < kMB / 1024; ++it) {
+        const int row = 8 * it + (l >> 3), p = (l & 7) ^ swz(row);
+        dma16(reinterpret_cast<const char*>(mb) + (uint32_t)(2 * (row * kC + 8 * p)), Qs.M + 1024 * it);
+      }
     };
     // Chunk c's chain operands must be in LDS by the barrier that ends
-    // iteration c-1, its Q and M by the one that ends iteration c.  Each
-    // producer waits until only its newest chain-operand copies are pending.
-    // The state-checkpoint pass has no outputs, so it copies no Q and M.
-    if (pw == 0) {
-      if (nch > 0) issue_a(0);
+    // iteration c-1, its Q and M by the one that ends iteration c.  The two
+    // producers split the copies about evenly (Q + Tt + gates: 26, M + K + V:
+    // 28 per chunk); each issues its output operand of chunk i before its
+    // chain operands of chunk i+2 and then waits until only the latter are
+    // pending (vector memory operations complete in issue order).  The
+    // state-checkpoint pass has no outputs, so it copies no Q and M.
+    auto produce = [&](auto first, auto out, auto chain_ops) {
+      constexpr int kOps = decltype(chain_ops)::value;
+      if (nch > 0) first(0);
       if (nch > 1) {
-        issue_a(1);
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kOpsA) : "memory");
+        first(1);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kOps) : "memory");
       } else {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
       barrier_lds();
       for (int i = 0; i <= nch; ++i) {
-        if (!CKPT && i < nch) issue_qm(i);
+        if (!CKPT && i < nch) out(i);
         if (i + 2 < nch) {
-          issue_a(i + 2);
-          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kOpsA) : "memory");
+          first(i + 2);
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kOps) : "memory");
         } else {
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
         barrier_lds();
       }
-    } else {
-      if (nch > 0) issue_kt(0);
-      if (nch > 1) {
-        issue_kt(1);
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kOpsKT) : "memory");
-      } else {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      }
-      barrier_lds();
-      for (int i = 0; i <= nch; ++i) {
-        if (i + 2 < nch) {
-          issue_kt(i + 2);
-          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kOpsKT) : "memory");
-        } else {
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        }
-        barrier_lds();
-      }
-    }
+    };
+    if (pw == 0)
+      produce(issue_t, issue_q, std::integral_constant<int, kOpsT>{});
+    else
+      produce(issue_kv, issue_m, std::integral_constant<int, kOpsKV>{});
     return;
   }
 
